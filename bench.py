@@ -1,0 +1,246 @@
+#!/usr/bin/env python3
+"""Throughput of the fused W4A4 + rank-r linear layer on one MI355X.
+
+A step is one call of the whole layer (quantization pass + residual
+contraction with the rank-r epilogue) over one batch of synthetic,
+seeded inputs already resident in HBM.  Successive steps rotate through
+enough copies of the inputs and outputs (> 512 MB) that the 256 MB
+Infinity Cache cannot serve them warm.  The two stages are bracketed by HIP
+events on the stream they run on, so the per-kernel durations come from the
+timed region itself.
+
+Prints one JSON line.  ``value`` is the effective TOPS of the whole call,
+2*M*N*K*batch / time.  ``roofline`` covers the dominant kernel (the
+contraction).  ``cpu_baseline`` times the CPU oracle on the same workload.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "effective TOPS of fused W4A4+rank-4 linear; % of int8 MFMA / HBM roofline"
+PEAK_INT8_TOPS = 5000.0      # MI355X dense int8 MFMA, 5.0 POP/s
+PEAK_HBM_GBS = 8000.0        # MI355X HBM3E, 8 TB/s
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+KERNEL_SOURCES = {
+    "tiled": os.path.join(ROOT, "w4a4_rank_assisted_amd", "csrc", "gemm_tiled.hip"),
+    "skinny": os.path.join(ROOT, "w4a4_rank_assisted_amd", "csrc", "gemm_skinny.hip"),
+}
+
+
+def source_hash(path: str) -> str:
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def algorithmic_bytes(M, K, N, r, batch, y_bytes):
+    """Minimum bytes the whole layer must move (inputs once, output once)."""
+    G = K // 64
+    x = M * K * 2 + K * 2 + batch * (K * r * 2)
+    w = batch * (K * N // 2 + G * N * 2 + r * N * 2 + N * 2)
+    y = batch * M * N * y_bytes
+    return x + w + y
+
+
+def contract_bytes(M, K, N, r, batch, y_bytes):
+    """Minimum bytes of the contraction stage: int4 activation codes and
+    their fp16 scales, U, the packed weights with their scales, L2, bias, Y."""
+    G = K // 64
+    a = M * K // 2 + M * G * 2 + batch * M * r * 4
+    w = batch * (K * N // 2 + G * N * 2 + r * N * 2 + N * 2)
+    return a + w + batch * M * N * y_bytes
+
+
+def read_traffic(kernel: str, layer: str):
+    """HBM bytes per launch measured by rocprofv3 counters, if they were
+    taken on the current kernel source; otherwise None."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    ent = rec.get(layer, {}).get(kernel)
+    if not ent or ent.get("source_sha256_16") != source_hash(KERNEL_SOURCES[kernel]):
+        return None
+    return ent.get("bytes_per_launch")
+
+
+def cpu_baseline(layer_dict, spec, seconds: float):
+    """The CPU oracle, as it stands, on the whole layer (all rows, every
+    projection), repeated until `seconds` of wall time have accumulated."""
+    import oracle
+
+    o = oracle.Oracle()
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        o.linear_batched(layer_dict)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= seconds or reps >= 20:
+            break
+    ops = spec.ops * reps
+    return {
+        "value": round(ops / el / 1e12, 6),
+        "unit": "TOPS",
+        "cores": o.num_threads(),
+        "kind": "oracle",
+        "sample": (f"whole {spec.name} layer ({spec.M}x{spec.K}->{spec.N}, batch {spec.batch}, "
+                   f"r {spec.r}): quantize + brute-force int32 group sums + fp64 output, "
+                   f"{reps} repetition(s), {el:.1f} s"),
+    }
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--layer", default="pixart_up",
+                    help="tiny | pixart_up | sana_qkv | flux_up | flux_down | qwen3_up | qwen3_down")
+    ap.add_argument("--tokens", type=int, default=None, help="M for the qwen3 layers (16/256/2048)")
+    ap.add_argument("--kernel", default="auto", choices=["auto", "tiled", "skinny"])
+    ap.add_argument("--y-dtype", default="bf16", choices=["bf16", "f32"])
+    ap.add_argument("--rotate-mb", type=float, default=640.0,
+                    help="total bytes of rotated input/output copies (defeats the 256 MB MALL)")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args(argv)
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: this layer's hot path runs on a single MI355X "
+              "(multi-GPU sharding is a design note, not built); use --gpus 1", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import w4a4_rank_assisted_amd as hsq
+    from synth import layer_spec, make_layer
+
+    dev = torch.device("cuda:0")
+    spec = layer_spec(args.layer, args.tokens)
+    lay = make_layer(args.layer, args.tokens)
+    M, K, N, r, B = spec.M, spec.K, spec.N, spec.r, spec.batch
+
+    def d16(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev)
+
+    lam = d16(lay["lam"])
+    L1 = d16(lay["L1"]) if r else None
+    L2 = d16(lay["L2"]) if r else None
+    bias = d16(lay["bias"])
+    X0 = d16(lay["X"])
+    sw0 = d16(lay["sw"])
+    packed0 = torch.cat([hsq.pack_weights(torch.from_numpy(lay["qw"][b]).to(dev))[0]
+                         for b in range(B)])
+    ydt = torch.bfloat16 if args.y_dtype == "bf16" else torch.float32
+    y_bytes = 2 if args.y_dtype == "bf16" else 4
+    set_bytes = (X0.numel() * 2 + packed0.numel() + sw0.numel() * 2 + B * M * N * y_bytes)
+    nsets = max(1, math.ceil(args.rotate_mb * 1e6 / set_bytes))
+    sets = []
+    for i in range(nsets):
+        sets.append(dict(X=X0.clone(), packed=packed0.clone(), sw=sw0.clone(),
+                         Y=torch.empty((B, M, N), dtype=ydt, device=dev)))
+    ws = torch.empty(hsq.workspace_bytes(M, K, N, r, B), dtype=torch.uint8, device=dev)
+    kernel = args.kernel
+    if kernel == "auto":
+        kernel = "skinny" if M <= 64 else "tiled"
+
+    def step(i, ev=None):
+        s = sets[i % nsets]
+        if ev is not None:
+            ev[0].record()
+        hsq.quantize_stage(s["X"], lam, L1, N=N, batch=B, workspace=ws)
+        if ev is not None:
+            ev[1].record()
+        hsq.contract_stage(M, K, s["packed"], s["sw"], L2, bias, s["Y"], N=N, batch=B, r=r,
+                           workspace=ws, kernel=kernel)
+        if ev is not None:
+            ev[2].record()
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t_start.record()
+    for i in range(args.steps):
+        step(i, evs[i])
+    t_end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+
+    total_ms = t_start.elapsed_time(t_end)
+    q_ms = [e[0].elapsed_time(e[1]) for e in evs]
+    c_ms = [e[1].elapsed_time(e[2]) for e in evs]
+    ms_step = total_ms / args.steps
+    q_avg, c_avg = float(np.mean(q_ms)), float(np.mean(c_ms))
+    ops = spec.ops
+    value = ops / (ms_step * 1e-3) / 1e12
+
+    # roofline of the dominant kernel (the contraction): compute-bound at
+    # large M (int8 MFMA), HBM-bound when the weights dominate (small M)
+    cbytes = contract_bytes(M, K, N, r, B, y_bytes)
+    intensity = ops / cbytes
+    ridge = PEAK_INT8_TOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
+    traffic = read_traffic(kernel, args.layer if args.tokens is None else f"{args.layer}_M{M}")
+    if intensity >= ridge:
+        ach = ops / (c_avg * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": round(ach, 2), "peak": PEAK_INT8_TOPS,
+                "unit": "TFLOP/s", "frac": round(ach / PEAK_INT8_TOPS, 4), "traffic": traffic,
+                "kernel": f"contract ({kernel})", "ops_per_launch": ops,
+                "note": "int8 MFMA operations (2 per multiply-accumulate) counted as FLOP"}
+    else:
+        ach = cbytes / (c_avg * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": traffic,
+                "kernel": f"contract ({kernel})", "bytes_per_launch": cbytes}
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "TOPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8",
+        "data": "synthetic",
+        "config": {
+            "workload": f"{spec.name}: {spec.description}",
+            "M": M, "K": K, "N": N, "rank": r, "batch": B, "group": 64,
+            "y_dtype": args.y_dtype, "contract_kernel": kernel,
+            "rotated_sets": nsets,
+        },
+        "stages_ms": {"quantize": round(q_avg, 5), "contract": round(c_avg, 5)},
+        "layer_hbm_frac": round(algorithmic_bytes(M, K, N, r, B, y_bytes) / (ms_step * 1e-3)
+                                / (PEAK_HBM_GBS * 1e9), 4),
+        "wall_s": round(wall, 4),
+        "roofline": roof,
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(lay, spec, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,187 @@
+/*
+ * hsq.h -- C ABI of libhsq: the inference-time W4A4 linear layer with a
+ * rank-r high-precision branch, for AMD Instinct MI355X (gfx950).
+ *
+ * The layer (Deflating the Hessian, abstract; thelatestinai.com paper page,
+ * Figure 1 caption): every weight is split into a high-precision low-rank
+ * component and a low-bit residual, W ~ L1*L2 + Q(R).  Weights and
+ * activations are 4-bit with one scale per 64-wide group of the input
+ * dimension (same page, Table 1 and Table 8 captions: W4A4, group-64).  A
+ * diagonal smoothing moves range from the activations to the weights
+ * without changing the full-precision product (H-SVDQuant explainer,
+ * rit.work, section on Hessian deflation, last paragraph).  As in the
+ * two-branch inference form of DiRotQ (papernotes.org, key design 2), the
+ * high-precision branch runs on the unquantized (smoothed) activations:
+ *
+ *   xh[m,k]  = X[m,k] * fl32(1 / lambda[k])                    smoothing
+ *   sx[m,g]  = fp16_rne(fl32(absmax_{k in g} |xh[m,k]| / 7))   (0 if absmax = 0; saturates at 65504)
+ *   qx[m,k]  = clamp(rint(xh[m,k] * fl32(1 / sx[m,g])), -8, 7) (all 0 if sx = 0)
+ *   U[m,j]   = sum_k xh[m,k] * L1[k,j]                         rank-r down projection
+ *   P[m,n,g] = sum_{k in g} qx[m,k] * qw[k,n]                  int32, exact
+ *   Y[m,n]   = sum_g P[m,n,g] * sx[m,g] * sw[g,n] + sum_j U[m,j] * L2[j,n] + bias[n]
+ *
+ * Group g covers input channels [64g, 64g + 64).  Rounding is IEEE-754
+ * round-to-nearest-even throughout; rint rounds ties to even.
+ *
+ * Conventions for every entry point
+ *   - All tensor pointers are DEVICE pointers (HIP global memory), owned and
+ *     allocated by the caller, 16-byte aligned, row-major and densely packed.
+ *     The library never allocates or frees memory.
+ *   - bf16 and fp16 values travel as uint16_t bit patterns.
+ *   - `stream` is a hipStream_t passed as void* (NULL: the null stream).
+ *     Work is enqueued asynchronously on it; the call returns once enqueued.
+ *   - Arguments are validated before anything is enqueued; on an error the
+ *     call returns a negative HSQ_E_* code and enqueues nothing.  Faults that
+ *     happen while kernels run surface at the caller's next synchronisation.
+ *   - The library keeps no state between calls and is thread-safe; no C++
+ *     exception crosses this interface.
+ *   - Limits: K % 64 == 0 and K >= 64; M, N >= 1; 0 <= r <= 32;
+ *     1 <= batch <= 16; M * K, M * N, K * N < 2^31.
+ */
+#ifndef HSQ_H
+#define HSQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes ---- */
+#define HSQ_OK            0
+#define HSQ_E_INVAL      -1  /* null pointer, size out of range, bad dtype or kernel choice */
+#define HSQ_E_SHAPE      -2  /* K not a positive multiple of 64, or a window outside the matrix */
+#define HSQ_E_ALIGN      -3  /* a pointer is not 16-byte aligned */
+#define HSQ_E_WORKSPACE  -4  /* workspace missing or smaller than the size function returns */
+#define HSQ_E_HIP        -5  /* the HIP runtime refused a launch */
+
+/* ---- output dtypes ---- */
+#define HSQ_F32   0
+#define HSQ_BF16  1
+
+/* ---- kernel choice for the residual contraction ---- */
+#define HSQ_KERNEL_AUTO    0  /* SKINNY for M <= 64, TILED otherwise */
+#define HSQ_KERNEL_TILED   1  /* LDS-tiled int8-MFMA kernel, one workgroup per output tile */
+#define HSQ_KERNEL_SKINNY  2  /* weight-streaming kernel for M <= 64: the waves of a
+                                 workgroup split K and reduce in a fixed order */
+
+/* Version of the packed-weight layout written by hsq_pack_weights. */
+int hsq_layout_version(void);
+
+/* Static text for a status code (never NULL). */
+const char *hsq_status_string(int status);
+
+/* Bytes of one packed residual (K x N int4 codes) as hsq_pack_weights
+ * writes it: N rounded up to 16 times K rounded up to 128, over 2.
+ * Returns 0 if K or N is invalid. */
+size_t hsq_packed_weight_bytes(int K, int N);
+
+/* Pack residual codes into the layout the contraction kernels read.
+ * Operation: the 4-bit residual Q(R) of W ~ L1*L2 + Q(R) (Deflating the
+ * Hessian, abstract), group-64 (Table 1 caption).
+ *   codes   in : K x N int8 (input channel x output channel), values in [-8, 7]
+ *   packed  out: hsq_packed_weight_bytes(K, N) bytes; padding is zero codes
+ *   d_status out: one device int; set to 0, then to 1 if any code lies
+ *                 outside [-8, 7] (that code's low nibble is stored).  The
+ *                 caller reads it after synchronising.
+ * Errors: HSQ_E_INVAL, HSQ_E_SHAPE, HSQ_E_ALIGN, HSQ_E_HIP. */
+int hsq_pack_weights(const int8_t *codes, int K, int N, uint8_t *packed, int *d_status,
+                     void *stream);
+
+/* Inverse of hsq_pack_weights (testing and inspection).
+ *   packed in : hsq_packed_weight_bytes(K, N) bytes
+ *   codes  out: K x N int8 in [-8, 7]
+ * Errors: HSQ_E_INVAL, HSQ_E_SHAPE, HSQ_E_ALIGN, HSQ_E_HIP. */
+int hsq_unpack_weights(const uint8_t *packed, int K, int N, int8_t *codes, void *stream);
+
+/* Smooth and quantize activations per token in 64-wide groups, and form the
+ * rank-r down projection of the smoothed, unquantized activations (the
+ * xh, sx, qx and U lines of the formula block above).
+ *   X      in : M x K bf16
+ *   lambda in : K fp16 smoothing factors (X is divided by them)
+ *   L1     in : K x r bf16 (may be NULL when r == 0)
+ *   qx     out: M x K/2 bytes; byte j of a row holds code 2j in its low
+ *               nibble and code 2j+1 in its high nibble, two's complement
+ *   sx     out: M x K/64 fp16 scales
+ *   U      out: M x r fp32 (may be NULL when r == 0)
+ * Errors: HSQ_E_INVAL, HSQ_E_SHAPE, HSQ_E_ALIGN, HSQ_E_HIP. */
+int hsq_quantize_act(const uint16_t *X, int M, int K, const uint16_t *lambda,
+                     const uint16_t *L1, int r, uint8_t *qx, uint16_t *sx, float *U,
+                     void *stream);
+
+/* Workspace bytes hsq_w4a4_lowrank_linear and hsq_w4a4_group_partials need
+ * for these sizes (any kernel choice).  Returns 0 if a size is invalid. */
+size_t hsq_workspace_bytes(int M, int K, int N, int r, int batch);
+
+/* The fused W4A4 + rank-r linear layer, for `batch` projections that share
+ * the input X and the smoothing factors (e.g. Q, K and V).  Computes Y of the
+ * formula block above: one pass over X quantizes it and forms U, then the
+ * int4 x int4 contraction keeps an int32 partial sum per 64-wide group,
+ * rescales it by sx * sw in fp32, and adds U * L2 and the bias.
+ *   X        in : M x K bf16
+ *   lambda   in : K fp16
+ *   packed_w in : batch blobs of hsq_packed_weight_bytes(K, N) bytes, back to back
+ *   sw       in : batch x K/64 x N fp16 weight scales
+ *   L1       in : batch x K x r bf16   (NULL when r == 0)
+ *   L2       in : batch x r x N bf16   (NULL when r == 0)
+ *   bias     in : batch x N bf16, or NULL for no bias
+ *   Y        out: batch x M x N, fp32 (y_dtype HSQ_F32) or bf16 (HSQ_BF16, RNE)
+ *   workspace   : ws_bytes >= hsq_workspace_bytes(M, K, N, r, batch) device
+ *                 bytes, scratch owned by the caller; its contents on entry
+ *                 do not matter and are clobbered.
+ * Errors: HSQ_E_INVAL, HSQ_E_SHAPE, HSQ_E_ALIGN, HSQ_E_WORKSPACE, HSQ_E_HIP. */
+int hsq_w4a4_lowrank_linear(const uint16_t *X, int M, int K, int N, int batch,
+                            const uint16_t *lambda, const uint8_t *packed_w,
+                            const uint16_t *sw, const uint16_t *L1, const uint16_t *L2, int r,
+                            const uint16_t *bias, void *Y, int y_dtype, void *workspace,
+                            size_t ws_bytes, void *stream);
+
+/* As hsq_w4a4_lowrank_linear, with the contraction kernel chosen by
+ * `kernel` (HSQ_KERNEL_*; SKINNY with M > 64 is HSQ_E_INVAL). */
+int hsq_w4a4_lowrank_linear_ex(const uint16_t *X, int M, int K, int N, int batch,
+                               const uint16_t *lambda, const uint8_t *packed_w,
+                               const uint16_t *sw, const uint16_t *L1, const uint16_t *L2,
+                               int r, const uint16_t *bias, void *Y, int y_dtype,
+                               void *workspace, size_t ws_bytes, int kernel, void *stream);
+
+/* The same layer in two stages on one stream, for callers that time or
+ * schedule them separately, or reuse one quantized input for several
+ * contractions with the same (M, K, batch, r).
+ *   hsq_w4a4_quantize_stage: the smoothing / quantization / U pass over X
+ *     (X, lambda, L1 as for the linear) into `workspace`.
+ *   hsq_w4a4_contract_stage: the residual contraction, rescale and U*L2 +
+ *     bias epilogue (packed_w, sw, L2, bias, Y as for the linear), reading
+ *     the workspace the quantize stage wrote for the same M, K, r and batch.
+ * Running both equals hsq_w4a4_lowrank_linear_ex.  The workspace must not
+ * be reused by another quantize stage until the contract stages that read it
+ * have run (stream order guarantees this on one stream).
+ * Errors: as hsq_w4a4_lowrank_linear_ex. */
+int hsq_w4a4_quantize_stage(const uint16_t *X, int M, int K, int N, int batch,
+                            const uint16_t *lambda, const uint16_t *L1, int r, void *workspace,
+                            size_t ws_bytes, void *stream);
+int hsq_w4a4_contract_stage(int M, int K, int N, int batch, const uint8_t *packed_w,
+                            const uint16_t *sw, const uint16_t *L2, int r, const uint16_t *bias,
+                            void *Y, int y_dtype, void *workspace, size_t ws_bytes, int kernel,
+                            void *stream);
+
+/* Test export: the per-group int32 partial sums P[m,n,g] (formula block
+ * above) of one projection, produced by the same quantization pass and the
+ * same contraction loop as hsq_w4a4_lowrank_linear_ex with this `kernel`,
+ * with the rescaling epilogue replaced by a store of P.  Only the window
+ * m in [m0, m0+mc), n in [n0, n0+nc) is written.
+ *   X, lambda, packed_w : as for the linear (one projection)
+ *   P        out: mc x nc x K/64 int32
+ *   workspace   : as for the linear with batch = 1, r = 0
+ * Errors: HSQ_E_INVAL, HSQ_E_SHAPE (window outside M x N), HSQ_E_ALIGN,
+ *         HSQ_E_WORKSPACE, HSQ_E_HIP. */
+int hsq_w4a4_group_partials(const uint16_t *X, int M, int K, int N, const uint16_t *lambda,
+                            const uint8_t *packed_w, int m0, int mc, int n0, int nc,
+                            int32_t *P, void *workspace, size_t ws_bytes, int kernel,
+                            void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* HSQ_H */

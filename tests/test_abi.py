@@ -1,0 +1,150 @@
+"""The C ABI on the host: the library loads, exports every function
+include/hsq.h declares, sizes its buffers, and rejects bad arguments before
+it enqueues anything (no GPU needed: no call here reaches a launch)."""
+
+import ctypes
+import re
+import subprocess
+
+import pytest
+
+import w4a4_rank_assisted_amd as hsq
+
+lib = hsq._load()
+A = 0x100000  # a 16-byte aligned fake device address: validation rejects before use
+P = ctypes.c_void_p
+
+
+def test_every_declared_function_is_exported():
+    names = hsq.header_functions()
+    assert len(names) >= 10
+    for n in names:
+        assert hasattr(lib, n), n
+    out = subprocess.run(["nm", "-D", "--defined-only", hsq.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (hsq_\w+)", out))
+    assert set(names) <= exported
+
+
+def test_constants_match_header():
+    text = open(hsq.HEADER).read()
+    consts = dict((k, int(v)) for k, v in re.findall(r"#define (HSQ_\w+)\s+(-?\d+)", text))
+    assert consts["HSQ_OK"] == hsq.OK and consts["HSQ_E_INVAL"] == hsq.E_INVAL
+    assert consts["HSQ_E_SHAPE"] == hsq.E_SHAPE and consts["HSQ_E_ALIGN"] == hsq.E_ALIGN
+    assert consts["HSQ_E_WORKSPACE"] == hsq.E_WORKSPACE and consts["HSQ_E_HIP"] == hsq.E_HIP
+    assert consts["HSQ_F32"] == hsq.F32 and consts["HSQ_BF16"] == hsq.BF16
+    assert consts["HSQ_KERNEL_TILED"] == hsq.KERNEL_TILED
+    assert consts["HSQ_KERNEL_SKINNY"] == hsq.KERNEL_SKINNY
+
+
+def test_status_strings():
+    for s in (0, -1, -2, -3, -4, -5, 7):
+        assert isinstance(lib.hsq_status_string(s), bytes)
+    assert lib.hsq_layout_version() == 1
+
+
+@pytest.mark.parametrize("K,N,expect", [
+    (64, 16, 1024),            # one 16-column tile, one (padded) group pair
+    (128, 16, 1024),
+    (192, 17, 2 * 2 * 1024),   # 2 column tiles x 2 group pairs
+    (1152, 4608, 288 * 9 * 1024),
+    (2240, 2240, 140 * 18 * 1024),  # 35 groups pad to 36
+    (63, 16, 0), (0, 16, 0), (64, 0, 0),
+])
+def test_packed_weight_bytes(K, N, expect):
+    assert lib.hsq_packed_weight_bytes(K, N) == expect
+
+
+def test_workspace_bytes_cover_the_internal_buffers():
+    M, K, N, r, b = 4096, 1152, 4608, 4, 1
+    ws = lib.hsq_workspace_bytes(M, K, N, r, b)
+    codes = (M // 16) * 18 * 1024            # tiled int8 codes, 18 groups
+    scales = (M // 16) * 18 * 16 * 4
+    assert ws >= codes + scales + M * r * 4
+    assert ws < 2 * (codes + scales) + 16 * M * r * 4
+    assert lib.hsq_workspace_bytes(0, K, N, r, b) == 0
+    assert lib.hsq_workspace_bytes(M, 100, N, r, b) == 0
+    assert lib.hsq_workspace_bytes(M, K, N, 33, b) == 0
+    assert lib.hsq_workspace_bytes(M, K, N, r, 0) == 0
+    # M = 1 still needs one row tile
+    assert lib.hsq_workspace_bytes(1, 64, 16, 0, 1) >= 2 * 1024
+
+
+def _linear(**kw):
+    a = dict(X=A, M=64, K=256, N=256, batch=1, lam=A, w=A, sw=A, L1=A, L2=A, r=4, bias=A, Y=A,
+             ydt=hsq.BF16, ws=A, wsb=1 << 30, kernel=0, stream=None)
+    a.update(kw)
+    return lib.hsq_w4a4_lowrank_linear_ex(
+        a["X"], a["M"], a["K"], a["N"], a["batch"], a["lam"], a["w"], a["sw"], a["L1"], a["L2"],
+        a["r"], a["bias"], a["Y"], a["ydt"], a["ws"], a["wsb"], a["kernel"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(X=None), hsq.E_INVAL),
+    (dict(lam=None), hsq.E_INVAL),
+    (dict(w=None), hsq.E_INVAL),
+    (dict(sw=None), hsq.E_INVAL),
+    (dict(Y=None), hsq.E_INVAL),
+    (dict(ws=None), hsq.E_INVAL),
+    (dict(L1=None), hsq.E_INVAL),
+    (dict(L2=None), hsq.E_INVAL),
+    (dict(M=0), hsq.E_INVAL),
+    (dict(N=0), hsq.E_INVAL),
+    (dict(K=100), hsq.E_SHAPE),
+    (dict(K=0), hsq.E_INVAL),
+    (dict(r=33), hsq.E_INVAL),
+    (dict(r=-1), hsq.E_INVAL),
+    (dict(batch=0), hsq.E_INVAL),
+    (dict(batch=17), hsq.E_INVAL),
+    (dict(ydt=2), hsq.E_INVAL),
+    (dict(kernel=3), hsq.E_INVAL),
+    (dict(kernel=hsq.KERNEL_SKINNY, M=65), hsq.E_INVAL),
+    (dict(X=A + 2), hsq.E_ALIGN),
+    (dict(w=A + 8), hsq.E_ALIGN),
+    (dict(Y=A + 4), hsq.E_ALIGN),
+    (dict(ws=A + 1), hsq.E_ALIGN),
+    (dict(wsb=0), hsq.E_WORKSPACE),
+    (dict(wsb=1000), hsq.E_WORKSPACE),
+    (dict(M=1 << 20, K=1 << 12), hsq.E_INVAL),  # M*K >= 2^31
+])
+def test_linear_rejects_before_launch(kw, code):
+    assert _linear(**kw) == code
+
+
+def test_linear_rank_zero_needs_no_factors():
+    # r = 0 with null L1/L2 passes argument checks and stops at the workspace
+    assert _linear(r=0, L1=None, L2=None, wsb=0) == hsq.E_WORKSPACE
+
+
+def test_plain_linear_entry_validates_too():
+    assert lib.hsq_w4a4_lowrank_linear(None, 64, 256, 256, 1, A, A, A, A, A, 4, A, A, 1, A,
+                                       1 << 30, None) == hsq.E_INVAL
+
+
+def test_partials_rejects_bad_windows():
+    f = lib.hsq_w4a4_group_partials
+    assert f(A, 64, 256, 256, A, A, 0, 64, 0, 256, None, A, 1 << 30, 0, None) == hsq.E_INVAL
+    assert f(A, 64, 256, 256, A, A, 0, 65, 0, 256, A, A, 1 << 30, 0, None) == hsq.E_SHAPE
+    assert f(A, 64, 256, 256, A, A, -1, 4, 0, 256, A, A, 1 << 30, 0, None) == hsq.E_SHAPE
+    assert f(A, 64, 256, 256, A, A, 0, 4, 250, 7, A, A, 1 << 30, 0, None) == hsq.E_SHAPE
+    assert f(A, 64, 256, 256, A, A, 0, 0, 0, 4, A, A, 1 << 30, 0, None) == hsq.E_SHAPE
+    assert f(A, 64, 250, 256, A, A, 0, 4, 0, 4, A, A, 1 << 30, 0, None) == hsq.E_SHAPE
+    assert f(A, 64, 256, 256, A, A, 0, 4, 0, 4, A, A, 0, 0, None) == hsq.E_WORKSPACE
+
+
+def test_quantize_and_pack_reject_before_launch():
+    q = lib.hsq_quantize_act
+    assert q(None, 4, 64, A, A, 4, A, A, A, None) == hsq.E_INVAL
+    assert q(A, 4, 96, A, A, 4, A, A, A, None) == hsq.E_SHAPE
+    assert q(A, 4, 64, A, None, 4, A, A, A, None) == hsq.E_INVAL
+    assert q(A, 4, 64, A, A, 4, A, A, None, None) == hsq.E_INVAL
+    assert q(A, 4, 64, A + 2, A, 4, A, A, A, None) == hsq.E_ALIGN
+    assert q(A, 0, 64, A, A, 4, A, A, A, None) == hsq.E_INVAL
+    p = lib.hsq_pack_weights
+    assert p(None, 64, 16, A, A, None) == hsq.E_INVAL
+    assert p(A, 64, 16, A, None, None) == hsq.E_INVAL
+    assert p(A, 65, 16, A, A, None) == hsq.E_SHAPE
+    assert p(A, 64, 16, A + 1, A, None) == hsq.E_ALIGN
+    u = lib.hsq_unpack_weights
+    assert u(A, 64, 0, A, None) == hsq.E_INVAL
+    assert u(A, 64, 16, A + 3, None) == hsq.E_ALIGN

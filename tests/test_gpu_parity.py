@@ -1,0 +1,271 @@
+"""HIP path vs the CPU oracle on the same seeded inputs, through the C ABI.
+
+Bars:
+  * activation codes, scales, packed bytes and per-group int32 partial sums:
+    bit-exact;
+  * U (rank-r down projection, fp32 on the GPU, fp64 in the oracle):
+    relative Frobenius <= 1e-5;
+  * Y: fp32 output within 1e-3 relative Frobenius of the oracle's fp64
+    result; bf16 output within 1e-3 of the oracle's result rounded to bf16
+    (bf16 rounding alone is ~1.6e-3 RMS relative, so an fp64 comparison of
+    a bf16 tensor cannot meet 1e-3).
+Full layer shapes run in the launch configuration the benchmark times; the
+oracle then checks a sample of output rows (rows are independent: the
+quantizer is per token) and windows of the partial sums.
+"""
+
+import functools
+import os
+
+import numpy as np
+import pytest
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():  # collected on CPU-only hosts, never run there
+    pytest.skip("needs a GPU", allow_module_level=True)
+
+import w4a4_rank_assisted_amd as hsq  # noqa: E402
+from synth import bf16_bits_to_f32, f64_to_bf16_bits, make_layer, make_random_layer  # noqa: E402
+
+DEV = torch.device("cuda:0")
+TOL = 1e-3
+
+
+def say(msg):
+    print(msg, flush=True)
+
+
+def dev16(a):
+    return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(DEV)
+
+
+def dev8(a):
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.int8)).to(DEV)
+
+
+def rel(a, b):
+    return float(np.linalg.norm(a - b) / max(np.linalg.norm(b), 1e-300))
+
+
+class Uploaded:
+    """A generated layer on the device, packed by the library."""
+
+    def __init__(self, lay):
+        self.lay = lay
+        self.B, self.K, self.N = lay["qw"].shape
+        self.M = lay["X"].shape[0]
+        self.r = lay["L1"].shape[2]
+        self.X = dev16(lay["X"])
+        self.lam = dev16(lay["lam"])
+        blobs = []
+        for b in range(self.B):
+            packed, st = hsq.pack_weights(dev8(lay["qw"][b]))
+            blobs.append(packed)
+            assert int(st[0].item()) == 0
+        self.packed = torch.cat(blobs)
+        self.sw = dev16(lay["sw"])
+        self.L1 = dev16(lay["L1"]) if self.r else None
+        self.L2 = dev16(lay["L2"]) if self.r else None
+        self.bias = dev16(lay["bias"])
+
+    def linear(self, y_dtype="f32", kernel="auto", bias=True):
+        Y = hsq.w4a4_lowrank_linear(self.X, self.lam, self.packed, self.sw, self.L1, self.L2,
+                                    self.bias if bias else None, N=self.N, batch=self.B,
+                                    y_dtype=y_dtype, kernel=kernel)
+        torch.cuda.synchronize()
+        return Y
+
+    def partials(self, m0, mc, n0, nc, kernel="auto"):
+        blob = self.packed[: hsq.packed_weight_bytes(self.K, self.N)]
+        P = hsq.w4a4_group_partials(self.X, self.lam, blob, self.N, m0, mc, n0, nc, kernel=kernel)
+        torch.cuda.synchronize()
+        return P.cpu().numpy()
+
+
+@functools.lru_cache(maxsize=2)
+def uploaded(name, M=None):
+    say(f"[gen] {name} M={M}")
+    return Uploaded(make_layer(name, M))
+
+
+def check_linear_rows(oracle, up, rows, kernel="auto"):
+    lay = up.lay
+    Yd = up.linear("f32", kernel).cpu().numpy()
+    Yb = up.linear("bf16", kernel).float().cpu().numpy()
+    for b in range(up.B):
+        r = up.r
+        ref = oracle.linear(lay["X"], lay["lam"], lay["qw"][b], lay["sw"][b],
+                            lay["L1"][b] if r else None, lay["L2"][b] if r else None,
+                            lay["bias"][b], rows=rows)
+        e32 = rel(Yd[b][rows].astype(np.float64), ref)
+        ref_b = bf16_bits_to_f32(f64_to_bf16_bits(ref)).astype(np.float64)
+        e16 = rel(Yb[b][rows].astype(np.float64), ref_b)
+        say(f"    proj {b}: fp32 rel {e32:.3e}  bf16 rel {e16:.3e}")
+        assert e32 <= TOL
+        assert e16 <= TOL
+
+
+# ------------------------------------------------------------- packing
+@pytest.mark.parametrize("K,N", [(64, 16), (192, 37), (1152, 4608), (2240, 130)])
+def test_pack_unpack_roundtrip(K, N):
+    rng = np.random.default_rng(K * 7 + N)
+    codes = rng.integers(-8, 8, (K, N), dtype=np.int8)
+    packed, st = hsq.pack_weights(dev8(codes))
+    back = hsq.unpack_weights(packed, K, N).cpu().numpy()
+    assert int(st[0].item()) == 0
+    assert np.array_equal(back, codes)
+
+
+def test_pack_flags_out_of_range_codes():
+    codes = np.zeros((128, 16), np.int8)
+    codes[5, 3] = 9
+    _, st = hsq.pack_weights(dev8(codes))
+    assert int(st[0].item()) == 1
+
+
+# ------------------------------------------------------------- codes
+@pytest.mark.parametrize("name,M", [("tiny", None), ("pixart_up", None), ("sana_qkv", None),
+                                    ("flux_up", None), ("flux_down", None), ("qwen3_up", 16),
+                                    ("qwen3_down", 16), ("qwen3_down", 2048)])
+def test_codes_scales_bit_exact(oracle, name, M):
+    up = uploaded(name, M)
+    lay = up.lay
+    say(f"[codes] {name} M={up.M} K={up.K}")
+    qx, sx, U = hsq.quantize_act(up.X, up.lam, up.L1[0] if up.r else None)
+    torch.cuda.synchronize()
+    q_ref, s_ref, xh = oracle.quantize(lay["X"], lay["lam"], want_xh=True)
+    assert np.array_equal(sx.cpu().numpy().view(np.uint16), s_ref)
+    assert np.array_equal(qx.cpu().numpy(), oracle.pack_act(q_ref))
+    if up.r:
+        U_ref = oracle.lowrank_down(xh, lay["L1"][0])
+        assert rel(U.cpu().numpy().astype(np.float64), U_ref) <= 1e-5
+
+
+# ------------------------------------------------------------- partials
+def test_partials_full_tiny_both_kernels(oracle):
+    up = uploaded("tiny")
+    q, _ = oracle.quantize(up.lay["X"], up.lay["lam"])
+    ref = oracle.group_partials(q, up.lay["qw"][0])
+    for kernel in ("tiled", "skinny"):
+        say(f"[partials] tiny {kernel}")
+        got = up.partials(0, up.M, 0, up.N, kernel)
+        assert np.array_equal(got, ref), kernel
+
+
+@pytest.mark.parametrize("name,M,windows", [
+    ("pixart_up", None, [(0, 40, 0, 70), (4000, 96, 4500, 108), (1234, 17, 2222, 33)]),
+    ("sana_qkv", None, [(0, 16, 0, 16), (4080, 16, 2200, 40)]),
+    ("flux_up", None, [(4600, 8, 12200, 88), (2048, 33, 6000, 50)]),
+    ("flux_down", None, [(0, 20, 3000, 72), (4500, 108, 0, 24)]),
+    ("qwen3_up", 16, [(0, 16, 0, 12288)]),
+    ("qwen3_down", 16, [(0, 16, 0, 4096)]),
+    ("qwen3_up", 256, [(100, 156, 12000, 288)]),
+    ("qwen3_down", 2048, [(2000, 48, 4000, 96)]),
+])
+def test_partials_windows_bit_exact(oracle, name, M, windows):
+    up = uploaded(name, M)
+    q, _ = oracle.quantize(up.lay["X"], up.lay["lam"])
+    for (m0, mc, n0, nc) in windows:
+        say(f"[partials] {name} M={up.M} window m[{m0},{m0 + mc}) n[{n0},{n0 + nc})")
+        got = up.partials(m0, mc, n0, nc)
+        ref = oracle.group_partials(q, up.lay["qw"][0], m0, mc, n0, nc)
+        assert np.array_equal(got, ref)
+
+
+# ------------------------------------------------------------- outputs
+def test_tiny_layer_full_output(oracle):
+    up = uploaded("tiny")
+    for kernel in ("tiled", "skinny", "auto"):
+        say(f"[linear] tiny {kernel}")
+        check_linear_rows(oracle, up, np.arange(up.M), kernel)
+
+
+def _sample_rows(M, n=48, seed=0):
+    rng = np.random.default_rng(seed)
+    rows = set([0, M - 1, M // 2]) | set(rng.choice(M, min(n, M), replace=False).tolist())
+    return np.array(sorted(rows))
+
+
+@pytest.mark.parametrize("name,M", [("pixart_up", None), ("sana_qkv", None), ("flux_up", None),
+                                    ("flux_down", None), ("qwen3_up", 16), ("qwen3_down", 16),
+                                    ("qwen3_up", 256), ("qwen3_down", 256),
+                                    ("qwen3_up", 2048), ("qwen3_down", 2048)])
+def test_full_size_outputs_sampled_rows(oracle, name, M):
+    up = uploaded(name, M)
+    say(f"[linear] {name} M={up.M} K={up.K} N={up.N} batch={up.B}")
+    check_linear_rows(oracle, up, _sample_rows(up.M, 24 if up.K > 4096 else 48))
+
+
+# ------------------------------------------------------------- edge cases
+@pytest.mark.parametrize("M,K,N,r,batch", [
+    (1, 64, 16, 4, 1),        # one token, one group, one tile
+    (5, 192, 33, 0, 1),       # rank 0, odd group count, ragged N
+    (70, 640, 300, 4, 1),     # ragged M and N over several tiles
+    (200, 384, 129, 32, 2),   # largest rank, two projections
+    (64, 256, 256, 7, 3),     # odd rank (unvectorised L1 path), three projections
+    (300, 1152, 520, 4, 1),   # more row tiles than one block
+])
+def test_ragged_shapes_match_oracle(oracle, M, K, N, r, batch):
+    lay = make_random_layer(M * 31 + N, M, K, N, r=r, batch=batch, outlier_channels=2)
+    up = Uploaded(lay)
+    kernels = ("tiled", "skinny") if M <= 64 else ("tiled",)
+    q, _ = oracle.quantize(lay["X"], lay["lam"])
+    for kernel in kernels:
+        say(f"[edge] M={M} K={K} N={N} r={r} batch={batch} {kernel}")
+        check_linear_rows(oracle, up, np.arange(M), kernel)
+        got = up.partials(0, M, 0, N, kernel)
+        assert np.array_equal(got, oracle.group_partials(q, lay["qw"][0]))
+
+
+def test_zero_groups_subnormal_and_saturated_scales(oracle):
+    M, K, N = 48, 512, 64
+    lay = make_random_layer(77, M, K, N, r=4)
+    x = bf16_bits_to_f32(lay["X"]).astype(np.float64)
+    x[3, :] = 0.0                      # a zero token
+    x[7, 64:128] = 0.0                 # one zero group
+    x[9, 128:192] *= 2.0 ** -20        # fp16-subnormal scales
+    x[11, 256:320] *= 2.0 ** -40       # scale underflows to zero
+    x[13, 0:64] *= 1.0e6               # scale saturates at 65504
+    lay["X"] = f64_to_bf16_bits(x)
+    lay["bias"][:] = 0
+    up = Uploaded(lay)
+    qx, sx, _ = hsq.quantize_act(up.X, up.lam, up.L1[0])
+    q_ref, s_ref = oracle.quantize(lay["X"], lay["lam"])
+    assert np.array_equal(sx.cpu().numpy().view(np.uint16), s_ref)
+    assert np.array_equal(qx.cpu().numpy(), oracle.pack_act(q_ref))
+    assert (s_ref == 0).sum() >= 10 and (s_ref == 0x7BFF).sum() >= 1
+    assert ((s_ref > 0) & (s_ref < 0x0400)).sum() >= 1
+    for kernel in ("tiled", "skinny"):
+        assert np.array_equal(up.partials(0, M, 0, N, kernel), oracle.group_partials(q_ref, lay["qw"][0]))
+        check_linear_rows(oracle, up, np.arange(M), kernel)
+
+
+def test_rank_zero_and_zero_residual_reductions(oracle):
+    lay = make_random_layer(78, 96, 256, 80, r=4)
+    lay["qw"][:] = 0
+    up = Uploaded(lay)
+    check_linear_rows(oracle, up, np.arange(96))
+    lay0 = make_random_layer(79, 96, 256, 80, r=0)
+    check_linear_rows(oracle, Uploaded(lay0), np.arange(96))
+
+
+def test_run_twice_bitwise_deterministic():
+    up = uploaded("pixart_up")
+    a = up.linear("f32").cpu().numpy()
+    b = up.linear("f32").cpu().numpy()
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+    small = Uploaded(make_layer("qwen3_up", 16))
+    a = small.linear("bf16").cpu().numpy()
+    b = small.linear("bf16").cpu().numpy()
+    assert np.array_equal(a.view(np.uint16), b.view(np.uint16))
+
+
+def test_misaligned_tensor_is_rejected():
+    up = uploaded("tiny")
+    Xbig = torch.empty(up.M * up.K + 1, dtype=torch.int16, device=DEV)
+    Xmis = Xbig[1:].view(up.M, up.K)
+    with pytest.raises(hsq.HsqError) as ei:
+        hsq.w4a4_lowrank_linear(Xmis, up.lam, up.packed, up.sw, up.L1, up.L2, up.bias, N=up.N)
+    assert ei.value.status == hsq.E_ALIGN

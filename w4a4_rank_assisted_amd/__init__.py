@@ -1,0 +1,280 @@
+"""Python binding of libhsq, the MI355X (gfx950) W4A4 + rank-r linear layer.
+
+Argument marshalling only: every step of the layer runs in the HIP kernels
+behind the C ABI declared in ``include/hsq.h``; PyTorch provides device
+memory and the current stream.  Importing this module never falls back to
+anything: if ``_lib/libhsq.so`` is missing or cannot be loaded, every call
+raises.
+
+Half-precision inputs may be passed as torch.bfloat16 / torch.float16
+tensors or as int16 / uint16 tensors holding the bit patterns.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+from typing import Optional
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "_lib", "libhsq.so")
+HEADER = os.path.join(os.path.dirname(_HERE), "include", "hsq.h")
+
+OK, E_INVAL, E_SHAPE, E_ALIGN, E_WORKSPACE, E_HIP = 0, -1, -2, -3, -4, -5
+F32, BF16 = 0, 1
+KERNEL_AUTO, KERNEL_TILED, KERNEL_SKINNY = 0, 1, 2
+_KERNELS = {"auto": KERNEL_AUTO, "tiled": KERNEL_TILED, "skinny": KERNEL_SKINNY}
+
+_lib = None
+
+
+class HsqError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        msg = _load().hsq_status_string(status).decode() if _lib is not None else str(status)
+        super().__init__(f"{what}: {msg} (status {status})")
+        self.status = status
+
+
+def _load():
+    """Load libhsq.so (raises OSError if it is missing: there is no fallback)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise OSError(f"{LIB_PATH} is missing; build it with w4a4_rank_assisted_amd.build.build()")
+        lib = ctypes.CDLL(LIB_PATH)
+        P, I, S = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+        sig = {
+            "hsq_layout_version": ([], I),
+            "hsq_status_string": ([I], ctypes.c_char_p),
+            "hsq_packed_weight_bytes": ([I, I], S),
+            "hsq_pack_weights": ([P, I, I, P, P, P], I),
+            "hsq_unpack_weights": ([P, I, I, P, P], I),
+            "hsq_quantize_act": ([P, I, I, P, P, I, P, P, P, P], I),
+            "hsq_workspace_bytes": ([I, I, I, I, I], S),
+            "hsq_w4a4_lowrank_linear": ([P, I, I, I, I, P, P, P, P, P, I, P, P, I, P, S, P], I),
+            "hsq_w4a4_lowrank_linear_ex": ([P, I, I, I, I, P, P, P, P, P, I, P, P, I, P, S, I, P], I),
+            "hsq_w4a4_group_partials": ([P, I, I, I, P, P, I, I, I, I, P, P, S, I, P], I),
+            "hsq_w4a4_quantize_stage": ([P, I, I, I, I, P, P, I, P, S, P], I),
+            "hsq_w4a4_contract_stage": ([I, I, I, I, P, P, P, I, P, P, I, P, S, I, P], I),
+        }
+        for name, (args, res) in sig.items():
+            fn = getattr(lib, name)
+            fn.argtypes = args
+            fn.restype = res
+        _lib = lib
+    return _lib
+
+
+def header_functions():
+    """Names of the functions include/hsq.h declares."""
+    with open(HEADER) as f:
+        text = f.read()
+    return sorted(set(re.findall(r"\b(hsq_[a-z0-9_]+)\s*\(", text)))
+
+
+# --------------------------------------------------------------- marshalling
+def _torch():
+    import torch
+
+    return torch
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else int(t.data_ptr())
+
+
+def _stream():
+    torch = _torch()
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _dev_tensor(t, name, dtypes, shape=None):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be on a HIP device")
+    if dtypes and t.dtype not in dtypes:
+        raise TypeError(f"{name}: dtype {t.dtype} not in {dtypes}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: shape {tuple(t.shape)} != {tuple(shape)}")
+    return t
+
+
+def _half_types():
+    torch = _torch()
+    return (torch.bfloat16, torch.float16, torch.int16, torch.uint16)
+
+
+def _check(status: int, what: str):
+    if status != OK:
+        raise HsqError(status, what)
+
+
+# ------------------------------------------------------------------ the API
+def layout_version() -> int:
+    return int(_load().hsq_layout_version())
+
+
+def packed_weight_bytes(K: int, N: int) -> int:
+    return int(_load().hsq_packed_weight_bytes(K, N))
+
+
+def workspace_bytes(M: int, K: int, N: int, r: int, batch: int = 1) -> int:
+    return int(_load().hsq_workspace_bytes(M, K, N, r, batch))
+
+
+def pack_weights(codes, packed=None, status=None):
+    """codes: (K, N) int8 device tensor -> (packed uint8 blob, device status int32)."""
+    torch = _torch()
+    lib = _load()
+    _dev_tensor(codes, "codes", (torch.int8,))
+    K, N = codes.shape
+    nbytes = lib.hsq_packed_weight_bytes(K, N)
+    if packed is None:
+        packed = torch.empty(nbytes, dtype=torch.uint8, device=codes.device)
+    if status is None:
+        status = torch.empty(4, dtype=torch.int32, device=codes.device)
+    _dev_tensor(packed, "packed", (torch.uint8,), (nbytes,))
+    _check(lib.hsq_pack_weights(_ptr(codes), K, N, _ptr(packed), _ptr(status), _stream()),
+           "hsq_pack_weights")
+    return packed, status
+
+
+def unpack_weights(packed, K: int, N: int):
+    torch = _torch()
+    lib = _load()
+    _dev_tensor(packed, "packed", (torch.uint8,))
+    codes = torch.empty((K, N), dtype=torch.int8, device=packed.device)
+    _check(lib.hsq_unpack_weights(_ptr(packed), K, N, _ptr(codes), _stream()), "hsq_unpack_weights")
+    return codes
+
+
+def quantize_act(X, lam, L1=None):
+    """X (M, K) bf16, lam (K,) fp16, L1 (K, r) bf16 or None ->
+    (qx (M, K/2) uint8, sx (M, K/64) int16 fp16 bits, U (M, r) fp32)."""
+    torch = _torch()
+    lib = _load()
+    _dev_tensor(X, "X", _half_types())
+    M, K = X.shape
+    _dev_tensor(lam, "lambda", _half_types(), (K,))
+    r = 0 if L1 is None else int(L1.shape[1])
+    if L1 is not None:
+        _dev_tensor(L1, "L1", _half_types(), (K, r))
+    dev = X.device
+    qx = torch.empty((M, K // 2), dtype=torch.uint8, device=dev)
+    sx = torch.empty((M, max(K // 64, 1)), dtype=torch.int16, device=dev)
+    U = torch.empty((M, max(r, 1)), dtype=torch.float32, device=dev)
+    _check(lib.hsq_quantize_act(_ptr(X), M, K, _ptr(lam), _ptr(L1), r, _ptr(qx), _ptr(sx),
+                                _ptr(U) if r else None, _stream()), "hsq_quantize_act")
+    return qx, sx, U[:, :r]
+
+
+def w4a4_lowrank_linear(X, lam, packed_w, sw, L1=None, L2=None, bias=None, *, N: int,
+                        batch: int = 1, y_dtype: str = "bf16", out=None, workspace=None,
+                        kernel: str = "auto"):
+    """The fused layer.  Shapes: X (M, K); lam (K,); packed_w (batch * blob,);
+    sw (batch, K/64, N); L1 (batch, K, r); L2 (batch, r, N); bias (batch, N).
+    Returns Y (batch, M, N) as bf16 or fp32."""
+    torch = _torch()
+    lib = _load()
+    _dev_tensor(X, "X", _half_types())
+    M, K = X.shape
+    G = K // 64
+    _dev_tensor(lam, "lambda", _half_types(), (K,))
+    _dev_tensor(packed_w, "packed_w", (torch.uint8,), (batch * lib.hsq_packed_weight_bytes(K, N),))
+    _dev_tensor(sw, "sw", _half_types(), (batch, G, N))
+    r = 0 if L1 is None else int(L1.shape[-1])
+    if r:
+        _dev_tensor(L1, "L1", _half_types(), (batch, K, r))
+        _dev_tensor(L2, "L2", _half_types(), (batch, r, N))
+    if bias is not None:
+        _dev_tensor(bias, "bias", _half_types(), (batch, N))
+    ydt = {"bf16": (BF16, torch.bfloat16), "f32": (F32, torch.float32)}[y_dtype]
+    if out is None:
+        out = torch.empty((batch, M, N), dtype=ydt[1], device=X.device)
+    _dev_tensor(out, "out", (ydt[1],), (batch, M, N))
+    need = lib.hsq_workspace_bytes(M, K, N, r, batch)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=X.device)
+    _dev_tensor(workspace, "workspace", (torch.uint8,))
+    _check(lib.hsq_w4a4_lowrank_linear_ex(
+        _ptr(X), M, K, N, batch, _ptr(lam), _ptr(packed_w), _ptr(sw),
+        _ptr(L1) if r else None, _ptr(L2) if r else None, r, _ptr(bias), _ptr(out), ydt[0],
+        _ptr(workspace), workspace.numel(), _KERNELS[kernel], _stream()),
+        "hsq_w4a4_lowrank_linear")
+    return out
+
+
+def quantize_stage(X, lam, L1, *, N: int, batch: int, workspace):
+    """First stage of the layer: quantize X and form U into ``workspace``."""
+    lib = _load()
+    M, K = X.shape
+    r = 0 if L1 is None else int(L1.shape[-1])
+    _check(lib.hsq_w4a4_quantize_stage(_ptr(X), M, K, N, batch, _ptr(lam), _ptr(L1) if r else None,
+                                       r, _ptr(workspace), workspace.numel(), _stream()),
+           "hsq_w4a4_quantize_stage")
+
+
+def contract_stage(M: int, K: int, packed_w, sw, L2, bias, out, *, N: int, batch: int, r: int,
+                   workspace, kernel: str = "auto"):
+    """Second stage: contraction + epilogue from the workspace into ``out``."""
+    torch = _torch()
+    lib = _load()
+    ydt = BF16 if out.dtype == torch.bfloat16 else F32
+    _check(lib.hsq_w4a4_contract_stage(M, K, N, batch, _ptr(packed_w), _ptr(sw),
+                                       _ptr(L2) if r else None, r, _ptr(bias), _ptr(out), ydt,
+                                       _ptr(workspace), workspace.numel(), _KERNELS[kernel],
+                                       _stream()),
+           "hsq_w4a4_contract_stage")
+
+
+def w4a4_group_partials(X, lam, packed_w, N: int, m0: int, mc: int, n0: int, nc: int,
+                        workspace=None, kernel: str = "auto"):
+    """int32 P (mc, nc, K/64) of the window, from the production kernels."""
+    torch = _torch()
+    lib = _load()
+    _dev_tensor(X, "X", _half_types())
+    M, K = X.shape
+    _dev_tensor(lam, "lambda", _half_types(), (K,))
+    _dev_tensor(packed_w, "packed_w", (torch.uint8,))
+    P = torch.empty((mc, nc, K // 64), dtype=torch.int32, device=X.device)
+    need = lib.hsq_workspace_bytes(M, K, N, 0, 1)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=X.device)
+    _check(lib.hsq_w4a4_group_partials(_ptr(X), M, K, N, _ptr(lam), _ptr(packed_w), m0, mc, n0,
+                                       nc, _ptr(P), _ptr(workspace), workspace.numel(),
+                                       _KERNELS[kernel], _stream()),
+           "hsq_w4a4_group_partials")
+    return P
+
+
+class Layer:
+    """A packed W4A4 + rank-r layer resident on the device: holds the packed
+    residual blobs, the scales, the low-rank factors, the bias and a reusable
+    workspace, and runs the fused call on the current stream."""
+
+    def __init__(self, lam, qw, sw, L1=None, L2=None, bias=None, max_tokens: int = 0):
+        torch = _torch()
+        self.batch, self.K, self.N = qw.shape
+        self.r = 0 if L1 is None else int(L1.shape[-1])
+        blobs = [pack_weights(qw[b].contiguous())[0] for b in range(self.batch)]
+        self.packed = torch.cat(blobs) if self.batch > 1 else blobs[0]
+        self.lam, self.sw, self.L1, self.L2, self.bias = lam, sw, L1, L2, bias
+        self.workspace = None
+        if max_tokens:
+            self.workspace = torch.empty(
+                workspace_bytes(max_tokens, self.K, self.N, self.r, self.batch),
+                dtype=torch.uint8, device=qw.device)
+
+    def __call__(self, X, y_dtype: str = "bf16", out=None, kernel: str = "auto"):
+        ws = self.workspace
+        need = workspace_bytes(X.shape[0], self.K, self.N, self.r, self.batch)
+        if ws is None or ws.numel() < need:
+            ws = None
+        return w4a4_lowrank_linear(X, self.lam, self.packed, self.sw, self.L1, self.L2, self.bias,
+                                   N=self.N, batch=self.batch, y_dtype=y_dtype, out=out,
+                                   workspace=ws, kernel=kernel)

@@ -1,0 +1,265 @@
+// api.hip -- the C ABI of libhsq (declared in include/hsq.h): argument
+// validation, workspace planning and kernel launches.  No allocation, no
+// state, no exceptions across the interface.
+#include "hsq.h"
+#include "hsq_internal.h"
+
+#include <climits>
+#include <cstdint>
+
+namespace hsq {
+
+WsLayout plan_workspace(int M, int K, int r, int batch) {
+  WsLayout L;
+  L.MT = ceil_div(M, kTile);
+  L.G = K / kGroup;
+  L.Gp = padded_groups(K);
+  L.Mpad = L.MT * kTile;
+  // Quantization pass: one workgroup per 16 rows and K-slice.  Split K until
+  // about four workgroups per CU exist (small token counts need the split to
+  // spread the pass over the chip); slices are whole 512-channel chunks.
+  const int kpad = L.Gp * kGroup;
+  const int chunks = ceil_div(kpad, 512);
+  int s = ceil_div(1024, L.MT);
+  if (s > chunks) s = chunks;
+  if (s < 1) s = 1;
+  L.kslice = ceil_div(chunks, s) * 512;
+  L.u_slices = ceil_div(kpad, L.kslice);
+  size_t off = 0;
+  L.qa_off = off;
+  off = align_up(off + (size_t)L.MT * L.Gp * 1024, 256);
+  L.sxs_off = off;
+  off = align_up(off + (size_t)L.MT * L.Gp * 16 * sizeof(float), 256);
+  L.uw_off = off;
+  off = align_up(off + (size_t)L.u_slices * batch * r * L.Mpad * sizeof(float), 256);
+  L.total = off;
+  return L;
+}
+
+}  // namespace hsq
+
+using namespace hsq;
+
+namespace {
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+int check_sizes(int M, int K, int N, int r, int batch) {
+  if (M < 1 || N < 1 || K < 1 || r < 0 || r > kMaxRank || batch < 1 || batch > kMaxBatch)
+    return HSQ_E_INVAL;
+  if (K % kGroup != 0) return HSQ_E_SHAPE;
+  if ((long long)M * K >= INT_MAX || (long long)M * N >= INT_MAX || (long long)K * N >= INT_MAX)
+    return HSQ_E_INVAL;
+  return HSQ_OK;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? HSQ_OK : HSQ_E_HIP; }
+
+size_t workspace_bytes(int M, int K, int N, int r, int batch) {
+  if (check_sizes(M, K, N, r, batch) != HSQ_OK) return 0;
+  return plan_workspace(M, K, r, batch).total;
+}
+
+// Argument checks shared by every form of the linear.  `quant` / `contract`
+// select which stage's pointers must be present.
+int validate(const uint16_t *X, int M, int K, int N, int batch, const uint16_t *lambda,
+             const uint8_t *packed_w, const uint16_t *sw, const uint16_t *L1, const uint16_t *L2,
+             int r, const uint16_t *bias, const void *Y, int y_dtype, const void *workspace,
+             size_t ws_bytes, int *kernel, bool quant, bool contract, const int32_t *P, int m0,
+             int mc, int n0, int nc) {
+  int st = check_sizes(M, K, N, r, batch);
+  if (st != HSQ_OK) return st;
+  const bool dump = P != nullptr;
+  if (!workspace) return HSQ_E_INVAL;
+  if (quant && (!X || !lambda || (r > 0 && !L1))) return HSQ_E_INVAL;
+  if (contract && !packed_w) return HSQ_E_INVAL;
+  if (contract && !dump && (!sw || !Y || (r > 0 && !L2))) return HSQ_E_INVAL;
+  if (contract && !dump && y_dtype != HSQ_F32 && y_dtype != HSQ_BF16) return HSQ_E_INVAL;
+  if (*kernel != HSQ_KERNEL_AUTO && *kernel != HSQ_KERNEL_TILED && *kernel != HSQ_KERNEL_SKINNY)
+    return HSQ_E_INVAL;
+  if (dump && (mc < 1 || nc < 1 || m0 < 0 || n0 < 0 || m0 + mc > M || n0 + nc > N))
+    return HSQ_E_SHAPE;
+  const void *ptrs[] = {X, lambda, packed_w, sw, L1, L2, bias, Y, workspace, P};
+  for (const void *p : ptrs)
+    if (p && !aligned16(p)) return HSQ_E_ALIGN;
+  if (*kernel == HSQ_KERNEL_AUTO) *kernel = M <= kSkinnyMaxM ? HSQ_KERNEL_SKINNY : HSQ_KERNEL_TILED;
+  if (*kernel == HSQ_KERNEL_SKINNY && M > kSkinnyMaxM) return HSQ_E_INVAL;
+  if (ws_bytes < plan_workspace(M, K, r, batch).total) return HSQ_E_WORKSPACE;
+  return HSQ_OK;
+}
+
+int quant_stage(const uint16_t *X, int M, int K, int batch, const uint16_t *lambda,
+                const uint16_t *L1, int r, void *workspace, hipStream_t s) {
+  const WsLayout L = plan_workspace(M, K, r, batch);
+  char *ws = (char *)workspace;
+  QuantArgs q{};
+  q.X = X;
+  q.lam = lambda;
+  q.L1 = r > 0 ? L1 : nullptr;
+  q.M = M; q.K = K; q.G = L.G;
+  q.r = r; q.batch = batch;
+  q.kslice = L.kslice;
+  q.kend = L.Gp * kGroup;
+  q.qa = (int8_t *)(ws + L.qa_off);
+  q.sxs = (float *)(ws + L.sxs_off);
+  q.uw = (float *)(ws + L.uw_off);
+  q.Gp = L.Gp; q.Mpad = L.Mpad; q.ucols = batch * r;
+  return hip_status(launch_quant(q, L.u_slices, s));
+}
+
+int contract_stage(int M, int K, int N, int batch, const uint8_t *packed_w, const uint16_t *sw,
+                   const uint16_t *L2, int r, const uint16_t *bias, void *Y, int y_dtype,
+                   void *workspace, int kernel, hipStream_t s, int32_t *P, int m0, int mc,
+                   int n0, int nc) {
+  const WsLayout L = plan_workspace(M, K, r, batch);
+  char *ws = (char *)workspace;
+  GemmArgs g{};
+  g.qa = (const int8_t *)(ws + L.qa_off);
+  g.sxs = (const float *)(ws + L.sxs_off);
+  g.w = packed_w;
+  g.w_stride = packed_bytes(K, N);
+  g.sw = sw;
+  g.uw = (const float *)(ws + L.uw_off);
+  g.u_slices = L.u_slices;
+  g.L2 = r > 0 ? L2 : nullptr;
+  g.bias = bias;
+  g.Y = Y;
+  g.y_bf16 = y_dtype == HSQ_BF16;
+  g.M = M; g.N = N; g.G = L.G; g.Gp = L.Gp; g.Mpad = L.Mpad; g.r = r; g.ucols = batch * r;
+  g.P = P; g.m0 = m0; g.mc = mc; g.n0 = n0; g.nc = nc;
+  const bool dump = P != nullptr;
+  return hip_status(kernel == HSQ_KERNEL_SKINNY ? launch_gemm_skinny(g, batch, dump, s)
+                                                : launch_gemm_tiled(g, batch, dump, s));
+}
+
+int run_linear(const uint16_t *X, int M, int K, int N, int batch, const uint16_t *lambda,
+               const uint8_t *packed_w, const uint16_t *sw, const uint16_t *L1,
+               const uint16_t *L2, int r, const uint16_t *bias, void *Y, int y_dtype,
+               void *workspace, size_t ws_bytes, int kernel, void *stream,
+               // partial-sum dump (test export); P == nullptr for the linear
+               int32_t *P, int m0, int mc, int n0, int nc) {
+  int st = validate(X, M, K, N, batch, lambda, packed_w, sw, L1, L2, r, bias, Y, y_dtype,
+                    workspace, ws_bytes, &kernel, true, true, P, m0, mc, n0, nc);
+  if (st != HSQ_OK) return st;
+  hipStream_t s = (hipStream_t)stream;
+  st = quant_stage(X, M, K, batch, lambda, L1, r, workspace, s);
+  if (st != HSQ_OK) return st;
+  return contract_stage(M, K, N, batch, packed_w, sw, L2, r, bias, Y, y_dtype, workspace, kernel,
+                        s, P, m0, mc, n0, nc);
+}
+
+}  // namespace
+
+extern "C" {
+
+int hsq_layout_version(void) { return 1; }
+
+const char *hsq_status_string(int status) {
+  switch (status) {
+    case HSQ_OK: return "ok";
+    case HSQ_E_INVAL: return "invalid argument";
+    case HSQ_E_SHAPE: return "invalid shape (K must be a positive multiple of 64; window inside the matrix)";
+    case HSQ_E_ALIGN: return "pointer not 16-byte aligned";
+    case HSQ_E_WORKSPACE: return "workspace missing or too small";
+    case HSQ_E_HIP: return "HIP launch failed";
+    default: return "unknown status";
+  }
+}
+
+size_t hsq_packed_weight_bytes(int K, int N) {
+  if (K < kGroup || K % kGroup != 0 || N < 1 || (long long)K * N >= INT_MAX) return 0;
+  return packed_bytes(K, N);
+}
+
+int hsq_pack_weights(const int8_t *codes, int K, int N, uint8_t *packed, int *d_status,
+                     void *stream) {
+  if (!codes || !packed || !d_status || N < 1 || K < 1) return HSQ_E_INVAL;
+  if (K % kGroup != 0) return HSQ_E_SHAPE;
+  if ((long long)K * N >= INT_MAX) return HSQ_E_INVAL;
+  if (!aligned16(codes) || !aligned16(packed) || !aligned16(d_status)) return HSQ_E_ALIGN;
+  return hip_status(launch_pack(codes, K, N, packed, d_status, (hipStream_t)stream));
+}
+
+int hsq_unpack_weights(const uint8_t *packed, int K, int N, int8_t *codes, void *stream) {
+  if (!codes || !packed || N < 1 || K < 1) return HSQ_E_INVAL;
+  if (K % kGroup != 0) return HSQ_E_SHAPE;
+  if ((long long)K * N >= INT_MAX) return HSQ_E_INVAL;
+  if (!aligned16(codes) || !aligned16(packed)) return HSQ_E_ALIGN;
+  return hip_status(launch_unpack(packed, K, N, codes, (hipStream_t)stream));
+}
+
+int hsq_quantize_act(const uint16_t *X, int M, int K, const uint16_t *lambda,
+                     const uint16_t *L1, int r, uint8_t *qx, uint16_t *sx, float *U,
+                     void *stream) {
+  int st = check_sizes(M, K, 1, r, 1);
+  if (st != HSQ_OK) return st;
+  if (!X || !lambda || !qx || !sx || (r > 0 && (!L1 || !U))) return HSQ_E_INVAL;
+  const void *ptrs[] = {X, lambda, L1, qx, sx, U};
+  for (const void *p : ptrs)
+    if (p && !aligned16(p)) return HSQ_E_ALIGN;
+  QuantArgs q{};
+  q.X = X;
+  q.lam = lambda;
+  q.L1 = r > 0 ? L1 : nullptr;
+  q.M = M; q.K = K; q.G = K / kGroup;
+  q.r = r; q.batch = 1;
+  q.kend = K;
+  q.kslice = ceil_div(K, 512) * 512;  // one slice: U is final
+  q.qx = qx; q.sx = sx; q.u_pub = r > 0 ? U : nullptr;
+  q.ucols = r;
+  return hip_status(launch_quant(q, 1, (hipStream_t)stream));
+}
+
+size_t hsq_workspace_bytes(int M, int K, int N, int r, int batch) {
+  return workspace_bytes(M, K, N, r, batch);
+}
+
+int hsq_w4a4_lowrank_linear(const uint16_t *X, int M, int K, int N, int batch,
+                            const uint16_t *lambda, const uint8_t *packed_w,
+                            const uint16_t *sw, const uint16_t *L1, const uint16_t *L2, int r,
+                            const uint16_t *bias, void *Y, int y_dtype, void *workspace,
+                            size_t ws_bytes, void *stream) {
+  return run_linear(X, M, K, N, batch, lambda, packed_w, sw, L1, L2, r, bias, Y, y_dtype,
+                    workspace, ws_bytes, HSQ_KERNEL_AUTO, stream, nullptr, 0, 0, 0, 0);
+}
+
+int hsq_w4a4_lowrank_linear_ex(const uint16_t *X, int M, int K, int N, int batch,
+                               const uint16_t *lambda, const uint8_t *packed_w,
+                               const uint16_t *sw, const uint16_t *L1, const uint16_t *L2,
+                               int r, const uint16_t *bias, void *Y, int y_dtype,
+                               void *workspace, size_t ws_bytes, int kernel, void *stream) {
+  return run_linear(X, M, K, N, batch, lambda, packed_w, sw, L1, L2, r, bias, Y, y_dtype,
+                    workspace, ws_bytes, kernel, stream, nullptr, 0, 0, 0, 0);
+}
+
+int hsq_w4a4_quantize_stage(const uint16_t *X, int M, int K, int N, int batch,
+                            const uint16_t *lambda, const uint16_t *L1, int r, void *workspace,
+                            size_t ws_bytes, void *stream) {
+  int kernel = HSQ_KERNEL_AUTO;
+  int st = validate(X, M, K, N, batch, lambda, nullptr, nullptr, L1, nullptr, r, nullptr, nullptr,
+                    HSQ_F32, workspace, ws_bytes, &kernel, true, false, nullptr, 0, 0, 0, 0);
+  if (st != HSQ_OK) return st;
+  return quant_stage(X, M, K, batch, lambda, L1, r, workspace, (hipStream_t)stream);
+}
+
+int hsq_w4a4_contract_stage(int M, int K, int N, int batch, const uint8_t *packed_w,
+                            const uint16_t *sw, const uint16_t *L2, int r, const uint16_t *bias,
+                            void *Y, int y_dtype, void *workspace, size_t ws_bytes, int kernel,
+                            void *stream) {
+  int st = validate(nullptr, M, K, N, batch, nullptr, packed_w, sw, nullptr, L2, r, bias, Y,
+                    y_dtype, workspace, ws_bytes, &kernel, false, true, nullptr, 0, 0, 0, 0);
+  if (st != HSQ_OK) return st;
+  return contract_stage(M, K, N, batch, packed_w, sw, L2, r, bias, Y, y_dtype, workspace, kernel,
+                        (hipStream_t)stream, nullptr, 0, 0, 0, 0);
+}
+
+int hsq_w4a4_group_partials(const uint16_t *X, int M, int K, int N, const uint16_t *lambda,
+                            const uint8_t *packed_w, int m0, int mc, int n0, int nc,
+                            int32_t *P, void *workspace, size_t ws_bytes, int kernel,
+                            void *stream) {
+  if (!P) return HSQ_E_INVAL;
+  return run_linear(X, M, K, N, 1, lambda, packed_w, nullptr, nullptr, nullptr, 0, nullptr,
+                    nullptr, HSQ_F32, workspace, ws_bytes, kernel, stream, P, m0, mc, n0, nc);
+}
+
+}  // extern "C"
