@@ -257,9 +257,9 @@ def test_run_twice_bitwise_deterministic():
     b = up.linear("f32").cpu().numpy()
     assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
     small = Uploaded(make_layer("qwen3_up", 16))
-    a = small.linear("bf16").cpu().numpy()
-    b = small.linear("bf16").cpu().numpy()
-    assert np.array_equal(a.view(np.uint16), b.view(np.uint16))
+    a = small.linear("bf16").view(torch.int16).cpu().numpy()
+    b = small.linear("bf16").view(torch.int16).cpu().numpy()
+    assert np.array_equal(a, b)
 
 
 def test_misaligned_tensor_is_rejected():

@@ -21,6 +21,7 @@ WsLayout plan_workspace(int M, int K, int r, int batch) {
   const int kpad = L.Gp * kGroup;
   const int chunks = ceil_div(kpad, 512);
   int s = ceil_div(1024, L.MT);
+  if (s > kMaxUSlices) s = kMaxUSlices;
   if (s > chunks) s = chunks;
   if (s < 1) s = 1;
   L.kslice = ceil_div(chunks, s) * 512;

@@ -7,18 +7,27 @@
 //
 // One 16x16x64 int8 MFMA covers exactly one group of one 16x16 output tile.
 // Operands: A = activation codes (int8, written by K1 in MFMA lane order),
-// B = residual codes unpacked from nibbles to 16*code while staging to LDS,
+// B = residual codes unpacked from nibbles to 16*code on the way into LDS,
 // so the MFMA yields 16*P.  The MFMA accumulator input is the bit pattern of
 // 1.5*2^23; the result bits then read as the float 1.5*2^23 + 16P exactly,
 // and two FMAs per element finish the group:
 //   u   = fma(D, sw, -1.5*2^23*sw)   (= 16P*sw rounded once; the constant
 //                                      product is exact: 3*2^22 * fp16)
 //   acc = fma(u, sx/16, acc)
+// Those two VALU FMAs per element and group, not the MFMA, bound the kernel
+// (a wave64 fp32 FMA takes 4 cycles, a 16x16x64 int8 MFMA 16 cycles for 4
+// elements per lane).  The loop keeps the VALU fed: within a stage the row
+// tiles run as a software pipeline (LDS read one step ahead, MFMAs of step
+// s, rescale of step s-1).
 //
-// Workgroup: 256 threads = 4 waves in 2x2, tile BM x BN; each wave owns
-// (BM/2) x (BN/2) = TM x TN MFMA tiles.  K advances two groups per stage;
-// stages are double-buffered in LDS with register prefetch, one barrier per
-// stage.
+// Workgroup: 256 threads = 4 waves in 2x2, tile BM x BN = 128 x 128; each
+// wave owns 64 x 64 = 4 x 4 MFMA tiles.  K advances one group per stage.
+// Global loads run two stages ahead into two register sets (slot = stage
+// parity, fixed at compile time by unrolling the stage loop by two); a set
+// is written to one of two LDS buffers one stage before it is consumed, so
+// each load has two stages of compute to arrive in.  One barrier per stage.
+// Workgroups are mapped so that each XCD (own L2) walks a compact block of
+// output tiles.
 #include "hsq_internal.h"
 
 namespace hsq {
@@ -26,98 +35,152 @@ namespace hsq {
 namespace {
 
 constexpr uint32_t kNibMask = 0xF0F0F0F0u;
+constexpr int BM = 128, BN = 128;
+constexpr int TMB = BM / 16, TNB = BN / 16;   // MFMA tiles per block
+constexpr int TM = TMB / 2, TN = TNB / 2;     // MFMA tiles per wave
+constexpr int kGroupM = 8;                    // m-blocks per tile-order group
 
-template <int BM, int BN>
-struct Smem {
-  static constexpr int TMB = BM / 16, TNB = BN / 16;
-  int8_t a[2][TMB][2][64][16];      // [buf][m-tile][group][lane][bytes]
-  int8_t b[2][2][TNB][64][16];      // [buf][group][n-tile][lane][bytes]
-  float2 sw[2][2][BN];              // [buf][group][col] = (sw, -magic*sw)
-  float sx[2][TMB][2][16];          // [buf][m-tile][group][row]
+struct alignas(16) Stages {
+  int8_t a[2][TMB][64][16];           // [buf][m-tile][lane][bytes]          16 KB
+  int8_t b[2][TNB][64][16];           // [buf][n-tile][lane][bytes]          16 KB
+  float2 sw[2][BN];                   // [buf][col] = (sw, -magic*sw)         2 KB
+  float sx[2][TMB][16];               // [buf][m-tile][row]                   1 KB
 };
 
-template <int BM, int BN, bool DUMP>
-__global__ __launch_bounds__(256, 2) void k_gemm_tiled(GemmArgs a) {
-  constexpr int TMB = BM / 16, TNB = BN / 16;
-  constexpr int TM = TMB / 2, TN = TNB / 2;        // per wave
-  constexpr int A_ITERS = TMB * 2 * 64 / 256;      // 16-byte chunks per thread
-  constexpr int B_ITERS = TNB * 64 / 256;
-  static_assert(A_ITERS >= 1 && B_ITERS >= 1, "tile too small");
-  static_assert(2 * BN == 256 && TMB * 32 == 256, "scale staging assumes BM = BN = 128");
-  __shared__ Smem<BM, BN> sm;
+// Epilogue operands of the block: U (rank columns padded to RPT) for its
+// BM rows, L2 for its BN columns, bias.  Filled at kernel start.
+template <int RPT>
+struct alignas(16) EpiSmem {
+  float u[RPT][BM];
+  float l2[RPT][BN];
+  float bias[BN];
+};
+template <>
+struct alignas(16) EpiSmem<0> {
+  float bias[BN];
+};
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+template <int RPT>
+struct alignas(16) Smem {
+  Stages st;
+  EpiSmem<RPT> ep;
+};
+
+template <int V>
+struct int_c {
+  static constexpr int value = V;
+};
+
+// Order pins.  An empty volatile asm that "rewrites" a register value makes
+// every later use depend on it, and volatile asm statements keep their
+// program order; the pins below fix the software pipeline that the
+// instruction selector would otherwise flatten into all-MFMAs-first, which
+// keeps every MFMA result alive at once and spills.
+__device__ __forceinline__ void pin(v4i &x) { asm volatile("" : "+v"(x)); }
+__device__ __forceinline__ void pin(float &x) { asm volatile("" : "+v"(x)); }
+
+// block index -> (m-block, n-block).  Consecutive workgroup ids go to
+// different XCDs (id % 8); regroup them so that XCD x owns a contiguous
+// range of the tile order, and walk that order in groups of kGroupM
+// m-blocks so concurrently running tiles share rows of A and columns of B.
+__device__ __forceinline__ void tile_of(int bid, int nblk, int mblk, int &mb, int &nb) {
+  const int T = nblk * mblk;
+  const int per = T / 8, rem = T % 8;
+  const int x = bid % 8, loc = bid / 8;
+  // XCD x owns [start(x), start(x) + per + (x < rem)); ids with loc == per
+  // exist only for x < rem.
+  const int t = x * per + min(x, rem) + loc;
+  const int span = kGroupM * nblk;
+  const int grp = t / span, first = grp * kGroupM;
+  const int gsz = min(mblk - first, kGroupM);
+  const int w = t % span;
+  mb = first + w % gsz;
+  nb = w / gsz;
+}
+
+typedef float v4f __attribute__((ext_vector_type(4)));
+
+template <bool DUMP, int RPT>
+__global__ __launch_bounds__(256, 2) void k_gemm_tiled(GemmArgs a, int nblk, int mblk) {
+  __shared__ Smem<RPT> smem;
+  Stages &sm = smem.st;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
-  const int proj = blockIdx.z;
-  const int mt0 = blockIdx.y * TMB;                 // first m-tile of this block
-  const int nt0 = blockIdx.x * TNB;
+  const int proj = blockIdx.y;
+  int mb, nb;
+  tile_of(blockIdx.x, nblk, mblk, mb, nb);
+  const int mt0 = mb * TMB, nt0 = nb * TNB;
   const int MT = a.Mpad / 16, NT = (a.N + 15) / 16;
-  const int GP = a.Gp / 2;
+  const int GP = a.Gp / 2;            // group pairs in the packed residual
   const uint8_t *w = a.w + (size_t)proj * a.w_stride;
-  const uint16_t *sw = a.sw + (size_t)proj * a.G * a.N;
+  const uint16_t *sw = DUMP ? nullptr : a.sw + (size_t)proj * a.G * a.N;
   if (DUMP && ((mt0 + TMB) * 16 <= a.m0 || mt0 * 16 >= a.m0 + a.mc ||
                (nt0 + TNB) * 16 <= a.n0 || nt0 * 16 >= a.n0 + a.nc))
     return;  // whole block outside the window (uniform: before any barrier)
 
-  uint4 ra[A_ITERS], rb[B_ITERS];
-  float rsw, rsx;
-
-  auto load_stage = [&](int gp) {
+  // ---- global -> registers (two slots) -> LDS (two buffers) ----
+  // Loads past the matrix edges read the last valid block (clamped
+  // addresses, straight-line code); the edge masks are applied on the way
+  // into LDS, where only masked rows / columns see those values.
+  const int G = a.G;
+  v4u ra[2][2];
+  v2u rb[2][2];
+  float rsx[2];
+  uint32_t rsw[2];
+  // Straight-line code with a fixed number of loads per stage (the stage
+  // index is clamped near the end instead of skipping the loads), so the
+  // compiler's wait counting stays exact and waits only for the older slot.
+  auto load_stage = [&](int g, auto slotc) __attribute__((always_inline)) {
+    constexpr int SL = decltype(slotc)::value;
+    g = min(g, a.Gp - 1);
 #pragma unroll
-    for (int i = 0; i < A_ITERS; ++i) {
-      int c = i * 256 + tid;
-      int mi = c >> 7, rem = c & 127;
-      ra[i] = (mt0 + mi < MT)
-                  ? *reinterpret_cast<const uint4 *>(
-                        a.qa + ((size_t)(mt0 + mi) * a.Gp + 2 * gp) * 1024 + (size_t)rem * 16)
-                  : make_uint4(0, 0, 0, 0);
+    for (int i = 0; i < 2; ++i) {
+      const int c = i * 256 + tid;                    // 16-byte chunk of the A tile
+      const int mi = c >> 6, l = c & 63;
+      const int mt = min(mt0 + mi, MT - 1);
+      ra[SL][i] = *reinterpret_cast<const v4u *>(a.qa + (((size_t)mt * a.Gp + g) * 64 + l) * 16);
     }
 #pragma unroll
-    for (int i = 0; i < B_ITERS; ++i) {
-      int c = i * 256 + tid;
-      int ni = c >> 6, l = c & 63;
-      rb[i] = (nt0 + ni < NT)
-                  ? *reinterpret_cast<const uint4 *>(
-                        w + ((size_t)(nt0 + ni) * GP + gp) * 1024 + (size_t)l * 16)
-                  : make_uint4(0, 0, 0, 0);
+    for (int i = 0; i < 2; ++i) {
+      const int c = i * 256 + tid;                    // lane slot of the packed B tile
+      const int ni = c >> 6, l = c & 63;
+      const int nt = min(nt0 + ni, NT - 1);
+      rb[SL][i] = *reinterpret_cast<const v2u *>(
+          w + (((size_t)nt * GP + (g >> 1)) * 64 + l) * 16 + 8 * (g & 1));
     }
     {
-      int gg = tid / BN, col = tid % BN;
-      int g = 2 * gp + gg, n = nt0 * 16 + col;
-      rsw = (g < a.G && n < a.N) ? f16_to_f32(sw[(size_t)g * a.N + n]) : 0.0f;
+      const int mi = (tid >> 4) & 7, row = tid & 15;
+      const int mt = min(mt0 + mi, MT - 1);
+      rsx[SL] = a.sxs[((size_t)mt * a.Gp + g) * 16 + row];
     }
-    {
-      int mi = tid >> 5, rem = tid & 31;
-      rsx = (mt0 + mi < MT) ? a.sxs[((size_t)(mt0 + mi) * a.Gp + 2 * gp) * 16 + rem] : 0.0f;
+    if (!DUMP) {
+      const int n = min(nt0 * 16 + (tid & 127), a.N - 1);
+      rsw[SL] = sw[(size_t)min(g, G - 1) * a.N + n];
     }
   };
-
-  auto store_stage = [&](int buf) {
+  auto store_stage = [&](int g, auto slotc, int buf) __attribute__((always_inline)) {
+    constexpr int SL = decltype(slotc)::value;
 #pragma unroll
-    for (int i = 0; i < A_ITERS; ++i) {
-      int c = i * 256 + tid;
-      int mi = c >> 7, rem = c & 127;
-      *reinterpret_cast<uint4 *>(&sm.a[buf][mi][rem >> 6][rem & 63][0]) = ra[i];
+    for (int i = 0; i < 2; ++i) {
+      const int c = i * 256 + tid;
+      *reinterpret_cast<v4u *>(&sm.a[buf][c >> 6][c & 63][0]) = ra[SL][i];
     }
 #pragma unroll
-    for (int i = 0; i < B_ITERS; ++i) {
-      int c = i * 256 + tid;
-      int ni = c >> 6, l = c & 63;
-      uint4 v = rb[i];
-      uint4 g0 = make_uint4(v.x & kNibMask, (v.x << 4) & kNibMask, v.y & kNibMask,
-                            (v.y << 4) & kNibMask);
-      uint4 g1 = make_uint4(v.z & kNibMask, (v.z << 4) & kNibMask, v.w & kNibMask,
-                            (v.w << 4) & kNibMask);
-      *reinterpret_cast<uint4 *>(&sm.b[buf][0][ni][l][0]) = g0;
-      *reinterpret_cast<uint4 *>(&sm.b[buf][1][ni][l][0]) = g1;
+    for (int i = 0; i < 2; ++i) {
+      const int c = i * 256 + tid;
+      const v2u v = rb[SL][i];
+      *reinterpret_cast<v4u *>(&sm.b[buf][c >> 6][c & 63][0]) =
+          (v4u){v.x & kNibMask, (v.x << 4) & kNibMask, v.y & kNibMask, (v.y << 4) & kNibMask};
     }
-    {
-      int gg = tid / BN, col = tid % BN;
-      sm.sw[buf][gg][col] = make_float2(rsw, -kMagic * rsw);
-    }
-    {
-      int mi = tid >> 5, rem = tid & 31;
-      sm.sx[buf][mi][rem >> 4][rem & 15] = rsx;
+    if (wave < 2) {
+      const int mi = tid >> 4, row = tid & 15;
+      sm.sx[buf][mi][row] = (mt0 + mi < MT) ? rsx[SL] : 0.0f;
+    } else if (!DUMP) {
+      const int col = tid - 128, n = nt0 * 16 + col;
+      const float sv = (g < G && n < a.N) ? f16_to_f32((uint16_t)rsw[SL]) : 0.0f;
+      sm.sw[buf][col] = make_float2(sv, -kMagic * sv);
     }
   };
 
@@ -132,127 +195,213 @@ __global__ __launch_bounds__(256, 2) void k_gemm_tiled(GemmArgs a) {
   const v4i magic = {kMagicBits, kMagicBits, kMagicBits, kMagicBits};
   const int rowq = 4 * (lane >> 4);   // first of the 4 rows this lane holds
   const int colq = lane & 15;
+  const int GS = a.Gp;                // stages: every (padded) group
 
-  load_stage(0);
-  store_stage(0);
+  // ---- epilogue operands: loads issued first, so that their latency
+  // overlaps the first stages' loads; parked in LDS below ----
+  constexpr int EU = RPT * BM / 256;  // (rank column, row) pairs per thread
+  float eu[EU > 0 ? EU : 1][kMaxUSlices], el2[EU > 0 ? EU : 1], ebias = 0.0f;
+  if (!DUMP) {
+    const uint16_t *L2 = a.L2 + (size_t)proj * a.r * a.N;
+#pragma unroll
+    for (int e = 0; e < EU; ++e) {
+      const int idx = e * 256 + tid, c = idx / BM, rr = idx % BM;
+      const int cc = min(c, a.r - 1);
+      const int m = min(mt0 * 16 + rr, a.Mpad - 1);
+#pragma unroll
+      for (int sl = 0; sl < kMaxUSlices; ++sl)
+        eu[e][sl] = a.uw[((size_t)min(sl, a.u_slices - 1) * a.ucols + (size_t)proj * a.r + cc) * a.Mpad + m];
+      el2[e] = bf16_to_f32(L2[(size_t)cc * a.N + min(nt0 * 16 + rr, a.N - 1)]);
+    }
+    if (a.bias) ebias = bf16_to_f32(a.bias[(size_t)proj * a.N + min(nt0 * 16 + (tid & (BN - 1)), a.N - 1)]);
+  }
+
+  load_stage(0, int_c<0>{});
+  load_stage(1, int_c<1>{});          // Gp >= 2
+  if (!DUMP) {
+#pragma unroll
+    for (int e = 0; e < EU; ++e) {
+      const int idx = e * 256 + tid, c = idx / BM, rr = idx % BM;
+      float u = 0.0f;
+#pragma unroll
+      for (int sl = 0; sl < kMaxUSlices; ++sl) u += sl < a.u_slices ? eu[e][sl] : 0.0f;
+      const bool live = c < a.r;
+      if constexpr (RPT > 0) {
+        smem.ep.u[c][rr] = (live && mt0 * 16 + rr < a.M) ? u : 0.0f;
+        smem.ep.l2[c][rr] = (live && nt0 * 16 + rr < a.N) ? el2[e] : 0.0f;
+      }
+    }
+    if (tid < BN) smem.ep.bias[tid] = (nt0 * 16 + tid < a.N) ? ebias : 0.0f;
+  }
+  store_stage(0, int_c<0>{}, 0);
   __syncthreads();
 
-  for (int gp = 0; gp < GP; ++gp) {
-    const int buf = gp & 1;
-    if (gp + 1 < GP) load_stage(gp + 1);
+  auto stage = [&](int g, auto slotc) __attribute__((always_inline)) {
+    constexpr int SL = decltype(slotc)::value;  // == g & 1 == LDS buffer
+    load_stage(g + 2, slotc);         // past the end: a clamped, unused reload
 
+    // ---- TM row tiles, software-pipelined ----
+    v4i bv[TN];
+    float2 swv[TN];
+    v4i d[TM][TN];
+    float4 sxv[TM];
+    v4i av[TM];
 #pragma unroll
-    for (int gg = 0; gg < 2; ++gg) {
-      v4i av[TM], bv[TN];
-      float4 sxv[TM];
-      float2 swv[TN];
+    for (int j = 0; j < TN; ++j) {
+      bv[j] = *reinterpret_cast<const v4i *>(&sm.b[SL][wn * TN + j][lane][0]);
+      swv[j] = sm.sw[SL][(wn * TN + j) * 16 + colq];
+    }
+    auto read_a = [&](int i) __attribute__((always_inline)) {
+      av[i] = *reinterpret_cast<const v4i *>(&sm.a[SL][wm * TM + i][lane][0]);
+      sxv[i] = *reinterpret_cast<const float4 *>(&sm.sx[SL][wm * TM + i][rowq]);
+    };
+    read_a(0);
 #pragma unroll
-      for (int i = 0; i < TM; ++i) {
-        av[i] = *reinterpret_cast<const v4i *>(&sm.a[buf][wm * TM + i][gg][lane][0]);
-        sxv[i] = *reinterpret_cast<const float4 *>(&sm.sx[buf][wm * TM + i][gg][rowq]);
+    for (int s = 0; s <= TM; ++s) {
+      if (s < TM) {
+        pin(av[s]);
+        if (s + 1 < TM) read_a(s + 1);
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+          d[s][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(av[s], bv[j], magic, 0, 0, 0);
       }
+      if (s == 0) continue;
+      const int ip = s - 1;                 // rescale the previous row tile
 #pragma unroll
       for (int j = 0; j < TN; ++j) {
-        bv[j] = *reinterpret_cast<const v4i *>(&sm.b[buf][gg][wn * TN + j][lane][0]);
-        swv[j] = sm.sw[buf][gg][(wn * TN + j) * 16 + colq];
-      }
+        if (DUMP) {
+          const int n = (nt0 + wn * TN + j) * 16 + colq;
 #pragma unroll
-      for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int j = 0; j < TN; ++j) {
-          v4i d = __builtin_amdgcn_mfma_i32_16x16x64_i8(av[i], bv[j], magic, 0, 0, 0);
-          if (DUMP) {
-            const int g = 2 * gp + gg;
-            const int n = (nt0 + wn * TN + j) * 16 + colq;
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-              const int m = (mt0 + wm * TM + i) * 16 + rowq + q;
-              if (g < a.G && m >= a.m0 && m < a.m0 + a.mc && n >= a.n0 && n < a.n0 + a.nc)
-                a.P[((size_t)(m - a.m0) * a.nc + (n - a.n0)) * a.G + g] = (d[q] - kMagicBits) >> 4;
-            }
-          } else {
-            const float s0 = sxv[i].x, s1 = sxv[i].y, s2 = sxv[i].z, s3 = sxv[i].w;
-            float u;
-            u = __builtin_fmaf(__int_as_float(d[0]), swv[j].x, swv[j].y);
-            acc[i][j][0] = __builtin_fmaf(u, s0, acc[i][j][0]);
-            u = __builtin_fmaf(__int_as_float(d[1]), swv[j].x, swv[j].y);
-            acc[i][j][1] = __builtin_fmaf(u, s1, acc[i][j][1]);
-            u = __builtin_fmaf(__int_as_float(d[2]), swv[j].x, swv[j].y);
-            acc[i][j][2] = __builtin_fmaf(u, s2, acc[i][j][2]);
-            u = __builtin_fmaf(__int_as_float(d[3]), swv[j].x, swv[j].y);
-            acc[i][j][3] = __builtin_fmaf(u, s3, acc[i][j][3]);
+          for (int q = 0; q < 4; ++q) {
+            const int m = (mt0 + wm * TM + ip) * 16 + rowq + q;
+            if (g < G && m >= a.m0 && m < a.m0 + a.mc && n >= a.n0 && n < a.n0 + a.nc)
+              a.P[((size_t)(m - a.m0) * a.nc + (n - a.n0)) * G + g] = (d[ip][j][q] - kMagicBits) >> 4;
           }
+        } else {
+          const float2 s2 = swv[j];
+          float u;
+          u = __builtin_fmaf(__int_as_float(d[ip][j][0]), s2.x, s2.y);
+          acc[ip][j][0] = __builtin_fmaf(u, sxv[ip].x, acc[ip][j][0]);
+          u = __builtin_fmaf(__int_as_float(d[ip][j][1]), s2.x, s2.y);
+          acc[ip][j][1] = __builtin_fmaf(u, sxv[ip].y, acc[ip][j][1]);
+          u = __builtin_fmaf(__int_as_float(d[ip][j][2]), s2.x, s2.y);
+          acc[ip][j][2] = __builtin_fmaf(u, sxv[ip].z, acc[ip][j][2]);
+          u = __builtin_fmaf(__int_as_float(d[ip][j][3]), s2.x, s2.y);
+          acc[ip][j][3] = __builtin_fmaf(u, sxv[ip].w, acc[ip][j][3]);
         }
+      }
+      if (!DUMP) {
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) pin(acc[ip][j][q]);
+      }
     }
 
-    if (gp + 1 < GP) store_stage(buf ^ 1);
+    // stage g+1 (loaded one stage ago) into the other LDS buffer
+    if (g + 1 < GS) store_stage(g + 1, int_c<SL ^ 1>{}, SL ^ 1);
     __syncthreads();
+  };
+  for (int g = 0; g < GS; g += 2) {   // GS is even
+    stage(g, int_c<0>{});
+    stage(g + 1, int_c<1>{});
   }
 
   if (DUMP) return;
 
   // ---- epilogue: Y = acc + U * L2 + bias ----
-  const uint16_t *L2 = a.L2 ? a.L2 + (size_t)proj * a.r * a.N : nullptr;
-  const uint16_t *bias = a.bias ? a.bias + (size_t)proj * a.N : nullptr;
+  // U * L2 as fp32 MFMAs (16x16x4: one per 16x16 tile and 4 rank columns);
+  // the stage loop ended with a barrier, so its LDS is free for the output
+  // transpose.
+  if constexpr (RPT > 0) {
+#pragma unroll
+  for (int cc = 0; cc < RPT / 4; ++cc) {
+    float ua[TM], lb[TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i) ua[i] = smem.ep.u[cc * 4 + (lane >> 4)][(wm * TM + i) * 16 + colq];
+#pragma unroll
+    for (int j = 0; j < TN; ++j) lb[j] = smem.ep.l2[cc * 4 + (lane >> 4)][(wn * TN + j) * 16 + colq];
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        v4f c4 = {acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]};
+        c4 = __builtin_amdgcn_mfma_f32_16x16x4f32(ua[i], lb[j], c4, 0, 0, 0);
+        acc[i][j][0] = c4[0]; acc[i][j][1] = c4[1]; acc[i][j][2] = c4[2]; acc[i][j][3] = c4[3];
+      }
+  }
+  }
+  float bj[TN];
+#pragma unroll
+  for (int j = 0; j < TN; ++j) bj[j] = smem.ep.bias[(wn * TN + j) * 16 + colq];
+
+  // output: per row tile, transpose the wave's 16 x 64 values through a
+  // wave-private LDS region and store 16 bytes per lane
+  char *tbuf = reinterpret_cast<char *>(&sm) + wave * 4096;
+  const int ybytes = a.y_bf16 ? 2 : 4;
+  const int per16 = 16 / ybytes;                      // values per 16-byte chunk
+  const bool vec_ok = (a.N % per16) == 0;
+  const int ncol0 = (nt0 + wn * TN) * 16;             // first column of the wave
 #pragma unroll
   for (int i = 0; i < TM; ++i) {
-    const int mrow = (mt0 + wm * TM + i) * 16 + rowq;  // rows mrow .. mrow+3
-    if (mrow >= a.M) continue;
-    float add[TN][4];
+    const int mrow0 = (mt0 + wm * TM + i) * 16;
 #pragma unroll
     for (int j = 0; j < TN; ++j)
 #pragma unroll
-      for (int q = 0; q < 4; ++q) add[j][q] = 0.0f;
-    for (int c = 0; c < a.r; ++c) {
-      float4 u = make_float4(0.f, 0.f, 0.f, 0.f);
-      for (int sl = 0; sl < a.u_slices; ++sl) {
-        const float4 v = *reinterpret_cast<const float4 *>(
-            a.uw + ((size_t)sl * a.ucols + (size_t)proj * a.r + c) * a.Mpad + mrow);
-        u.x += v.x; u.y += v.y; u.z += v.z; u.w += v.w;
-      }
-#pragma unroll
-      for (int j = 0; j < TN; ++j) {
-        const int n = (nt0 + wn * TN + j) * 16 + colq;
-        const float l2 = n < a.N ? bf16_to_f32(L2[(size_t)c * a.N + n]) : 0.0f;
-        add[j][0] = __builtin_fmaf(u.x, l2, add[j][0]);
-        add[j][1] = __builtin_fmaf(u.y, l2, add[j][1]);
-        add[j][2] = __builtin_fmaf(u.z, l2, add[j][2]);
-        add[j][3] = __builtin_fmaf(u.w, l2, add[j][3]);
-      }
-    }
-#pragma unroll
-    for (int j = 0; j < TN; ++j) {
-      const int n = (nt0 + wn * TN + j) * 16 + colq;
-      if (n >= a.N) continue;
-      const float bb = bias ? bf16_to_f32(bias[n]) : 0.0f;
-#pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const int m = mrow + q;
-        if (m >= a.M) break;
-        const float y = acc[i][j][q] + add[j][q] + bb;
-        const size_t off = ((size_t)proj * a.M + m) * a.N + n;
+        const float y = acc[i][j][q] + bj[j];
+        const int off = (rowq + q) * 64 + j * 16 + colq;  // [row][col] in the 16 x 64 tile
         if (a.y_bf16)
-          reinterpret_cast<uint16_t *>(a.Y)[off] = f32_to_bf16(y);
+          reinterpret_cast<uint16_t *>(tbuf)[off] = f32_to_bf16(y);
         else
-          reinterpret_cast<float *>(a.Y)[off] = y;
+          reinterpret_cast<float *>(tbuf)[off] = y;
+      }
+    // 16 rows x 64 columns; chunk k of the tile = (row k / (64/per16), chunk k % (64/per16))
+    const int cpr = 64 / per16;                         // chunks per row
+    for (int k = lane; k < 16 * cpr; k += 64) {
+      const int row = k / cpr, ch = k % cpr;
+      const int m = mrow0 + row, n = ncol0 + ch * per16;
+      if (m >= a.M) continue;
+      const v4u v = *reinterpret_cast<const v4u *>(tbuf + (row * 64 + ch * per16) * ybytes);
+      char *dst = reinterpret_cast<char *>(a.Y) + (((size_t)proj * a.M + m) * a.N + n) * ybytes;
+      if (vec_ok && n + per16 <= a.N) {
+        *reinterpret_cast<v4u *>(dst) = v;
+      } else if (a.y_bf16) {  // ragged N: element stores
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          if (n + e < a.N)
+            reinterpret_cast<uint16_t *>(dst)[e] = (uint16_t)(v[e >> 1] >> (16 * (e & 1)));
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (n + e < a.N) reinterpret_cast<uint32_t *>(dst)[e] = v[e];
       }
     }
   }
 }
 
+template <int RPT>
+hipError_t launch_rpt(const GemmArgs &a, int batch, int nblk, int mblk, hipStream_t s) {
+  hipLaunchKernelGGL((k_gemm_tiled<false, RPT>), dim3((unsigned)(nblk * mblk), (unsigned)batch),
+                     dim3(256), 0, s, a, nblk, mblk);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_gemm_tiled(const GemmArgs &a, int batch, bool dump, hipStream_t s) {
-  constexpr int BM = 128, BN = 128;
+  const int nblk = ceil_div(a.N, BN), mblk = ceil_div(a.M, BM);
   if (dump) {
-    // blocks up to the last one touching the window; the others exit at once
-    dim3 grid((unsigned)((a.n0 + a.nc - 1) / BN + 1), (unsigned)((a.m0 + a.mc - 1) / BM + 1), 1u);
-    hipLaunchKernelGGL((k_gemm_tiled<BM, BN, true>), grid, dim3(256), 0, s, a);
+    // every tile of one projection; blocks outside the window exit at once
+    hipLaunchKernelGGL((k_gemm_tiled<true, 0>), dim3((unsigned)(nblk * mblk), 1u), dim3(256), 0, s,
+                       a, nblk, mblk);
     return hipGetLastError();
   }
-  dim3 grid((unsigned)ceil_div(a.N, BN), (unsigned)ceil_div(a.M, BM), (unsigned)batch);
-  hipLaunchKernelGGL((k_gemm_tiled<BM, BN, false>), grid, dim3(256), 0, s, a);
-  return hipGetLastError();
+  if (a.r == 0) return launch_rpt<0>(a, batch, nblk, mblk, s);
+  if (a.r <= 4) return launch_rpt<4>(a, batch, nblk, mblk, s);
+  if (a.r <= 8) return launch_rpt<8>(a, batch, nblk, mblk, s);
+  if (a.r <= 16) return launch_rpt<16>(a, batch, nblk, mblk, s);
+  return launch_rpt<32>(a, batch, nblk, mblk, s);
 }
 
 }  // namespace hsq

@@ -15,6 +15,7 @@ constexpr int kTile = 16;        // rows / columns per MFMA tile (16x16x64 i8)
 constexpr int kMaxRank = 32;     // largest rank r of the high-precision branch
 constexpr int kMaxBatch = 16;    // projections sharing one input
 constexpr int kRankBlock = 32;   // rank columns one quantization pass accumulates
+constexpr int kMaxUSlices = 4;   // K-slices of U the contraction kernels sum
 
 // Bits of the float 1.5 * 2^23: adding an integer n (|n| < 2^22) to these
 // bits gives the float 1.5 * 2^23 + n exactly.  The contraction kernels feed
@@ -124,6 +125,8 @@ hipError_t launch_gemm_skinny(const GemmArgs &a, int batch, bool dump, hipStream
 namespace hsq {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
+typedef unsigned v4u __attribute__((ext_vector_type(4)));
+typedef unsigned v2u __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ float bf16_to_f32(uint32_t b) {
   return __uint_as_float(b << 16);
