@@ -105,6 +105,7 @@ int hsq_unpack_weights(const uint8_t *packed, int K, int N, int8_t *codes, void 
  *               nibble and code 2j+1 in its high nibble, two's complement
  *   sx     out: M x K/64 fp16 scales
  *   U      out: M x r fp32 (may be NULL when r == 0)
+ * K <= 24576 for this entry point (HSQ_E_INVAL beyond).
  * Errors: HSQ_E_INVAL, HSQ_E_SHAPE, HSQ_E_ALIGN, HSQ_E_HIP. */
 int hsq_quantize_act(const uint16_t *X, int M, int K, const uint16_t *lambda,
                      const uint16_t *L1, int r, uint8_t *qx, uint16_t *sx, float *U,

@@ -140,6 +140,7 @@ def test_quantize_and_pack_reject_before_launch():
     assert q(A, 4, 64, A, A, 4, A, A, None, None) == hsq.E_INVAL
     assert q(A, 4, 64, A + 2, A, 4, A, A, A, None) == hsq.E_ALIGN
     assert q(A, 0, 64, A, A, 4, A, A, A, None) == hsq.E_INVAL
+    assert q(A, 4, 24576 + 64, A, A, 4, A, A, A, None) == hsq.E_INVAL
     p = lib.hsq_pack_weights
     assert p(None, 64, 16, A, A, None) == hsq.E_INVAL
     assert p(A, 64, 16, A, None, None) == hsq.E_INVAL

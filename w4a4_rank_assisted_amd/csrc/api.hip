@@ -15,17 +15,9 @@ WsLayout plan_workspace(int M, int K, int r, int batch) {
   L.G = K / kGroup;
   L.Gp = padded_groups(K);
   L.Mpad = L.MT * kTile;
-  // Quantization pass: one workgroup per 16 rows and K-slice.  Split K until
-  // about four workgroups per CU exist (small token counts need the split to
-  // spread the pass over the chip); slices are whole 512-channel chunks.
-  const int kpad = L.Gp * kGroup;
-  const int chunks = ceil_div(kpad, 512);
-  int s = ceil_div(1024, L.MT);
-  if (s > kMaxUSlices) s = kMaxUSlices;
-  if (s > chunks) s = chunks;
-  if (s < 1) s = 1;
-  L.kslice = ceil_div(chunks, s) * 512;
-  L.u_slices = ceil_div(kpad, L.kslice);
+  // Quantization pass: K is split into slices of up to 64 groups (at most
+  // kMaxUSlices); their U partials are summed by the contraction kernels.
+  L.u_slices = quant_slices(K);
   size_t off = 0;
   L.qa_off = off;
   off = align_up(off + (size_t)L.MT * L.Gp * 1024, 256);
@@ -99,7 +91,6 @@ int quant_stage(const uint16_t *X, int M, int K, int batch, const uint16_t *lamb
   q.L1 = r > 0 ? L1 : nullptr;
   q.M = M; q.K = K; q.G = L.G;
   q.r = r; q.batch = batch;
-  q.kslice = L.kslice;
   q.kend = L.Gp * kGroup;
   q.qa = (int8_t *)(ws + L.qa_off);
   q.sxs = (float *)(ws + L.sxs_off);
@@ -194,6 +185,7 @@ int hsq_quantize_act(const uint16_t *X, int M, int K, const uint16_t *lambda,
                      void *stream) {
   int st = check_sizes(M, K, 1, r, 1);
   if (st != HSQ_OK) return st;
+  if (K > kQuantActMaxK) return HSQ_E_INVAL;
   if (!X || !lambda || !qx || !sx || (r > 0 && (!L1 || !U))) return HSQ_E_INVAL;
   const void *ptrs[] = {X, lambda, L1, qx, sx, U};
   for (const void *p : ptrs)
@@ -205,7 +197,6 @@ int hsq_quantize_act(const uint16_t *X, int M, int K, const uint16_t *lambda,
   q.M = M; q.K = K; q.G = K / kGroup;
   q.r = r; q.batch = 1;
   q.kend = K;
-  q.kslice = ceil_div(K, 512) * 512;  // one slice: U is final
   q.qx = qx; q.sx = sx; q.u_pub = r > 0 ? U : nullptr;
   q.ucols = r;
   return hip_status(launch_quant(q, 1, (hipStream_t)stream));

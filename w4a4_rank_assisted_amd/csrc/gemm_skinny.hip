@@ -18,11 +18,15 @@ namespace hsq {
 namespace {
 
 constexpr uint32_t kNibMask = 0xF0F0F0F0u;
-constexpr int kDepth = 4;  // group pairs of weights in flight per lane
 
 template <int MT, bool DUMP>
-__global__ __launch_bounds__(1024) void k_gemm_skinny(GemmArgs a, int W) {
-  extern __shared__ float red[];  // [W][MT][4][64]
+__global__ __launch_bounds__(512) void k_gemm_skinny(GemmArgs a, int W) {
+  // dynamic LDS: partial tiles [W][MT][4][64], then U [r][16*MT] (slices
+  // summed), L2 [r][16], bias [16]
+  extern __shared__ float red[];
+  float *eu = red + W * MT * 4 * 64;
+  float *el2 = eu + a.r * MT * 16;
+  float *eb = el2 + a.r * 16;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int nt = blockIdx.x + (DUMP ? a.n0 / 16 : 0);
   const int proj = blockIdx.y;
@@ -37,36 +41,82 @@ __global__ __launch_bounds__(1024) void k_gemm_skinny(GemmArgs a, int W) {
   const uint16_t *swp = a.sw ? a.sw + (size_t)proj * a.G * a.N + (ncol ? n : 0) : nullptr;
   const v4i magic = {kMagicBits, kMagicBits, kMagicBits, kMagicBits};
 
+  // epilogue operands into LDS first (their loads overlap the weight stream;
+  // the barrier before the epilogue orders them)
+  if (!DUMP) {
+    const int nthr = W * 64;
+    for (int p = tid; p < a.r * MT * 16; p += nthr) {
+      const int c = p / (MT * 16), row = p % (MT * 16);
+      float u = 0.0f;
+#pragma unroll
+      for (int sl = 0; sl < kMaxUSlices; ++sl) {
+        const float v = a.uw[((size_t)min(sl, a.u_slices - 1) * a.ucols + (size_t)proj * a.r + c) * a.Mpad + row];
+        u += sl < a.u_slices ? v : 0.0f;
+      }
+      eu[c * MT * 16 + row] = u;
+    }
+    for (int p = tid; p < a.r * 16; p += nthr) {
+      const int c = p / 16, col = p % 16;
+      el2[p] = bf16_to_f32(a.L2[((size_t)proj * a.r + c) * a.N + min(nt * 16 + col, a.N - 1)]);
+    }
+    if (tid < 16)
+      eb[tid] = a.bias ? bf16_to_f32(a.bias[(size_t)proj * a.N + min(nt * 16 + tid, a.N - 1)]) : 0.0f;
+  }
+
   float acc[MT][4];
 #pragma unroll
   for (int i = 0; i < MT; ++i)
 #pragma unroll
     for (int q = 0; q < 4; ++q) acc[i][q] = 0.0f;
 
-  uint4 wbuf[kDepth];
-  uint32_t sbuf[kDepth];
-  auto fetch = [&](int gp, uint4 &wv, uint32_t &sv) {
-    wv = *reinterpret_cast<const uint4 *>(wp + (size_t)gp * 1024);
-    sv = 0;
+  // prefetch ring: D group pairs of weights, weight scales, activation
+  // codes and activation scales in flight per lane (D = 4 / MT registers
+  // budget); every operand of a group pair is loaded D pairs ahead
+  constexpr int D = MT == 1 ? 4 : (MT == 2 ? 2 : 1);
+  v4u wbuf[D];
+  uint32_t sbuf[D];
+  v4i abuf[D][MT][2];
+  v4f xbuf[D][MT][2];
+  auto fetch = [&](int gp, int u) __attribute__((always_inline)) {
+    wbuf[u] = *reinterpret_cast<const v4u *>(wp + (size_t)gp * 1024);
+    sbuf[u] = 0;
     if (!DUMP && ncol) {
       const int g = 2 * gp;
-      uint32_t lo = swp[(size_t)g * a.N];
-      uint32_t hi = (g + 1 < a.G) ? swp[(size_t)(g + 1) * a.N] : 0u;
-      sv = lo | (hi << 16);
+      const uint32_t lo = swp[(size_t)g * a.N];
+      const uint32_t hi = (g + 1 < a.G) ? swp[(size_t)(g + 1) * a.N] : 0u;
+      sbuf[u] = lo | (hi << 16);
     }
+#pragma unroll
+    for (int i = 0; i < MT; ++i)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int g = 2 * gp + h;
+        abuf[u][i][h] = *reinterpret_cast<const v4i *>(a.qa + (((size_t)i * a.Gp + g) * 64 + lane) * 16);
+        if (!DUMP)
+          xbuf[u][i][h] = *reinterpret_cast<const v4f *>(a.sxs + ((size_t)i * a.Gp + g) * 16 + rowq);
+      }
   };
 #pragma unroll
-  for (int u = 0; u < kDepth; ++u)
-    if (gp0 + u < gp1) fetch(gp0 + u, wbuf[u], sbuf[u]);
+  for (int u = 0; u < D; ++u)
+    if (gp0 + u < gp1) fetch(gp0 + u, u);
 
-  for (int base = gp0; base < gp1; base += kDepth) {
+  for (int base = gp0; base < gp1; base += D) {
 #pragma unroll
-    for (int u = 0; u < kDepth; ++u) {
+    for (int u = 0; u < D; ++u) {
       const int gp = base + u;
       if (gp >= gp1) break;
-      const uint4 wv = wbuf[u];
+      const v4u wv = wbuf[u];
       const uint32_t sv = sbuf[u];
-      if (gp + kDepth < gp1) fetch(gp + kDepth, wbuf[u], sbuf[u]);
+      v4i av[MT][2];
+      v4f sx[MT][2];
+#pragma unroll
+      for (int i = 0; i < MT; ++i)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          av[i][h] = abuf[u][i][h];
+          sx[i][h] = xbuf[u][i][h];
+        }
+      if (gp + D < gp1) fetch(gp + D, u);
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         const int g = 2 * gp + h;
@@ -77,9 +127,7 @@ __global__ __launch_bounds__(1024) void k_gemm_skinny(GemmArgs a, int W) {
         const float nsw = -kMagic * swf;
 #pragma unroll
         for (int i = 0; i < MT; ++i) {
-          const v4i av = *reinterpret_cast<const v4i *>(
-              a.qa + (((size_t)i * a.Gp + g) * 64 + lane) * 16);
-          const v4i d = __builtin_amdgcn_mfma_i32_16x16x64_i8(av, b, magic, 0, 0, 0);
+          const v4i d = __builtin_amdgcn_mfma_i32_16x16x64_i8(av[i][h], b, magic, 0, 0, 0);
           if (DUMP) {
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
@@ -88,17 +136,15 @@ __global__ __launch_bounds__(1024) void k_gemm_skinny(GemmArgs a, int W) {
                 a.P[((size_t)(m - a.m0) * a.nc + (n - a.n0)) * a.G + g] = (d[q] - kMagicBits) >> 4;
             }
           } else {
-            const float4 sx = *reinterpret_cast<const float4 *>(
-                a.sxs + ((size_t)i * a.Gp + g) * 16 + rowq);
             float t;
             t = __builtin_fmaf(__int_as_float(d[0]), swf, nsw);
-            acc[i][0] = __builtin_fmaf(t, sx.x, acc[i][0]);
+            acc[i][0] = __builtin_fmaf(t, sx[i][h][0], acc[i][0]);
             t = __builtin_fmaf(__int_as_float(d[1]), swf, nsw);
-            acc[i][1] = __builtin_fmaf(t, sx.y, acc[i][1]);
+            acc[i][1] = __builtin_fmaf(t, sx[i][h][1], acc[i][1]);
             t = __builtin_fmaf(__int_as_float(d[2]), swf, nsw);
-            acc[i][2] = __builtin_fmaf(t, sx.z, acc[i][2]);
+            acc[i][2] = __builtin_fmaf(t, sx[i][h][2], acc[i][2]);
             t = __builtin_fmaf(__int_as_float(d[3]), swf, nsw);
-            acc[i][3] = __builtin_fmaf(t, sx.w, acc[i][3]);
+            acc[i][3] = __builtin_fmaf(t, sx[i][h][3], acc[i][3]);
           }
         }
       }
@@ -113,8 +159,6 @@ __global__ __launch_bounds__(1024) void k_gemm_skinny(GemmArgs a, int W) {
     for (int q = 0; q < 4; ++q) red[((wave * MT + i) * 4 + q) * 64 + lane] = acc[i][q];
   __syncthreads();
 
-  const uint16_t *L2 = a.L2 ? a.L2 + (size_t)proj * a.r * a.N : nullptr;
-  const uint16_t *bias = a.bias ? a.bias + (size_t)proj * a.N : nullptr;
   for (int i = wave; i < MT; i += W) {
     float y[4] = {0.f, 0.f, 0.f, 0.f};
     for (int v = 0; v < W; ++v)
@@ -123,19 +167,11 @@ __global__ __launch_bounds__(1024) void k_gemm_skinny(GemmArgs a, int W) {
     const int mrow = i * 16 + rowq;
     if (!ncol || mrow >= a.M) continue;
     for (int c = 0; c < a.r; ++c) {
-      float4 u = make_float4(0.f, 0.f, 0.f, 0.f);
-      for (int sl = 0; sl < a.u_slices; ++sl) {
-        const float4 v = *reinterpret_cast<const float4 *>(
-            a.uw + ((size_t)sl * a.ucols + (size_t)proj * a.r + c) * a.Mpad + mrow);
-        u.x += v.x; u.y += v.y; u.z += v.z; u.w += v.w;
-      }
-      const float l2 = bf16_to_f32(L2[(size_t)c * a.N + n]);
-      y[0] = __builtin_fmaf(u.x, l2, y[0]);
-      y[1] = __builtin_fmaf(u.y, l2, y[1]);
-      y[2] = __builtin_fmaf(u.z, l2, y[2]);
-      y[3] = __builtin_fmaf(u.w, l2, y[3]);
+      const float l2 = el2[c * 16 + colq];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) y[q] = __builtin_fmaf(eu[c * MT * 16 + mrow + q], l2, y[q]);
     }
-    const float bb = bias ? bf16_to_f32(bias[n]) : 0.0f;
+    const float bb = eb[colq];
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int m = mrow + q;
@@ -154,10 +190,10 @@ hipError_t launch_mt(const GemmArgs &a, int batch, bool dump, hipStream_t s) {
   const int NT = ceil_div(a.N, kTile), GP = a.Gp / 2;
   // waves per workgroup: enough to put ~4 waves on every SIMD of the chip
   int W = ceil_div(4096, NT * batch);
-  if (W > 16) W = 16;
+  if (W > 8) W = 8;
   if (W > GP) W = GP;
   if (W < 1) W = 1;
-  const size_t lds = (size_t)W * MT * 4 * 64 * sizeof(float);
+  const size_t lds = ((size_t)W * MT * 4 * 64 + (size_t)a.r * MT * 16 + (size_t)a.r * 16 + 16) * sizeof(float);
   if (dump) {
     const int nt0 = a.n0 / 16, nt1 = (a.n0 + a.nc - 1) / 16;
     hipLaunchKernelGGL((k_gemm_skinny<MT, true>), dim3((unsigned)(nt1 - nt0 + 1), 1u),

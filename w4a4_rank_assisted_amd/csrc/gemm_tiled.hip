@@ -98,8 +98,6 @@ __device__ __forceinline__ void tile_of(int bid, int nblk, int mblk, int &mb, in
   nb = w / gsz;
 }
 
-typedef float v4f __attribute__((ext_vector_type(4)));
-
 template <bool DUMP, int RPT>
 __global__ __launch_bounds__(256, 2) void k_gemm_tiled(GemmArgs a, int nblk, int mblk) {
   __shared__ Smem<RPT> smem;

@@ -16,6 +16,7 @@ constexpr int kMaxRank = 32;     // largest rank r of the high-precision branch
 constexpr int kMaxBatch = 16;    // projections sharing one input
 constexpr int kRankBlock = 32;   // rank columns one quantization pass accumulates
 constexpr int kMaxUSlices = 4;   // K-slices of U the contraction kernels sum
+constexpr int kQuantActMaxK = 24576;  // hsq_quantize_act: 1/lambda of all K in LDS
 
 // Bits of the float 1.5 * 2^23: adding an integer n (|n| < 2^22) to these
 // bits gives the float 1.5 * 2^23 + n exactly.  The contraction kernels feed
@@ -56,8 +57,7 @@ inline size_t packed_bytes(int K, int N) {
 // ---------------------------------------------------------------------------
 struct WsLayout {
   int MT = 0, G = 0, Gp = 0, Mpad = 0;
-  int u_slices = 0;      // S_u
-  int kslice = 0;        // channels per quantization K-slice
+  int u_slices = 0;      // S_u: K-slices of the quantization pass
   size_t qa_off = 0, sxs_off = 0, uw_off = 0, total = 0;
 };
 
@@ -77,7 +77,6 @@ struct QuantArgs {
   int M, K, G;
   int r, batch;
   int c0, cb;              // rank columns [c0, c0 + cb) of the batch*r columns
-  int kslice;              // channels per blockIdx.y slice (multiple of 512)
   int kend;                // channels processed: K (public) or 64*Gp (internal)
   int write_codes;         // 0: rank pass only
   // public outputs (packed codes, fp16 scales, U as M x r)
@@ -113,6 +112,7 @@ hipError_t launch_pack(const int8_t *codes, int K, int N, uint8_t *packed, int *
                        hipStream_t s);
 hipError_t launch_unpack(const uint8_t *packed, int K, int N, int8_t *codes, hipStream_t s);
 hipError_t launch_quant(const QuantArgs &a, int slices, hipStream_t s);
+int quant_slices(int K);  // K-slices of the internal quantization pass
 hipError_t launch_gemm_tiled(const GemmArgs &a, int batch, bool dump, hipStream_t s);
 hipError_t launch_gemm_skinny(const GemmArgs &a, int batch, bool dump, hipStream_t s);
 
@@ -127,6 +127,7 @@ namespace hsq {
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef unsigned v4u __attribute__((ext_vector_type(4)));
 typedef unsigned v2u __attribute__((ext_vector_type(2)));
+typedef float v4f __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ float bf16_to_f32(uint32_t b) {
   return __uint_as_float(b << 16);
