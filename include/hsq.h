@@ -72,6 +72,11 @@ int hsq_layout_version(void);
 /* Static text for a status code (never NULL). */
 const char *hsq_status_string(int status);
 
+/* The HIP runtime's text for the error behind the last HSQ_E_HIP returned
+ * on the calling host thread ("no HIP error" if there was none).  Static
+ * storage, never NULL. */
+const char *hsq_last_hip_error(void);
+
 /* Bytes of one packed residual (K x N int4 codes) as hsq_pack_weights
  * writes it: N rounded up to 16 times K rounded up to 128, over 2.
  * Returns 0 if K or N is invalid. */
@@ -105,7 +110,7 @@ int hsq_unpack_weights(const uint8_t *packed, int K, int N, int8_t *codes, void 
  *               nibble and code 2j+1 in its high nibble, two's complement
  *   sx     out: M x K/64 fp16 scales
  *   U      out: M x r fp32 (may be NULL when r == 0)
- * K <= 24576 for this entry point (HSQ_E_INVAL beyond).
+ * K <= 12288 for this entry point (HSQ_E_INVAL beyond).
  * Errors: HSQ_E_INVAL, HSQ_E_SHAPE, HSQ_E_ALIGN, HSQ_E_HIP. */
 int hsq_quantize_act(const uint16_t *X, int M, int K, const uint16_t *lambda,
                      const uint16_t *L1, int r, uint8_t *qx, uint16_t *sx, float *U,

@@ -140,7 +140,7 @@ def test_quantize_and_pack_reject_before_launch():
     assert q(A, 4, 64, A, A, 4, A, A, None, None) == hsq.E_INVAL
     assert q(A, 4, 64, A + 2, A, 4, A, A, A, None) == hsq.E_ALIGN
     assert q(A, 0, 64, A, A, 4, A, A, A, None) == hsq.E_INVAL
-    assert q(A, 4, 24576 + 64, A, A, 4, A, A, A, None) == hsq.E_INVAL
+    assert q(A, 4, 12288 + 64, A, A, 4, A, A, A, None) == hsq.E_INVAL
     p = lib.hsq_pack_weights
     assert p(None, 64, 16, A, A, None) == hsq.E_INVAL
     assert p(A, 64, 16, A, None, None) == hsq.E_INVAL
@@ -149,3 +149,15 @@ def test_quantize_and_pack_reject_before_launch():
     u = lib.hsq_unpack_weights
     assert u(A, 64, 0, A, None) == hsq.E_INVAL
     assert u(A, 64, 16, A + 3, None) == hsq.E_ALIGN
+
+
+def test_last_hip_error_is_static_text():
+    # no HIP call has failed on this thread (none reach the runtime here)
+    assert lib.hsq_last_hip_error() == b"no HIP error"
+
+
+def test_one_hip_runtime_in_the_process():
+    # the binding loads torch before libhsq, so both use one HIP runtime
+    maps = open("/proc/self/maps").read()
+    hip = {line.split()[-1] for line in maps.splitlines() if "libamdhip64" in line}
+    assert len(hip) == 1, hip

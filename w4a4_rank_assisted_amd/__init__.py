@@ -32,6 +32,8 @@ _lib = None
 class HsqError(RuntimeError):
     def __init__(self, status: int, what: str):
         msg = _load().hsq_status_string(status).decode() if _lib is not None else str(status)
+        if status == E_HIP and _lib is not None:
+            msg += ": " + _lib.hsq_last_hip_error().decode()
         super().__init__(f"{what}: {msg} (status {status})")
         self.status = status
 
@@ -42,11 +44,17 @@ def _load():
     if _lib is None:
         if not os.path.exists(LIB_PATH):
             raise OSError(f"{LIB_PATH} is missing; build it with w4a4_rank_assisted_amd.build.build()")
+        # torch first: its HIP runtime is then the one libhsq binds to (same
+        # soname), so the device pointers and streams torch hands over belong
+        # to the runtime the kernels are launched with.  Loaded the other way
+        # round, the process would hold two HIP / HSA runtimes.
+        import torch  # noqa: F401
         lib = ctypes.CDLL(LIB_PATH)
         P, I, S = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
         sig = {
             "hsq_layout_version": ([], I),
             "hsq_status_string": ([I], ctypes.c_char_p),
+            "hsq_last_hip_error": ([], ctypes.c_char_p),
             "hsq_packed_weight_bytes": ([I, I], S),
             "hsq_pack_weights": ([P, I, I, P, P, P], I),
             "hsq_unpack_weights": ([P, I, I, P, P], I),

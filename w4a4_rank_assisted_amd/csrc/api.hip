@@ -15,9 +15,9 @@ WsLayout plan_workspace(int M, int K, int r, int batch) {
   L.G = K / kGroup;
   L.Gp = padded_groups(K);
   L.Mpad = L.MT * kTile;
-  // Quantization pass: K is split into slices of up to 64 groups (at most
-  // kMaxUSlices); their U partials are summed by the contraction kernels.
-  L.u_slices = quant_slices(K);
+  // Quantization pass: K is split into slices whose U partials are summed
+  // by the contraction kernels.
+  L.u_slices = quant_slices(M, K, r, batch);
   size_t off = 0;
   L.qa_off = off;
   off = align_up(off + (size_t)L.MT * L.Gp * 1024, 256);
@@ -46,7 +46,14 @@ int check_sizes(int M, int K, int N, int r, int batch) {
   return HSQ_OK;
 }
 
-int hip_status(hipError_t e) { return e == hipSuccess ? HSQ_OK : HSQ_E_HIP; }
+// The HIP error behind the last HSQ_E_HIP of this host thread.
+thread_local hipError_t g_last_hip_error = hipSuccess;
+
+int hip_status(hipError_t e) {
+  if (e == hipSuccess) return HSQ_OK;
+  g_last_hip_error = e;
+  return HSQ_E_HIP;
+}
 
 size_t workspace_bytes(int M, int K, int N, int r, int batch) {
   if (check_sizes(M, K, N, r, batch) != HSQ_OK) return 0;
@@ -96,7 +103,7 @@ int quant_stage(const uint16_t *X, int M, int K, int batch, const uint16_t *lamb
   q.sxs = (float *)(ws + L.sxs_off);
   q.uw = (float *)(ws + L.uw_off);
   q.Gp = L.Gp; q.Mpad = L.Mpad; q.ucols = batch * r;
-  return hip_status(launch_quant(q, L.u_slices, s));
+  return hip_status(launch_quant(q, s));
 }
 
 int contract_stage(int M, int K, int N, int batch, const uint8_t *packed_w, const uint16_t *sw,
@@ -158,6 +165,10 @@ const char *hsq_status_string(int status) {
   }
 }
 
+const char *hsq_last_hip_error(void) {
+  return g_last_hip_error == hipSuccess ? "no HIP error" : hipGetErrorString(g_last_hip_error);
+}
+
 size_t hsq_packed_weight_bytes(int K, int N) {
   if (K < kGroup || K % kGroup != 0 || N < 1 || (long long)K * N >= INT_MAX) return 0;
   return packed_bytes(K, N);
@@ -199,7 +210,7 @@ int hsq_quantize_act(const uint16_t *X, int M, int K, const uint16_t *lambda,
   q.kend = K;
   q.qx = qx; q.sx = sx; q.u_pub = r > 0 ? U : nullptr;
   q.ucols = r;
-  return hip_status(launch_quant(q, 1, (hipStream_t)stream));
+  return hip_status(launch_quant(q, (hipStream_t)stream));
 }
 
 size_t hsq_workspace_bytes(int M, int K, int N, int r, int batch) {

@@ -53,6 +53,8 @@ __global__ __launch_bounds__(512) void k_gemm_skinny(GemmArgs a, int W) {
         const float v = a.uw[((size_t)min(sl, a.u_slices - 1) * a.ucols + (size_t)proj * a.r + c) * a.Mpad + row];
         u += sl < a.u_slices ? v : 0.0f;
       }
+      for (int sl = kMaxUSlices; sl < a.u_slices; ++sl)
+        u += a.uw[((size_t)sl * a.ucols + (size_t)proj * a.r + c) * a.Mpad + row];
       eu[c * MT * 16 + row] = u;
     }
     for (int p = tid; p < a.r * 16; p += nthr) {

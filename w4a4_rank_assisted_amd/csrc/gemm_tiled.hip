@@ -198,7 +198,8 @@ __global__ __launch_bounds__(256, 2) void k_gemm_tiled(GemmArgs a, int nblk, int
   // ---- epilogue operands: loads issued first, so that their latency
   // overlaps the first stages' loads; parked in LDS below ----
   constexpr int EU = RPT * BM / 256;  // (rank column, row) pairs per thread
-  float eu[EU > 0 ? EU : 1][kMaxUSlices], el2[EU > 0 ? EU : 1], ebias = 0.0f;
+  constexpr int US = RPT <= 8 ? kMaxUSlices : kMaxUSlices / 2;  // U slices prefetched
+  float eu[EU > 0 ? EU : 1][US], el2[EU > 0 ? EU : 1], ebias = 0.0f;
   if (!DUMP) {
     const uint16_t *L2 = a.L2 + (size_t)proj * a.r * a.N;
 #pragma unroll
@@ -207,7 +208,7 @@ __global__ __launch_bounds__(256, 2) void k_gemm_tiled(GemmArgs a, int nblk, int
       const int cc = min(c, a.r - 1);
       const int m = min(mt0 * 16 + rr, a.Mpad - 1);
 #pragma unroll
-      for (int sl = 0; sl < kMaxUSlices; ++sl)
+      for (int sl = 0; sl < US; ++sl)
         eu[e][sl] = a.uw[((size_t)min(sl, a.u_slices - 1) * a.ucols + (size_t)proj * a.r + cc) * a.Mpad + m];
       el2[e] = bf16_to_f32(L2[(size_t)cc * a.N + min(nt0 * 16 + rr, a.N - 1)]);
     }
@@ -222,7 +223,12 @@ __global__ __launch_bounds__(256, 2) void k_gemm_tiled(GemmArgs a, int nblk, int
       const int idx = e * 256 + tid, c = idx / BM, rr = idx % BM;
       float u = 0.0f;
 #pragma unroll
-      for (int sl = 0; sl < kMaxUSlices; ++sl) u += sl < a.u_slices ? eu[e][sl] : 0.0f;
+      for (int sl = 0; sl < US; ++sl) u += sl < a.u_slices ? eu[e][sl] : 0.0f;
+      if (a.u_slices > US) {              // long K: the remaining slices, in order
+        const int cc = min(c, a.r - 1), m = min(mt0 * 16 + rr, a.Mpad - 1);
+        for (int sl = US; sl < a.u_slices; ++sl)
+          u += a.uw[((size_t)sl * a.ucols + (size_t)proj * a.r + cc) * a.Mpad + m];
+      }
       const bool live = c < a.r;
       if constexpr (RPT > 0) {
         smem.ep.u[c][rr] = (live && mt0 * 16 + rr < a.M) ? u : 0.0f;

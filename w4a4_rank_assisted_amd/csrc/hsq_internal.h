@@ -15,8 +15,9 @@ constexpr int kTile = 16;        // rows / columns per MFMA tile (16x16x64 i8)
 constexpr int kMaxRank = 32;     // largest rank r of the high-precision branch
 constexpr int kMaxBatch = 16;    // projections sharing one input
 constexpr int kRankBlock = 32;   // rank columns one quantization pass accumulates
-constexpr int kMaxUSlices = 4;   // K-slices of U the contraction kernels sum
-constexpr int kQuantActMaxK = 24576;  // hsq_quantize_act: 1/lambda of all K in LDS
+constexpr int kMaxUSlices = 8;   // U slices the contraction kernels prefetch (more: summed in a loop)
+constexpr int kMaxSliceGroups = 192;  // groups per workgroup of the quantization pass (LDS)
+constexpr int kQuantActMaxK = kMaxSliceGroups * kGroup;  // hsq_quantize_act: one slice
 
 // Bits of the float 1.5 * 2^23: adding an integer n (|n| < 2^22) to these
 // bits gives the float 1.5 * 2^23 + n exactly.  The contraction kernels feed
@@ -111,8 +112,11 @@ struct GemmArgs {
 hipError_t launch_pack(const int8_t *codes, int K, int N, uint8_t *packed, int *status,
                        hipStream_t s);
 hipError_t launch_unpack(const uint8_t *packed, int K, int N, int8_t *codes, hipStream_t s);
-hipError_t launch_quant(const QuantArgs &a, int slices, hipStream_t s);
-int quant_slices(int K);  // K-slices of the internal quantization pass
+// The quantization pass plans its own grid from (M, K, r, batch) and whether
+// it writes the public or the internal outputs; quant_slices() is the number
+// of K-slices (U partials) of the internal pass.
+hipError_t launch_quant(const QuantArgs &a, hipStream_t s);
+int quant_slices(int M, int K, int r, int batch);
 hipError_t launch_gemm_tiled(const GemmArgs &a, int batch, bool dump, hipStream_t s);
 hipError_t launch_gemm_skinny(const GemmArgs &a, int batch, bool dump, hipStream_t s);
 

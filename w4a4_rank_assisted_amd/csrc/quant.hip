@@ -7,217 +7,363 @@
 // activations (Deflating the Hessian, Table 1 caption), high-precision
 // branch on unquantized inputs (DiRotQ notes, key design 2).
 //
-// Mapping: one lane per (token, 64-channel group).  A lane loads its group
-// with eight 16-byte loads, finds the absmax in registers, computes the fp16
-// scale and its reciprocal once, writes the codes, and forms its group's
-// share of U.  A wave holds 16 tokens x 4 groups, so lanes that share a group
-// read the same 1/lambda (LDS) and L1 (cache) addresses; a workgroup of 256
-// lanes owns R tokens x (256/R) group slots and loops its lanes over the
-// K-slice's groups.  It computes 1/lambda for the slice's channels into LDS
-// (exact IEEE division) and sums the U shares of each token through LDS in a
-// fixed order.  Large K is split into at most four K-slices, whose U
-// partials the consumer sums.  The pass is HBM-bound: X is read once, codes
-// and scales are written once.
+// Mapping: one lane per (token, 64-channel group) item.  A workgroup owns a
+// K-slice of ng groups and a run of tokens, taken `rows` = 256/ng tokens at a
+// time (lane t = token t/ng, group t%ng).  A lane loads its group with eight
+// 16-byte loads, finds the absmax in registers, computes the fp16 scale and
+// its reciprocal once, writes the codes and forms its group's share of U.
+// The slice's 1/lambda (exact IEEE division) and, when they fit, its L1 rows
+// are staged in LDS once per workgroup, one padded row per group, so that
+// lanes of one token read different banks and lanes of different tokens
+// read the same words (broadcast).  The first X loads are issued before the
+// staging and each row step prefetches the next, so a lane waits for about
+// one memory round trip per step.  The U shares of a token are summed
+// through LDS in a fixed order; K-slices leave U partials that the
+// consumers sum.  The pass is HBM-bound: X is read once, codes and scales
+// are written once.
 #include "hsq_internal.h"
 
 namespace hsq {
 
 namespace {
 
-constexpr int kSliceGroups = 64;      // groups per K-slice of the internal pass
+constexpr int kLamStride = kGroup + 4;            // LDS floats per group row of 1/lambda
+constexpr size_t kL1StageBytes = 36 * 1024;       // LDS for staged L1 rows
+constexpr int kStageSliceGroups = 32;             // groups per slice when L1 is staged
+constexpr int kTargetSlices = 8;                  // U partials the consumers prefetch
+constexpr int kTargetBlocks = 1024;               // workgroups before a launch iterates rows
+constexpr int kMaxIters = 16;
 
-template <int NR, bool PUB>
-__global__ __launch_bounds__(256) void k_quant(QuantArgs a, int ng, int R) {
-  // dynamic LDS: 1/lambda of the slice's channels, then the U shares
-  extern __shared__ float lds[];
-  float *inv_lam = lds;                           // ng * 64
-  float *upart = lds + ng * kGroup;               // NR * 256
+constexpr int l1_stride(int nr) { return kGroup * nr + 4; }  // LDS floats per group of L1
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int WR = R / 16;                          // waves along the token axis
-  const int GW = 256 / R;                         // group slots of the workgroup
-  const int rl = (lane & 15) + 16 * (wave % WR);  // token of this lane
-  const int gs = (lane >> 4) + 4 * (wave / WR);   // group slot of this lane
-  const int gend = a.kend / kGroup;               // groups to write (G or Gp)
-  const int gb = blockIdx.y * ng;                 // first group of the slice
-  const int gn = min(ng, gend - gb);              // groups in this slice
-  const int m = blockIdx.x * R + rl;
-  const int mrows = PUB ? a.M : a.Mpad;           // rows this pass writes
+int rank_block(int cb) {
+  return cb == 0 ? 0 : cb <= 4 ? 4 : cb <= 8 ? 8 : cb <= 12 ? 12 : cb <= 16 ? 16 : 32;
+}
 
-  for (int i = tid; i < gn * kGroup; i += 256) {
-    const int k = gb * kGroup + i;
-    inv_lam[i] = (k < a.K) ? 1.0f / f16_to_f32(a.lam[k]) : 0.0f;
+size_t stage_bytes(int ng, int nr) { return sizeof(float) * (size_t)ng * l1_stride(nr); }
+
+struct QuantPlan {
+  int slices, ng, rows, iters, nr, stage;
+  size_t lds;
+};
+
+// Staging and LDS size of one rank block of nr columns under plan p.
+QuantPlan for_block(QuantPlan p, int nr) {
+  p.nr = nr;
+  p.stage = nr > 0 && stage_bytes(p.ng, nr) <= kL1StageBytes;
+  p.lds = sizeof(float) * ((size_t)(p.ng + 1) * kLamStride + 4 * 256) + (p.stage ? stage_bytes(p.ng, nr) : 0);
+  return p;
+}
+
+QuantPlan plan(int M, int K, int r, int batch, bool pub) {
+  QuantPlan p{};
+  const int gend = pub ? K / kGroup : padded_groups(K);
+  const int total = r * batch;
+  p.nr = rank_block(total < kRankBlock ? total : kRankBlock);
+  if (pub) {
+    p.slices = 1;
+    p.ng = gend;                                   // <= kMaxSliceGroups (entry point checks K)
+  } else {
+    int cap = kStageSliceGroups;
+    if (p.nr > 0) {
+      const int fit = (int)(kL1StageBytes / (sizeof(float) * l1_stride(p.nr)));
+      if (fit >= 8 && fit < cap) cap = fit;
+    }
+    p.slices = ceil_div(gend, cap);
+    if (p.slices > kTargetSlices) {
+      p.slices = kTargetSlices;
+      if (ceil_div(gend, p.slices) > kMaxSliceGroups) p.slices = ceil_div(gend, kMaxSliceGroups);
+    }
+    p.ng = ceil_div(gend, p.slices);
   }
-  __syncthreads();
+  p.rows = 256 / p.ng;
+  const int mrows = pub ? M : ceil_div(M, kTile) * kTile;
+  const int row_blocks = ceil_div(mrows, p.rows);
+  int it = row_blocks * p.slices / kTargetBlocks;
+  p.iters = it < 1 ? 1 : (it > kMaxIters ? kMaxIters : it);
+  return for_block(p, p.nr);
+}
 
-  float acc[NR > 0 ? NR : 1];
-#pragma unroll
-  for (int c = 0; c < (NR > 0 ? NR : 1); ++c) acc[c] = 0.0f;
+template <int NR, bool PUB, bool STAGE>
+__global__ __launch_bounds__(256) void k_quant(QuantArgs a, int ng, int rows, int iters) {
+  // dynamic LDS: 1/lambda [ng + 1][kLamStride] (last row zero), U shares [4][256],
+  // staged L1 [ng][64*NR + 4] (group row: channel-major, NR columns)
+  extern __shared__ float lds[];
+  float *inv_lam = lds;
+  float *upart = inv_lam + (ng + 1) * kLamStride;
+  float *l1s = upart + 4 * 256;
 
-  if (m < mrows) {
-    for (int gi = gs; gi < gn; gi += GW) {
-      const int g = gb + gi;
-      const bool in = m < a.M && g < a.G;         // outside: pad row / group, zeros
-      float xh[kGroup];
-      {
-        v4u raw[8];
-#pragma unroll
-        for (int t = 0; t < 8; ++t)
-          raw[t] = in ? *reinterpret_cast<const v4u *>(a.X + (size_t)m * a.K + (size_t)g * kGroup + 8 * t)
-                      : (v4u){0u, 0u, 0u, 0u};
-#pragma unroll
-        for (int t = 0; t < 8; ++t)
-#pragma unroll
-          for (int h = 0; h < 4; ++h) {
-            const int i = 8 * t + 2 * h;
-            xh[i] = bf16_to_f32(raw[t][h] & 0xFFFFu) * inv_lam[gi * kGroup + i];
-            xh[i + 1] = bf16_to_f32(raw[t][h] >> 16) * inv_lam[gi * kGroup + i + 1];
-          }
-      }
+  const int tid = threadIdx.x;
+  const int gend = a.kend / kGroup;                // groups to write (G or Gp)
+  const int gb = blockIdx.y * ng;                  // first group of the slice
+  const int gn = min(ng, gend - gb);               // groups in this slice
+  const int rl = tid / ng, gi = tid % ng;          // (token, group) of this lane
+  const int g = gb + gi;
+  const int mrows = PUB ? a.M : a.Mpad;            // rows this pass writes
+  const int mbase = blockIdx.x * rows * iters;
+  const bool lane_ok = rl < rows && gi < gn;
+  const bool g_in = lane_ok && g < a.G;            // else a pad group: zeros
 
-      if (a.write_codes) {
-        float amax = 0.0f;
+  // ---- loads, oldest first: slice tables, then X (the table stores below
+  // wait for the tables only; X stays in flight until the first row step)
+  // 1/lambda: thread t loads channels 8(t%8) .. +7 of slice group t/8
+  const bool lam_ok = tid < gn * 8 && gb + (tid >> 3) < a.G;
+  const v4u lv = *reinterpret_cast<const v4u *>(
+      a.lam + (size_t)min(gb + (tid >> 3), a.G - 1) * kGroup + 8 * (tid & 7));
+  // L1 (r % 4 == 0): J chunks of four columns per thread, clamped addresses
+  constexpr int J = 8;
+  const bool vec_l1 = STAGE && (a.r & 3) == 0;
+  const int cb4 = a.cb >> 2, n4 = gn * kGroup * cb4;
+  auto l1_chunk = [&](int p) __attribute__((always_inline)) {
+    const int c4 = cb4 == 1 ? 0 : p % cb4, rest = cb4 == 1 ? p : p / cb4;
+    const int k = min((gb + (rest >> 6)) * kGroup + (rest & 63), a.K - 1);
+    const int cc = a.c0 + 4 * c4, b = cc / a.r, jj = cc % a.r;
+    return reinterpret_cast<const v2u *>(a.L1 + ((size_t)b * a.K + k) * a.r + jj);
+  };
+  auto l1_store = [&](int p, v2u v) __attribute__((always_inline)) {
+    const int c4 = cb4 == 1 ? 0 : p % cb4, rest = cb4 == 1 ? p : p / cb4;
+    const int gg = rest >> 6, i = rest & 63;
+    *reinterpret_cast<v4f *>(l1s + gg * l1_stride(NR) + i * NR + 4 * c4) =
+        gb + gg < a.G ? (v4f){bf16_to_f32(v.x & 0xFFFFu), bf16_to_f32(v.x >> 16),
+                              bf16_to_f32(v.y & 0xFFFFu), bf16_to_f32(v.y >> 16)}
+                      : (v4f){0.f, 0.f, 0.f, 0.f};
+  };
+  // one chunk per channel (four rank columns of one projection): its loads
+  // go out with the others; wider blocks are staged in a loop below
+  const bool fast_l1 = vec_l1 && cb4 == 1;
+  // (issued unconditionally -- a branch here would make the compiler wait
+  // for them before the X loads; unused, they read the first L1 chunk)
+  v2u l1v[J];
+  if (STAGE) {
+    const uint16_t *l1 = fast_l1 ? a.L1 + ((size_t)(a.c0 / a.r) * a.K) * a.r + a.c0 % a.r : a.L1;
+    const int kstride = fast_l1 ? a.r : 0;
 #pragma unroll
-        for (int i = 0; i < kGroup; ++i) amax = fmaxf(amax, fabsf(xh[i]));
-        uint16_t s16 = 0;
-        if (amax != 0.0f) {
-          s16 = f32_to_f16(amax / 7.0f);
-          if (s16 == 0x7C00u) s16 = 0x7BFFu;      // saturate at 65504
-        }
-        const float s = f16_to_f32(s16);
-        const float inv_s = (s16 != 0) ? 1.0f / s : 0.0f;
-        uint32_t w[16];                           // 64 codes: int8 (internal) / nibbles (public)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) w[i] = 0;
-#pragma unroll
-        for (int i = 0; i < kGroup; ++i) {
-          const float t = __builtin_rintf(xh[i] * inv_s);  // ties to even
-          const int q = (int)fminf(fmaxf(t, -8.0f), 7.0f);
-          if (PUB)
-            w[i >> 3] |= (uint32_t)(q & 0xF) << (4 * (i & 7));
-          else
-            w[i >> 2] |= (uint32_t)(q & 0xFF) << (8 * (i & 3));
-        }
-        if (PUB) {
-          if (in) {
-            v4u *dst = reinterpret_cast<v4u *>(a.qx + (size_t)m * (a.K / 2) + (size_t)g * 32);
-            dst[0] = (v4u){w[0], w[1], w[2], w[3]};
-            dst[1] = (v4u){w[4], w[5], w[6], w[7]};
-            a.sx[(size_t)m * a.G + g] = s16;
-          }
-        } else {
-          // MFMA A-operand order: lane slot (m % 16) + 16 * kq holds
-          // channels 64g + 16kq .. +15 of row m
-          const int mt = m >> 4;
-          int8_t *base = a.qa + ((size_t)mt * a.Gp + g) * 1024 + (size_t)(m & 15) * 16;
-#pragma unroll
-          for (int kq = 0; kq < 4; ++kq)
-            *reinterpret_cast<v4u *>(base + kq * 256) =
-                (v4u){w[4 * kq], w[4 * kq + 1], w[4 * kq + 2], w[4 * kq + 3]};
-          a.sxs[((size_t)mt * a.Gp + g) * 16 + (m & 15)] = s * 0.0625f;
-        }
-      }
-
-      if (NR > 0 && in) {
-        // this group's share of U for rank columns c0 .. c0+cb-1
-        if ((a.r & 3) == 0) {
-          // four columns of one projection per 8-byte L1 row chunk
-#pragma unroll
-          for (int c = 0; c < NR; c += 4) {
-            if (c >= a.cb) break;
-            const int cc = a.c0 + c, b = cc / a.r, j = cc % a.r;
-            const uint16_t *l1 = a.L1 + ((size_t)b * a.K + (size_t)g * kGroup) * a.r + j;
-            float s0 = acc[c], s1 = acc[c + 1], s2 = acc[c + 2], s3 = acc[c + 3];
-#pragma unroll
-            for (int i0 = 0; i0 < kGroup; i0 += 16) {
-#pragma unroll
-              for (int i = i0; i < i0 + 16; ++i) {
-                const v2u v = *reinterpret_cast<const v2u *>(l1 + (size_t)i * a.r);
-                s0 = __builtin_fmaf(xh[i], bf16_to_f32(v.x & 0xFFFFu), s0);
-                s1 = __builtin_fmaf(xh[i], bf16_to_f32(v.x >> 16), s1);
-                s2 = __builtin_fmaf(xh[i], bf16_to_f32(v.y & 0xFFFFu), s2);
-                s3 = __builtin_fmaf(xh[i], bf16_to_f32(v.y >> 16), s3);
-              }
-              // at most 16 L1 loads in flight: no load moves across this
-              asm volatile("" : "+v"(s0), "+v"(s1), "+v"(s2), "+v"(s3) : : "memory");
-            }
-            acc[c] = s0; acc[c + 1] = s1; acc[c + 2] = s2; acc[c + 3] = s3;
-          }
-        } else {
-#pragma unroll
-          for (int c = 0; c < NR; ++c) {
-            if (c >= a.cb) break;
-            const int cc = a.c0 + c, b = cc / a.r, j = cc % a.r;
-            const uint16_t *l1 = a.L1 + ((size_t)b * a.K + (size_t)g * kGroup) * a.r + j;
-            float sacc = acc[c];
-#pragma unroll
-            for (int i0 = 0; i0 < kGroup; i0 += 16) {
-#pragma unroll
-              for (int i = i0; i < i0 + 16; ++i)
-                sacc = __builtin_fmaf(xh[i], bf16_to_f32(l1[(size_t)i * a.r]), sacc);
-              asm volatile("" : "+v"(sacc) : : "memory");
-            }
-            acc[c] = sacc;
-          }
-        }
-      }
+    for (int j = 0; j < J; ++j) {
+      const int rest = min(tid + 256 * j, n4 - 1);
+      const int k = min(gb * kGroup + rest, a.K - 1);
+      l1v[j] = *reinterpret_cast<const v2u *>(l1 + (size_t)k * kstride);
     }
   }
 
-  if (NR > 0) {
-    // sum the shares of each token over its group slots (fixed order)
+  v4u raw[8];
+  auto load_x = [&](int m) __attribute__((always_inline)) {
+    // clamped: rows past M and pad groups read a valid row and are zeroed
+    // through the zero 1/lambda row below
+    const v4u *src = reinterpret_cast<const v4u *>(a.X + (size_t)min(m, a.M - 1) * a.K +
+                                                   (size_t)min(g, a.G - 1) * kGroup);
 #pragma unroll
-    for (int c = 0; c < NR; ++c) upart[(c * GW + gs) * R + rl] = acc[c];
-    __syncthreads();
-    for (int p = tid; p < R * a.cb; p += 256) {
-      const int r0 = p % R, c = p / R;
-      const int mm = blockIdx.x * R + r0;
-      if (mm >= mrows) continue;
-      float s = 0.0f;
-      for (int q = 0; q < GW; ++q) s += upart[(c * GW + q) * R + r0];
-      if (PUB)
-        a.u_pub[(size_t)mm * a.r + a.c0 + c] = s;
-      else
-        a.uw[((size_t)blockIdx.y * a.ucols + a.c0 + c) * a.Mpad + mm] = s;
+    for (int t = 0; t < 8; ++t) raw[t] = src[t];
+  };
+  load_x(mbase + rl);
+
+  // ---- slice tables into LDS ----
+  auto lam_store = [&](int p, v4u v, bool ok) __attribute__((always_inline)) {
+    float f[8];
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+      f[2 * h] = ok ? 1.0f / f16_to_f32((uint16_t)(v[h] & 0xFFFFu)) : 0.0f;
+      f[2 * h + 1] = ok ? 1.0f / f16_to_f32((uint16_t)(v[h] >> 16)) : 0.0f;
+    }
+    v4f *dst = reinterpret_cast<v4f *>(inv_lam + (p >> 3) * kLamStride + 8 * (p & 7));
+    dst[0] = (v4f){f[0], f[1], f[2], f[3]};
+    dst[1] = (v4f){f[4], f[5], f[6], f[7]};
+  };
+  if (tid < gn * 8) lam_store(tid, lv, lam_ok);
+  for (int p = tid + 256; p < gn * 8; p += 256) {  // slices of more than 32 groups
+    const bool ok = gb + (p >> 3) < a.G;
+    const v4u v = *reinterpret_cast<const v4u *>(
+        a.lam + (size_t)min(gb + (p >> 3), a.G - 1) * kGroup + 8 * (p & 7));
+    lam_store(p, v, ok);
+  }
+  if (tid < kGroup) inv_lam[ng * kLamStride + tid] = 0.0f;  // zero row: rows past M
+  if (fast_l1) {
+#pragma unroll
+    for (int j = 0; j < J; ++j)
+      if (tid + 256 * j < n4) l1_store(tid + 256 * j, l1v[j]);
+    for (int p = tid + 256 * J; p < n4; p += 256) l1_store(p, *l1_chunk(p));
+  } else if (vec_l1) {
+    for (int p = tid; p < n4; p += 256) l1_store(p, *l1_chunk(p));
+  } else if (STAGE) {
+    // odd ranks: one column per element
+    for (int p = tid; p < gn * kGroup * a.cb; p += 256) {
+      const int c = p % a.cb, rest = p / a.cb, gg = rest >> 6, i = rest & 63;
+      const int k = min((gb + gg) * kGroup + i, a.K - 1);
+      const int cc = a.c0 + c, b = cc / a.r, jj = cc % a.r;
+      l1s[gg * l1_stride(NR) + i * NR + c] =
+          gb + gg < a.G ? bf16_to_f32(a.L1[((size_t)b * a.K + k) * a.r + jj]) : 0.0f;
+    }
+  }
+  __syncthreads();
+
+  const float *l1_row = l1s + gi * l1_stride(NR);
+
+  for (int it = 0; it < iters; ++it) {
+    const int mb = mbase + it * rows;
+    if (mb >= mrows) break;                        // uniform over the workgroup
+    const int m = mb + rl;
+    const bool live = lane_ok && m < mrows;
+    const bool in = g_in && m < a.M;
+    const float *lam_row = inv_lam + (in ? gi : ng) * kLamStride;
+
+    float xh[kGroup];
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      const v4f l0 = *reinterpret_cast<const v4f *>(lam_row + 8 * t);
+      const v4f l1 = *reinterpret_cast<const v4f *>(lam_row + 8 * t + 4);
+      xh[8 * t + 0] = bf16_to_f32(raw[t].x & 0xFFFFu) * l0.x;
+      xh[8 * t + 1] = bf16_to_f32(raw[t].x >> 16) * l0.y;
+      xh[8 * t + 2] = bf16_to_f32(raw[t].y & 0xFFFFu) * l0.z;
+      xh[8 * t + 3] = bf16_to_f32(raw[t].y >> 16) * l0.w;
+      xh[8 * t + 4] = bf16_to_f32(raw[t].z & 0xFFFFu) * l1.x;
+      xh[8 * t + 5] = bf16_to_f32(raw[t].z >> 16) * l1.y;
+      xh[8 * t + 6] = bf16_to_f32(raw[t].w & 0xFFFFu) * l1.z;
+      xh[8 * t + 7] = bf16_to_f32(raw[t].w >> 16) * l1.w;
+    }
+    if (it + 1 < iters) load_x(m + rows);          // next row step, in flight meanwhile
+
+    if (live && a.write_codes) {
+      float amax = 0.0f;
+#pragma unroll
+      for (int i = 0; i < kGroup; ++i) amax = fmaxf(amax, fabsf(xh[i]));
+      uint16_t s16 = 0;
+      if (amax != 0.0f) {
+        s16 = f32_to_f16(amax / 7.0f);
+        if (s16 == 0x7C00u) s16 = 0x7BFFu;         // saturate at 65504
+      }
+      const float s = f16_to_f32(s16);
+      const float inv_s = (s16 != 0) ? 1.0f / s : 0.0f;
+      // code = clamp(rint(fl32(xh / s)), -8, 7): adding 1.5 * 2^23 rounds the
+      // fp32 quotient to an integer (ties to even) in the low mantissa bits;
+      // the clamp works on those bits (a quotient beyond +-2^22 lands outside
+      // the clamp window on the right side).  The low byte of the clamped
+      // bits is the two's-complement code.
+      int c[kGroup];
+#pragma unroll
+      for (int i = 0; i < kGroup; ++i) {
+        const float t = xh[i] * inv_s;
+        const int b = __float_as_int(t + kMagic);
+        c[i] = min(max(b, kMagicBits - 8), kMagicBits + 7);
+      }
+      if (PUB) {
+        if (in) {
+          uint32_t w[8];
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            uint32_t v = 0;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) v |= (uint32_t)(c[8 * j + e] & 0xF) << (4 * e);
+            w[j] = v;
+          }
+          v4u *dst = reinterpret_cast<v4u *>(a.qx + (size_t)m * (a.K / 2) + (size_t)g * 32);
+          dst[0] = (v4u){w[0], w[1], w[2], w[3]};
+          dst[1] = (v4u){w[4], w[5], w[6], w[7]};
+          a.sx[(size_t)m * a.G + g] = s16;
+        }
+      } else {
+        uint32_t w[16];                            // int8 codes, 4 per word
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          const uint32_t lo = __builtin_amdgcn_perm((uint32_t)c[4 * j + 1], (uint32_t)c[4 * j], 0x0c0c0400u);
+          const uint32_t hi = __builtin_amdgcn_perm((uint32_t)c[4 * j + 3], (uint32_t)c[4 * j + 2], 0x0c0c0400u);
+          w[j] = __builtin_amdgcn_perm(hi, lo, 0x05040100u);
+        }
+        // MFMA A-operand order: lane slot (m % 16) + 16 * kq holds
+        // channels 64g + 16kq .. +15 of row m
+        const int mt = m >> 4;
+        int8_t *base = a.qa + ((size_t)mt * a.Gp + g) * 1024 + (size_t)(m & 15) * 16;
+#pragma unroll
+        for (int kq = 0; kq < 4; ++kq)
+          *reinterpret_cast<v4u *>(base + kq * 256) =
+              (v4u){w[4 * kq], w[4 * kq + 1], w[4 * kq + 2], w[4 * kq + 3]};
+        a.sxs[((size_t)mt * a.Gp + g) * 16 + (m & 15)] = s * 0.0625f;
+      }
+    }
+
+    // ---- U: four rank columns at a time, summed over the slice's groups ----
+    if (NR > 0) {
+#pragma unroll
+      for (int c4 = 0; c4 < NR; c4 += 4) {
+        if (c4 >= a.cb) break;                     // uniform
+        if (STAGE) {
+          float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
+          if (in) {
+#pragma unroll
+            for (int i = 0; i < kGroup; ++i) {
+              const v4f l = *reinterpret_cast<const v4f *>(l1_row + i * NR + c4);
+              s0 = __builtin_fmaf(xh[i], l.x, s0);
+              s1 = __builtin_fmaf(xh[i], l.y, s1);
+              s2 = __builtin_fmaf(xh[i], l.z, s2);
+              s3 = __builtin_fmaf(xh[i], l.w, s3);
+            }
+          }
+          upart[0 * 256 + tid] = s0;
+          upart[1 * 256 + tid] = s1;
+          upart[2 * 256 + tid] = s2;
+          upart[3 * 256 + tid] = s3;
+        } else {
+          // L1 rows from the cache, one column at a time, 16 channels in flight
+#pragma unroll 1
+          for (int e = 0; e < 4; ++e) {
+            float acc = 0.0f;
+            if (in && c4 + e < a.cb) {
+              const int cc = a.c0 + c4 + e, b = cc / a.r, j = cc % a.r;
+              const uint16_t *l1 = a.L1 + ((size_t)b * a.K + (size_t)g * kGroup) * a.r + j;
+#pragma unroll
+              for (int i0 = 0; i0 < kGroup; i0 += 16) {
+#pragma unroll
+                for (int i = i0; i < i0 + 16; ++i) acc = __builtin_fmaf(xh[i], bf16_to_f32(l1[(size_t)i * a.r]), acc);
+                asm volatile("" : "+v"(acc) : : "memory");
+              }
+            }
+            upart[e * 256 + tid] = acc;
+          }
+        }
+        __syncthreads();
+        const int cw = min(4, a.cb - c4);
+        for (int p = tid; p < rows * cw; p += 256) {   // rows * cw > 256 when ng < 4
+          const int r0 = p % rows, e = p / rows;
+          const int mm = mb + r0;
+          if (mm < mrows) {
+            const float *src = upart + e * 256 + r0 * ng;
+            float s = 0.0f;
+            for (int q = 0; q < gn; ++q) s += src[q];
+            if (PUB)
+              a.u_pub[(size_t)mm * a.r + a.c0 + c4 + e] = s;
+            else
+              a.uw[((size_t)blockIdx.y * a.ucols + a.c0 + c4 + e) * a.Mpad + mm] = s;
+          }
+        }
+        __syncthreads();
+      }
     }
   }
 }
 
-template <bool PUB>
-hipError_t launch_variant(const QuantArgs &a, dim3 grid, int ng, int R, hipStream_t s) {
-  const int cb = a.cb;
-  const int nr = cb == 0 ? 0 : cb <= 4 ? 4 : cb <= 8 ? 8 : cb <= 16 ? 16 : 32;
-  const size_t lds = sizeof(float) * ((size_t)ng * kGroup + (size_t)256 * (nr ? nr : 1));
+template <bool PUB, bool STAGE>
+hipError_t launch_nr(const QuantArgs &a, const QuantPlan &p, int nr, dim3 grid, hipStream_t s) {
   switch (nr) {
-    case 0: hipLaunchKernelGGL((k_quant<0, PUB>), grid, dim3(256), lds, s, a, ng, R); break;
-    case 4: hipLaunchKernelGGL((k_quant<4, PUB>), grid, dim3(256), lds, s, a, ng, R); break;
-    case 8: hipLaunchKernelGGL((k_quant<8, PUB>), grid, dim3(256), lds, s, a, ng, R); break;
-    case 16: hipLaunchKernelGGL((k_quant<16, PUB>), grid, dim3(256), lds, s, a, ng, R); break;
-    default: hipLaunchKernelGGL((k_quant<32, PUB>), grid, dim3(256), lds, s, a, ng, R); break;
+    case 0: hipLaunchKernelGGL((k_quant<0, PUB, false>), grid, dim3(256), p.lds, s, a, p.ng, p.rows, p.iters); break;
+    case 4: hipLaunchKernelGGL((k_quant<4, PUB, STAGE>), grid, dim3(256), p.lds, s, a, p.ng, p.rows, p.iters); break;
+    case 8: hipLaunchKernelGGL((k_quant<8, PUB, STAGE>), grid, dim3(256), p.lds, s, a, p.ng, p.rows, p.iters); break;
+    case 12: hipLaunchKernelGGL((k_quant<12, PUB, STAGE>), grid, dim3(256), p.lds, s, a, p.ng, p.rows, p.iters); break;
+    case 16: hipLaunchKernelGGL((k_quant<16, PUB, STAGE>), grid, dim3(256), p.lds, s, a, p.ng, p.rows, p.iters); break;
+    default: hipLaunchKernelGGL((k_quant<32, PUB, STAGE>), grid, dim3(256), p.lds, s, a, p.ng, p.rows, p.iters); break;
   }
   return hipGetLastError();
 }
 
 }  // namespace
 
-int quant_slices(int K) {
-  const int s = ceil_div(padded_groups(K), kSliceGroups);
-  return s < 1 ? 1 : (s > kMaxUSlices ? kMaxUSlices : s);
-}
+int quant_slices(int M, int K, int r, int batch) { return plan(M, K, r, batch, false).slices; }
 
 // One launch per block of up to 32 rank columns; codes and scales are
-// written by the first.  `slices` K-slices (gridDim.y): 1 for the public
-// pass, quant_slices(K) for the internal one.
-hipError_t launch_quant(const QuantArgs &a0, int slices, hipStream_t s) {
+// written by the first.
+hipError_t launch_quant(const QuantArgs &a0, hipStream_t s) {
   const bool pub = a0.qx != nullptr;
-  const int gend = a0.kend / kGroup;
-  const int ng = ceil_div(gend, slices);          // groups per slice
-  if ((size_t)ng * kGroup * sizeof(float) > 96 * 1024) return hipErrorInvalidValue;
-  // tokens per workgroup: 16 when the slice has many groups (16 group
-  // slots), up to 64 for short slices (4 group slots)
-  const int R = ng >= 12 ? 16 : (ng >= 6 ? 32 : 64);
+  const QuantPlan p = plan(a0.M, a0.K, a0.r, a0.batch, pub);
+  if (p.ng < 1 || p.ng > kMaxSliceGroups) return hipErrorInvalidValue;
   const int mrows = pub ? a0.M : a0.Mpad;
-  dim3 grid((unsigned)ceil_div(mrows, R), (unsigned)slices);
+  dim3 grid((unsigned)ceil_div(mrows, p.rows * p.iters), (unsigned)p.slices);
   const int total = a0.r * a0.batch;
   int c0 = 0;
   do {
@@ -225,8 +371,15 @@ hipError_t launch_quant(const QuantArgs &a0, int slices, hipStream_t s) {
     a.c0 = c0;
     a.cb = total - c0 < kRankBlock ? total - c0 : kRankBlock;
     a.write_codes = (c0 == 0);
-    hipError_t e = pub ? launch_variant<true>(a, grid, ng, R, s)
-                       : launch_variant<false>(a, grid, ng, R, s);
+    // a later rank block may be narrower than the first: same grid, its own
+    // template and LDS size
+    const int nr = rank_block(a.cb);
+    const QuantPlan q = for_block(p, nr);
+    hipError_t e;
+    if (pub)
+      e = q.stage ? launch_nr<true, true>(a, q, nr, grid, s) : launch_nr<true, false>(a, q, nr, grid, s);
+    else
+      e = q.stage ? launch_nr<false, true>(a, q, nr, grid, s) : launch_nr<false, false>(a, q, nr, grid, s);
     if (e != hipSuccess) return e;
     c0 += kRankBlock;
   } while (c0 < total);
