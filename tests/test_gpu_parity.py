@@ -269,3 +269,30 @@ def test_misaligned_tensor_is_rejected():
     with pytest.raises(hsq.HsqError) as ei:
         hsq.w4a4_lowrank_linear(Xmis, up.lam, up.packed, up.sw, up.L1, up.L2, up.bias, N=up.N)
     assert ei.value.status == hsq.E_ALIGN
+
+
+@pytest.mark.parametrize("M", [16, 200])
+def test_graph_replay_matches_eager(M):
+    # the layer captured in a HIP graph and replayed several times, with
+    # eager calls of the same layer (other buffers) in between; every replay
+    # must equal the eager result bit for bit (the kernels are deterministic)
+    lay = make_random_layer(90 + M, M, 512, 300, r=4, batch=2)
+    up = Uploaded(lay)
+    say(f"[graph] M={M} K=512 N=300 r=4 batch=2")
+    eager = up.linear("f32").view(torch.int32).cpu().numpy()
+    out = torch.empty((up.B, M, up.N), dtype=torch.float32, device=DEV)
+    ws = torch.empty(hsq.workspace_bytes(M, up.K, up.N, up.r, up.B), dtype=torch.uint8, device=DEV)
+    cap = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(cap):
+        with torch.cuda.graph(g, stream=cap):
+            hsq.w4a4_lowrank_linear(up.X, up.lam, up.packed, up.sw, up.L1, up.L2, up.bias,
+                                    N=up.N, batch=up.B, y_dtype="f32", out=out, workspace=ws)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        out.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(out.view(torch.int32).cpu().numpy(), eager), f"replay {rep}"
+        again = up.linear("f32").view(torch.int32).cpu().numpy()   # eager work in between
+        assert np.array_equal(again, eager)

@@ -4,13 +4,16 @@
 //
 // Same arithmetic as the tiled kernel (hsq.h formula block; one 16x16x64
 // int8 MFMA per group and output tile, magic-constant accumulator, two FMAs
-// per element and group).  Mapping: a workgroup owns one 16-column tile of
-// one projection; its W waves split the K groups into contiguous ranges, so
-// every weight byte is loaded by exactly one lane, straight from HBM into
-// registers with 16-byte loads, several group pairs in flight per lane.
-// The activation codes (M*K bytes) are small and served from L2.  The W
-// partial tiles are summed through LDS in wave order (deterministic), and
-// the epilogue adds U * L2 and the bias -- no split-K buffer, one launch.
+// per element and group).  Mapping: a workgroup owns CT adjacent 16-column
+// tiles of one projection; its W waves split the K groups into runs of P
+// group pairs (P, CT fixed at compile time).  For a run, a wave issues the
+// loads of all P x CT weight blocks (1 KB each, 16 bytes per lane, straight
+// from HBM into registers) together with the run's activation codes and
+// scales (shared by the CT tiles, from the cache) before it computes
+// anything, so the whole weight stream of the chip is in flight at once.
+// The W partial tiles are summed through LDS by a fixed halving tree
+// (deterministic), and the epilogue adds U * L2 and the bias -- no split-K
+// buffer, one launch.
 #include "hsq_internal.h"
 
 namespace hsq {
@@ -18,162 +21,244 @@ namespace hsq {
 namespace {
 
 constexpr uint32_t kNibMask = 0xF0F0F0F0u;
+// cache policy of the weight stream (read once): non-temporal
+constexpr int kStreamLoad = 2;
+// waves per workgroup: up to 16 for one or two row tiles, 8 for more (whose
+// registers need the larger per-wave budget)
+constexpr int max_waves(int mt) { return mt <= 2 ? 16 : 8; }
 
-template <int MT, bool DUMP>
-__global__ __launch_bounds__(512) void k_gemm_skinny(GemmArgs a, int W) {
-  // dynamic LDS: partial tiles [W][MT][4][64], then U [r][16*MT] (slices
-  // summed), L2 [r][16], bias [16]
+template <int MT, int P, int CT, bool DUMP>
+__global__ __launch_bounds__(64 * max_waves(MT)) void k_gemm_skinny(GemmArgs a, int W) {
+  // dynamic LDS: partial tiles [ceil(W/2)][CT][MT][4][64], then U [r][16*MT]
+  // (slices summed), L2 [r][16*CT], bias [16*CT]
   extern __shared__ float red[];
-  float *eu = red + W * MT * 4 * 64;
+  const int H0 = (W + 1) / 2;
+  float *eu = red + H0 * CT * MT * 4 * 64;
   float *el2 = eu + a.r * MT * 16;
-  float *eb = el2 + a.r * 16;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int nt = blockIdx.x + (DUMP ? a.n0 / 16 : 0);
+  float *eb = el2 + a.r * 16 * CT;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int NT = (a.N + 15) / 16;
+  const int nt0 = (blockIdx.x + (DUMP ? a.n0 / (16 * CT) : 0)) * CT;   // first column tile
   const int proj = blockIdx.y;
-  const int GP = a.Gp / 2;
-  const int per = (GP + W - 1) / W;
-  const int gp0 = wave * per;
-  const int gp1 = min(GP, gp0 + per);
+  const int GP = a.Gp / 2, G = a.G;
   const int colq = lane & 15, rowq = 4 * (lane >> 4);
-  const int n = nt * 16 + colq;
-  const bool ncol = n < a.N;
-  const uint8_t *wp = a.w + (size_t)proj * a.w_stride + (size_t)nt * GP * 1024 + (size_t)lane * 16;
-  const uint16_t *swp = a.sw ? a.sw + (size_t)proj * a.G * a.N + (ncol ? n : 0) : nullptr;
   const v4i magic = {kMagicBits, kMagicBits, kMagicBits, kMagicBits};
 
-  // epilogue operands into LDS first (their loads overlap the weight stream;
-  // the barrier before the epilogue orders them)
-  if (!DUMP) {
-    const int nthr = W * 64;
-    for (int p = tid; p < a.r * MT * 16; p += nthr) {
-      const int c = p / (MT * 16), row = p % (MT * 16);
-      float u = 0.0f;
+  const __amdgpu_buffer_rsrc_t rs_w =
+      buffer_rsrc(a.w + (size_t)proj * a.w_stride, (uint32_t)NT * GP * 1024);
+  const __amdgpu_buffer_rsrc_t rs_a = buffer_rsrc(a.qa, (uint32_t)MT * a.Gp * 1024);
+  const __amdgpu_buffer_rsrc_t rs_x = buffer_rsrc(a.sxs, (uint32_t)MT * a.Gp * 64);
+  const __amdgpu_buffer_rsrc_t rs_s =
+      buffer_rsrc(DUMP ? nullptr : a.sw + (size_t)proj * G * a.N, DUMP ? 0u : (uint32_t)G * a.N * 2);
+  uint32_t offw[CT], offsw[CT];
 #pragma unroll
-      for (int sl = 0; sl < kMaxUSlices; ++sl) {
-        const float v = a.uw[((size_t)min(sl, a.u_slices - 1) * a.ucols + (size_t)proj * a.r + c) * a.Mpad + row];
-        u += sl < a.u_slices ? v : 0.0f;
-      }
-      for (int sl = kMaxUSlices; sl < a.u_slices; ++sl)
-        u += a.uw[((size_t)sl * a.ucols + (size_t)proj * a.r + c) * a.Mpad + row];
-      eu[c * MT * 16 + row] = u;
-    }
-    for (int p = tid; p < a.r * 16; p += nthr) {
-      const int c = p / 16, col = p % 16;
-      el2[p] = bf16_to_f32(a.L2[((size_t)proj * a.r + c) * a.N + min(nt * 16 + col, a.N - 1)]);
-    }
-    if (tid < 16)
-      eb[tid] = a.bias ? bf16_to_f32(a.bias[(size_t)proj * a.N + min(nt * 16 + tid, a.N - 1)]) : 0.0f;
+  for (int c = 0; c < CT; ++c) {
+    const int nt = min(nt0 + c, NT - 1);            // past the last tile: clamped, not stored
+    offw[c] = ((uint32_t)nt * GP * 64 + lane) * 16;
+    offsw[c] = (uint32_t)min(nt * 16 + colq, a.N - 1) * 2;
   }
 
-  float acc[MT][4];
+  float acc[CT][MT][4];
 #pragma unroll
-  for (int i = 0; i < MT; ++i)
+  for (int c = 0; c < CT; ++c)
 #pragma unroll
-    for (int q = 0; q < 4; ++q) acc[i][q] = 0.0f;
+    for (int i = 0; i < MT; ++i)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) acc[c][i][q] = 0.0f;
 
-  // prefetch ring: D group pairs of weights, weight scales, activation
-  // codes and activation scales in flight per lane (D = 4 / MT registers
-  // budget); every operand of a group pair is loaded D pairs ahead
-  constexpr int D = MT == 1 ? 4 : (MT == 2 ? 2 : 1);
-  v4u wbuf[D];
-  uint32_t sbuf[D];
-  v4i abuf[D][MT][2];
-  v4f xbuf[D][MT][2];
-  auto fetch = [&](int gp, int u) __attribute__((always_inline)) {
-    wbuf[u] = *reinterpret_cast<const v4u *>(wp + (size_t)gp * 1024);
-    sbuf[u] = 0;
-    if (!DUMP && ncol) {
-      const int g = 2 * gp;
-      const uint32_t lo = swp[(size_t)g * a.N];
-      const uint32_t hi = (g + 1 < a.G) ? swp[(size_t)(g + 1) * a.N] : 0u;
-      sbuf[u] = lo | (hi << 16);
-    }
+  // epilogue operands: loads issued first, parked in LDS after the main loop
+  // (thread t holds U element t, L2 element t and bias t; more elements than
+  // threads loop at the end)
+  const int EUN = a.r * MT * 16, ELN = a.r * 16 * CT, nthr = W * 64;
+  float upre[kMaxUSlices], l2pre = 0.0f, bpre = 0.0f;
+  if (!DUMP) {
+    // branch-free: empty resources (r == 0, no bias) read as zero
+    const __amdgpu_buffer_rsrc_t rs_u =
+        buffer_rsrc(a.uw, (uint32_t)a.u_slices * a.ucols * a.Mpad * 4);
+    const __amdgpu_buffer_rsrc_t rs_l =
+        buffer_rsrc(a.r > 0 ? a.L2 + (size_t)proj * a.r * a.N : nullptr, (uint32_t)a.r * a.N * 2);
+    const __amdgpu_buffer_rsrc_t rs_b =
+        buffer_rsrc(a.bias ? a.bias + (size_t)proj * a.N : nullptr, a.bias ? (uint32_t)a.N * 2 : 0u);
+    const int e = min(tid, max(EUN - 1, 0));
+    const uint32_t offu = (uint32_t)(((size_t)proj * a.r + e / (MT * 16)) * a.Mpad + e % (MT * 16)) * 4;
+#pragma unroll
+    for (int sl = 0; sl < kMaxUSlices; ++sl)
+      upre[sl] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+          rs_u, offu, min(sl, a.u_slices - 1) * a.ucols * a.Mpad * 4, 0));
+    const int e2 = min(tid, max(ELN - 1, 0));         // (rank column, block column)
+    l2pre = bf16_to_f32(__builtin_amdgcn_raw_buffer_load_b16(
+        rs_l, (uint32_t)((e2 / (16 * CT)) * a.N + min(nt0 * 16 + e2 % (16 * CT), a.N - 1)) * 2, 0, 0));
+    bpre = bf16_to_f32(__builtin_amdgcn_raw_buffer_load_b16(
+        rs_b, (uint32_t)min(nt0 * 16 + tid % (16 * CT), a.N - 1) * 2, 0, 0));
+  }
+
+  // activation codes / scales of one group pair, raw weight scales of its
+  // CT column tiles
+  struct Act {
+    v4i av[MT][2];
+    v4f sx[MT][2];
+    uint32_t sw[CT][2];
+  };
+  auto load_act = [&](int gp, Act &t) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < MT; ++i)
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         const int g = 2 * gp + h;
-        abuf[u][i][h] = *reinterpret_cast<const v4i *>(a.qa + (((size_t)i * a.Gp + g) * 64 + lane) * 16);
+        t.av[i][h] = __builtin_bit_cast(
+            v4i, __builtin_amdgcn_raw_buffer_load_b128(rs_a, (uint32_t)(i * a.Gp * 64 + lane) * 16, g * 1024, 0));
         if (!DUMP)
-          xbuf[u][i][h] = *reinterpret_cast<const v4f *>(a.sxs + ((size_t)i * a.Gp + g) * 16 + rowq);
+          t.sx[i][h] = __builtin_bit_cast(
+              v4f, __builtin_amdgcn_raw_buffer_load_b128(rs_x, (uint32_t)(i * a.Gp * 16 + rowq) * 4, g * 64, 0));
       }
+    if (!DUMP) {
+      // a pad group (g = G) reads group G-1: its codes are zero, so it adds
+      // fma(1.5*2^23, sw, -1.5*2^23*sw) = 0 exactly whatever sw is
+#pragma unroll
+      for (int c = 0; c < CT; ++c)
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+          t.sw[c][h] = __builtin_amdgcn_raw_buffer_load_b16(rs_s, offsw[c], min(2 * gp + h, G - 1) * a.N * 2, 0);
+    }
   };
-#pragma unroll
-  for (int u = 0; u < D; ++u)
-    if (gp0 + u < gp1) fetch(gp0 + u, u);
 
-  for (int base = gp0; base < gp1; base += D) {
+  // runs of P group pairs: wave w takes pairs [c0, c0 + P) for c0 = P*w,
+  // P*(w + W), ...
+  for (int c0 = wave * P; c0 < GP; c0 += W * P) {
+    const int pn = min(P, GP - c0);               // pairs in this run (uniform)
+    v4u wv[P][CT];
+    Act t[P];
 #pragma unroll
-    for (int u = 0; u < D; ++u) {
-      const int gp = base + u;
-      if (gp >= gp1) break;
-      const v4u wv = wbuf[u];
-      const uint32_t sv = sbuf[u];
-      v4i av[MT][2];
-      v4f sx[MT][2];
+    for (int p = 0; p < P; ++p) {
+      const int gp = min(c0 + p, GP - 1);
+      load_act(gp, t[p]);
 #pragma unroll
-      for (int i = 0; i < MT; ++i)
+      for (int c = 0; c < CT; ++c)
+        wv[p][c] = __builtin_amdgcn_raw_buffer_load_b128(rs_w, offw[c], gp * 1024, kStreamLoad);
+    }
+    // keep every load of the run ahead of its first use (the scheduler would
+    // otherwise trade memory parallelism for registers)
+    __builtin_amdgcn_sched_barrier(0);
+    // every pair of the run is computed (no branch the loads could sink
+    // into); a pair past the run end gets weight scale 0, which makes its
+    // contribution exactly 0
+#pragma unroll
+    for (int p = 0; p < P; ++p) {
+      const int gp = c0 + p;
+#pragma unroll
+      for (int c = 0; c < CT; ++c)
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
-          av[i][h] = abuf[u][i][h];
-          sx[i][h] = xbuf[u][i][h];
-        }
-      if (gp + D < gp1) fetch(gp + D, u);
+          const int g = 2 * gp + h;
+          const uint32_t w0 = h ? wv[p][c].z : wv[p][c].x, w1 = h ? wv[p][c].w : wv[p][c].y;
+          const v4i b = {(int)(w0 & kNibMask), (int)((w0 << 4) & kNibMask), (int)(w1 & kNibMask),
+                         (int)((w1 << 4) & kNibMask)};
+          const float swf = (DUMP || p >= pn) ? 0.0f : f16_to_f32((uint16_t)t[p].sw[c][h]);
+          const float nsw = -kMagic * swf;
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int g = 2 * gp + h;
-        const uint32_t w0 = h ? wv.z : wv.x, w1 = h ? wv.w : wv.y;
-        const v4i b = {(int)(w0 & kNibMask), (int)((w0 << 4) & kNibMask), (int)(w1 & kNibMask),
-                       (int)((w1 << 4) & kNibMask)};
-        const float swf = f16_to_f32((uint16_t)(h ? sv >> 16 : sv & 0xFFFFu));
-        const float nsw = -kMagic * swf;
+          for (int i = 0; i < MT; ++i) {
+            const v4i d = __builtin_amdgcn_mfma_i32_16x16x64_i8(t[p].av[i][h], b, magic, 0, 0, 0);
+            if (DUMP) {
+              const int n = (nt0 + c) * 16 + colq;
 #pragma unroll
-        for (int i = 0; i < MT; ++i) {
-          const v4i d = __builtin_amdgcn_mfma_i32_16x16x64_i8(av[i][h], b, magic, 0, 0, 0);
-          if (DUMP) {
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-              const int m = i * 16 + rowq + q;
-              if (g < a.G && m >= a.m0 && m < a.m0 + a.mc && n >= a.n0 && n < a.n0 + a.nc)
-                a.P[((size_t)(m - a.m0) * a.nc + (n - a.n0)) * a.G + g] = (d[q] - kMagicBits) >> 4;
+              for (int q = 0; q < 4; ++q) {
+                const int m = i * 16 + rowq + q;
+                if (p < pn && g < G && m >= a.m0 && m < a.m0 + a.mc && n >= a.n0 && n < a.n0 + a.nc)
+                  a.P[((size_t)(m - a.m0) * a.nc + (n - a.n0)) * G + g] = (d[q] - kMagicBits) >> 4;
+              }
+            } else {
+              float u;
+              u = __builtin_fmaf(__int_as_float(d[0]), swf, nsw);
+              acc[c][i][0] = __builtin_fmaf(u, t[p].sx[i][h][0], acc[c][i][0]);
+              u = __builtin_fmaf(__int_as_float(d[1]), swf, nsw);
+              acc[c][i][1] = __builtin_fmaf(u, t[p].sx[i][h][1], acc[c][i][1]);
+              u = __builtin_fmaf(__int_as_float(d[2]), swf, nsw);
+              acc[c][i][2] = __builtin_fmaf(u, t[p].sx[i][h][2], acc[c][i][2]);
+              u = __builtin_fmaf(__int_as_float(d[3]), swf, nsw);
+              acc[c][i][3] = __builtin_fmaf(u, t[p].sx[i][h][3], acc[c][i][3]);
             }
-          } else {
-            float t;
-            t = __builtin_fmaf(__int_as_float(d[0]), swf, nsw);
-            acc[i][0] = __builtin_fmaf(t, sx[i][h][0], acc[i][0]);
-            t = __builtin_fmaf(__int_as_float(d[1]), swf, nsw);
-            acc[i][1] = __builtin_fmaf(t, sx[i][h][1], acc[i][1]);
-            t = __builtin_fmaf(__int_as_float(d[2]), swf, nsw);
-            acc[i][2] = __builtin_fmaf(t, sx[i][h][2], acc[i][2]);
-            t = __builtin_fmaf(__int_as_float(d[3]), swf, nsw);
-            acc[i][3] = __builtin_fmaf(t, sx[i][h][3], acc[i][3]);
           }
         }
-      }
     }
   }
   if (DUMP) return;
 
-  // ---- ordered reduction of the W partial tiles, then the epilogue ----
+  // epilogue operands into LDS (the barriers below order them)
+  if (tid < EUN) {
+    float u = 0.0f;
 #pragma unroll
-  for (int i = 0; i < MT; ++i)
-#pragma unroll
-    for (int q = 0; q < 4; ++q) red[((wave * MT + i) * 4 + q) * 64 + lane] = acc[i][q];
-  __syncthreads();
+    for (int sl = 0; sl < kMaxUSlices; ++sl) u += sl < a.u_slices ? upre[sl] : 0.0f;
+    const int c = tid / (MT * 16), row = tid % (MT * 16);
+    for (int sl = kMaxUSlices; sl < a.u_slices; ++sl)   // long K: the remaining slices
+      u += a.uw[((size_t)sl * a.ucols + (size_t)proj * a.r + c) * a.Mpad + row];
+    eu[tid] = u;
+  }
+  for (int p = tid + nthr; p < EUN; p += nthr) {       // more elements than threads
+    const int c = p / (MT * 16), row = p % (MT * 16);
+    float u = 0.0f;
+    for (int sl = 0; sl < a.u_slices; ++sl)
+      u += a.uw[((size_t)sl * a.ucols + (size_t)proj * a.r + c) * a.Mpad + row];
+    eu[p] = u;
+  }
+  if (tid < ELN) el2[tid] = l2pre;
+  for (int p = tid + nthr; p < ELN; p += nthr)
+    el2[p] = bf16_to_f32(a.L2[((size_t)proj * a.r + p / (16 * CT)) * a.N + min(nt0 * 16 + p % (16 * CT), a.N - 1)]);
+  if (tid < 16 * CT) eb[tid] = bpre;
 
-  for (int i = wave; i < MT; i += W) {
-    float y[4] = {0.f, 0.f, 0.f, 0.f};
-    for (int v = 0; v < W; ++v)
+  // ---- halving tree over the W partial tiles (fixed pairing: wave w adds
+  // wave w + h at each level), then the epilogue in wave 0.. ----
+  constexpr int E = CT * MT * 4;                       // values per lane
+  for (int w = W; w > 1;) {
+    const int h = (w + 1) / 2;                          // waves [h, w) hand over
+    if (wave >= h && wave < w) {
+      float *dst = red + (wave - h) * E * 64;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) y[q] += red[((v * MT + i) * 4 + q) * 64 + lane];
-    const int mrow = i * 16 + rowq;
-    if (!ncol || mrow >= a.M) continue;
-    for (int c = 0; c < a.r; ++c) {
-      const float l2 = el2[c * 16 + colq];
+      for (int c = 0; c < CT; ++c)
 #pragma unroll
-      for (int q = 0; q < 4; ++q) y[q] = __builtin_fmaf(eu[c * MT * 16 + mrow + q], l2, y[q]);
+        for (int i = 0; i < MT; ++i)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) dst[((c * MT + i) * 4 + q) * 64 + lane] = acc[c][i][q];
     }
-    const float bb = eb[colq];
+    __syncthreads();
+    if (wave < w - h) {
+      const float *src = red + wave * E * 64;
+#pragma unroll
+      for (int c = 0; c < CT; ++c)
+#pragma unroll
+        for (int i = 0; i < MT; ++i)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) acc[c][i][q] += src[((c * MT + i) * 4 + q) * 64 + lane];
+    }
+    __syncthreads();
+    w = h;
+  }
+  if (W == 1) __syncthreads();                          // epilogue operands
+
+  // wave 0 holds the sums: hand them to the waves that write (c, i) tiles
+  if (wave == 0) {
+#pragma unroll
+    for (int c = 0; c < CT; ++c)
+#pragma unroll
+      for (int i = 0; i < MT; ++i)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) red[((c * MT + i) * 4 + q) * 64 + lane] = acc[c][i][q];
+  }
+  __syncthreads();
+  for (int ci = wave; ci < CT * MT; ci += W) {
+    const int c = ci / MT, i = ci % MT;
+    const int n = (nt0 + c) * 16 + colq;
+    const int mrow = i * 16 + rowq;
+    if (n >= a.N || mrow >= a.M) continue;
+    float y[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) y[q] = red[((c * MT + i) * 4 + q) * 64 + lane];
+    for (int k = 0; k < a.r; ++k) {
+      const float l2 = el2[k * 16 * CT + c * 16 + colq];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) y[q] = __builtin_fmaf(eu[k * MT * 16 + mrow + q], l2, y[q]);
+    }
+    const float bb = eb[c * 16 + colq];
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int m = mrow + q;
@@ -187,31 +272,66 @@ __global__ __launch_bounds__(512) void k_gemm_skinny(GemmArgs a, int W) {
   }
 }
 
-template <int MT>
-hipError_t launch_mt(const GemmArgs &a, int batch, bool dump, hipStream_t s) {
-  const int NT = ceil_div(a.N, kTile), GP = a.Gp / 2;
-  // waves per workgroup: enough to put ~4 waves on every SIMD of the chip
-  int W = ceil_div(4096, NT * batch);
-  if (W > 8) W = 8;
-  if (W > GP) W = GP;
-  if (W < 1) W = 1;
-  const size_t lds = ((size_t)W * MT * 4 * 64 + (size_t)a.r * MT * 16 + (size_t)a.r * 16 + 16) * sizeof(float);
+template <int MT, int P, int CT>
+hipError_t launch_cfg(const GemmArgs &a, int batch, bool dump, int W, hipStream_t s) {
+  const int NT = ceil_div(a.N, kTile);
+  const size_t lds = ((size_t)(W + 1) / 2 * CT * MT * 4 * 64 + (size_t)a.r * MT * 16 + (size_t)a.r * 16 * CT +
+                      16 * CT) * sizeof(float);
   if (dump) {
-    const int nt0 = a.n0 / 16, nt1 = (a.n0 + a.nc - 1) / 16;
-    hipLaunchKernelGGL((k_gemm_skinny<MT, true>), dim3((unsigned)(nt1 - nt0 + 1), 1u),
+    const int g0 = a.n0 / (16 * CT), g1 = (a.n0 + a.nc - 1) / (16 * CT);
+    hipLaunchKernelGGL((k_gemm_skinny<MT, P, CT, true>), dim3((unsigned)(g1 - g0 + 1), 1u),
                        dim3((unsigned)(64 * W)), 0, s, a, W);
   } else {
-    hipLaunchKernelGGL((k_gemm_skinny<MT, false>), dim3((unsigned)NT, (unsigned)batch),
+    hipLaunchKernelGGL((k_gemm_skinny<MT, P, CT, false>), dim3((unsigned)ceil_div(NT, CT), (unsigned)batch),
                        dim3((unsigned)(64 * W)), lds, s, a, W);
   }
   return hipGetLastError();
+}
+
+// Waves W: enough runs of P group pairs to cover K, at most max_waves(MT)
+// per workgroup (longer K loops over runs, balanced).
+int waves_for(int GP, int P, int mt) {
+  const int runs = ceil_div(GP, P);
+  return ceil_div(runs, ceil_div(runs, max_waves(mt)));
+}
+
+// One row tile: runs of 4 pairs x 1 column tile, or 2 pairs x CT column
+// tiles (the activation operands of a pair then serve CT weight blocks).
+// Cost = sequential runs per wave x rounds of 4096 waves (about what the
+// chip holds at this register use), with a penalty when fewer workgroups
+// than CUs stream; the cheapest shape wins, wider CT on ties.
+hipError_t launch_mt1(const GemmArgs &a, int batch, bool dump, hipStream_t s) {
+  const int NT = ceil_div(a.N, kTile), GP = a.Gp / 2;
+  auto cost = [&](int P, int CT) {
+    const int W = waves_for(GP, P, 1);
+    const long long wgs = (long long)ceil_div(NT, CT) * batch;
+    const long long waves = wgs * W;
+    long long c = (long long)ceil_div(ceil_div(GP, P), W) * ((waves + 4095) / 4096) * 4;
+    if (wgs < 256) c += (256 - wgs) * 4 / 256 + 1;   // idle CUs
+    return c;
+  };
+  int best = 0;
+  const long long cs[4] = {cost(4, 1), cost(2, 2), cost(2, 3), cost(2, 4)};
+  for (int k = 1; k < 4; ++k)
+    if (cs[k] <= cs[best]) best = k;
+  switch (best) {
+    case 3: return launch_cfg<1, 2, 4>(a, batch, dump, waves_for(GP, 2, 1), s);
+    case 2: return launch_cfg<1, 2, 3>(a, batch, dump, waves_for(GP, 2, 1), s);
+    case 1: return launch_cfg<1, 2, 2>(a, batch, dump, waves_for(GP, 2, 1), s);
+    default: return launch_cfg<1, 4, 1>(a, batch, dump, waves_for(GP, 4, 1), s);
+  }
+}
+
+template <int MT>
+hipError_t launch_mt(const GemmArgs &a, int batch, bool dump, hipStream_t s) {
+  return launch_cfg<MT, 2, 1>(a, batch, dump, waves_for(a.Gp / 2, 2, MT), s);
 }
 
 }  // namespace
 
 hipError_t launch_gemm_skinny(const GemmArgs &a, int batch, bool dump, hipStream_t s) {
   switch (ceil_div(a.M, kTile)) {
-    case 1: return launch_mt<1>(a, batch, dump, s);
+    case 1: return launch_mt1(a, batch, dump, s);
     case 2: return launch_mt<2>(a, batch, dump, s);
     case 3: return launch_mt<3>(a, batch, dump, s);
     case 4: return launch_mt<4>(a, batch, dump, s);

@@ -127,6 +127,23 @@ __global__ __launch_bounds__(256, 2) void k_gemm_tiled(GemmArgs a, int nblk, int
   v2u rb[2][2];
   float rsx[2];
   uint32_t rsw[2];
+  // Addresses: buffer resources over the operands, a fixed 32-bit byte
+  // offset per lane (computed once) and a per-stage scalar offset, so a
+  // stage costs no vector address math.
+  const __amdgpu_buffer_rsrc_t rs_a = buffer_rsrc(a.qa, (uint32_t)MT * a.Gp * 1024);
+  const __amdgpu_buffer_rsrc_t rs_w = buffer_rsrc(w, (uint32_t)NT * GP * 1024);
+  const __amdgpu_buffer_rsrc_t rs_x = buffer_rsrc(a.sxs, (uint32_t)MT * a.Gp * 64);
+  const __amdgpu_buffer_rsrc_t rs_s = buffer_rsrc(sw, DUMP ? 0u : (uint32_t)G * a.N * 2);
+  uint32_t offa[2], offb[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int c = i * 256 + tid;                      // 16-byte chunk of the A / B tile
+    const int mt = min(mt0 + (c >> 6), MT - 1), nt = min(nt0 + (c >> 6), NT - 1);
+    offa[i] = ((uint32_t)mt * a.Gp * 64 + (c & 63)) * 16;
+    offb[i] = ((uint32_t)nt * GP * 64 + (c & 63)) * 16;
+  }
+  const uint32_t offsx = ((uint32_t)min(mt0 + ((tid >> 4) & 7), MT - 1) * a.Gp * 16 + (tid & 15)) * 4;
+  const uint32_t offsw = (uint32_t)min(nt0 * 16 + (tid & 127), a.N - 1) * 2;
   // Straight-line code with a fixed number of loads per stage (the stage
   // index is clamped near the end instead of skipping the loads), so the
   // compiler's wait counting stays exact and waits only for the older slot.
@@ -135,28 +152,11 @@ __global__ __launch_bounds__(256, 2) void k_gemm_tiled(GemmArgs a, int nblk, int
     g = min(g, a.Gp - 1);
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-      const int c = i * 256 + tid;                    // 16-byte chunk of the A tile
-      const int mi = c >> 6, l = c & 63;
-      const int mt = min(mt0 + mi, MT - 1);
-      ra[SL][i] = *reinterpret_cast<const v4u *>(a.qa + (((size_t)mt * a.Gp + g) * 64 + l) * 16);
+      ra[SL][i] = __builtin_amdgcn_raw_buffer_load_b128(rs_a, offa[i], g * 1024, 0);
+      rb[SL][i] = __builtin_amdgcn_raw_buffer_load_b64(rs_w, offb[i], (g >> 1) * 1024 + 8 * (g & 1), 0);
     }
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int c = i * 256 + tid;                    // lane slot of the packed B tile
-      const int ni = c >> 6, l = c & 63;
-      const int nt = min(nt0 + ni, NT - 1);
-      rb[SL][i] = *reinterpret_cast<const v2u *>(
-          w + (((size_t)nt * GP + (g >> 1)) * 64 + l) * 16 + 8 * (g & 1));
-    }
-    {
-      const int mi = (tid >> 4) & 7, row = tid & 15;
-      const int mt = min(mt0 + mi, MT - 1);
-      rsx[SL] = a.sxs[((size_t)mt * a.Gp + g) * 16 + row];
-    }
-    if (!DUMP) {
-      const int n = min(nt0 * 16 + (tid & 127), a.N - 1);
-      rsw[SL] = sw[(size_t)min(g, G - 1) * a.N + n];
-    }
+    rsx[SL] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs_x, offsx, g * 64, 0));
+    if (!DUMP) rsw[SL] = __builtin_amdgcn_raw_buffer_load_b16(rs_s, offsw, min(g, G - 1) * a.N * 2, 0);
   };
   auto store_stage = [&](int g, auto slotc, int buf) __attribute__((always_inline)) {
     constexpr int SL = decltype(slotc)::value;
