@@ -101,6 +101,118 @@ def cpu_baseline(layer_dict, spec, seconds: float):
     }
 
 
+def device_info(torch):
+    p = torch.cuda.get_device_properties(0)
+    return {"name": p.name, "arch": getattr(p, "gcnArchName", ""), "cus": p.multi_processor_count,
+            "hbm_gib": round(p.total_memory / 2**30, 1), "hip": torch.version.hip}
+
+
+def _csv_rows(path):
+    import csv
+    with open(path, newline="") as f:
+        return list(csv.DictReader(f))
+
+
+def _find(d, suffix):
+    for root, _, files in os.walk(d):
+        for f in files:
+            if f.endswith(suffix):
+                return os.path.join(root, f)
+    return None
+
+
+def summarize_profiles(args):
+    """Summaries of rocprofv3 output directories (csv output format).
+
+    A directory with a kernel-trace ``*_kernel_stats.csv`` gives per-kernel
+    launch counts and average durations.  Directories with
+    ``*_counter_collection.csv`` give per-dispatch counter averages; when
+    both FETCH_SIZE and WRITE_SIZE appear (separate passes over the same
+    command) together with the reference copy (``--copy-mb``), the
+    contraction's HBM bytes per launch are scaled by what the counters read
+    for the copy, whose true traffic is known (read + write of its size).
+    With --write-traffic the result goes into profiles/traffic.json, keyed by
+    layer and kernel, together with the hash of the kernel source it was
+    measured on."""
+    out = []
+    counters = {}
+    copy = {}
+    meta = {}
+    for d in args.summarize:
+        ks = _find(d, "kernel_stats.csv")
+        if ks:
+            out.append(f"kernel stats ({d}):")
+            out.append(f"  {'kernel':70s} {'calls':>6s} {'avg us':>10s} {'min us':>10s} {'max us':>10s}")
+            for r in sorted(_csv_rows(ks), key=lambda r: -float(r["TotalDurationNs"])):
+                out.append(f"  {r['Name'][:70]:70s} {int(r['Calls']):6d} "
+                           f"{float(r['AverageNs']) / 1e3:10.2f} {float(r['MinNs']) / 1e3:10.2f} "
+                           f"{float(r['MaxNs']) / 1e3:10.2f}")
+        cc = _find(d, "counter_collection.csv")
+        if cc:
+            per = {}
+            for r in _csv_rows(cc):
+                key = (r["Dispatch_Id"], r["Kernel_Name"])
+                per.setdefault(key, {}).setdefault(r["Counter_Name"], 0.0)
+                per[key][r["Counter_Name"]] += float(r["Counter_Value"])
+            byname = {}
+            for (did, name), vals in sorted(per.items(), key=lambda kv: int(kv[0][0])):
+                for c, v in vals.items():
+                    byname.setdefault(name, {}).setdefault(c, []).append(v)
+            out.append(f"counters ({d}), average per dispatch:")
+            for name, cs in sorted(byname.items()):
+                short = name[:70]
+                txt = ", ".join(f"{c} {sum(v) / len(v):.6g} (n={len(v)})" for c, v in cs.items())
+                out.append(f"  {short:70s} {txt}")
+                for c, v in cs.items():
+                    if "copyBuffer" in name:
+                        # the reference copies are the last three copies of the run
+                        copy[c] = sum(v[-3:]) / len(v[-3:])
+                    elif "k_gemm" in name:
+                        # skip the first launches (warm-up, graph upload)
+                        vv = v[2:] if len(v) > 4 else v
+                        counters.setdefault(name, {})[c] = sum(vv) / len(vv)
+    text = "\n".join(out)
+    print(text)
+    if copy and counters:
+        log = [l for l in out]
+        res = {}
+        for name, cs in counters.items():
+            if "FETCH_SIZE" not in cs or "WRITE_SIZE" not in cs:
+                continue
+            kern = "skinny" if "skinny" in name else "tiled"
+            res[kern] = cs
+        if res and "FETCH_SIZE" in copy and "WRITE_SIZE" in copy and args.copy_mb > 0:
+            nb = int(args.copy_mb * 1e6) // 16 * 16
+            f_fac = (nb / 1024) / copy["FETCH_SIZE"]      # true KiB read per counted KiB
+            w_fac = (nb / 1024) / copy["WRITE_SIZE"]
+            layer = args.layer if args.tokens is None else f"{args.layer}_M{args.tokens}"
+            print(f"copy calibration: {args.copy_mb} MB; FETCH_SIZE factor {f_fac:.4f}, "
+                  f"WRITE_SIZE factor {w_fac:.4f}")
+            if args.write_traffic:
+                try:
+                    with open(TRAFFIC_FILE) as f:
+                        rec = json.load(f)
+                except (OSError, ValueError):
+                    rec = {}
+                for kern, cs in res.items():
+                    fetch = cs["FETCH_SIZE"] * 1024 * f_fac
+                    write = cs["WRITE_SIZE"] * 1024 * w_fac
+                    rec.setdefault(layer, {})[kern] = {
+                        "bytes_per_launch": int(fetch + write),
+                        "fetch_bytes": int(fetch), "write_bytes": int(write),
+                        "fetch_kib_counted": round(cs["FETCH_SIZE"], 1),
+                        "write_kib_counted": round(cs["WRITE_SIZE"], 1),
+                        "copy_factor_fetch": round(f_fac, 4), "copy_factor_write": round(w_fac, 4),
+                        "source_sha256_16": source_hash(KERNEL_SOURCES[kern]),
+                    }
+                    print(f"{layer} {kern}: {int(fetch + write)} bytes per launch "
+                          f"(fetch {int(fetch)}, write {int(write)})")
+                with open(TRAFFIC_FILE, "w") as f:
+                    json.dump(rec, f, indent=1, sort_keys=True)
+                    f.write("\n")
+    return 0
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -115,7 +227,17 @@ def main(argv=None):
                     help="total bytes of rotated input/output copies (defeats the 256 MB MALL)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-mb", type=float, default=0.0,
+                    help="after the timed region, run 3 device-to-device copies of this many MB "
+                         "(the reference kernel for scaling rocprofv3 byte counters)")
+    ap.add_argument("--summarize", nargs="+", metavar="DIR",
+                    help="summarize rocprofv3 output directories instead of running "
+                         "(see summarize_profiles)")
+    ap.add_argument("--write-traffic", action="store_true",
+                    help="with --summarize: record the measured HBM bytes in profiles/traffic.json")
     args = ap.parse_args(argv)
+    if args.summarize:
+        return summarize_profiles(args)
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -211,6 +333,35 @@ def main(argv=None):
     q_avg = timed("quantize") / args.steps
     c_avg = timed("contract") / args.steps
     ms_step = total_ms / args.steps
+
+    # per-step spread: one-step graphs (one per input set), each replay
+    # bracketed by events on the capture stream
+    one = []
+    for k in range(min(nsets, args.steps)):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(cap):
+            with torch.cuda.graph(g, stream=cap):
+                step(k)
+        one.append(g)
+    pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+             for _ in range(args.steps)]
+    with torch.cuda.stream(cap):
+        for i in range(args.steps):
+            pairs[i][0].record(cap)
+            one[i % len(one)].replay()
+            pairs[i][1].record(cap)
+    torch.cuda.synchronize()
+    per_step = np.array([a.elapsed_time(b) for a, b in pairs]) * 1e3
+    spread = {q: round(float(np.percentile(per_step, p)), 2)
+              for q, p in (("p10", 10), ("p50", 50), ("p90", 90))}
+
+    if args.copy_mb > 0:
+        nb = int(args.copy_mb * 1e6) // 16 * 16
+        src = torch.empty(nb, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
     ops = spec.ops
     value = ops / (ms_step * 1e-3) / 1e12
 
@@ -253,6 +404,8 @@ def main(argv=None):
         },
         "stages_ms": {"quantize": round(q_avg, 5), "contract": round(c_avg, 5),
                       "timing": "HIP graph replay, events on the capture stream"},
+        "step_us": spread,
+        "device": device_info(torch),
         "layer_hbm_frac": round(algorithmic_bytes(M, K, N, r, B, y_bytes) / (ms_step * 1e-3)
                                 / (PEAK_HBM_GBS * 1e9), 4),
         "wall_s": round(wall, 4),
