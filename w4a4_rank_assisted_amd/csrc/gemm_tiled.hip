@@ -37,8 +37,13 @@ namespace {
 constexpr uint32_t kNibMask = 0xF0F0F0F0u;
 constexpr int BM = 128, BN = 128;
 constexpr int TMB = BM / 16, TNB = BN / 16;   // MFMA tiles per block
-constexpr int TM = TMB / 2, TN = TNB / 2;     // MFMA tiles per wave
+constexpr int WM = 2, WN = 4;                 // waves along M and N
+constexpr int NTH = 64 * WM * WN;             // threads per workgroup
+constexpr int TM = TMB / WM, TN = TNB / WN;   // MFMA tiles per wave (64 x 32 outputs)
 constexpr int kGroupM = 8;                    // m-blocks per tile-order group
+constexpr int kSlots = 2;                     // register slots: loads run kSlots stages ahead
+static_assert(TMB * 64 == NTH && TNB * 64 == NTH, "one A chunk and one B slot per thread");
+static_assert(TMB * 16 <= NTH / 2 && BN <= NTH / 2, "scale loads: sx in the first half, sw in the second");
 
 struct alignas(16) Stages {
   int8_t a[2][TMB][64][16];           // [buf][m-tile][lane][bytes]          16 KB
@@ -99,13 +104,13 @@ __device__ __forceinline__ void tile_of(int bid, int nblk, int mblk, int &mb, in
 }
 
 template <bool DUMP, int RPT>
-__global__ __launch_bounds__(256, 2) void k_gemm_tiled(GemmArgs a, int nblk, int mblk) {
+__global__ __launch_bounds__(NTH, 2) void k_gemm_tiled(GemmArgs a, int nblk, int mblk) {
   __shared__ Smem<RPT> smem;
   Stages &sm = smem.st;
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / WN, wn = wave % WN;
   const int proj = blockIdx.y;
   int mb, nb;
   tile_of(blockIdx.x, nblk, mblk, mb, nb);
@@ -123,10 +128,10 @@ __global__ __launch_bounds__(256, 2) void k_gemm_tiled(GemmArgs a, int nblk, int
   // addresses, straight-line code); the edge masks are applied on the way
   // into LDS, where only masked rows / columns see those values.
   const int G = a.G;
-  v4u ra[2][2];
-  v2u rb[2][2];
-  float rsx[2];
-  uint32_t rsw[2];
+  v4u ra[kSlots];
+  v2u rb[kSlots];
+  float rsx[kSlots];
+  uint32_t rsw[kSlots];
   // Addresses: buffer resources over the operands, a fixed 32-bit byte
   // offset per lane (computed once) and a per-stage scalar offset, so a
   // stage costs no vector address math.
@@ -134,49 +139,36 @@ __global__ __launch_bounds__(256, 2) void k_gemm_tiled(GemmArgs a, int nblk, int
   const __amdgpu_buffer_rsrc_t rs_w = buffer_rsrc(w, (uint32_t)NT * GP * 1024);
   const __amdgpu_buffer_rsrc_t rs_x = buffer_rsrc(a.sxs, (uint32_t)MT * a.Gp * 64);
   const __amdgpu_buffer_rsrc_t rs_s = buffer_rsrc(sw, DUMP ? 0u : (uint32_t)G * a.N * 2);
-  uint32_t offa[2], offb[2];
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int c = i * 256 + tid;                      // 16-byte chunk of the A / B tile
-    const int mt = min(mt0 + (c >> 6), MT - 1), nt = min(nt0 + (c >> 6), NT - 1);
-    offa[i] = ((uint32_t)mt * a.Gp * 64 + (c & 63)) * 16;
-    offb[i] = ((uint32_t)nt * GP * 64 + (c & 63)) * 16;
-  }
-  const uint32_t offsx = ((uint32_t)min(mt0 + ((tid >> 4) & 7), MT - 1) * a.Gp * 16 + (tid & 15)) * 4;
-  const uint32_t offsw = (uint32_t)min(nt0 * 16 + (tid & 127), a.N - 1) * 2;
+  // thread t: 16-byte chunk t of the A tile, lane slot t of the B tile;
+  // the first half also one activation scale, the second one weight scale
+  const uint32_t offa = ((uint32_t)min(mt0 + (tid >> 6), MT - 1) * a.Gp * 64 + (tid & 63)) * 16;
+  const uint32_t offb = ((uint32_t)min(nt0 + (tid >> 6), NT - 1) * GP * 64 + (tid & 63)) * 16;
+  const uint32_t offsx = ((uint32_t)min(mt0 + ((tid >> 4) & (TMB - 1)), MT - 1) * a.Gp * 16 + (tid & 15)) * 4;
+  const uint32_t offsw = (uint32_t)min(nt0 * 16 + (tid & (BN - 1)), a.N - 1) * 2;
   // Straight-line code with a fixed number of loads per stage (the stage
   // index is clamped near the end instead of skipping the loads), so the
   // compiler's wait counting stays exact and waits only for the older slot.
   auto load_stage = [&](int g, auto slotc) __attribute__((always_inline)) {
     constexpr int SL = decltype(slotc)::value;
     g = min(g, a.Gp - 1);
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      ra[SL][i] = __builtin_amdgcn_raw_buffer_load_b128(rs_a, offa[i], g * 1024, 0);
-      rb[SL][i] = __builtin_amdgcn_raw_buffer_load_b64(rs_w, offb[i], (g >> 1) * 1024 + 8 * (g & 1), 0);
-    }
+    ra[SL] = __builtin_amdgcn_raw_buffer_load_b128(rs_a, offa, g * 1024, 0);
+    rb[SL] = __builtin_amdgcn_raw_buffer_load_b64(rs_w, offb, (g >> 1) * 1024 + 8 * (g & 1), 0);
     rsx[SL] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs_x, offsx, g * 64, 0));
     if (!DUMP) rsw[SL] = __builtin_amdgcn_raw_buffer_load_b16(rs_s, offsw, min(g, G - 1) * a.N * 2, 0);
   };
   auto store_stage = [&](int g, auto slotc, int buf) __attribute__((always_inline)) {
     constexpr int SL = decltype(slotc)::value;
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int c = i * 256 + tid;
-      *reinterpret_cast<v4u *>(&sm.a[buf][c >> 6][c & 63][0]) = ra[SL][i];
-    }
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int c = i * 256 + tid;
-      const v2u v = rb[SL][i];
-      *reinterpret_cast<v4u *>(&sm.b[buf][c >> 6][c & 63][0]) =
+    *reinterpret_cast<v4u *>(&sm.a[buf][tid >> 6][tid & 63][0]) = ra[SL];
+    {
+      const v2u v = rb[SL];
+      *reinterpret_cast<v4u *>(&sm.b[buf][tid >> 6][tid & 63][0]) =
           (v4u){v.x & kNibMask, (v.x << 4) & kNibMask, v.y & kNibMask, (v.y << 4) & kNibMask};
     }
-    if (wave < 2) {
+    if (tid < TMB * 16) {
       const int mi = tid >> 4, row = tid & 15;
       sm.sx[buf][mi][row] = (mt0 + mi < MT) ? rsx[SL] : 0.0f;
-    } else if (!DUMP) {
-      const int col = tid - 128, n = nt0 * 16 + col;
+    } else if (!DUMP && tid >= NTH / 2 && tid < NTH / 2 + BN) {
+      const int col = tid - NTH / 2, n = nt0 * 16 + col;
       const float sv = (g < G && n < a.N) ? f16_to_f32((uint16_t)rsw[SL]) : 0.0f;
       sm.sw[buf][col] = make_float2(sv, -kMagic * sv);
     }
@@ -197,14 +189,14 @@ __global__ __launch_bounds__(256, 2) void k_gemm_tiled(GemmArgs a, int nblk, int
 
   // ---- epilogue operands: loads issued first, so that their latency
   // overlaps the first stages' loads; parked in LDS below ----
-  constexpr int EU = RPT * BM / 256;  // (rank column, row) pairs per thread
+  constexpr int EU = RPT * BM / NTH;  // (rank column, row) pairs per thread
   constexpr int US = RPT <= 8 ? kMaxUSlices : kMaxUSlices / 2;  // U slices prefetched
   float eu[EU > 0 ? EU : 1][US], el2[EU > 0 ? EU : 1], ebias = 0.0f;
   if (!DUMP) {
     const uint16_t *L2 = a.L2 + (size_t)proj * a.r * a.N;
 #pragma unroll
     for (int e = 0; e < EU; ++e) {
-      const int idx = e * 256 + tid, c = idx / BM, rr = idx % BM;
+      const int idx = e * NTH + tid, c = idx / BM, rr = idx % BM;
       const int cc = min(c, a.r - 1);
       const int m = min(mt0 * 16 + rr, a.Mpad - 1);
 #pragma unroll
@@ -216,11 +208,15 @@ __global__ __launch_bounds__(256, 2) void k_gemm_tiled(GemmArgs a, int nblk, int
   }
 
   load_stage(0, int_c<0>{});
-  load_stage(1, int_c<1>{});          // Gp >= 2
+  load_stage(1, int_c<1>{});          // Gp >= 2; later stages past the end are clamped reloads
+  if constexpr (kSlots > 2) {
+    load_stage(2, int_c<2 % kSlots>{});
+    load_stage(3, int_c<3 % kSlots>{});
+  }
   if (!DUMP) {
 #pragma unroll
     for (int e = 0; e < EU; ++e) {
-      const int idx = e * 256 + tid, c = idx / BM, rr = idx % BM;
+      const int idx = e * NTH + tid, c = idx / BM, rr = idx % BM;
       float u = 0.0f;
 #pragma unroll
       for (int sl = 0; sl < US; ++sl) u += sl < a.u_slices ? eu[e][sl] : 0.0f;
@@ -240,76 +236,126 @@ __global__ __launch_bounds__(256, 2) void k_gemm_tiled(GemmArgs a, int nblk, int
   store_stage(0, int_c<0>{}, 0);
   __syncthreads();
 
-  auto stage = [&](int g, auto slotc) __attribute__((always_inline)) {
-    constexpr int SL = decltype(slotc)::value;  // == g & 1 == LDS buffer
-    load_stage(g + 2, slotc);         // past the end: a clamped, unused reload
+  // ---- the stage loop: TM row tiles per stage, software-pipelined across
+  // stages.  Step s of stage g issues the MFMAs of row s and rescales the
+  // row before it: row s-1 of stage g, or, at s = 0, the last row of stage
+  // g-1 (its MFMA results, weight scales and activation scales are carried
+  // over), so the pipeline never drains at a stage boundary.
+  v4i d[TM][TN];                      // MFMA results (row TM-1 carried)
+  float2 swv[2][TN];                  // weight scales per LDS buffer
+  float4 sxv[TM], sx_carry;           // activation scales; last row of the previous stage
+#pragma unroll
+  for (int j = 0; j < TN; ++j) {
+    d[TM - 1][j] = magic;             // a first carry that adds exactly 0
+    swv[1][j] = make_float2(0.0f, 0.0f);
+  }
+  sx_carry = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
 
-    // ---- TM row tiles, software-pipelined ----
+  // rescale one row tile: acc += (D - magic) * sw * sx, or, for the test
+  // export, the group partials of the window
+  auto rescale = [&](int ip, const float2 (&sw2)[TN], const float4 sx4, int gg)
+      __attribute__((always_inline)) {
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      if (DUMP) {
+        const int n = (nt0 + wn * TN + j) * 16 + colq;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int m = (mt0 + wm * TM + ip) * 16 + rowq + q;
+          if (gg >= 0 && gg < G && m >= a.m0 && m < a.m0 + a.mc && n >= a.n0 && n < a.n0 + a.nc)
+            a.P[((size_t)(m - a.m0) * a.nc + (n - a.n0)) * G + gg] = (d[ip][j][q] - kMagicBits) >> 4;
+        }
+      } else {
+        const float2 s2 = sw2[j];
+        const float u0 = __builtin_fmaf(__int_as_float(d[ip][j][0]), s2.x, s2.y);
+        const float u1 = __builtin_fmaf(__int_as_float(d[ip][j][1]), s2.x, s2.y);
+        const float u2 = __builtin_fmaf(__int_as_float(d[ip][j][2]), s2.x, s2.y);
+        const float u3 = __builtin_fmaf(__int_as_float(d[ip][j][3]), s2.x, s2.y);
+        acc[ip][j][0] = __builtin_fmaf(u0, sx4.x, acc[ip][j][0]);
+        acc[ip][j][1] = __builtin_fmaf(u1, sx4.y, acc[ip][j][1]);
+        acc[ip][j][2] = __builtin_fmaf(u2, sx4.z, acc[ip][j][2]);
+        acc[ip][j][3] = __builtin_fmaf(u3, sx4.w, acc[ip][j][3]);
+      }
+    }
+    if (!DUMP) {
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) pin(acc[ip][j][q]);
+    }
+  };
+
+  auto stage = [&](int g, auto slotc) __attribute__((always_inline)) {
+    constexpr int SL = decltype(slotc)::value;  // register slot == g % kSlots
+    constexpr int BUF = SL & 1;                   // LDS buffer == g & 1
+    load_stage(g + kSlots, slotc);    // past the end: a clamped, unused reload
+
     v4i bv[TN];
-    float2 swv[TN];
-    v4i d[TM][TN];
-    float4 sxv[TM];
     v4i av[TM];
 #pragma unroll
     for (int j = 0; j < TN; ++j) {
-      bv[j] = *reinterpret_cast<const v4i *>(&sm.b[SL][wn * TN + j][lane][0]);
-      swv[j] = sm.sw[SL][(wn * TN + j) * 16 + colq];
+      bv[j] = *reinterpret_cast<const v4i *>(&sm.b[BUF][wn * TN + j][lane][0]);
+      swv[BUF][j] = sm.sw[BUF][(wn * TN + j) * 16 + colq];
     }
     auto read_a = [&](int i) __attribute__((always_inline)) {
-      av[i] = *reinterpret_cast<const v4i *>(&sm.a[SL][wm * TM + i][lane][0]);
-      sxv[i] = *reinterpret_cast<const float4 *>(&sm.sx[SL][wm * TM + i][rowq]);
+      av[i] = *reinterpret_cast<const v4i *>(&sm.a[BUF][wm * TM + i][lane][0]);
+      sxv[i] = *reinterpret_cast<const float4 *>(&sm.sx[BUF][wm * TM + i][rowq]);
     };
     read_a(0);
 #pragma unroll
-    for (int s = 0; s <= TM; ++s) {
-      if (s < TM) {
-        pin(av[s]);
-        if (s + 1 < TM) read_a(s + 1);
+    for (int s = 0; s < TM; ++s) {
+      // step boundary: nothing moves across it
+      __builtin_amdgcn_sched_barrier(0);
+      pin(av[s]);
+      if (s + 1 < TM) read_a(s + 1);
+      if (s == 0) {
+        // the carried row: rescaled before this step's MFMAs overwrite
+        // nothing of it (they write row 0)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+          d[0][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(av[0], bv[j], magic, 0, 0, 0);
+        rescale(TM - 1, swv[BUF ^ 1], sx_carry, g - 1);
+      } else {
 #pragma unroll
         for (int j = 0; j < TN; ++j)
           d[s][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(av[s], bv[j], magic, 0, 0, 0);
+        rescale(s - 1, swv[BUF], sxv[s - 1], g);
       }
-      if (s == 0) continue;
-      const int ip = s - 1;                 // rescale the previous row tile
-#pragma unroll
-      for (int j = 0; j < TN; ++j) {
-        if (DUMP) {
-          const int n = (nt0 + wn * TN + j) * 16 + colq;
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const int m = (mt0 + wm * TM + ip) * 16 + rowq + q;
-            if (g < G && m >= a.m0 && m < a.m0 + a.mc && n >= a.n0 && n < a.n0 + a.nc)
-              a.P[((size_t)(m - a.m0) * a.nc + (n - a.n0)) * G + g] = (d[ip][j][q] - kMagicBits) >> 4;
-          }
-        } else {
-          const float2 s2 = swv[j];
-          float u;
-          u = __builtin_fmaf(__int_as_float(d[ip][j][0]), s2.x, s2.y);
-          acc[ip][j][0] = __builtin_fmaf(u, sxv[ip].x, acc[ip][j][0]);
-          u = __builtin_fmaf(__int_as_float(d[ip][j][1]), s2.x, s2.y);
-          acc[ip][j][1] = __builtin_fmaf(u, sxv[ip].y, acc[ip][j][1]);
-          u = __builtin_fmaf(__int_as_float(d[ip][j][2]), s2.x, s2.y);
-          acc[ip][j][2] = __builtin_fmaf(u, sxv[ip].z, acc[ip][j][2]);
-          u = __builtin_fmaf(__int_as_float(d[ip][j][3]), s2.x, s2.y);
-          acc[ip][j][3] = __builtin_fmaf(u, sxv[ip].w, acc[ip][j][3]);
-        }
-      }
+      // issue order within the step: one MFMA, then the eight rescale FMAs
+      // of one tile, and so on, so the matrix core works while the VALU
+      // rescales
       if (!DUMP) {
 #pragma unroll
-        for (int j = 0; j < TN; ++j)
-#pragma unroll
-          for (int q = 0; q < 4; ++q) pin(acc[ip][j][q]);
+        for (int j = 0; j < TN; ++j) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
+        }
       }
     }
+    __builtin_amdgcn_sched_barrier(0);
+    sx_carry = sxv[TM - 1];
 
-    // stage g+1 (loaded one stage ago) into the other LDS buffer
-    if (g + 1 < GS) store_stage(g + 1, int_c<SL ^ 1>{}, SL ^ 1);
+    // stage g+1 (loaded kSlots-1 stages ago) into the other LDS buffer
+    if (g + 1 < GS) store_stage(g + 1, int_c<(SL + 1) % kSlots>{}, BUF ^ 1);
     __syncthreads();
   };
-  for (int g = 0; g < GS; g += 2) {   // GS is even
+  // stages in fours (compile-time register slots), then the remaining two
+  // (GS is even)
+  int g = 0;
+  for (; g + kSlots <= GS; g += kSlots) {
+    stage(g, int_c<0>{});
+    stage(g + 1, int_c<1>{});
+    if constexpr (kSlots > 2) {
+      stage(g + 2, int_c<2 % kSlots>{});
+      stage(g + 3, int_c<3 % kSlots>{});
+    }
+  }
+  if (g < GS) {
     stage(g, int_c<0>{});
     stage(g + 1, int_c<1>{});
   }
+  // drain: the last row of the last stage (GS - 1 is odd: LDS buffer 1)
+  rescale(TM - 1, swv[1], sx_carry, GS - 1);
 
   if (DUMP) return;
 
@@ -341,7 +387,8 @@ __global__ __launch_bounds__(256, 2) void k_gemm_tiled(GemmArgs a, int nblk, int
 
   // output: per row tile, transpose the wave's 16 x 64 values through a
   // wave-private LDS region and store 16 bytes per lane
-  char *tbuf = reinterpret_cast<char *>(&sm) + wave * 4096;
+  constexpr int WC = TN * 16;                         // columns of the wave
+  char *tbuf = reinterpret_cast<char *>(&sm) + wave * (16 * WC * 4);
   const int ybytes = a.y_bf16 ? 2 : 4;
   const int per16 = 16 / ybytes;                      // values per 16-byte chunk
   const bool vec_ok = (a.N % per16) == 0;
@@ -354,19 +401,19 @@ __global__ __launch_bounds__(256, 2) void k_gemm_tiled(GemmArgs a, int nblk, int
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const float y = acc[i][j][q] + bj[j];
-        const int off = (rowq + q) * 64 + j * 16 + colq;  // [row][col] in the 16 x 64 tile
+        const int off = (rowq + q) * WC + j * 16 + colq;  // [row][col] in the 16 x WC tile
         if (a.y_bf16)
           reinterpret_cast<uint16_t *>(tbuf)[off] = f32_to_bf16(y);
         else
           reinterpret_cast<float *>(tbuf)[off] = y;
       }
-    // 16 rows x 64 columns; chunk k of the tile = (row k / (64/per16), chunk k % (64/per16))
-    const int cpr = 64 / per16;                         // chunks per row
+    // 16 rows x WC columns; chunk k of the tile = (row k / cpr, chunk k % cpr)
+    const int cpr = WC / per16;                         // chunks per row
     for (int k = lane; k < 16 * cpr; k += 64) {
       const int row = k / cpr, ch = k % cpr;
       const int m = mrow0 + row, n = ncol0 + ch * per16;
       if (m >= a.M) continue;
-      const v4u v = *reinterpret_cast<const v4u *>(tbuf + (row * 64 + ch * per16) * ybytes);
+      const v4u v = *reinterpret_cast<const v4u *>(tbuf + (row * WC + ch * per16) * ybytes);
       char *dst = reinterpret_cast<char *>(a.Y) + (((size_t)proj * a.M + m) * a.N + n) * ybytes;
       if (vec_ok && n + per16 <= a.N) {
         *reinterpret_cast<v4u *>(dst) = v;
@@ -387,7 +434,7 @@ __global__ __launch_bounds__(256, 2) void k_gemm_tiled(GemmArgs a, int nblk, int
 template <int RPT>
 hipError_t launch_rpt(const GemmArgs &a, int batch, int nblk, int mblk, hipStream_t s) {
   hipLaunchKernelGGL((k_gemm_tiled<false, RPT>), dim3((unsigned)(nblk * mblk), (unsigned)batch),
-                     dim3(256), 0, s, a, nblk, mblk);
+                     dim3(NTH), 0, s, a, nblk, mblk);
   return hipGetLastError();
 }
 
@@ -397,7 +444,7 @@ hipError_t launch_gemm_tiled(const GemmArgs &a, int batch, bool dump, hipStream_
   const int nblk = ceil_div(a.N, BN), mblk = ceil_div(a.M, BM);
   if (dump) {
     // every tile of one projection; blocks outside the window exit at once
-    hipLaunchKernelGGL((k_gemm_tiled<true, 0>), dim3((unsigned)(nblk * mblk), 1u), dim3(256), 0, s,
+    hipLaunchKernelGGL((k_gemm_tiled<true, 0>), dim3((unsigned)(nblk * mblk), 1u), dim3(NTH), 0, s,
                        a, nblk, mblk);
     return hipGetLastError();
   }
