@@ -205,7 +205,9 @@ def test_full_size_outputs_sampled_rows(oracle, name, M):
     (70, 640, 300, 4, 1),     # ragged M and N over several tiles
     (200, 384, 129, 32, 2),   # largest rank, two projections
     (64, 256, 256, 7, 3),     # odd rank (unvectorised L1 path), three projections
-    (300, 1152, 520, 4, 1),   # more row tiles than one block
+    (300, 1152, 520, 4, 1),   # more row tiles than one block (2 K splits)
+    (130, 4096, 130, 4, 1),   # few tiles, long K: 8 K splits, ragged M and N
+    (100, 2240, 200, 4, 3),   # 4 K splits, a pad group, three projections
 ])
 def test_ragged_shapes_match_oracle(oracle, M, K, N, r, batch):
     lay = make_random_layer(M * 31 + N, M, K, N, r=r, batch=batch, outlier_channels=2)
@@ -256,10 +258,11 @@ def test_run_twice_bitwise_deterministic():
     a = up.linear("f32").cpu().numpy()
     b = up.linear("f32").cpu().numpy()
     assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
-    small = Uploaded(make_layer("qwen3_up", 16))
-    a = small.linear("bf16").view(torch.int16).cpu().numpy()
-    b = small.linear("bf16").view(torch.int16).cpu().numpy()
-    assert np.array_equal(a, b)
+    for M in (16, 256):               # skinny; tiled with K splits
+        small = Uploaded(make_layer("qwen3_down", M))
+        a = small.linear("bf16").view(torch.int16).cpu().numpy()
+        b = small.linear("bf16").view(torch.int16).cpu().numpy()
+        assert np.array_equal(a, b)
 
 
 def test_misaligned_tensor_is_rejected():
@@ -276,9 +279,11 @@ def test_graph_replay_matches_eager(M):
     # the layer captured in a HIP graph and replayed several times, with
     # eager calls of the same layer (other buffers) in between; every replay
     # must equal the eager result bit for bit (the kernels are deterministic)
-    lay = make_random_layer(90 + M, M, 512, 300, r=4, batch=2)
+    # (M = 200: the tiled kernel in two K splits, partial tiles and the
+    # reduce pass both inside the graph)
+    lay = make_random_layer(90 + M, M, 1024, 300, r=4, batch=2)
     up = Uploaded(lay)
-    say(f"[graph] M={M} K=512 N=300 r=4 batch=2")
+    say(f"[graph] M={M} K=1024 N=300 r=4 batch=2")
     eager = up.linear("f32").view(torch.int32).cpu().numpy()
     out = torch.empty((up.B, M, up.N), dtype=torch.float32, device=DEV)
     ws = torch.empty(hsq.workspace_bytes(M, up.K, up.N, up.r, up.B), dtype=torch.uint8, device=DEV)

@@ -9,7 +9,7 @@
 
 namespace hsq {
 
-WsLayout plan_workspace(int M, int K, int r, int batch) {
+WsLayout plan_workspace(int M, int K, int N, int r, int batch) {
   WsLayout L;
   L.MT = ceil_div(M, kTile);
   L.G = K / kGroup;
@@ -25,6 +25,8 @@ WsLayout plan_workspace(int M, int K, int r, int batch) {
   off = align_up(off + (size_t)L.MT * L.Gp * 16 * sizeof(float), 256);
   L.uw_off = off;
   off = align_up(off + (size_t)L.u_slices * batch * r * L.Mpad * sizeof(float), 256);
+  L.part_off = off;
+  off = align_up(off + tiled_partial_bytes(M, N, K, batch), 256);
   L.total = off;
   return L;
 }
@@ -57,7 +59,7 @@ int hip_status(hipError_t e) {
 
 size_t workspace_bytes(int M, int K, int N, int r, int batch) {
   if (check_sizes(M, K, N, r, batch) != HSQ_OK) return 0;
-  return plan_workspace(M, K, r, batch).total;
+  return plan_workspace(M, K, N, r, batch).total;
 }
 
 // Argument checks shared by every form of the linear.  `quant` / `contract`
@@ -84,13 +86,13 @@ int validate(const uint16_t *X, int M, int K, int N, int batch, const uint16_t *
     if (p && !aligned16(p)) return HSQ_E_ALIGN;
   if (*kernel == HSQ_KERNEL_AUTO) *kernel = M <= kSkinnyMaxM ? HSQ_KERNEL_SKINNY : HSQ_KERNEL_TILED;
   if (*kernel == HSQ_KERNEL_SKINNY && M > kSkinnyMaxM) return HSQ_E_INVAL;
-  if (ws_bytes < plan_workspace(M, K, r, batch).total) return HSQ_E_WORKSPACE;
+  if (ws_bytes < plan_workspace(M, K, N, r, batch).total) return HSQ_E_WORKSPACE;
   return HSQ_OK;
 }
 
-int quant_stage(const uint16_t *X, int M, int K, int batch, const uint16_t *lambda,
+int quant_stage(const uint16_t *X, int M, int K, int N, int batch, const uint16_t *lambda,
                 const uint16_t *L1, int r, void *workspace, hipStream_t s) {
-  const WsLayout L = plan_workspace(M, K, r, batch);
+  const WsLayout L = plan_workspace(M, K, N, r, batch);
   char *ws = (char *)workspace;
   QuantArgs q{};
   q.X = X;
@@ -110,7 +112,7 @@ int contract_stage(int M, int K, int N, int batch, const uint8_t *packed_w, cons
                    const uint16_t *L2, int r, const uint16_t *bias, void *Y, int y_dtype,
                    void *workspace, int kernel, hipStream_t s, int32_t *P, int m0, int mc,
                    int n0, int nc) {
-  const WsLayout L = plan_workspace(M, K, r, batch);
+  const WsLayout L = plan_workspace(M, K, N, r, batch);
   char *ws = (char *)workspace;
   GemmArgs g{};
   g.qa = (const int8_t *)(ws + L.qa_off);
@@ -126,6 +128,7 @@ int contract_stage(int M, int K, int N, int batch, const uint8_t *packed_w, cons
   g.y_bf16 = y_dtype == HSQ_BF16;
   g.M = M; g.N = N; g.G = L.G; g.Gp = L.Gp; g.Mpad = L.Mpad; g.r = r; g.ucols = batch * r;
   g.P = P; g.m0 = m0; g.mc = mc; g.n0 = n0; g.nc = nc;
+  g.part = (float *)(ws + L.part_off);
   const bool dump = P != nullptr;
   return hip_status(kernel == HSQ_KERNEL_SKINNY ? launch_gemm_skinny(g, batch, dump, s)
                                                 : launch_gemm_tiled(g, batch, dump, s));
@@ -141,7 +144,7 @@ int run_linear(const uint16_t *X, int M, int K, int N, int batch, const uint16_t
                     workspace, ws_bytes, &kernel, true, true, P, m0, mc, n0, nc);
   if (st != HSQ_OK) return st;
   hipStream_t s = (hipStream_t)stream;
-  st = quant_stage(X, M, K, batch, lambda, L1, r, workspace, s);
+  st = quant_stage(X, M, K, N, batch, lambda, L1, r, workspace, s);
   if (st != HSQ_OK) return st;
   return contract_stage(M, K, N, batch, packed_w, sw, L2, r, bias, Y, y_dtype, workspace, kernel,
                         s, P, m0, mc, n0, nc);
@@ -242,7 +245,7 @@ int hsq_w4a4_quantize_stage(const uint16_t *X, int M, int K, int N, int batch,
   int st = validate(X, M, K, N, batch, lambda, nullptr, nullptr, L1, nullptr, r, nullptr, nullptr,
                     HSQ_F32, workspace, ws_bytes, &kernel, true, false, nullptr, 0, 0, 0, 0);
   if (st != HSQ_OK) return st;
-  return quant_stage(X, M, K, batch, lambda, L1, r, workspace, (hipStream_t)stream);
+  return quant_stage(X, M, K, N, batch, lambda, L1, r, workspace, (hipStream_t)stream);
 }
 
 int hsq_w4a4_contract_stage(int M, int K, int N, int batch, const uint8_t *packed_w,

@@ -20,14 +20,20 @@
 // tiles run as a software pipeline (LDS read one step ahead, MFMAs of step
 // s, rescale of step s-1).
 //
-// Workgroup: 256 threads = 4 waves in 2x2, tile BM x BN = 128 x 128; each
-// wave owns 64 x 64 = 4 x 4 MFMA tiles.  K advances one group per stage.
-// Global loads run two stages ahead into two register sets (slot = stage
-// parity, fixed at compile time by unrolling the stage loop by two); a set
-// is written to one of two LDS buffers one stage before it is consumed, so
-// each load has two stages of compute to arrive in.  One barrier per stage.
-// Workgroups are mapped so that each XCD (own L2) walks a compact block of
-// output tiles.
+// Workgroup: 512 threads = 8 waves in 2 (M) x 4 (N), tile BM x BN =
+// 128 x 128; each wave owns 64 x 32 outputs = 4 x 2 MFMA tiles.  K advances
+// one group per stage.  Global loads run two stages ahead into two register
+// sets (slot = stage parity, fixed at compile time by unrolling the stage
+// loop by two); a set is written to one of two LDS buffers one stage before
+// it is consumed, so each load has two stages of compute to arrive in.  One
+// barrier per stage.  Workgroups are mapped so that each XCD (own L2) walks
+// a compact block of output tiles.
+//
+// Split K: when the output has too few tiles to fill the chip (a few hundred
+// tokens against a long K), S workgroups share a tile, each over a range of
+// group pairs, and store their fp32 accumulators as partial tiles in the
+// workspace; a second launch of the same kernel sums the S partials of a
+// tile in split order (deterministic) and runs the epilogue.
 #include "hsq_internal.h"
 
 namespace hsq {
@@ -42,6 +48,13 @@ constexpr int NTH = 64 * WM * WN;             // threads per workgroup
 constexpr int TM = TMB / WM, TN = TNB / WN;   // MFMA tiles per wave (64 x 32 outputs)
 constexpr int kGroupM = 8;                    // m-blocks per tile-order group
 constexpr int kSlots = 2;                     // register slots: loads run kSlots stages ahead
+// kernel modes: the whole K range with the epilogue, one split's partial
+// tile, or the sum of the partial tiles with the epilogue
+constexpr int kFull = 0, kSplit = 1, kReduce = 2;
+constexpr int kCUs = 256;                     // compute units of the MI355X
+constexpr int kMaxSplits = 16;
+constexpr int kMinSplitPairs = 4;             // group pairs per split, at least
+constexpr int kAccPerThread = TM * TN * 4;
 static_assert(TMB * 64 == NTH && TNB * 64 == NTH, "one A chunk and one B slot per thread");
 static_assert(TMB * 16 <= NTH / 2 && BN <= NTH / 2, "scale loads: sx in the first half, sw in the second");
 
@@ -103,8 +116,10 @@ __device__ __forceinline__ void tile_of(int bid, int nblk, int mblk, int &mb, in
   nb = w / gsz;
 }
 
-template <bool DUMP, int RPT>
+template <bool DUMP, int RPT, int MODE>
 __global__ __launch_bounds__(NTH, 2) void k_gemm_tiled(GemmArgs a, int nblk, int mblk) {
+  static_assert(MODE != kSplit || RPT == 0, "a split pass has no epilogue");
+  constexpr bool EPI = !DUMP && MODE != kSplit;   // this pass writes Y
   __shared__ Smem<RPT> smem;
   Stages &sm = smem.st;
 
@@ -122,6 +137,16 @@ __global__ __launch_bounds__(NTH, 2) void k_gemm_tiled(GemmArgs a, int nblk, int
   if (DUMP && ((mt0 + TMB) * 16 <= a.m0 || mt0 * 16 >= a.m0 + a.mc ||
                (nt0 + TNB) * 16 <= a.n0 || nt0 * 16 >= a.n0 + a.nc))
     return;  // whole block outside the window (uniform: before any barrier)
+  // stages [g0, g1): every (padded) group, or one split's group pairs
+  int g0 = 0, g1 = a.Gp;
+  if (MODE == kSplit) {
+    const int S = (int)gridDim.z, z = (int)blockIdx.z, pairs = a.Gp / 2;
+    g0 = 2 * (z * pairs / S);
+    g1 = 2 * ((z + 1) * pairs / S);
+  }
+  // this tile's partial tiles: [proj][tile][split][chunk][thread] float4
+  float *part_tile = a.part + (((size_t)proj * nblk * mblk + (size_t)mb * nblk + nb) * a.splits) *
+                                  (NTH * kAccPerThread);
 
   // ---- global -> registers (two slots) -> LDS (two buffers) ----
   // Loads past the matrix edges read the last valid block (clamped
@@ -185,14 +210,13 @@ __global__ __launch_bounds__(NTH, 2) void k_gemm_tiled(GemmArgs a, int nblk, int
   const v4i magic = {kMagicBits, kMagicBits, kMagicBits, kMagicBits};
   const int rowq = 4 * (lane >> 4);   // first of the 4 rows this lane holds
   const int colq = lane & 15;
-  const int GS = a.Gp;                // stages: every (padded) group
 
   // ---- epilogue operands: loads issued first, so that their latency
   // overlaps the first stages' loads; parked in LDS below ----
   constexpr int EU = RPT * BM / NTH;  // (rank column, row) pairs per thread
   constexpr int US = RPT <= 8 ? kMaxUSlices : kMaxUSlices / 2;  // U slices prefetched
   float eu[EU > 0 ? EU : 1][US], el2[EU > 0 ? EU : 1], ebias = 0.0f;
-  if (!DUMP) {
+  if (EPI) {
     const uint16_t *L2 = a.L2 + (size_t)proj * a.r * a.N;
 #pragma unroll
     for (int e = 0; e < EU; ++e) {
@@ -207,13 +231,15 @@ __global__ __launch_bounds__(NTH, 2) void k_gemm_tiled(GemmArgs a, int nblk, int
     if (a.bias) ebias = bf16_to_f32(a.bias[(size_t)proj * a.N + min(nt0 * 16 + (tid & (BN - 1)), a.N - 1)]);
   }
 
-  load_stage(0, int_c<0>{});
-  load_stage(1, int_c<1>{});          // Gp >= 2; later stages past the end are clamped reloads
-  if constexpr (kSlots > 2) {
-    load_stage(2, int_c<2 % kSlots>{});
-    load_stage(3, int_c<3 % kSlots>{});
+  if constexpr (MODE != kReduce) {
+    load_stage(g0, int_c<0>{});
+    load_stage(g0 + 1, int_c<1>{});   // g1 - g0 >= 2; stages past the end are clamped reloads
+    if constexpr (kSlots > 2) {
+      load_stage(g0 + 2, int_c<2 % kSlots>{});
+      load_stage(g0 + 3, int_c<3 % kSlots>{});
+    }
   }
-  if (!DUMP) {
+  if (EPI) {
 #pragma unroll
     for (int e = 0; e < EU; ++e) {
       const int idx = e * NTH + tid, c = idx / BM, rr = idx % BM;
@@ -233,8 +259,10 @@ __global__ __launch_bounds__(NTH, 2) void k_gemm_tiled(GemmArgs a, int nblk, int
     }
     if (tid < BN) smem.ep.bias[tid] = (nt0 * 16 + tid < a.N) ? ebias : 0.0f;
   }
-  store_stage(0, int_c<0>{}, 0);
+  if constexpr (MODE != kReduce) store_stage(g0, int_c<0>{}, 0);
   __syncthreads();
+
+  if constexpr (MODE != kReduce) {
 
   // ---- the stage loop: TM row tiles per stage, software-pipelined across
   // stages.  Step s of stage g issues the MFMAs of row s and rescales the
@@ -336,13 +364,13 @@ __global__ __launch_bounds__(NTH, 2) void k_gemm_tiled(GemmArgs a, int nblk, int
     sx_carry = sxv[TM - 1];
 
     // stage g+1 (loaded kSlots-1 stages ago) into the other LDS buffer
-    if (g + 1 < GS) store_stage(g + 1, int_c<(SL + 1) % kSlots>{}, BUF ^ 1);
+    if (g + 1 < g1) store_stage(g + 1, int_c<(SL + 1) % kSlots>{}, BUF ^ 1);
     __syncthreads();
   };
-  // stages in fours (compile-time register slots), then the remaining two
-  // (GS is even)
-  int g = 0;
-  for (; g + kSlots <= GS; g += kSlots) {
+  // stages in groups of kSlots (compile-time register slots), then the
+  // remaining two (g0 and g1 are even)
+  int g = g0;
+  for (; g + kSlots <= g1; g += kSlots) {
     stage(g, int_c<0>{});
     stage(g + 1, int_c<1>{});
     if constexpr (kSlots > 2) {
@@ -350,18 +378,47 @@ __global__ __launch_bounds__(NTH, 2) void k_gemm_tiled(GemmArgs a, int nblk, int
       stage(g + 3, int_c<3 % kSlots>{});
     }
   }
-  if (g < GS) {
+  if (g < g1) {
     stage(g, int_c<0>{});
     stage(g + 1, int_c<1>{});
   }
-  // drain: the last row of the last stage (GS - 1 is odd: LDS buffer 1)
-  rescale(TM - 1, swv[1], sx_carry, GS - 1);
+  // drain: the last row of the last stage (g1 - 1 is odd: LDS buffer 1)
+  rescale(TM - 1, swv[1], sx_carry, g1 - 1);
+  }  // MODE != kReduce
 
   if (DUMP) return;
 
+  if constexpr (MODE == kSplit) {
+    // this split's partial tile: chunk c = (i, j) as one float4 per thread,
+    // 1 KB contiguous per wave and chunk
+    float *dst = part_tile + (size_t)blockIdx.z * (NTH * kAccPerThread);
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+        *reinterpret_cast<v4f *>(dst + ((i * TN + j) * NTH + tid) * 4) =
+            (v4f){acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]};
+    return;
+  }
+  if constexpr (MODE == kReduce) {
+    // the partial tiles in split order
+#pragma unroll 1
+    for (int z = 0; z < a.splits; ++z) {
+      const float *src = part_tile + (size_t)z * (NTH * kAccPerThread);
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+          const v4f v = *reinterpret_cast<const v4f *>(src + ((i * TN + j) * NTH + tid) * 4);
+          acc[i][j][0] += v[0]; acc[i][j][1] += v[1]; acc[i][j][2] += v[2]; acc[i][j][3] += v[3];
+        }
+    }
+  }
+
   // ---- epilogue: Y = acc + U * L2 + bias ----
   // U * L2 as fp32 MFMAs (16x16x4: one per 16x16 tile and 4 rank columns);
-  // the stage loop ended with a barrier, so its LDS is free for the output
+  // the stage loop ended with a barrier (the reduce pass has none: its
+  // stage buffers were never used), so that LDS is free for the output
   // transpose.
   if constexpr (RPT > 0) {
 #pragma unroll
@@ -431,28 +488,69 @@ __global__ __launch_bounds__(NTH, 2) void k_gemm_tiled(GemmArgs a, int nblk, int
   }
 }
 
-template <int RPT>
+template <int RPT, int MODE>
 hipError_t launch_rpt(const GemmArgs &a, int batch, int nblk, int mblk, hipStream_t s) {
-  hipLaunchKernelGGL((k_gemm_tiled<false, RPT>), dim3((unsigned)(nblk * mblk), (unsigned)batch),
+  hipLaunchKernelGGL((k_gemm_tiled<false, RPT, MODE>), dim3((unsigned)(nblk * mblk), (unsigned)batch),
                      dim3(NTH), 0, s, a, nblk, mblk);
   return hipGetLastError();
 }
 
+template <int MODE>
+hipError_t launch_epi(const GemmArgs &a, int batch, int nblk, int mblk, hipStream_t s) {
+  if (a.r == 0) return launch_rpt<0, MODE>(a, batch, nblk, mblk, s);
+  if (a.r <= 4) return launch_rpt<4, MODE>(a, batch, nblk, mblk, s);
+  if (a.r <= 8) return launch_rpt<8, MODE>(a, batch, nblk, mblk, s);
+  if (a.r <= 16) return launch_rpt<16, MODE>(a, batch, nblk, mblk, s);
+  return launch_rpt<32, MODE>(a, batch, nblk, mblk, s);
+}
+
 }  // namespace
+
+// Split K when the tiles alone leave compute units idle.  Cost of S splits:
+// workgroups per CU (rounded up) x group pairs per workgroup, i.e. the
+// busiest CU's work; the cheapest S wins, and on a tie a larger S only while
+// fewer than two workgroups per CU run (one leaves each SIMD two waves).
+// Each split keeps at least kMinSplitPairs group pairs.
+int tiled_splits(int M, int N, int K, int batch) {
+  const long long tiles = (long long)ceil_div(N, BN) * ceil_div(M, BM) * batch;
+  const int pairs = padded_groups(K) / 2;
+  if (tiles >= kCUs) return 1;
+  int best = 1;
+  long long best_cost = -1;
+  for (int S = 1; S <= kMaxSplits && S * kMinSplitPairs <= pairs; ++S) {
+    const long long c = (tiles * S + kCUs - 1) / kCUs * ceil_div(pairs, S);
+    if (best_cost < 0 || c < best_cost || (c == best_cost && tiles * best < 2 * kCUs)) {
+      best = S;
+      best_cost = c;
+    }
+  }
+  return best;
+}
+
+size_t tiled_partial_bytes(int M, int N, int K, int batch) {
+  const int S = tiled_splits(M, N, K, batch);
+  if (S <= 1) return 0;
+  return (size_t)S * ceil_div(N, BN) * ceil_div(M, BM) * batch * NTH * kAccPerThread * sizeof(float);
+}
 
 hipError_t launch_gemm_tiled(const GemmArgs &a, int batch, bool dump, hipStream_t s) {
   const int nblk = ceil_div(a.N, BN), mblk = ceil_div(a.M, BM);
   if (dump) {
     // every tile of one projection; blocks outside the window exit at once
-    hipLaunchKernelGGL((k_gemm_tiled<true, 0>), dim3((unsigned)(nblk * mblk), 1u), dim3(NTH), 0, s,
-                       a, nblk, mblk);
+    hipLaunchKernelGGL((k_gemm_tiled<true, 0, kFull>), dim3((unsigned)(nblk * mblk), 1u), dim3(NTH), 0,
+                       s, a, nblk, mblk);
     return hipGetLastError();
   }
-  if (a.r == 0) return launch_rpt<0>(a, batch, nblk, mblk, s);
-  if (a.r <= 4) return launch_rpt<4>(a, batch, nblk, mblk, s);
-  if (a.r <= 8) return launch_rpt<8>(a, batch, nblk, mblk, s);
-  if (a.r <= 16) return launch_rpt<16>(a, batch, nblk, mblk, s);
-  return launch_rpt<32>(a, batch, nblk, mblk, s);
+  const int S = tiled_splits(a.M, a.N, a.G * kGroup, batch);
+  if (S <= 1) return launch_epi<kFull>(a, batch, nblk, mblk, s);
+  GemmArgs b = a;
+  b.splits = S;
+  hipLaunchKernelGGL((k_gemm_tiled<false, 0, kSplit>),
+                     dim3((unsigned)(nblk * mblk), (unsigned)batch, (unsigned)S), dim3(NTH), 0, s, b,
+                     nblk, mblk);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return launch_epi<kReduce>(b, batch, nblk, mblk, s);
 }
 
 }  // namespace hsq

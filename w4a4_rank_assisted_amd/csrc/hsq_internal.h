@@ -55,15 +55,17 @@ inline size_t packed_bytes(int K, int N) {
 //         contraction works on 16 * P), zero for pad rows / groups
 //   uw  : S_u x (batch*r) x (16*MT) fp32, one slice of U per K-slice of the
 //         quantization pass, summed in slice order by the consumer
+//   part: split-K partial tiles of the tiled contraction when its grid is
+//         too small for the chip (tiled_partial_bytes; empty otherwise)
 // ---------------------------------------------------------------------------
 struct WsLayout {
   int MT = 0, G = 0, Gp = 0, Mpad = 0;
   int u_slices = 0;      // S_u: K-slices of the quantization pass
-  size_t qa_off = 0, sxs_off = 0, uw_off = 0, total = 0;
+  size_t qa_off = 0, sxs_off = 0, uw_off = 0, part_off = 0, total = 0;
 };
 
-// Plans the workspace for (M, K, r, batch).  Pure host arithmetic.
-WsLayout plan_workspace(int M, int K, int r, int batch);
+// Plans the workspace for (M, K, N, r, batch).  Pure host arithmetic.
+WsLayout plan_workspace(int M, int K, int N, int r, int batch);
 
 // Largest token count the skinny kernel accepts (4 row tiles).
 constexpr int kSkinnyMaxM = 64;
@@ -107,6 +109,10 @@ struct GemmArgs {
   // partial-sum dump window (test export)
   int32_t *P;
   int m0, mc, n0, nc;
+  // split-K partial tiles of the tiled contraction (workspace) and their
+  // number per output tile
+  float *part;
+  int splits;
 };
 
 hipError_t launch_pack(const int8_t *codes, int K, int N, uint8_t *packed, int *status,
@@ -118,6 +124,10 @@ hipError_t launch_unpack(const uint8_t *packed, int K, int N, int8_t *codes, hip
 hipError_t launch_quant(const QuantArgs &a, hipStream_t s);
 int quant_slices(int M, int K, int r, int batch);
 hipError_t launch_gemm_tiled(const GemmArgs &a, int batch, bool dump, hipStream_t s);
+// Split-K factor of the tiled contraction for this shape (1: no split) and
+// the workspace bytes of its partial tiles.
+int tiled_splits(int M, int N, int K, int batch);
+size_t tiled_partial_bytes(int M, int N, int K, int batch);
 hipError_t launch_gemm_skinny(const GemmArgs &a, int batch, bool dump, hipStream_t s);
 
 }  // namespace hsq
