@@ -122,6 +122,7 @@ hipError_t launch_unpack(const uint8_t *packed, int K, int N, int8_t *codes, hip
 // it writes the public or the internal outputs; quant_slices() is the number
 // of K-slices (U partials) of the internal pass.
 hipError_t launch_quant(const QuantArgs &a, hipStream_t s);
+hipError_t launch_quant_tiles(const QuantArgs &a, hipStream_t s);
 int quant_slices(int M, int K, int r, int batch);
 hipError_t launch_gemm_tiled(const GemmArgs &a, int batch, bool dump, hipStream_t s);
 // Split-K factor of the tiled contraction for this shape (1: no split) and

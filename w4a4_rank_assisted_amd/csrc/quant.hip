@@ -354,12 +354,11 @@ hipError_t launch_nr(const QuantArgs &a, const QuantPlan &p, int nr, dim3 grid, 
 
 }  // namespace
 
-int quant_slices(int M, int K, int r, int batch) { return plan(M, K, r, batch, false).slices; }
-
 // One launch per block of up to 32 rank columns; codes and scales are
 // written by the first.
 hipError_t launch_quant(const QuantArgs &a0, hipStream_t s) {
   const bool pub = a0.qx != nullptr;
+  if (!pub) return launch_quant_tiles(a0, s);
   const QuantPlan p = plan(a0.M, a0.K, a0.r, a0.batch, pub);
   if (p.ng < 1 || p.ng > kMaxSliceGroups) return hipErrorInvalidValue;
   const int mrows = pub ? a0.M : a0.Mpad;
