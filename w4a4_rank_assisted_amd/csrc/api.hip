@@ -105,7 +105,7 @@ int quant_stage(const uint16_t *X, int M, int K, int N, int batch, const uint16_
   q.sxs = (float *)(ws + L.sxs_off);
   q.uw = (float *)(ws + L.uw_off);
   q.Gp = L.Gp; q.Mpad = L.Mpad; q.ucols = batch * r;
-  return hip_status(launch_quant(q, s));
+  return hip_status(launch_quant_tiles(q, s));
 }
 
 int contract_stage(int M, int K, int N, int batch, const uint8_t *packed_w, const uint16_t *sw,
@@ -213,7 +213,7 @@ int hsq_quantize_act(const uint16_t *X, int M, int K, const uint16_t *lambda,
   q.kend = K;
   q.qx = qx; q.sx = sx; q.u_pub = r > 0 ? U : nullptr;
   q.ucols = r;
-  return hip_status(launch_quant(q, (hipStream_t)stream));
+  return hip_status(launch_quant_act(q, (hipStream_t)stream));
 }
 
 size_t hsq_workspace_bytes(int M, int K, int N, int r, int batch) {

@@ -11,9 +11,9 @@
 // from HBM into registers) together with the run's activation codes and
 // scales (shared by the CT tiles, from the cache) before it computes
 // anything, so the whole weight stream of the chip is in flight at once.
-// The W partial tiles are summed through LDS by a fixed halving tree
-// (deterministic), and the epilogue adds U * L2 and the bias -- no split-K
-// buffer, one launch.
+// The W partial tiles meet in LDS after one barrier; each thread then sums
+// one output over the waves in wave order (deterministic) and adds U * L2
+// and the bias -- no split-K buffer, one launch.
 #include "hsq_internal.h"
 
 namespace hsq {
@@ -29,11 +29,10 @@ constexpr int max_waves(int mt) { return mt <= 2 ? 16 : 8; }
 
 template <int MT, int P, int CT, bool DUMP>
 __global__ __launch_bounds__(64 * max_waves(MT)) void k_gemm_skinny(GemmArgs a, int W) {
-  // dynamic LDS: partial tiles [ceil(W/2)][CT][MT][4][64], then U [r][16*MT]
+  // dynamic LDS: partial tiles [W][CT][MT][4][64], then U [r][16*MT]
   // (slices summed), L2 [r][16*CT], bias [16*CT]
   extern __shared__ float red[];
-  const int H0 = (W + 1) / 2;
-  float *eu = red + H0 * CT * MT * 4 * 64;
+  float *eu = red + W * CT * MT * 4 * 64;
   float *el2 = eu + a.r * MT * 16;
   float *eb = el2 + a.r * 16 * CT;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -206,76 +205,41 @@ __global__ __launch_bounds__(64 * max_waves(MT)) void k_gemm_skinny(GemmArgs a, 
     el2[p] = bf16_to_f32(a.L2[((size_t)proj * a.r + p / (16 * CT)) * a.N + min(nt0 * 16 + p % (16 * CT), a.N - 1)]);
   if (tid < 16 * CT) eb[tid] = bpre;
 
-  // ---- halving tree over the W partial tiles (fixed pairing: wave w adds
-  // wave w + h at each level), then the epilogue in wave 0.. ----
+  // ---- the W partial tiles: parked, then each output summed over the
+  // waves in order, plus U * L2 and the bias ----
   constexpr int E = CT * MT * 4;                       // values per lane
-  for (int w = W; w > 1;) {
-    const int h = (w + 1) / 2;                          // waves [h, w) hand over
-    if (wave >= h && wave < w) {
-      float *dst = red + (wave - h) * E * 64;
-#pragma unroll
-      for (int c = 0; c < CT; ++c)
-#pragma unroll
-        for (int i = 0; i < MT; ++i)
-#pragma unroll
-          for (int q = 0; q < 4; ++q) dst[((c * MT + i) * 4 + q) * 64 + lane] = acc[c][i][q];
-    }
-    __syncthreads();
-    if (wave < w - h) {
-      const float *src = red + wave * E * 64;
-#pragma unroll
-      for (int c = 0; c < CT; ++c)
-#pragma unroll
-        for (int i = 0; i < MT; ++i)
-#pragma unroll
-          for (int q = 0; q < 4; ++q) acc[c][i][q] += src[((c * MT + i) * 4 + q) * 64 + lane];
-    }
-    __syncthreads();
-    w = h;
-  }
-  if (W == 1) __syncthreads();                          // epilogue operands
-
-  // wave 0 holds the sums: hand them to the waves that write (c, i) tiles
-  if (wave == 0) {
+  {
+    float *dst = red + wave * E * 64;
 #pragma unroll
     for (int c = 0; c < CT; ++c)
 #pragma unroll
       for (int i = 0; i < MT; ++i)
 #pragma unroll
-        for (int q = 0; q < 4; ++q) red[((c * MT + i) * 4 + q) * 64 + lane] = acc[c][i][q];
+        for (int q = 0; q < 4; ++q) dst[((c * MT + i) * 4 + q) * 64 + lane] = acc[c][i][q];
   }
-  __syncthreads();
-  for (int ci = wave; ci < CT * MT; ci += W) {
-    const int c = ci / MT, i = ci % MT;
-    const int n = (nt0 + c) * 16 + colq;
-    const int mrow = i * 16 + rowq;
-    if (n >= a.N || mrow >= a.M) continue;
-    float y[4];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) y[q] = red[((c * MT + i) * 4 + q) * 64 + lane];
-    for (int k = 0; k < a.r; ++k) {
-      const float l2 = el2[k * 16 * CT + c * 16 + colq];
-#pragma unroll
-      for (int q = 0; q < 4; ++q) y[q] = __builtin_fmaf(eu[k * MT * 16 + mrow + q], l2, y[q]);
-    }
-    const float bb = eb[c * 16 + colq];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int m = mrow + q;
-      if (m >= a.M) break;
-      const size_t off = ((size_t)proj * a.M + m) * a.N + n;
-      if (a.y_bf16)
-        reinterpret_cast<uint16_t *>(a.Y)[off] = f32_to_bf16(y[q] + bb);
-      else
-        reinterpret_cast<float *>(a.Y)[off] = y[q] + bb;
-    }
+  __syncthreads();                                      // partial tiles and epilogue operands
+  for (int o = tid; o < E * 64; o += nthr) {
+    const int e = o >> 6, l = o & 63;                   // value e of lane l
+    const int c = e / (MT * 4), i = (e >> 2) % MT, q = e & 3;
+    const int n = (nt0 + c) * 16 + (l & 15);
+    const int m = i * 16 + 4 * (l >> 4) + q;
+    float y = 0.0f;
+    for (int w = 0; w < W; ++w) y += red[w * E * 64 + o];
+    if (n >= a.N || m >= a.M) continue;
+    for (int k = 0; k < a.r; ++k) y = __builtin_fmaf(eu[k * MT * 16 + m], el2[k * 16 * CT + c * 16 + (l & 15)], y);
+    y += eb[c * 16 + (l & 15)];
+    const size_t off = ((size_t)proj * a.M + m) * a.N + n;
+    if (a.y_bf16)
+      reinterpret_cast<uint16_t *>(a.Y)[off] = f32_to_bf16(y);
+    else
+      reinterpret_cast<float *>(a.Y)[off] = y;
   }
 }
 
 template <int MT, int P, int CT>
 hipError_t launch_cfg(const GemmArgs &a, int batch, bool dump, int W, hipStream_t s) {
   const int NT = ceil_div(a.N, kTile);
-  const size_t lds = ((size_t)(W + 1) / 2 * CT * MT * 4 * 64 + (size_t)a.r * MT * 16 + (size_t)a.r * 16 * CT +
+  const size_t lds = ((size_t)W * CT * MT * 4 * 64 + (size_t)a.r * MT * 16 + (size_t)a.r * 16 * CT +
                       16 * CT) * sizeof(float);
   if (dump) {
     const int g0 = a.n0 / (16 * CT), g1 = (a.n0 + a.nc - 1) / (16 * CT);

@@ -118,10 +118,10 @@ struct GemmArgs {
 hipError_t launch_pack(const int8_t *codes, int K, int N, uint8_t *packed, int *status,
                        hipStream_t s);
 hipError_t launch_unpack(const uint8_t *packed, int K, int N, int8_t *codes, hipStream_t s);
-// The quantization pass plans its own grid from (M, K, r, batch) and whether
-// it writes the public or the internal outputs; quant_slices() is the number
-// of K-slices (U partials) of the internal pass.
-hipError_t launch_quant(const QuantArgs &a, hipStream_t s);
+// Quantization passes: the public layout (hsq_quantize_act, batch 1) and the
+// fused linear's internal layout; each plans its own grid.  quant_slices()
+// is the number of K-slices (U partials) of the internal pass.
+hipError_t launch_quant_act(const QuantArgs &a, hipStream_t s);
 hipError_t launch_quant_tiles(const QuantArgs &a, hipStream_t s);
 int quant_slices(int M, int K, int r, int batch);
 hipError_t launch_gemm_tiled(const GemmArgs &a, int batch, bool dump, hipStream_t s);

@@ -1,26 +1,28 @@
-// quant.hip -- K1: one pass over X that smooths it, quantizes it per token in
-// 64-wide groups to symmetric int4, and accumulates the rank-r down
-// projection U = xh * L1 of the smoothed, unquantized activations.
+// quant.hip -- the public quantization pass (hsq_quantize_act): one pass over
+// X that smooths it, quantizes it per token in 64-wide groups to symmetric
+// int4, and forms the rank-r down projection U = xh * L1 of the smoothed,
+// unquantized activations, in the public layout (row-major packed nibbles,
+// fp16 scales M x G, U as M x r).  The fused linear uses its own pass in the
+// contraction's operand order (quant_tiles.hip); both follow the same
+// arithmetic.
 //
 // Operation (hsq.h formula block): smoothing by a diagonal scale (H-SVDQuant
 // explainer, rit.work, section on Hessian deflation), group-64 4-bit
 // activations (Deflating the Hessian, Table 1 caption), high-precision
 // branch on unquantized inputs (DiRotQ notes, key design 2).
 //
-// Mapping: one lane per (token, 64-channel group) item.  A workgroup owns a
-// K-slice of ng groups and a run of tokens, taken `rows` = 256/ng tokens at a
-// time (lane t = token t/ng, group t%ng).  A lane loads its group with eight
+// Mapping: one lane per (token, 64-channel group) item.  A workgroup owns
+// all ng = K/64 groups (K <= 12288) and a run of tokens, taken `rows` =
+// 256/ng tokens at a time (lane t = token t/ng, group t%ng).  A lane loads its group with eight
 // 16-byte loads, finds the absmax in registers, computes the fp16 scale and
 // its reciprocal once, writes the codes and forms its group's share of U.
-// The slice's 1/lambda (exact IEEE division) and, when they fit, its L1 rows
+// The 1/lambda (exact IEEE division) and, when they fit, the L1 rows
 // are staged in LDS once per workgroup, one padded row per group, so that
 // lanes of one token read different banks and lanes of different tokens
 // read the same words (broadcast).  The first X loads are issued before the
 // staging and each row step prefetches the next, so a lane waits for about
 // one memory round trip per step.  The U shares of a token are summed
-// through LDS in a fixed order; K-slices leave U partials that the
-// consumers sum.  The pass is HBM-bound: X is read once, codes and scales
-// are written once.
+// through LDS in a fixed order.
 #include "hsq_internal.h"
 
 namespace hsq {
@@ -29,8 +31,6 @@ namespace {
 
 constexpr int kLamStride = kGroup + 4;            // LDS floats per group row of 1/lambda
 constexpr size_t kL1StageBytes = 36 * 1024;       // LDS for staged L1 rows
-constexpr int kStageSliceGroups = 32;             // groups per slice when L1 is staged
-constexpr int kTargetSlices = 8;                  // U partials the consumers prefetch
 constexpr int kTargetBlocks = 1024;               // workgroups before a launch iterates rows
 constexpr int kMaxIters = 16;
 
@@ -55,36 +55,19 @@ QuantPlan for_block(QuantPlan p, int nr) {
   return p;
 }
 
-QuantPlan plan(int M, int K, int r, int batch, bool pub) {
+QuantPlan plan(int M, int K, int r) {
   QuantPlan p{};
-  const int gend = pub ? K / kGroup : padded_groups(K);
-  const int total = r * batch;
-  p.nr = rank_block(total < kRankBlock ? total : kRankBlock);
-  if (pub) {
-    p.slices = 1;
-    p.ng = gend;                                   // <= kMaxSliceGroups (entry point checks K)
-  } else {
-    int cap = kStageSliceGroups;
-    if (p.nr > 0) {
-      const int fit = (int)(kL1StageBytes / (sizeof(float) * l1_stride(p.nr)));
-      if (fit >= 8 && fit < cap) cap = fit;
-    }
-    p.slices = ceil_div(gend, cap);
-    if (p.slices > kTargetSlices) {
-      p.slices = kTargetSlices;
-      if (ceil_div(gend, p.slices) > kMaxSliceGroups) p.slices = ceil_div(gend, kMaxSliceGroups);
-    }
-    p.ng = ceil_div(gend, p.slices);
-  }
+  p.nr = rank_block(r < kRankBlock ? r : kRankBlock);
+  p.slices = 1;
+  p.ng = K / kGroup;                               // <= kMaxSliceGroups (entry point checks K)
   p.rows = 256 / p.ng;
-  const int mrows = pub ? M : ceil_div(M, kTile) * kTile;
-  const int row_blocks = ceil_div(mrows, p.rows);
+  const int row_blocks = ceil_div(M, p.rows);
   int it = row_blocks * p.slices / kTargetBlocks;
   p.iters = it < 1 ? 1 : (it > kMaxIters ? kMaxIters : it);
   return for_block(p, p.nr);
 }
 
-template <int NR, bool PUB, bool STAGE>
+template <int NR, bool STAGE>
 __global__ __launch_bounds__(256) void k_quant(QuantArgs a, int ng, int rows, int iters) {
   // dynamic LDS: 1/lambda [ng + 1][kLamStride] (last row zero), U shares [4][256],
   // staged L1 [ng][64*NR + 4] (group row: channel-major, NR columns)
@@ -99,7 +82,7 @@ __global__ __launch_bounds__(256) void k_quant(QuantArgs a, int ng, int rows, in
   const int gn = min(ng, gend - gb);               // groups in this slice
   const int rl = tid / ng, gi = tid % ng;          // (token, group) of this lane
   const int g = gb + gi;
-  const int mrows = PUB ? a.M : a.Mpad;            // rows this pass writes
+  const int mrows = a.M;
   const int mbase = blockIdx.x * rows * iters;
   const bool lane_ok = rl < rows && gi < gn;
   const bool g_in = lane_ok && g < a.G;            // else a pad group: zeros
@@ -169,7 +152,7 @@ __global__ __launch_bounds__(256) void k_quant(QuantArgs a, int ng, int rows, in
     dst[1] = (v4f){f[4], f[5], f[6], f[7]};
   };
   if (tid < gn * 8) lam_store(tid, lv, lam_ok);
-  for (int p = tid + 256; p < gn * 8; p += 256) {  // slices of more than 32 groups
+  for (int p = tid + 256; p < gn * 8; p += 256) {  // more than 32 groups
     const bool ok = gb + (p >> 3) < a.G;
     const v4u v = *reinterpret_cast<const v4u *>(
         a.lam + (size_t)min(gb + (p >> 3), a.G - 1) * kGroup + 8 * (p & 7));
@@ -244,38 +227,19 @@ __global__ __launch_bounds__(256) void k_quant(QuantArgs a, int ng, int rows, in
         const int b = __float_as_int(t + kMagic);
         c[i] = min(max(b, kMagicBits - 8), kMagicBits + 7);
       }
-      if (PUB) {
-        if (in) {
-          uint32_t w[8];
+      if (in) {
+        uint32_t w[8];
 #pragma unroll
-          for (int j = 0; j < 8; ++j) {
-            uint32_t v = 0;
+        for (int j = 0; j < 8; ++j) {
+          uint32_t v = 0;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) v |= (uint32_t)(c[8 * j + e] & 0xF) << (4 * e);
-            w[j] = v;
-          }
-          v4u *dst = reinterpret_cast<v4u *>(a.qx + (size_t)m * (a.K / 2) + (size_t)g * 32);
-          dst[0] = (v4u){w[0], w[1], w[2], w[3]};
-          dst[1] = (v4u){w[4], w[5], w[6], w[7]};
-          a.sx[(size_t)m * a.G + g] = s16;
+          for (int e = 0; e < 8; ++e) v |= (uint32_t)(c[8 * j + e] & 0xF) << (4 * e);
+          w[j] = v;
         }
-      } else {
-        uint32_t w[16];                            // int8 codes, 4 per word
-#pragma unroll
-        for (int j = 0; j < 16; ++j) {
-          const uint32_t lo = __builtin_amdgcn_perm((uint32_t)c[4 * j + 1], (uint32_t)c[4 * j], 0x0c0c0400u);
-          const uint32_t hi = __builtin_amdgcn_perm((uint32_t)c[4 * j + 3], (uint32_t)c[4 * j + 2], 0x0c0c0400u);
-          w[j] = __builtin_amdgcn_perm(hi, lo, 0x05040100u);
-        }
-        // MFMA A-operand order: lane slot (m % 16) + 16 * kq holds
-        // channels 64g + 16kq .. +15 of row m
-        const int mt = m >> 4;
-        int8_t *base = a.qa + ((size_t)mt * a.Gp + g) * 1024 + (size_t)(m & 15) * 16;
-#pragma unroll
-        for (int kq = 0; kq < 4; ++kq)
-          *reinterpret_cast<v4u *>(base + kq * 256) =
-              (v4u){w[4 * kq], w[4 * kq + 1], w[4 * kq + 2], w[4 * kq + 3]};
-        a.sxs[((size_t)mt * a.Gp + g) * 16 + (m & 15)] = s * 0.0625f;
+        v4u *dst = reinterpret_cast<v4u *>(a.qx + (size_t)m * (a.K / 2) + (size_t)g * 32);
+        dst[0] = (v4u){w[0], w[1], w[2], w[3]};
+        dst[1] = (v4u){w[4], w[5], w[6], w[7]};
+        a.sx[(size_t)m * a.G + g] = s16;
       }
     }
 
@@ -327,10 +291,7 @@ __global__ __launch_bounds__(256) void k_quant(QuantArgs a, int ng, int rows, in
             const float *src = upart + e * 256 + r0 * ng;
             float s = 0.0f;
             for (int q = 0; q < gn; ++q) s += src[q];
-            if (PUB)
-              a.u_pub[(size_t)mm * a.r + a.c0 + c4 + e] = s;
-            else
-              a.uw[((size_t)blockIdx.y * a.ucols + a.c0 + c4 + e) * a.Mpad + mm] = s;
+            a.u_pub[(size_t)mm * a.r + a.c0 + c4 + e] = s;
           }
         }
         __syncthreads();
@@ -339,15 +300,15 @@ __global__ __launch_bounds__(256) void k_quant(QuantArgs a, int ng, int rows, in
   }
 }
 
-template <bool PUB, bool STAGE>
+template <bool STAGE>
 hipError_t launch_nr(const QuantArgs &a, const QuantPlan &p, int nr, dim3 grid, hipStream_t s) {
   switch (nr) {
-    case 0: hipLaunchKernelGGL((k_quant<0, PUB, false>), grid, dim3(256), p.lds, s, a, p.ng, p.rows, p.iters); break;
-    case 4: hipLaunchKernelGGL((k_quant<4, PUB, STAGE>), grid, dim3(256), p.lds, s, a, p.ng, p.rows, p.iters); break;
-    case 8: hipLaunchKernelGGL((k_quant<8, PUB, STAGE>), grid, dim3(256), p.lds, s, a, p.ng, p.rows, p.iters); break;
-    case 12: hipLaunchKernelGGL((k_quant<12, PUB, STAGE>), grid, dim3(256), p.lds, s, a, p.ng, p.rows, p.iters); break;
-    case 16: hipLaunchKernelGGL((k_quant<16, PUB, STAGE>), grid, dim3(256), p.lds, s, a, p.ng, p.rows, p.iters); break;
-    default: hipLaunchKernelGGL((k_quant<32, PUB, STAGE>), grid, dim3(256), p.lds, s, a, p.ng, p.rows, p.iters); break;
+    case 0: hipLaunchKernelGGL((k_quant<0, false>), grid, dim3(256), p.lds, s, a, p.ng, p.rows, p.iters); break;
+    case 4: hipLaunchKernelGGL((k_quant<4, STAGE>), grid, dim3(256), p.lds, s, a, p.ng, p.rows, p.iters); break;
+    case 8: hipLaunchKernelGGL((k_quant<8, STAGE>), grid, dim3(256), p.lds, s, a, p.ng, p.rows, p.iters); break;
+    case 12: hipLaunchKernelGGL((k_quant<12, STAGE>), grid, dim3(256), p.lds, s, a, p.ng, p.rows, p.iters); break;
+    case 16: hipLaunchKernelGGL((k_quant<16, STAGE>), grid, dim3(256), p.lds, s, a, p.ng, p.rows, p.iters); break;
+    default: hipLaunchKernelGGL((k_quant<32, STAGE>), grid, dim3(256), p.lds, s, a, p.ng, p.rows, p.iters); break;
   }
   return hipGetLastError();
 }
@@ -356,14 +317,11 @@ hipError_t launch_nr(const QuantArgs &a, const QuantPlan &p, int nr, dim3 grid, 
 
 // One launch per block of up to 32 rank columns; codes and scales are
 // written by the first.
-hipError_t launch_quant(const QuantArgs &a0, hipStream_t s) {
-  const bool pub = a0.qx != nullptr;
-  if (!pub) return launch_quant_tiles(a0, s);
-  const QuantPlan p = plan(a0.M, a0.K, a0.r, a0.batch, pub);
+hipError_t launch_quant_act(const QuantArgs &a0, hipStream_t s) {
+  const QuantPlan p = plan(a0.M, a0.K, a0.r);
   if (p.ng < 1 || p.ng > kMaxSliceGroups) return hipErrorInvalidValue;
-  const int mrows = pub ? a0.M : a0.Mpad;
-  dim3 grid((unsigned)ceil_div(mrows, p.rows * p.iters), (unsigned)p.slices);
-  const int total = a0.r * a0.batch;
+  dim3 grid((unsigned)ceil_div(a0.M, p.rows * p.iters), 1u);
+  const int total = a0.r;
   int c0 = 0;
   do {
     QuantArgs a = a0;
@@ -374,11 +332,7 @@ hipError_t launch_quant(const QuantArgs &a0, hipStream_t s) {
     // template and LDS size
     const int nr = rank_block(a.cb);
     const QuantPlan q = for_block(p, nr);
-    hipError_t e;
-    if (pub)
-      e = q.stage ? launch_nr<true, true>(a, q, nr, grid, s) : launch_nr<true, false>(a, q, nr, grid, s);
-    else
-      e = q.stage ? launch_nr<false, true>(a, q, nr, grid, s) : launch_nr<false, false>(a, q, nr, grid, s);
+    const hipError_t e = q.stage ? launch_nr<true>(a, q, nr, grid, s) : launch_nr<false>(a, q, nr, grid, s);
     if (e != hipSuccess) return e;
     c0 += kRankBlock;
   } while (c0 < total);

@@ -50,7 +50,7 @@ size_t plan_lds(int gpb, int nr, int waves) {
 }
 
 // K-slices: enough for the staged tables to fit kSliceLdsBytes and, up to
-// kMaxUSlices, for about kTargetWaves waves; few row tiles get wider
+// kMaxUSlices, for about kTargetWaves waves of 4; few row tiles get wider
 // workgroups (up to 16 waves, at most one per group of the slice).
 TilePlan tile_plan(int M, int K, int r, int batch) {
   TilePlan p{};
@@ -67,7 +67,9 @@ TilePlan tile_plan(int M, int K, int r, int batch) {
   if (S > Gp) S = Gp;
   p.gpb = ceil_div(Gp, S);
   p.slices = ceil_div(Gp, p.gpb);
-  p.waves = 4;
+  // waves per workgroup: 8 when each gets two or more groups of the slice
+  // (more loads in flight per CU), else 4
+  p.waves = p.gpb >= 16 ? 8 : 4;
   if ((long long)MT * p.slices * 4 < kTargetWaves / 2) p.waves = p.gpb < 4 ? 4 : (p.gpb > 16 ? 16 : p.gpb);
   return p;
 }
