@@ -59,7 +59,7 @@ def test_workspace_bytes_cover_the_internal_buffers():
     M, K, N, r, b = 4096, 1152, 4608, 4, 1
     ws = lib.hsq_workspace_bytes(M, K, N, r, b)
     codes = (M // 16) * 18 * 1024            # tiled int8 codes, 18 groups
-    scales = (M // 16) * 18 * 16 * 4
+    scales = (M // 16) * 18 * 16 * 2       # fp16 activation scales
     assert ws >= codes + scales + M * r * 4
     assert ws < 2 * (codes + scales) + 16 * M * r * 4
     assert lib.hsq_workspace_bytes(0, K, N, r, b) == 0

@@ -22,7 +22,7 @@ WsLayout plan_workspace(int M, int K, int N, int r, int batch) {
   L.qa_off = off;
   off = align_up(off + (size_t)L.MT * L.Gp * 1024, 256);
   L.sxs_off = off;
-  off = align_up(off + (size_t)L.MT * L.Gp * 16 * sizeof(float), 256);
+  off = align_up(off + (size_t)L.MT * L.Gp * 16 * sizeof(uint16_t), 256);
   L.uw_off = off;
   off = align_up(off + (size_t)L.u_slices * batch * r * L.Mpad * sizeof(float), 256);
   L.part_off = off;
@@ -102,7 +102,7 @@ int quant_stage(const uint16_t *X, int M, int K, int N, int batch, const uint16_
   q.r = r; q.batch = batch;
   q.kend = L.Gp * kGroup;
   q.qa = (int8_t *)(ws + L.qa_off);
-  q.sxs = (float *)(ws + L.sxs_off);
+  q.sxs = (uint16_t *)(ws + L.sxs_off);
   q.uw = (float *)(ws + L.uw_off);
   q.Gp = L.Gp; q.Mpad = L.Mpad; q.ucols = batch * r;
   return hip_status(launch_quant_tiles(q, s));
@@ -116,7 +116,7 @@ int contract_stage(int M, int K, int N, int batch, const uint8_t *packed_w, cons
   char *ws = (char *)workspace;
   GemmArgs g{};
   g.qa = (const int8_t *)(ws + L.qa_off);
-  g.sxs = (const float *)(ws + L.sxs_off);
+  g.sxs = (const uint16_t *)(ws + L.sxs_off);
   g.w = packed_w;
   g.w_stride = packed_bytes(K, N);
   g.sw = sw;

@@ -47,7 +47,7 @@ __global__ __launch_bounds__(64 * max_waves(MT)) void k_gemm_skinny(GemmArgs a, 
   const __amdgpu_buffer_rsrc_t rs_w =
       buffer_rsrc(a.w + (size_t)proj * a.w_stride, (uint32_t)NT * GP * 1024);
   const __amdgpu_buffer_rsrc_t rs_a = buffer_rsrc(a.qa, (uint32_t)MT * a.Gp * 1024);
-  const __amdgpu_buffer_rsrc_t rs_x = buffer_rsrc(a.sxs, (uint32_t)MT * a.Gp * 64);
+  const __amdgpu_buffer_rsrc_t rs_x = buffer_rsrc(a.sxs, (uint32_t)MT * a.Gp * 32);
   const __amdgpu_buffer_rsrc_t rs_s =
       buffer_rsrc(DUMP ? nullptr : a.sw + (size_t)proj * G * a.N, DUMP ? 0u : (uint32_t)G * a.N * 2);
   uint32_t offw[CT], offsw[CT];
@@ -96,7 +96,7 @@ __global__ __launch_bounds__(64 * max_waves(MT)) void k_gemm_skinny(GemmArgs a, 
   // CT column tiles
   struct Act {
     v4i av[MT][2];
-    v4f sx[MT][2];
+    v4h sx[MT][2];
     uint32_t sw[CT][2];
   };
   auto load_act = [&](int gp, Act &t) __attribute__((always_inline)) {
@@ -109,7 +109,7 @@ __global__ __launch_bounds__(64 * max_waves(MT)) void k_gemm_skinny(GemmArgs a, 
             v4i, __builtin_amdgcn_raw_buffer_load_b128(rs_a, (uint32_t)(i * a.Gp * 64 + lane) * 16, g * 1024, 0));
         if (!DUMP)
           t.sx[i][h] = __builtin_bit_cast(
-              v4f, __builtin_amdgcn_raw_buffer_load_b128(rs_x, (uint32_t)(i * a.Gp * 16 + rowq) * 4, g * 64, 0));
+              v4h, __builtin_amdgcn_raw_buffer_load_b64(rs_x, (uint32_t)(i * a.Gp * 16 + rowq) * 2, g * 32, 0));
       }
     if (!DUMP) {
       // a pad group (g = G) reads group G-1: its codes are zero, so it adds
@@ -153,7 +153,8 @@ __global__ __launch_bounds__(64 * max_waves(MT)) void k_gemm_skinny(GemmArgs a, 
           const uint32_t w0 = h ? wv[p][c].z : wv[p][c].x, w1 = h ? wv[p][c].w : wv[p][c].y;
           const v4i b = {(int)(w0 & kNibMask), (int)((w0 << 4) & kNibMask), (int)(w1 & kNibMask),
                          (int)((w1 << 4) & kNibMask)};
-          const float swf = (DUMP || p >= pn) ? 0.0f : f16_to_f32((uint16_t)t[p].sw[c][h]);
+          // sw / 16: the MFMA yields 16 * P
+          const float swf = (DUMP || p >= pn) ? 0.0f : f16_to_f32((uint16_t)t[p].sw[c][h]) * 0.0625f;
           const float nsw = -kMagic * swf;
 #pragma unroll
           for (int i = 0; i < MT; ++i) {
@@ -169,13 +170,13 @@ __global__ __launch_bounds__(64 * max_waves(MT)) void k_gemm_skinny(GemmArgs a, 
             } else {
               float u;
               u = __builtin_fmaf(__int_as_float(d[0]), swf, nsw);
-              acc[c][i][0] = __builtin_fmaf(u, t[p].sx[i][h][0], acc[c][i][0]);
+              acc[c][i][0] = __builtin_fmaf(u, (float)t[p].sx[i][h][0], acc[c][i][0]);
               u = __builtin_fmaf(__int_as_float(d[1]), swf, nsw);
-              acc[c][i][1] = __builtin_fmaf(u, t[p].sx[i][h][1], acc[c][i][1]);
+              acc[c][i][1] = __builtin_fmaf(u, (float)t[p].sx[i][h][1], acc[c][i][1]);
               u = __builtin_fmaf(__int_as_float(d[2]), swf, nsw);
-              acc[c][i][2] = __builtin_fmaf(u, t[p].sx[i][h][2], acc[c][i][2]);
+              acc[c][i][2] = __builtin_fmaf(u, (float)t[p].sx[i][h][2], acc[c][i][2]);
               u = __builtin_fmaf(__int_as_float(d[3]), swf, nsw);
-              acc[c][i][3] = __builtin_fmaf(u, t[p].sx[i][h][3], acc[c][i][3]);
+              acc[c][i][3] = __builtin_fmaf(u, (float)t[p].sx[i][h][3], acc[c][i][3]);
             }
           }
         }

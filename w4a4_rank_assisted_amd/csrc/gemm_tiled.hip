@@ -11,9 +11,9 @@
 // so the MFMA yields 16*P.  The MFMA accumulator input is the bit pattern of
 // 1.5*2^23; the result bits then read as the float 1.5*2^23 + 16P exactly,
 // and two FMAs per element finish the group:
-//   u   = fma(D, sw, -1.5*2^23*sw)   (= 16P*sw rounded once; the constant
-//                                      product is exact: 3*2^22 * fp16)
-//   acc = fma(u, sx/16, acc)
+//   u   = fma(D, sw/16, -1.5*2^23*sw/16)   (= P*sw rounded once; the
+//                                            constant product is exact)
+//   acc = fma(u, sx, acc)                   (sx read as fp16: v_fma_mix_f32)
 // Those two VALU FMAs per element and group, not the MFMA, bound the kernel
 // (a wave64 fp32 FMA takes 4 cycles, a 16x16x64 int8 MFMA 16 cycles for 4
 // elements per lane).  The loop keeps the VALU fed: within a stage the row
@@ -62,7 +62,7 @@ struct alignas(16) Stages {
   int8_t a[2][TMB][64][16];           // [buf][m-tile][lane][bytes]          16 KB
   int8_t b[2][TNB][64][16];           // [buf][n-tile][lane][bytes]          16 KB
   float2 sw[2][BN];                   // [buf][col] = (sw, -magic*sw)         2 KB
-  float sx[2][TMB][16];               // [buf][m-tile][row]                   1 KB
+  uint16_t sx[2][TMB][16];            // [buf][m-tile][row] fp16             512 B
 };
 
 // Epilogue operands of the block: U (rank columns padded to RPT) for its
@@ -155,20 +155,20 @@ __global__ __launch_bounds__(NTH, 2) void k_gemm_tiled(GemmArgs a, int nblk, int
   const int G = a.G;
   v4u ra[kSlots];
   v2u rb[kSlots];
-  float rsx[kSlots];
+  uint32_t rsx[kSlots];
   uint32_t rsw[kSlots];
   // Addresses: buffer resources over the operands, a fixed 32-bit byte
   // offset per lane (computed once) and a per-stage scalar offset, so a
   // stage costs no vector address math.
   const __amdgpu_buffer_rsrc_t rs_a = buffer_rsrc(a.qa, (uint32_t)MT * a.Gp * 1024);
   const __amdgpu_buffer_rsrc_t rs_w = buffer_rsrc(w, (uint32_t)NT * GP * 1024);
-  const __amdgpu_buffer_rsrc_t rs_x = buffer_rsrc(a.sxs, (uint32_t)MT * a.Gp * 64);
+  const __amdgpu_buffer_rsrc_t rs_x = buffer_rsrc(a.sxs, (uint32_t)MT * a.Gp * 32);
   const __amdgpu_buffer_rsrc_t rs_s = buffer_rsrc(sw, DUMP ? 0u : (uint32_t)G * a.N * 2);
   // thread t: 16-byte chunk t of the A tile, lane slot t of the B tile;
   // the first half also one activation scale, the second one weight scale
   const uint32_t offa = ((uint32_t)min(mt0 + (tid >> 6), MT - 1) * a.Gp * 64 + (tid & 63)) * 16;
   const uint32_t offb = ((uint32_t)min(nt0 + (tid >> 6), NT - 1) * GP * 64 + (tid & 63)) * 16;
-  const uint32_t offsx = ((uint32_t)min(mt0 + ((tid >> 4) & (TMB - 1)), MT - 1) * a.Gp * 16 + (tid & 15)) * 4;
+  const uint32_t offsx = ((uint32_t)min(mt0 + ((tid >> 4) & (TMB - 1)), MT - 1) * a.Gp * 16 + (tid & 15)) * 2;
   const uint32_t offsw = (uint32_t)min(nt0 * 16 + (tid & (BN - 1)), a.N - 1) * 2;
   // Straight-line code with a fixed number of loads per stage (the stage
   // index is clamped near the end instead of skipping the loads), so the
@@ -178,7 +178,7 @@ __global__ __launch_bounds__(NTH, 2) void k_gemm_tiled(GemmArgs a, int nblk, int
     g = min(g, a.Gp - 1);
     ra[SL] = __builtin_amdgcn_raw_buffer_load_b128(rs_a, offa, g * 1024, 0);
     rb[SL] = __builtin_amdgcn_raw_buffer_load_b64(rs_w, offb, (g >> 1) * 1024 + 8 * (g & 1), 0);
-    rsx[SL] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs_x, offsx, g * 64, 0));
+    rsx[SL] = __builtin_amdgcn_raw_buffer_load_b16(rs_x, offsx, g * 32, 0);
     if (!DUMP) rsw[SL] = __builtin_amdgcn_raw_buffer_load_b16(rs_s, offsw, min(g, G - 1) * a.N * 2, 0);
   };
   auto store_stage = [&](int g, auto slotc, int buf) __attribute__((always_inline)) {
@@ -191,11 +191,11 @@ __global__ __launch_bounds__(NTH, 2) void k_gemm_tiled(GemmArgs a, int nblk, int
     }
     if (tid < TMB * 16) {
       const int mi = tid >> 4, row = tid & 15;
-      sm.sx[buf][mi][row] = (mt0 + mi < MT) ? rsx[SL] : 0.0f;
+      sm.sx[buf][mi][row] = (mt0 + mi < MT) ? (uint16_t)rsx[SL] : (uint16_t)0;
     } else if (!DUMP && tid >= NTH / 2 && tid < NTH / 2 + BN) {
       const int col = tid - NTH / 2, n = nt0 * 16 + col;
       const float sv = (g < G && n < a.N) ? f16_to_f32((uint16_t)rsw[SL]) : 0.0f;
-      sm.sw[buf][col] = make_float2(sv, -kMagic * sv);
+      sm.sw[buf][col] = make_float2(sv * 0.0625f, -kMagic * 0.0625f * sv);
     }
   };
 
@@ -271,17 +271,17 @@ __global__ __launch_bounds__(NTH, 2) void k_gemm_tiled(GemmArgs a, int nblk, int
   // over), so the pipeline never drains at a stage boundary.
   v4i d[TM][TN];                      // MFMA results (row TM-1 carried)
   float2 swv[2][TN];                  // weight scales per LDS buffer
-  float4 sxv[TM], sx_carry;           // activation scales; last row of the previous stage
+  v4h sxv[TM], sx_carry;              // activation scales (fp16); last row of the previous stage
 #pragma unroll
   for (int j = 0; j < TN; ++j) {
     d[TM - 1][j] = magic;             // a first carry that adds exactly 0
     swv[1][j] = make_float2(0.0f, 0.0f);
   }
-  sx_carry = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+  sx_carry = (v4h){0, 0, 0, 0};
 
   // rescale one row tile: acc += (D - magic) * sw * sx, or, for the test
   // export, the group partials of the window
-  auto rescale = [&](int ip, const float2 (&sw2)[TN], const float4 sx4, int gg)
+  auto rescale = [&](int ip, const float2 (&sw2)[TN], const v4h sx4, int gg)
       __attribute__((always_inline)) {
 #pragma unroll
     for (int j = 0; j < TN; ++j) {
@@ -299,10 +299,10 @@ __global__ __launch_bounds__(NTH, 2) void k_gemm_tiled(GemmArgs a, int nblk, int
         const float u1 = __builtin_fmaf(__int_as_float(d[ip][j][1]), s2.x, s2.y);
         const float u2 = __builtin_fmaf(__int_as_float(d[ip][j][2]), s2.x, s2.y);
         const float u3 = __builtin_fmaf(__int_as_float(d[ip][j][3]), s2.x, s2.y);
-        acc[ip][j][0] = __builtin_fmaf(u0, sx4.x, acc[ip][j][0]);
-        acc[ip][j][1] = __builtin_fmaf(u1, sx4.y, acc[ip][j][1]);
-        acc[ip][j][2] = __builtin_fmaf(u2, sx4.z, acc[ip][j][2]);
-        acc[ip][j][3] = __builtin_fmaf(u3, sx4.w, acc[ip][j][3]);
+        acc[ip][j][0] = __builtin_fmaf(u0, (float)sx4.x, acc[ip][j][0]);
+        acc[ip][j][1] = __builtin_fmaf(u1, (float)sx4.y, acc[ip][j][1]);
+        acc[ip][j][2] = __builtin_fmaf(u2, (float)sx4.z, acc[ip][j][2]);
+        acc[ip][j][3] = __builtin_fmaf(u3, (float)sx4.w, acc[ip][j][3]);
       }
     }
     if (!DUMP) {
@@ -327,7 +327,7 @@ __global__ __launch_bounds__(NTH, 2) void k_gemm_tiled(GemmArgs a, int nblk, int
     }
     auto read_a = [&](int i) __attribute__((always_inline)) {
       av[i] = *reinterpret_cast<const v4i *>(&sm.a[BUF][wm * TM + i][lane][0]);
-      sxv[i] = *reinterpret_cast<const float4 *>(&sm.sx[BUF][wm * TM + i][rowq]);
+      sxv[i] = *reinterpret_cast<const v4h *>(&sm.sx[BUF][wm * TM + i][rowq]);
     };
     read_a(0);
 #pragma unroll

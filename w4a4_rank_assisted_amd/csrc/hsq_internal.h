@@ -51,8 +51,8 @@ inline size_t packed_bytes(int K, int N) {
 //   qa  : MT x Gp x 64 lanes x 16 int8 codes   (MFMA A-operand order:
 //         lane l of block (mt, g) holds row 16mt + l%16, channels
 //         64g + 16(l/16) + p, p = 0..15; pad rows / groups are zero)
-//   sxs : MT x Gp x 16 fp32, the activation scale divided by 16 (the
-//         contraction works on 16 * P), zero for pad rows / groups
+//   sxs : MT x Gp x 16 fp16, the activation scale of (row, group), zero for
+//         pad rows / groups (read straight into v_fma_mix_f32)
 //   uw  : S_u x (batch*r) x (16*MT) fp32, one slice of U per K-slice of the
 //         quantization pass, summed in slice order by the consumer
 //   part: split-K partial tiles of the tiled contraction when its grid is
@@ -88,14 +88,14 @@ struct QuantArgs {
   float *u_pub;
   // internal outputs (tiled codes, fp32 scales / 16, U slices)
   int8_t *qa;
-  float *sxs;
+  uint16_t *sxs;
   float *uw;
   int Gp, Mpad, ucols;
 };
 
 struct GemmArgs {
   const int8_t *qa;
-  const float *sxs;
+  const uint16_t *sxs;
   const uint8_t *w;        // packed residual of projection 0
   size_t w_stride;         // bytes between projections
   const uint16_t *sw;      // batch x G x N fp16
@@ -143,6 +143,7 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 typedef unsigned v4u __attribute__((ext_vector_type(4)));
 typedef unsigned v2u __attribute__((ext_vector_type(2)));
 typedef float v4f __attribute__((ext_vector_type(4)));
+typedef _Float16 v4h __attribute__((ext_vector_type(4)));
 
 // Buffer resource over `bytes` bytes at p (raw, untyped; reads past the end
 // return zero).  Loads through it take a 32-bit per-lane offset plus a

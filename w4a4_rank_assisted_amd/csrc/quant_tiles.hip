@@ -1,6 +1,6 @@
 // quant_tiles.hip -- K1 of the fused linear: one pass over X that smooths it,
 // quantizes it per token in 64-wide groups to symmetric int4 (written as int8
-// codes in the contraction's MFMA operand order, with fp32 scales / 16), and
+// codes in the contraction's MFMA operand order, with fp16 scales), and
 // accumulates the rank-r down projection U = xh * L1 of the smoothed,
 // unquantized activations.
 //
@@ -218,7 +218,7 @@ __global__ __launch_bounds__(1024) void k_quant_tiles(QuantArgs a, int gpb) {
       }
       const size_t blk = (size_t)mt * a.Gp + g;
       *reinterpret_cast<v4u *>(a.qa + blk * 1024 + (size_t)lane * 16) = w;
-      if (kq == 0) a.sxs[blk * 16 + row] = s * 0.0625f;
+      if (kq == 0) a.sxs[blk * 16 + row] = s16;
     }
 
     if constexpr (NR > 0) {
