@@ -268,7 +268,8 @@ __global__ __launch_bounds__(NTH, 2) void k_gemm_tiled(GemmArgs a, int nblk, int
   // stages.  Step s of stage g issues the MFMAs of row s and rescales the
   // row before it: row s-1 of stage g, or, at s = 0, the last row of stage
   // g-1 (its MFMA results, weight scales and activation scales are carried
-  // over), so the pipeline never drains at a stage boundary.
+  // over; its FMAs go first, while the stage's first LDS reads are in
+  // flight), so the pipeline never drains at a stage boundary.
   v4i d[TM][TN];                      // MFMA results (row TM-1 carried)
   float2 swv[2][TN];                  // weight scales per LDS buffer
   v4h sxv[TM], sx_carry;              // activation scales (fp16); last row of the previous stage
@@ -334,16 +335,21 @@ __global__ __launch_bounds__(NTH, 2) void k_gemm_tiled(GemmArgs a, int nblk, int
     for (int s = 0; s < TM; ++s) {
       // step boundary: nothing moves across it
       __builtin_amdgcn_sched_barrier(0);
-      pin(av[s]);
-      if (s + 1 < TM) read_a(s + 1);
       if (s == 0) {
-        // the carried row: rescaled before this step's MFMAs overwrite
-        // nothing of it (they write row 0)
+        // the carried row first: its FMAs need no LDS data, so they cover
+        // the latency of this stage's first reads (issued just above)
+        if (TM > 1) read_a(1);
+        rescale(TM - 1, swv[BUF ^ 1], sx_carry, g - 1);
+        __builtin_amdgcn_sched_barrier(0);
+        pin(av[0]);
 #pragma unroll
         for (int j = 0; j < TN; ++j)
           d[0][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(av[0], bv[j], magic, 0, 0, 0);
-        rescale(TM - 1, swv[BUF ^ 1], sx_carry, g - 1);
-      } else {
+        continue;
+      }
+      pin(av[s]);
+      if (s + 1 < TM) read_a(s + 1);
+      {
 #pragma unroll
         for (int j = 0; j < TN; ++j)
           d[s][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(av[s], bv[j], magic, 0, 0, 0);
