@@ -66,38 +66,14 @@ __global__ __launch_bounds__(64 * max_waves(MT)) void k_gemm_skinny(GemmArgs a, 
 #pragma unroll
       for (int q = 0; q < 4; ++q) acc[c][i][q] = 0.0f;
 
-  // epilogue operands: loads issued first, parked in LDS after the main loop
-  // (thread t holds U element t, L2 element t and bias t; more elements than
-  // threads loop at the end)
   const int EUN = a.r * MT * 16, ELN = a.r * 16 * CT, nthr = W * 64;
-  float upre[kMaxUSlices], l2pre = 0.0f, bpre = 0.0f;
-  if (!DUMP) {
-    // branch-free: empty resources (r == 0, no bias) read as zero
-    const __amdgpu_buffer_rsrc_t rs_u =
-        buffer_rsrc(a.uw, (uint32_t)a.u_slices * a.ucols * a.Mpad * 4);
-    const __amdgpu_buffer_rsrc_t rs_l =
-        buffer_rsrc(a.r > 0 ? a.L2 + (size_t)proj * a.r * a.N : nullptr, (uint32_t)a.r * a.N * 2);
-    const __amdgpu_buffer_rsrc_t rs_b =
-        buffer_rsrc(a.bias ? a.bias + (size_t)proj * a.N : nullptr, a.bias ? (uint32_t)a.N * 2 : 0u);
-    const int e = min(tid, max(EUN - 1, 0));
-    const uint32_t offu = (uint32_t)(((size_t)proj * a.r + e / (MT * 16)) * a.Mpad + e % (MT * 16)) * 4;
-#pragma unroll
-    for (int sl = 0; sl < kMaxUSlices; ++sl)
-      upre[sl] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
-          rs_u, offu, min(sl, a.u_slices - 1) * a.ucols * a.Mpad * 4, 0));
-    const int e2 = min(tid, max(ELN - 1, 0));         // (rank column, block column)
-    l2pre = bf16_to_f32(__builtin_amdgcn_raw_buffer_load_b16(
-        rs_l, (uint32_t)((e2 / (16 * CT)) * a.N + min(nt0 * 16 + e2 % (16 * CT), a.N - 1)) * 2, 0, 0));
-    bpre = bf16_to_f32(__builtin_amdgcn_raw_buffer_load_b16(
-        rs_b, (uint32_t)min(nt0 * 16 + tid % (16 * CT), a.N - 1) * 2, 0, 0));
-  }
 
   // activation codes / scales of one group pair, raw weight scales of its
   // CT column tiles
   struct Act {
     v4i av[MT][2];
     v4h sx[MT][2];
-    uint32_t sw[CT][2];
+    v2h sw[CT];                         // the pair's two groups, fp16
   };
   auto load_act = [&](int gp, Act &t) __attribute__((always_inline)) {
 #pragma unroll
@@ -118,7 +94,8 @@ __global__ __launch_bounds__(64 * max_waves(MT)) void k_gemm_skinny(GemmArgs a, 
       for (int c = 0; c < CT; ++c)
 #pragma unroll
         for (int h = 0; h < 2; ++h)
-          t.sw[c][h] = __builtin_amdgcn_raw_buffer_load_b16(rs_s, offsw[c], min(2 * gp + h, G - 1) * a.N * 2, 0);
+          t.sw[c][h] = __builtin_bit_cast(
+              _Float16, __builtin_amdgcn_raw_buffer_load_b16(rs_s, offsw[c], min(2 * gp + h, G - 1) * a.N * 2, 0));
     }
   };
 
@@ -154,7 +131,7 @@ __global__ __launch_bounds__(64 * max_waves(MT)) void k_gemm_skinny(GemmArgs a, 
           const v4i b = {(int)(w0 & kNibMask), (int)((w0 << 4) & kNibMask), (int)(w1 & kNibMask),
                          (int)((w1 << 4) & kNibMask)};
           // sw / 16: the MFMA yields 16 * P
-          const float swf = (DUMP || p >= pn) ? 0.0f : f16_to_f32((uint16_t)t[p].sw[c][h]) * 0.0625f;
+          const float swf = (DUMP || p >= pn) ? 0.0f : (float)t[p].sw[c][h] * 0.0625f;
           const float nsw = -kMagic * swf;
 #pragma unroll
           for (int i = 0; i < MT; ++i) {
@@ -177,6 +154,10 @@ __global__ __launch_bounds__(64 * max_waves(MT)) void k_gemm_skinny(GemmArgs a, 
               acc[c][i][2] = __builtin_fmaf(u, (float)t[p].sx[i][h][2], acc[c][i][2]);
               u = __builtin_fmaf(__int_as_float(d[3]), swf, nsw);
               acc[c][i][3] = __builtin_fmaf(u, (float)t[p].sx[i][h][3], acc[c][i][3]);
+              // each MFMA result is consumed before the next MFMA issues (the
+              // scheduler would otherwise keep all of them alive at once)
+#pragma unroll
+              for (int q = 0; q < 4; ++q) asm volatile("" : "+v"(acc[c][i][q]));
             }
           }
         }
@@ -184,27 +165,20 @@ __global__ __launch_bounds__(64 * max_waves(MT)) void k_gemm_skinny(GemmArgs a, 
   }
   if (DUMP) return;
 
-  // epilogue operands into LDS (the barriers below order them)
-  if (tid < EUN) {
-    float u = 0.0f;
-#pragma unroll
-    for (int sl = 0; sl < kMaxUSlices; ++sl) u += sl < a.u_slices ? upre[sl] : 0.0f;
-    const int c = tid / (MT * 16), row = tid % (MT * 16);
-    for (int sl = kMaxUSlices; sl < a.u_slices; ++sl)   // long K: the remaining slices
-      u += a.uw[((size_t)sl * a.ucols + (size_t)proj * a.r + c) * a.Mpad + row];
-    eu[tid] = u;
-  }
-  for (int p = tid + nthr; p < EUN; p += nthr) {       // more elements than threads
+  // epilogue operands into LDS, loaded only now: held across the weight
+  // stream they would cost registers the stream needs (the barrier below
+  // orders them)
+  for (int p = tid; p < EUN; p += nthr) {               // U: the slices summed in order
     const int c = p / (MT * 16), row = p % (MT * 16);
     float u = 0.0f;
     for (int sl = 0; sl < a.u_slices; ++sl)
       u += a.uw[((size_t)sl * a.ucols + (size_t)proj * a.r + c) * a.Mpad + row];
     eu[p] = u;
   }
-  if (tid < ELN) el2[tid] = l2pre;
-  for (int p = tid + nthr; p < ELN; p += nthr)
+  for (int p = tid; p < ELN; p += nthr)
     el2[p] = bf16_to_f32(a.L2[((size_t)proj * a.r + p / (16 * CT)) * a.N + min(nt0 * 16 + p % (16 * CT), a.N - 1)]);
-  if (tid < 16 * CT) eb[tid] = bpre;
+  if (tid < 16 * CT)
+    eb[tid] = a.bias ? bf16_to_f32(a.bias[(size_t)proj * a.N + min(nt0 * 16 + tid, a.N - 1)]) : 0.0f;
 
   // ---- the W partial tiles: parked, then each output summed over the
   // waves in order, plus U * L2 and the bias ----

@@ -144,6 +144,7 @@ typedef unsigned v4u __attribute__((ext_vector_type(4)));
 typedef unsigned v2u __attribute__((ext_vector_type(2)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef _Float16 v4h __attribute__((ext_vector_type(4)));
+typedef _Float16 v2h __attribute__((ext_vector_type(2)));
 
 // Buffer resource over `bytes` bytes at p (raw, untyped; reads past the end
 // return zero).  Loads through it take a 32-bit per-lane offset plus a
