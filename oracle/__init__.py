@@ -17,7 +17,8 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "hsq_oracle.c")
 _LIB = os.path.join(_HERE, "liboracle.so")
-GROUP = 64
+GROUP = 64          # the default group width; 128 is the other one supported
+GROUPS = (64, 128)
 
 _lib = None
 
@@ -56,14 +57,20 @@ def _bind(lib):
     lib.oracle_f32_to_f16_rne.restype = ctypes.c_uint16
     lib.oracle_quantize_act.argtypes = [P, I, I, P, P, P, P]
     lib.oracle_quantize_act.restype = None
+    lib.oracle_quantize_act_g.argtypes = [P, I, I, I, P, P, P, P]
+    lib.oracle_quantize_act_g.restype = None
     lib.oracle_pack_act.argtypes = [P, I, I, P]
     lib.oracle_pack_act.restype = None
     lib.oracle_group_partials.argtypes = [P, P, I, I, I, I, I, I, I, P]
     lib.oracle_group_partials.restype = None
+    lib.oracle_group_partials_g.argtypes = [P, P, I, I, I, I, I, I, I, I, P]
+    lib.oracle_group_partials_g.restype = None
     lib.oracle_lowrank_down.argtypes = [P, I, I, P, I, P]
     lib.oracle_lowrank_down.restype = None
     lib.oracle_linear.argtypes = [P, I, I, I, P, P, P, P, P, I, P, P, I, P]
     lib.oracle_linear.restype = None
+    lib.oracle_linear_g.argtypes = [P, I, I, I, I, P, P, P, P, P, I, P, P, I, P]
+    lib.oracle_linear_g.restype = None
     lib.oracle_num_threads.argtypes = []
     lib.oracle_num_threads.restype = I
     lib.oracle_set_num_threads.argtypes = [I]
@@ -102,16 +109,16 @@ class Oracle:
         self.lib.oracle_set_num_threads(int(n))
 
     # steps 1-4
-    def quantize(self, X, lam, want_xh: bool = False):
+    def quantize(self, X, lam, want_xh: bool = False, group: int = GROUP):
         X = _c(X, np.uint16)
         lam = _c(lam, np.uint16)
         M, K = X.shape
-        if K % GROUP:
-            raise ValueError("K must be a multiple of 64")
+        if group not in GROUPS or K % group:
+            raise ValueError("group must be 64 or 128 and divide K")
         q = np.empty((M, K), np.int8)
-        sx = np.empty((M, K // GROUP), np.uint16)
+        sx = np.empty((M, K // group), np.uint16)
         xh = np.empty((M, K), np.float32) if want_xh else None
-        self.lib.oracle_quantize_act(_ptr(X), M, K, _ptr(lam), _ptr(q), _ptr(sx), _ptr(xh))
+        self.lib.oracle_quantize_act_g(_ptr(X), M, K, group, _ptr(lam), _ptr(q), _ptr(sx), _ptr(xh))
         return (q, sx, xh) if want_xh else (q, sx)
 
     def pack_act(self, q):
@@ -122,17 +129,17 @@ class Oracle:
         return out
 
     # step 5
-    def group_partials(self, qa, qw, m0=0, mc=None, n0=0, nc=None):
+    def group_partials(self, qa, qw, m0=0, mc=None, n0=0, nc=None, group: int = GROUP):
         qa = _c(qa, np.int8)
         qw = _c(qw, np.int8)
         M, K = qa.shape
         K2, N = qw.shape
-        assert K == K2 and K % GROUP == 0
+        assert K == K2 and group in GROUPS and K % group == 0
         mc = M - m0 if mc is None else mc
         nc = N - n0 if nc is None else nc
         assert 0 <= m0 and m0 + mc <= M and 0 <= n0 and n0 + nc <= N
-        P = np.empty((mc, nc, K // GROUP), np.int32)
-        self.lib.oracle_group_partials(_ptr(qa), _ptr(qw), M, K, N, m0, mc, n0, nc, _ptr(P))
+        P = np.empty((mc, nc, K // group), np.int32)
+        self.lib.oracle_group_partials_g(_ptr(qa), _ptr(qw), M, K, N, group, m0, mc, n0, nc, _ptr(P))
         return P
 
     def lowrank_down(self, xh, L1):
@@ -146,14 +153,16 @@ class Oracle:
         return U
 
     # steps 1-7
-    def linear(self, X, lam, qw, sw, L1=None, L2=None, bias=None, rows=None):
-        """fp64 Y for one projection; ``rows`` selects output rows (None: all)."""
+    def linear(self, X, lam, qw, sw, L1=None, L2=None, bias=None, rows=None, group: int = GROUP):
+        """fp64 Y for one projection; ``rows`` selects output rows (None: all);
+        sw is (K/group) x N."""
         X = _c(X, np.uint16)
         lam = _c(lam, np.uint16)
         qw = _c(qw, np.int8)
         sw = _c(sw, np.uint16)
         M, K = X.shape
         N = qw.shape[1]
+        assert group in GROUPS and K % group == 0 and sw.shape == (K // group, N)
         r = 0 if L1 is None else int(L1.shape[1])
         L1c = _c(L1, np.uint16) if r else None
         L2c = _c(L2, np.uint16) if r else None
@@ -165,16 +174,18 @@ class Oracle:
             nrows = rows_c.size
             assert np.all((rows_c >= 0) & (rows_c < M))
         Y = np.empty((nrows, N), np.float64)
-        self.lib.oracle_linear(_ptr(X), M, K, N, _ptr(lam), _ptr(qw), _ptr(sw), _ptr(L1c),
-                               _ptr(L2c), r, _ptr(bc), _ptr(rows_c), nrows, _ptr(Y))
+        self.lib.oracle_linear_g(_ptr(X), M, K, N, group, _ptr(lam), _ptr(qw), _ptr(sw), _ptr(L1c),
+                                 _ptr(L2c), r, _ptr(bc), _ptr(rows_c), nrows, _ptr(Y))
         return Y
 
     def linear_batched(self, layer: dict, rows=None):
-        """Y for every projection of a generated layer: (B, rows, N) fp64."""
+        """Y for every projection of a generated layer: (B, rows, N) fp64
+        (the layer's "group", 64 when absent)."""
         B = layer["qw"].shape[0]
         r = layer["L1"].shape[2]
+        group = int(layer.get("group", GROUP))
         return np.stack([
             self.linear(layer["X"], layer["lam"], layer["qw"][b], layer["sw"][b],
                         layer["L1"][b] if r else None, layer["L2"][b] if r else None,
-                        layer["bias"][b], rows=rows)
+                        layer["bias"][b], rows=rows, group=group)
             for b in range(B)])

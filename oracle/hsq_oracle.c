@@ -13,7 +13,10 @@
  *   Deflating the Hessian (abstract): each weight is split into a low-bit
  *   residual and a high-precision low-rank component, W ~ L1*L2 + Q(R).
  *   Deflating the Hessian (Table 1 caption; Table 8 caption): 4-bit weights
- *   and 4-bit activations, group-64.
+ *   and 4-bit activations, group-64 for the diffusion transformers;
+ *   (Table 3, 4, 6 and 7 captions): group-128 for the Qwen3-8B runs.  The
+ *   group width is a parameter (64 or 128) of the functions ending in _g;
+ *   the others are their group-64 forms.
  *   H-SVDQuant explainer (rit.work), section on Hessian deflation, last
  *   paragraph: a diagonal scaling moves range between weights and
  *   activations and leaves the full-precision transform unchanged.
@@ -23,7 +26,7 @@
  * Arithmetic contract (the pages print no inference formula; these are the
  * readings this library states and both sides follow):
  *   xh[m,k]  = fl32( float(X[m,k]) * fl32(1 / float(lambda[k])) )
- *   amax     = max over the 64-wide group of |xh|
+ *   amax     = max over the group (64 or 128 channels) of |xh|
  *   s        = 0 if amax == 0, else f16_rne( fl32(amax / 7) ), saturated at 65504
  *   q[m,k]   = 0 if s == 0, else clamp( rint( fl32(xh * fl32(1 / float(s))) ), -8, 7 )
  *   P[m,n,g] = sum_{k in g} q[m,k] * qw[k,n]                   (exact integer)
@@ -43,7 +46,8 @@
 #include <omp.h>
 #endif
 
-#define ORACLE_GROUP 64
+#define ORACLE_GROUP 64          /* the default group width */
+#define ORACLE_MAX_GROUP 128
 
 /* ---- number formats, written from the IEEE-754 / bfloat16 definitions ---- */
 
@@ -100,31 +104,32 @@ uint16_t oracle_f32_to_f16_rne(float x)
     return (uint16_t)(sign | bits);
 }
 
-/* ---- step 1-4: smoothing and per-token group-64 symmetric int4 codes ---- */
+/* ---- step 1-4: smoothing and per-token group-wise symmetric int4 codes ---- */
 
-/* Quantize rows [0, M) of X (M x K bf16, row-major).
+/* Quantize rows [0, M) of X (M x K bf16, row-major) in groups of `group`
+ * consecutive channels (64 or 128).
  *   lam  : K fp16 smoothing factors (x is divided by lambda, via its
  *          fp32 reciprocal).
  *   q    : M x K int8 codes out.
- *   sx   : M x (K/64) fp16 scales out.
+ *   sx   : M x (K/group) fp16 scales out.
  *   xh   : optional M x K fp32 smoothed activations out (NULL to skip).
- * K must be a multiple of 64; inputs must be finite. */
-void oracle_quantize_act(const uint16_t *X, int M, int K, const uint16_t *lam,
-                         int8_t *q, uint16_t *sx, float *xh)
+ * K must be a multiple of group; inputs must be finite. */
+void oracle_quantize_act_g(const uint16_t *X, int M, int K, int group, const uint16_t *lam,
+                           int8_t *q, uint16_t *sx, float *xh)
 {
-    int G = K / ORACLE_GROUP;
+    int G = K / group;
     float *inv_lam = (float *)malloc(sizeof(float) * (size_t)K);
     for (int k = 0; k < K; ++k)
         inv_lam[k] = 1.0f / oracle_f16_to_f32(lam[k]);
 
 #pragma omp parallel for schedule(static)
     for (int m = 0; m < M; ++m) {
-        float v[ORACLE_GROUP];
+        float v[ORACLE_MAX_GROUP];
         for (int g = 0; g < G; ++g) {
-            size_t base = (size_t)m * K + (size_t)g * ORACLE_GROUP;
+            size_t base = (size_t)m * K + (size_t)g * group;
             float amax = 0.0f;
-            for (int j = 0; j < ORACLE_GROUP; ++j) {
-                int k = g * ORACLE_GROUP + j;
+            for (int j = 0; j < group; ++j) {
+                int k = g * group + j;
                 v[j] = oracle_bf16_to_f32(X[base + j]) * inv_lam[k];
                 if (fabsf(v[j]) > amax)
                     amax = fabsf(v[j]);
@@ -139,12 +144,12 @@ void oracle_quantize_act(const uint16_t *X, int M, int K, const uint16_t *lam,
             }
             sx[(size_t)m * G + g] = s16;
             if (s16 == 0) {
-                for (int j = 0; j < ORACLE_GROUP; ++j)
+                for (int j = 0; j < group; ++j)
                     q[base + j] = 0;
                 continue;
             }
             float inv_s = 1.0f / oracle_f16_to_f32(s16);
-            for (int j = 0; j < ORACLE_GROUP; ++j) {
+            for (int j = 0; j < group; ++j) {
                 float t = v[j] * inv_s;
                 float r = rintf(t);                   /* ties to even */
                 int c = r > 7.0f ? 7 : (r < -8.0f ? -8 : (int)r);
@@ -153,6 +158,12 @@ void oracle_quantize_act(const uint16_t *X, int M, int K, const uint16_t *lam,
         }
     }
     free(inv_lam);
+}
+
+void oracle_quantize_act(const uint16_t *X, int M, int K, const uint16_t *lam,
+                         int8_t *q, uint16_t *sx, float *xh)
+{
+    oracle_quantize_act_g(X, M, K, ORACLE_GROUP, lam, q, sx, xh);
 }
 
 /* Canonical packed activation layout: byte j of a row holds code k = 2j in
@@ -169,12 +180,13 @@ void oracle_pack_act(const int8_t *q, int M, int K, uint8_t *packed)
 
 /* ---- step 5: per-group integer partial sums, brute force ---- */
 
-/* P[(m-m0)][(n-n0)][g] = sum_{k in group g} qa[m,k] * qw[k,n]
- * qa: M x K int8 (row-major), qw: K x N int8 (row-major, in x out). */
-void oracle_group_partials(const int8_t *qa, const int8_t *qw, int M, int K, int N,
-                           int m0, int mc, int n0, int nc, int32_t *P)
+/* P[(m-m0)][(n-n0)][g] = sum_{k in group g} qa[m,k] * qw[k,n], groups of
+ * `group` channels; qa: M x K int8 (row-major), qw: K x N int8 (row-major,
+ * in x out). */
+void oracle_group_partials_g(const int8_t *qa, const int8_t *qw, int M, int K, int N, int group,
+                             int m0, int mc, int n0, int nc, int32_t *P)
 {
-    int G = K / ORACLE_GROUP;
+    int G = K / group;
     (void)M;
 #pragma omp parallel for schedule(static)
     for (int i = 0; i < mc; ++i) {
@@ -183,14 +195,20 @@ void oracle_group_partials(const int8_t *qa, const int8_t *qw, int M, int K, int
             int n = n0 + jn;
             for (int g = 0; g < G; ++g) {
                 int32_t acc = 0;
-                for (int t = 0; t < ORACLE_GROUP; ++t) {
-                    int k = g * ORACLE_GROUP + t;
+                for (int t = 0; t < group; ++t) {
+                    int k = g * group + t;
                     acc += (int32_t)qa[(size_t)m * K + k] * (int32_t)qw[(size_t)k * N + n];
                 }
                 P[((size_t)i * nc + jn) * G + g] = acc;
             }
         }
     }
+}
+
+void oracle_group_partials(const int8_t *qa, const int8_t *qw, int M, int K, int N,
+                           int m0, int mc, int n0, int nc, int32_t *P)
+{
+    oracle_group_partials_g(qa, qw, M, K, N, ORACLE_GROUP, m0, mc, n0, nc, P);
 }
 
 /* ---- step 4b: the rank-r down projection on the smoothed, unquantized x ---- */
@@ -212,18 +230,19 @@ void oracle_lowrank_down(const float *xh, int M, int K, const uint16_t *L1, int 
 
 /* ---- steps 1-7 together, for a chosen set of output rows ---- */
 
-/* Y[i][n] for rows m = rows[i] (rows == NULL: all M rows, i == m), fp64.
- *   X (M x K bf16), lam (K fp16), qw (K x N int8 codes), sw ((K/64) x N fp16),
+/* Y[i][n] for rows m = rows[i] (rows == NULL: all M rows, i == m), fp64,
+ * with groups of `group` channels (64 or 128).
+ *   X (M x K bf16), lam (K fp16), qw (K x N int8 codes), sw ((K/group) x N fp16),
  *   L1 (K x r bf16), L2 (r x N bf16), bias (N bf16 or NULL); r may be 0.
  * Each chosen row is quantized on its own (rows are independent: the
  * quantizer is per token), then every (n, g) partial is a brute-force
  * integer dot product. */
-void oracle_linear(const uint16_t *X, int M, int K, int N, const uint16_t *lam,
-                   const int8_t *qw, const uint16_t *sw, const uint16_t *L1,
-                   const uint16_t *L2, int r, const uint16_t *bias,
-                   const int *rows, int nrows, double *Y)
+void oracle_linear_g(const uint16_t *X, int M, int K, int N, int group, const uint16_t *lam,
+                     const int8_t *qw, const uint16_t *sw, const uint16_t *L1,
+                     const uint16_t *L2, int r, const uint16_t *bias,
+                     const int *rows, int nrows, double *Y)
 {
-    int G = K / ORACLE_GROUP;
+    int G = K / group;
     int count = rows ? nrows : M;
 #pragma omp parallel
     {
@@ -234,15 +253,15 @@ void oracle_linear(const uint16_t *X, int M, int K, int N, const uint16_t *lam,
 #pragma omp for schedule(dynamic, 1)
         for (int i = 0; i < count; ++i) {
             int m = rows ? rows[i] : i;
-            oracle_quantize_act(X + (size_t)m * K, 1, K, lam, q, s, xh);
+            oracle_quantize_act_g(X + (size_t)m * K, 1, K, group, lam, q, s, xh);
             if (r > 0)
                 oracle_lowrank_down(xh, 1, K, L1, r, u);
             for (int n = 0; n < N; ++n) {
                 double y = 0.0;
                 for (int g = 0; g < G; ++g) {
                     int32_t p = 0;
-                    for (int t = 0; t < ORACLE_GROUP; ++t) {
-                        int k = g * ORACLE_GROUP + t;
+                    for (int t = 0; t < group; ++t) {
+                        int k = g * group + t;
                         p += (int32_t)q[k] * (int32_t)qw[(size_t)k * N + n];
                     }
                     y += (double)p * (double)oracle_f16_to_f32(s[g]) *
@@ -260,6 +279,14 @@ void oracle_linear(const uint16_t *X, int M, int K, int N, const uint16_t *lam,
         free(xh);
         free(u);
     }
+}
+
+void oracle_linear(const uint16_t *X, int M, int K, int N, const uint16_t *lam,
+                   const int8_t *qw, const uint16_t *sw, const uint16_t *L1,
+                   const uint16_t *L2, int r, const uint16_t *bias,
+                   const int *rows, int nrows, double *Y)
+{
+    oracle_linear_g(X, M, K, N, ORACLE_GROUP, lam, qw, sw, L1, L2, r, bias, rows, nrows, Y);
 }
 
 int oracle_num_threads(void)

@@ -15,10 +15,11 @@ Layer dictionaries hold, with ``B`` = number of projections sharing X:
   X    (M, K)     uint16 bf16 bits    activations, row-major
   lam  (K,)       uint16 fp16 bits    smoothing factors (x is divided by them)
   qw   (B, K, N)  int8                residual codes, in x out
-  sw   (B, G, N)  uint16 fp16 bits    residual scale per 64-wide K group
+  sw   (B, G, N)  uint16 fp16 bits    residual scale per K group (G = K / group)
   L1   (B, K, r)  uint16 bf16 bits    input-side low-rank factor
   L2   (B, r, N)  uint16 bf16 bits    output-side low-rank factor
   bias (B, N)     uint16 bf16 bits
+  group           int                 channels per quantization group (64 or 128)
 """
 
 from __future__ import annotations
@@ -29,7 +30,7 @@ from typing import Dict, Optional
 import numpy as np
 
 ROOT_SEED = 261011315
-GROUP = 64
+GROUP = 64          # default group width; 128 is the other one the library supports
 
 
 # ---------------------------------------------------------------- conversions
@@ -86,10 +87,11 @@ class LayerSpec:
     x_recipe: str = "smoke"
     x_rows: int = 0   # rows drawn before slicing to M (0: M)
     description: str = ""
+    group: int = GROUP
 
     @property
     def G(self) -> int:
-        return self.K // GROUP
+        return self.K // self.group
 
     @property
     def ops(self) -> int:
@@ -118,12 +120,16 @@ LAYERS: Dict[str, LayerSpec] = {
 }
 
 
-def layer_spec(name: str, M: Optional[int] = None) -> LayerSpec:
+def layer_spec(name: str, M: Optional[int] = None, group: Optional[int] = None) -> LayerSpec:
     s = LAYERS[name]
     if M is not None and M != s.M:
         if s.x_rows and M > s.x_rows:
             raise ValueError(f"{name}: M={M} exceeds the {s.x_rows} drawn rows")
         s = dataclasses.replace(s, M=M)
+    if group is not None and group != s.group:
+        if group not in (64, 128) or s.K % group:
+            raise ValueError(f"{name}: group {group} does not divide K = {s.K}")
+        s = dataclasses.replace(s, group=group)
     return s
 
 
@@ -185,25 +191,26 @@ def _draw_projection(spec: LayerSpec, b: int):
     return qw, sw, L1, L2, bias
 
 
-def _sqrt_balanced_lambda(x_bf16: np.ndarray, qw: np.ndarray, sw: np.ndarray) -> np.ndarray:
+def _sqrt_balanced_lambda(x_bf16: np.ndarray, qw: np.ndarray, sw: np.ndarray, group: int) -> np.ndarray:
     """lambda_j = fp16(sqrt(a_j / w_j)); a_j = max_m |X[m, j]|,
-    w_j = max over projections and n of |qw[j, n] * sw[j // 64, n]|."""
+    w_j = max over projections and n of |qw[j, n] * sw[j // group, n]|."""
     a = np.abs(bf16_bits_to_f32(x_bf16)).max(axis=0).astype(np.float64)
     B, K, N = qw.shape
     w = np.zeros(K, dtype=np.float64)
     swf = f16_bits_to_f32(sw).astype(np.float64)  # (B, G, N)
     for b in range(B):
-        for g in range(K // GROUP):
-            blk = np.abs(qw[b, g * GROUP:(g + 1) * GROUP, :].astype(np.float64)) * swf[b, g][None, :]
-            w[g * GROUP:(g + 1) * GROUP] = np.maximum(w[g * GROUP:(g + 1) * GROUP], blk.max(axis=1))
+        for g in range(K // group):
+            blk = np.abs(qw[b, g * group:(g + 1) * group, :].astype(np.float64)) * swf[b, g][None, :]
+            w[g * group:(g + 1) * group] = np.maximum(w[g * group:(g + 1) * group], blk.max(axis=1))
     lam = np.sqrt(np.where((a > 0) & (w > 0), a / np.where(w > 0, w, 1.0), 1.0))
     lam = np.clip(lam, 2.0 ** -14, 60000.0)
     return f64_to_f16_bits(lam)
 
 
-def make_layer(name: str, M: Optional[int] = None) -> dict:
-    """All tensors of one named layer (see ``LAYERS``), deterministic."""
-    spec = layer_spec(name, M)
+def make_layer(name: str, M: Optional[int] = None, group: Optional[int] = None) -> dict:
+    """All tensors of one named layer (see ``LAYERS``), deterministic; `group`
+    overrides its quantization group width (64 or 128)."""
+    spec = layer_spec(name, M, group)
     x64 = _draw_x(spec)
     X_all = f64_to_bf16_bits(x64)
     del x64
@@ -217,28 +224,28 @@ def make_layer(name: str, M: Optional[int] = None) -> dict:
         lam = f64_to_f16_bits(np.exp(_rng(spec.cfg, spec.layer, _T_LAM).uniform(
             np.log(0.5), np.log(2.0), spec.K)))
     else:
-        lam = _sqrt_balanced_lambda(X_all, qw, sw)  # from all drawn rows
+        lam = _sqrt_balanced_lambda(X_all, qw, sw, spec.group)  # from all drawn rows
     X = np.ascontiguousarray(X_all[: spec.M])
-    return dict(spec=spec, X=X, lam=lam, qw=qw, sw=sw, L1=L1, L2=L2, bias=bias)
+    return dict(spec=spec, X=X, lam=lam, qw=qw, sw=sw, L1=L1, L2=L2, bias=bias, group=spec.group)
 
 
 def make_random_layer(seed: int, M: int, K: int, N: int, r: int = 4, batch: int = 1,
                       outlier_channels: int = 0, outlier_scale: float = 20.0,
-                      x_scale: float = 1.0, zero_bias: bool = False) -> dict:
+                      x_scale: float = 1.0, zero_bias: bool = False, group: int = GROUP) -> dict:
     """A generic seeded layer for edge-case tests (ragged M/N, other ranks).
 
     Same distributions as the smoke layer: X ~ N(0, x_scale^2) with optional
     outlier channels, lambda log-uniform in [0.5, 2], codes uniform in
     [-8, 7], weight scales log-uniform in [1e-3, 1e-2], L1/L2/bias
     ~ N(0, 0.02^2)."""
-    if K % GROUP:
-        raise ValueError("K must be a multiple of 64")
+    if group not in (64, 128) or K % group:
+        raise ValueError("K must be a multiple of the group width (64 or 128)")
     rng = np.random.default_rng(np.random.SeedSequence([ROOT_SEED, 1000 + seed, M, K, N, r, batch]))
     x = rng.standard_normal((M, K)) * x_scale
     if outlier_channels:
         idx = rng.choice(K, outlier_channels, replace=False)
         x[:, idx] *= outlier_scale
-    G = K // GROUP
+    G = K // group
     qw = rng.integers(-8, 8, size=(batch, K, N), dtype=np.int8)
     sw = f64_to_f16_bits(np.exp(rng.uniform(np.log(1e-3), np.log(1e-2), (batch, G, N))))
     L1 = f64_to_bf16_bits(rng.normal(0.0, 0.02, (batch, K, r)))
@@ -248,5 +255,6 @@ def make_random_layer(seed: int, M: int, K: int, N: int, r: int = 4, batch: int 
     else:
         bias = f64_to_bf16_bits(rng.normal(0.0, 0.02, (batch, N)))
     lam = f64_to_f16_bits(np.exp(rng.uniform(np.log(0.5), np.log(2.0), K)))
-    spec = LayerSpec(f"random{seed}", 0, 0, M, K, N, r=r, batch=batch, x_recipe="random")
-    return dict(spec=spec, X=f64_to_bf16_bits(x), lam=lam, qw=qw, sw=sw, L1=L1, L2=L2, bias=bias)
+    spec = LayerSpec(f"random{seed}", 0, 0, M, K, N, r=r, batch=batch, x_recipe="random", group=group)
+    return dict(spec=spec, X=f64_to_bf16_bits(x), lam=lam, qw=qw, sw=sw, L1=L1, L2=L2, bias=bias,
+                group=group)

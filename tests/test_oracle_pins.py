@@ -94,12 +94,14 @@ def _deq_scale(sx):
     return f16_bits_to_f32(sx).astype(np.float64)
 
 
-@pytest.mark.parametrize("seed", [0, 1, 2])
-def test_quantizer_invariants(oracle, seed):
-    X, lam = _random_x(seed, 37, 320)
-    q, sx, xh = oracle.quantize(X, lam, want_xh=True)
+@pytest.mark.parametrize("seed,group,K", [(0, 64, 320), (1, 64, 320), (2, 64, 320),
+                                          (0, 128, 384), (1, 128, 384)])
+def test_quantizer_invariants(oracle, seed, group, K):
+    X, lam = _random_x(seed, 37, K)
+    q, sx, xh = oracle.quantize(X, lam, want_xh=True, group=group)
     M, K = X.shape
-    G = K // 64
+    G = K // group
+    assert sx.shape == (M, G)
     s = _deq_scale(sx)
     # codes of symmetric absmax/7 quantization lie in [-7, 7]
     assert q.min() >= -7 and q.max() <= 7
@@ -107,8 +109,8 @@ def test_quantizer_invariants(oracle, seed):
     ref_xh = bf16_bits_to_f32(X).astype(np.float64) / f16_bits_to_f32(lam).astype(np.float64)
     assert np.allclose(xh, ref_xh, rtol=2.5e-7, atol=0)
     for g in range(G):
-        blk = xh[:, 64 * g:64 * (g + 1)].astype(np.float64)
-        qb = q[:, 64 * g:64 * (g + 1)].astype(np.float64)
+        blk = xh[:, group * g:group * (g + 1)].astype(np.float64)
+        qb = q[:, group * g:group * (g + 1)].astype(np.float64)
         amax = np.abs(blk).max(axis=1)
         # the scale is absmax/7 to fp16 precision (relative 2^-11)
         assert np.all(np.abs(s[:, g] - amax / 7) <= amax / 7 * 2.0 ** -11)
@@ -159,6 +161,30 @@ def test_quantizer_groups_and_tokens_are_independent(oracle):
     assert not np.array_equal(q1[4, 64:128], q2[4, 64:128])
 
 
+def test_group128_equals_group64_when_halves_share_absmax(oracle):
+    # Where both 64-channel halves of every 128-group have the same absmax
+    # (the second half is the first, negated and reversed), a 128-wide group
+    # has the scale of each of its halves, so group-128 and group-64 give
+    # the same codes and the same scales (repeated).
+    X, lam = _random_x(9, 11, 256)
+    x = bf16_bits_to_f32(X).astype(np.float64)
+    lamf = f16_bits_to_f32(lam).astype(np.float64)
+    lam2 = lam.copy()
+    for j in range(0, 256, 128):
+        x[:, j + 64:j + 128] = -x[:, j:j + 64][:, ::-1]
+        lam2[j + 64:j + 128] = lam[j:j + 64][::-1]      # the same divisor for the mirrored channel
+    Xm = f64_to_bf16_bits(x)
+    assert np.all(lamf > 0)
+    q64, s64 = oracle.quantize(Xm, lam2, group=64)
+    q128, s128 = oracle.quantize(Xm, lam2, group=128)
+    assert np.array_equal(q64, q128)
+    assert np.array_equal(s64[:, 0::2], s128) and np.array_equal(s64[:, 1::2], s128)
+    # and in general the two differ: a group-128 scale covers both halves
+    q64r, s64r = oracle.quantize(X, lam, group=64)
+    _, s128r = oracle.quantize(X, lam, group=128)
+    assert np.array_equal(s128r.view(np.uint16), np.maximum(s64r[:, 0::2], s64r[:, 1::2]))
+
+
 def test_pack_act_hand_example(oracle):
     q = np.array([[1, -1, 7, -8, 0, 3, -3, 0]], dtype=np.int8)
     # byte j: code 2j in the low nibble, 2j+1 in the high nibble
@@ -177,6 +203,23 @@ def test_group_partials_match_numpy_integer_matmul(oracle):
         assert np.array_equal(P[:, :, g], ref)
     W = oracle.group_partials(qa, qw, 3, 7, 10, 20)
     assert np.array_equal(W, P[3:10, 10:30])
+
+
+def test_group128_partials_are_sums_of_group64_partials(oracle):
+    rng = np.random.default_rng(12)
+    M, K, N = 13, 384, 29
+    qa = rng.integers(-8, 8, (M, K), dtype=np.int8)
+    qw = rng.integers(-8, 8, (K, N), dtype=np.int8)
+    P64 = oracle.group_partials(qa, qw, group=64)
+    P128 = oracle.group_partials(qa, qw, group=128)
+    assert P128.shape == (M, N, K // 128)
+    assert np.array_equal(P128, P64[:, :, 0::2] + P64[:, :, 1::2])
+    for g in range(K // 128):
+        ref = qa[:, 128 * g:128 * (g + 1)].astype(np.int64) @ qw[128 * g:128 * (g + 1)].astype(np.int64)
+        assert np.array_equal(P128[:, :, g], ref)
+    # the closed-form extreme doubles with the group width
+    assert np.all(oracle.group_partials(np.full((2, 128), -8, np.int8), np.full((128, 3), -8, np.int8),
+                                        group=128) == 128 * 64)
 
 
 def test_group_partials_closed_form_extremes(oracle):
@@ -199,10 +242,11 @@ def test_lowrank_down_matches_numpy(oracle):
 # ---------------------------------------------------------- linear, fp64
 def _dense_reference(oracle, lay, b=0, rank=True, zero_w=False):
     """Y from dense fp64 products of the dequantized matrices (numpy)."""
-    q, sx, xh = oracle.quantize(lay["X"], lay["lam"], want_xh=True)
-    A = q.astype(np.float64) * np.repeat(_deq_scale(sx), 64, axis=1)
+    group = lay["group"]
+    q, sx, xh = oracle.quantize(lay["X"], lay["lam"], want_xh=True, group=group)
+    A = q.astype(np.float64) * np.repeat(_deq_scale(sx), group, axis=1)
     qw = np.zeros_like(lay["qw"][b]) if zero_w else lay["qw"][b]
-    W = qw.astype(np.float64) * np.repeat(f16_bits_to_f32(lay["sw"][b]).astype(np.float64), 64, axis=0)
+    W = qw.astype(np.float64) * np.repeat(f16_bits_to_f32(lay["sw"][b]).astype(np.float64), group, axis=0)
     Y = A @ W + bf16_bits_to_f32(lay["bias"][b]).astype(np.float64)[None, :]
     if rank and lay["L1"].shape[2]:
         L1 = bf16_bits_to_f32(lay["L1"][b]).astype(np.float64)
@@ -215,25 +259,29 @@ def _rel(a, b):
     return np.linalg.norm(a - b) / max(np.linalg.norm(b), 1e-300)
 
 
-def test_linear_equals_dense_dequantized_form(oracle):
-    lay = make_random_layer(21, 17, 384, 29, r=4, outlier_channels=2)
+@pytest.mark.parametrize("group", [64, 128])
+def test_linear_equals_dense_dequantized_form(oracle, group):
+    lay = make_random_layer(21, 17, 384, 29, r=4, outlier_channels=2, group=group)
     Y = oracle.linear(lay["X"], lay["lam"], lay["qw"][0], lay["sw"][0], lay["L1"][0],
-                      lay["L2"][0], lay["bias"][0])
+                      lay["L2"][0], lay["bias"][0], group=group)
     assert _rel(Y, _dense_reference(oracle, lay)) < 1e-13
 
 
-def test_rank_zero_is_plain_w4a4(oracle):
-    lay = make_random_layer(22, 11, 256, 19, r=0)
-    Y = oracle.linear(lay["X"], lay["lam"], lay["qw"][0], lay["sw"][0], None, None, lay["bias"][0])
+@pytest.mark.parametrize("group", [64, 128])
+def test_rank_zero_is_plain_w4a4(oracle, group):
+    lay = make_random_layer(22, 11, 256, 19, r=0, group=group)
+    Y = oracle.linear(lay["X"], lay["lam"], lay["qw"][0], lay["sw"][0], None, None, lay["bias"][0],
+                      group=group)
     assert _rel(Y, _dense_reference(oracle, lay, rank=False)) < 1e-13
 
 
-def test_zero_residual_is_pure_low_rank(oracle):
-    lay = make_random_layer(23, 12, 192, 21, r=4)
+@pytest.mark.parametrize("group", [64, 128])
+def test_zero_residual_is_pure_low_rank(oracle, group):
+    lay = make_random_layer(23, 12, 256, 21, r=4, group=group)
     zw = np.zeros_like(lay["qw"][0])
     Y = oracle.linear(lay["X"], lay["lam"], zw, lay["sw"][0], lay["L1"][0], lay["L2"][0],
-                      lay["bias"][0])
-    q, sx, xh = oracle.quantize(lay["X"], lay["lam"], want_xh=True)
+                      lay["bias"][0], group=group)
+    q, sx, xh = oracle.quantize(lay["X"], lay["lam"], want_xh=True, group=group)
     L1 = bf16_bits_to_f32(lay["L1"][0]).astype(np.float64)
     L2 = bf16_bits_to_f32(lay["L2"][0]).astype(np.float64)
     ref = xh.astype(np.float64) @ L1 @ L2 + bf16_bits_to_f32(lay["bias"][0]).astype(np.float64)
