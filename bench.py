@@ -44,22 +44,28 @@ def source_hash(path: str) -> str:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def algorithmic_bytes(M, K, N, r, batch, y_bytes):
+def algorithmic_bytes(M, K, N, r, batch, y_bytes, group=64):
     """Minimum bytes the whole layer must move (inputs once, output once)."""
-    G = K // 64
+    G = K // group
     x = M * K * 2 + K * 2 + batch * (K * r * 2)
     w = batch * (K * N // 2 + G * N * 2 + r * N * 2 + N * 2)
     y = batch * M * N * y_bytes
     return x + w + y
 
 
-def contract_bytes(M, K, N, r, batch, y_bytes):
+def contract_bytes(M, K, N, r, batch, y_bytes, group=64):
     """Minimum bytes of the contraction stage: int4 activation codes and
     their fp16 scales, U, the packed weights with their scales, L2, bias, Y."""
-    G = K // 64
+    G = K // group
     a = M * K // 2 + M * G * 2 + batch * M * r * 4
     w = batch * (K * N // 2 + G * N * 2 + r * N * 2 + N * 2)
     return a + w + batch * M * N * y_bytes
+
+
+def traffic_key(layer: str, tokens, M: int, group: int) -> str:
+    """Entry name of a layer in the traffic file."""
+    key = layer if tokens is None else f"{layer}_M{M}"
+    return key if group == 64 else f"{key}_g{group}"
 
 
 def read_traffic(kernel: str, layer: str):
@@ -185,7 +191,7 @@ def summarize_profiles(args):
             nb = int(args.copy_mb * 1e6) // 16 * 16
             f_fac = (nb / 1024) / copy["FETCH_SIZE"]      # true KiB read per counted KiB
             w_fac = (nb / 1024) / copy["WRITE_SIZE"]
-            layer = args.layer if args.tokens is None else f"{args.layer}_M{args.tokens}"
+            layer = traffic_key(args.layer, args.tokens, args.tokens, args.group)
             print(f"copy calibration: {args.copy_mb} MB; FETCH_SIZE factor {f_fac:.4f}, "
                   f"WRITE_SIZE factor {w_fac:.4f}")
             if args.write_traffic:
@@ -221,6 +227,8 @@ def main(argv=None):
     ap.add_argument("--layer", default="pixart_up",
                     help="tiny | pixart_up | sana_qkv | flux_up | flux_down | qwen3_up | qwen3_down")
     ap.add_argument("--tokens", type=int, default=None, help="M for the qwen3 layers (16/256/2048)")
+    ap.add_argument("--group", type=int, default=64, choices=[64, 128],
+                    help="quantization group width (the pages' Qwen3-8B runs use 128)")
     ap.add_argument("--kernel", default="auto", choices=["auto", "tiled", "skinny"])
     ap.add_argument("--y-dtype", default="bf16", choices=["bf16", "f32"])
     ap.add_argument("--rotate-mb", type=float, default=640.0,
@@ -252,8 +260,8 @@ def main(argv=None):
     from synth import layer_spec, make_layer
 
     dev = torch.device("cuda:0")
-    spec = layer_spec(args.layer, args.tokens)
-    lay = make_layer(args.layer, args.tokens)
+    spec = layer_spec(args.layer, args.tokens, args.group)
+    lay = make_layer(args.layer, args.tokens, args.group)
     M, K, N, r, B = spec.M, spec.K, spec.N, spec.r, spec.batch
 
     def d16(a):
@@ -275,18 +283,18 @@ def main(argv=None):
     for i in range(nsets):
         sets.append(dict(X=X0.clone(), packed=packed0.clone(), sw=sw0.clone(),
                          Y=torch.empty((B, M, N), dtype=ydt, device=dev)))
-    ws = torch.empty(hsq.workspace_bytes(M, K, N, r, B), dtype=torch.uint8, device=dev)
+    ws = torch.empty(hsq.workspace_bytes(M, K, N, r, B, args.group), dtype=torch.uint8, device=dev)
     kernel = args.kernel
     if kernel == "auto":
         kernel = "skinny" if M <= 64 else "tiled"
 
     def quant(i):
-        hsq.quantize_stage(sets[i % nsets]["X"], lam, L1, N=N, batch=B, workspace=ws)
+        hsq.quantize_stage(sets[i % nsets]["X"], lam, L1, N=N, batch=B, workspace=ws, group=args.group)
 
     def contract(i):
         s = sets[i % nsets]
         hsq.contract_stage(M, K, s["packed"], s["sw"], L2, bias, s["Y"], N=N, batch=B, r=r,
-                           workspace=ws, kernel=kernel)
+                           workspace=ws, kernel=kernel, group=args.group)
 
     def step(i):
         quant(i)
@@ -367,10 +375,10 @@ def main(argv=None):
 
     # roofline of the dominant kernel (the contraction): compute-bound at
     # large M (int8 MFMA), HBM-bound when the weights dominate (small M)
-    cbytes = contract_bytes(M, K, N, r, B, y_bytes)
+    cbytes = contract_bytes(M, K, N, r, B, y_bytes, args.group)
     intensity = ops / cbytes
     ridge = PEAK_INT8_TOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
-    traffic = read_traffic(kernel, args.layer if args.tokens is None else f"{args.layer}_M{M}")
+    traffic = read_traffic(kernel, traffic_key(args.layer, args.tokens, M, args.group))
     if intensity >= ridge:
         ach = ops / (c_avg * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": round(ach, 2), "peak": PEAK_INT8_TOPS,
@@ -398,7 +406,7 @@ def main(argv=None):
         "data": "synthetic",
         "config": {
             "workload": f"{spec.name}: {spec.description}",
-            "M": M, "K": K, "N": N, "rank": r, "batch": B, "group": 64,
+            "M": M, "K": K, "N": N, "rank": r, "batch": B, "group": args.group,
             "y_dtype": args.y_dtype, "contract_kernel": kernel,
             "rotated_sets": nsets,
         },
@@ -406,7 +414,7 @@ def main(argv=None):
                       "timing": "HIP graph replay, events on the capture stream"},
         "step_us": spread,
         "device": device_info(torch),
-        "layer_hbm_frac": round(algorithmic_bytes(M, K, N, r, B, y_bytes) / (ms_step * 1e-3)
+        "layer_hbm_frac": round(algorithmic_bytes(M, K, N, r, B, y_bytes, args.group) / (ms_step * 1e-3)
                                 / (PEAK_HBM_GBS * 1e9), 4),
         "wall_s": round(wall, 4),
         "roofline": roof,

@@ -20,8 +20,11 @@
  *   P[m,n,g] = sum_{k in g} qx[m,k] * qw[k,n]                  int32, exact
  *   Y[m,n]   = sum_g P[m,n,g] * sx[m,g] * sw[g,n] + sum_j U[m,j] * L2[j,n] + bias[n]
  *
- * Group g covers input channels [64g, 64g + 64).  Rounding is IEEE-754
- * round-to-nearest-even throughout; rint rounds ties to even.
+ * Group g covers input channels [64g, 64g + 64).  The entry points whose
+ * names end in _g take the group width as an argument, 64 or 128 (group g
+ * then covers [group*g, group*g + group)); the Qwen3-8B experiments of the
+ * same page use group-128 (Table 3, 4, 6 and 7 captions).  Rounding is
+ * IEEE-754 round-to-nearest-even throughout; rint rounds ties to even.
  *
  * Conventions for every entry point
  *   - All tensor pointers are DEVICE pointers (HIP global memory), owned and
@@ -63,6 +66,9 @@ extern "C" {
 /* ---- kernel choice for the residual contraction ---- */
 #define HSQ_KERNEL_AUTO    0  /* SKINNY for M <= 64, TILED otherwise */
 #define HSQ_KERNEL_TILED   1  /* LDS-tiled int8-MFMA kernel, one workgroup per output tile */
+#define HSQ_GROUP_64     64
+#define HSQ_GROUP_128   128
+
 #define HSQ_KERNEL_SKINNY  2  /* weight-streaming kernel for M <= 64: the waves of a
                                  workgroup split K and reduce in a fixed order */
 
@@ -185,6 +191,32 @@ int hsq_w4a4_group_partials(const uint16_t *X, int M, int K, int N, const uint16
                             const uint8_t *packed_w, int m0, int mc, int n0, int nc,
                             int32_t *P, void *workspace, size_t ws_bytes, int kernel,
                             void *stream);
+
+/* ---- the same layer with the group width as an argument ----
+ * group is HSQ_GROUP_64 or HSQ_GROUP_128 (anything else: HSQ_E_INVAL) and
+ * must divide K (HSQ_E_SHAPE otherwise).  Every scale array then has K/group
+ * groups: sw is batch x K/group x N fp16, P is mc x nc x K/group int32.
+ * The packed weights are the same for both widths (hsq_pack_weights).  With
+ * group = 64 each function equals its counterpart above.  A group-128
+ * scale covers two 64-channel blocks: the contraction accumulates their two
+ * int32 block sums before the one rescale by sx * sw. */
+size_t hsq_workspace_bytes_g(int M, int K, int N, int r, int batch, int group);
+int hsq_w4a4_lowrank_linear_g(const uint16_t *X, int M, int K, int N, int batch, int group,
+                              const uint16_t *lambda, const uint8_t *packed_w,
+                              const uint16_t *sw, const uint16_t *L1, const uint16_t *L2,
+                              int r, const uint16_t *bias, void *Y, int y_dtype,
+                              void *workspace, size_t ws_bytes, int kernel, void *stream);
+int hsq_w4a4_quantize_stage_g(const uint16_t *X, int M, int K, int N, int batch, int group,
+                              const uint16_t *lambda, const uint16_t *L1, int r, void *workspace,
+                              size_t ws_bytes, void *stream);
+int hsq_w4a4_contract_stage_g(int M, int K, int N, int batch, int group, const uint8_t *packed_w,
+                              const uint16_t *sw, const uint16_t *L2, int r, const uint16_t *bias,
+                              void *Y, int y_dtype, void *workspace, size_t ws_bytes, int kernel,
+                              void *stream);
+int hsq_w4a4_group_partials_g(const uint16_t *X, int M, int K, int N, int group,
+                              const uint16_t *lambda, const uint8_t *packed_w, int m0, int mc,
+                              int n0, int nc, int32_t *P, void *workspace, size_t ws_bytes,
+                              int kernel, void *stream);
 
 #ifdef __cplusplus
 }

@@ -173,3 +173,25 @@ def test_one_hip_runtime_in_the_process():
     maps = open("/proc/self/maps").read()
     hip = {line.split()[-1] for line in maps.splitlines() if "libamdhip64" in line}
     assert len(hip) == 1, hip
+
+
+def test_group_width_entry_points_validate():
+    ws = lib.hsq_workspace_bytes_g
+    assert ws(64, 256, 256, 4, 1, 64) == lib.hsq_workspace_bytes(64, 256, 256, 4, 1)
+    assert ws(64, 256, 256, 4, 1, 128) > 0
+    assert ws(64, 256, 256, 4, 1, 96) == 0          # not a supported width
+    assert ws(64, 320, 256, 4, 1, 128) == 0         # 128 does not divide K
+    # group-128 scales take half the bytes of group-64 ones
+    assert ws(4096, 4096, 12288, 4, 1, 128) < ws(4096, 4096, 12288, 4, 1, 64)
+    f = lib.hsq_w4a4_lowrank_linear_g
+    args = (A, A, A, A, A, 4, A, A, hsq.BF16, A, 1 << 30, 0, None)
+    assert f(A, 64, 256, 256, 1, 96, *args) == hsq.E_INVAL
+    assert f(A, 64, 320, 256, 1, 128, *args) == hsq.E_SHAPE
+    assert f(None, 64, 256, 256, 1, 128, *args) == hsq.E_INVAL
+    assert f(A, 64, 256, 256, 1, 128, A, A, A, A, A, 4, A, A, hsq.BF16, A, 0, 0, None) == hsq.E_WORKSPACE
+    q = lib.hsq_w4a4_quantize_stage_g
+    assert q(A, 64, 320, 256, 1, 128, A, A, 4, A, 1 << 30, None) == hsq.E_SHAPE
+    c = lib.hsq_w4a4_contract_stage_g
+    assert c(64, 256, 256, 1, 32, A, A, A, 4, A, A, hsq.BF16, A, 1 << 30, 0, None) == hsq.E_INVAL
+    pg = lib.hsq_w4a4_group_partials_g
+    assert pg(A, 64, 256, 256, 128, A, A, 0, 65, 0, 256, A, A, 1 << 30, 0, None) == hsq.E_SHAPE

@@ -54,6 +54,7 @@ class Uploaded:
 
     def __init__(self, lay):
         self.lay = lay
+        self.group = int(lay.get("group", 64))
         self.B, self.K, self.N = lay["qw"].shape
         self.M = lay["X"].shape[0]
         self.r = lay["L1"].shape[2]
@@ -73,21 +74,22 @@ class Uploaded:
     def linear(self, y_dtype="f32", kernel="auto", bias=True):
         Y = hsq.w4a4_lowrank_linear(self.X, self.lam, self.packed, self.sw, self.L1, self.L2,
                                     self.bias if bias else None, N=self.N, batch=self.B,
-                                    y_dtype=y_dtype, kernel=kernel)
+                                    y_dtype=y_dtype, kernel=kernel, group=self.group)
         torch.cuda.synchronize()
         return Y
 
     def partials(self, m0, mc, n0, nc, kernel="auto"):
         blob = self.packed[: hsq.packed_weight_bytes(self.K, self.N)]
-        P = hsq.w4a4_group_partials(self.X, self.lam, blob, self.N, m0, mc, n0, nc, kernel=kernel)
+        P = hsq.w4a4_group_partials(self.X, self.lam, blob, self.N, m0, mc, n0, nc, kernel=kernel,
+                                    group=self.group)
         torch.cuda.synchronize()
         return P.cpu().numpy()
 
 
 @functools.lru_cache(maxsize=2)
-def uploaded(name, M=None):
-    say(f"[gen] {name} M={M}")
-    return Uploaded(make_layer(name, M))
+def uploaded(name, M=None, group=None):
+    say(f"[gen] {name} M={M} group={group or 64}")
+    return Uploaded(make_layer(name, M, group))
 
 
 def check_linear_rows(oracle, up, rows, kernel="auto"):
@@ -98,7 +100,7 @@ def check_linear_rows(oracle, up, rows, kernel="auto"):
         r = up.r
         ref = oracle.linear(lay["X"], lay["lam"], lay["qw"][b], lay["sw"][b],
                             lay["L1"][b] if r else None, lay["L2"][b] if r else None,
-                            lay["bias"][b], rows=rows)
+                            lay["bias"][b], rows=rows, group=up.group)
         e32 = rel(Yd[b][rows].astype(np.float64), ref)
         ref_b = bf16_bits_to_f32(f64_to_bf16_bits(ref)).astype(np.float64)
         e16 = rel(Yb[b][rows].astype(np.float64), ref_b)
@@ -301,3 +303,97 @@ def test_graph_replay_matches_eager(M):
         assert np.array_equal(out.view(torch.int32).cpu().numpy(), eager), f"replay {rep}"
         again = up.linear("f32").view(torch.int32).cpu().numpy()   # eager work in between
         assert np.array_equal(again, eager)
+
+
+# ------------------------------------------------------------- group 128
+# The Qwen3-8B runs of the pages use group-128 (Deflating the Hessian,
+# Table 3 caption); a group-128 scale covers two 64-channel MFMA blocks.
+def _workspace_codes_scales(up, ws):
+    """Decode the codes and scales the quantize stage wrote into the layer's
+    workspace (layout: MT x Gp blocks of 1 KiB, lane slot l = row l%16 and
+    channels 16*(l/16) .. +15 of the block; then MT x SG x 16 fp16 scales)."""
+    MT, Gp = -(-up.M // 16), -(-up.K // 64 // 2) * 2
+    SG = up.K // up.group if up.group == 128 else Gp
+    raw = ws.cpu().numpy()
+    qa = raw[: MT * Gp * 1024].view(np.int8).reshape(MT, Gp, 4, 16, 16)   # mt, g, kq, row, p
+    codes = qa.transpose(0, 3, 1, 2, 4).reshape(MT * 16, Gp * 64)[: up.M, : up.K]
+    off = -(-(MT * Gp * 1024) // 256) * 256
+    sx = raw[off: off + MT * SG * 16 * 2].view(np.uint16).reshape(MT, SG, 16)
+    scales = sx.transpose(0, 2, 1).reshape(MT * 16, SG)[: up.M, : up.K // up.group]
+    return codes, scales
+
+
+@pytest.mark.parametrize("name,M", [("qwen3_up", 16), ("qwen3_down", 256), ("qwen3_up", 2048)])
+def test_group128_codes_scales_bit_exact(oracle, name, M):
+    up = uploaded(name, M, 128)
+    say(f"[codes g128] {name} M={up.M} K={up.K}")
+    ws = torch.empty(hsq.workspace_bytes(up.M, up.K, up.N, up.r, up.B, 128), dtype=torch.uint8, device=DEV)
+    hsq.quantize_stage(up.X, up.lam, up.L1, N=up.N, batch=up.B, workspace=ws, group=128)
+    torch.cuda.synchronize()
+    codes, scales = _workspace_codes_scales(up, ws)
+    q_ref, s_ref = oracle.quantize(up.lay["X"], up.lay["lam"], group=128)
+    assert np.array_equal(scales, s_ref)
+    assert np.array_equal(codes, q_ref)
+
+
+@pytest.mark.parametrize("name,M,windows", [
+    ("qwen3_up", 16, [(0, 16, 0, 12288)]),
+    ("qwen3_down", 16, [(0, 16, 0, 4096)]),
+    ("qwen3_down", 256, [(0, 37, 3900, 196)]),
+    ("qwen3_up", 2048, [(2000, 48, 4000, 96)]),
+])
+def test_group128_partials_windows_bit_exact(oracle, name, M, windows):
+    up = uploaded(name, M, 128)
+    q, _ = oracle.quantize(up.lay["X"], up.lay["lam"], group=128)
+    for (m0, mc, n0, nc) in windows:
+        say(f"[partials g128] {name} M={up.M} window m[{m0},{m0 + mc}) n[{n0},{n0 + nc})")
+        got = up.partials(m0, mc, n0, nc)
+        ref = oracle.group_partials(q, up.lay["qw"][0], m0, mc, n0, nc, group=128)
+        assert np.array_equal(got, ref)
+
+
+@pytest.mark.parametrize("name,M", [("qwen3_up", 16), ("qwen3_down", 16), ("qwen3_up", 256),
+                                    ("qwen3_down", 256), ("qwen3_up", 2048), ("qwen3_down", 2048)])
+def test_group128_full_size_outputs_sampled_rows(oracle, name, M):
+    up = uploaded(name, M, 128)
+    say(f"[linear g128] {name} M={up.M} K={up.K} N={up.N}")
+    check_linear_rows(oracle, up, _sample_rows(up.M, 24 if up.K > 4096 else 48))
+
+
+@pytest.mark.parametrize("M,K,N,r,batch", [
+    (5, 256, 33, 0, 1),       # rank 0, ragged N, one row tile
+    (48, 512, 64, 32, 2),     # largest rank, three row tiles, two projections
+    (70, 640, 300, 4, 1),     # five groups: the tiled kernel's pad stage
+    (130, 4096, 130, 4, 1),   # K splits, ragged M and N
+    (100, 2304, 200, 4, 3),   # K splits, three projections
+])
+def test_group128_ragged_shapes_match_oracle(oracle, M, K, N, r, batch):
+    lay = make_random_layer(M * 37 + N, M, K, N, r=r, batch=batch, outlier_channels=2, group=128)
+    up = Uploaded(lay)
+    kernels = ("tiled", "skinny") if M <= 64 else ("tiled",)
+    q, _ = oracle.quantize(lay["X"], lay["lam"], group=128)
+    for kernel in kernels:
+        say(f"[edge g128] M={M} K={K} N={N} r={r} batch={batch} {kernel}")
+        check_linear_rows(oracle, up, np.arange(M), kernel)
+        got = up.partials(0, M, 0, N, kernel)
+        assert np.array_equal(got, oracle.group_partials(q, lay["qw"][0], group=128))
+
+
+def test_group_entry_at_64_equals_plain_entry():
+    # hsq_w4a4_lowrank_linear_g with group 64 runs exactly what the plain
+    # (group-64) entry point runs
+    up = uploaded("qwen3_up", 256)
+    lib = hsq._load()
+    outs = []
+    for fn in ("g", "ex"):
+        out = torch.empty((up.B, up.M, up.N), dtype=torch.float32, device=DEV)
+        ws = torch.empty(hsq.workspace_bytes(up.M, up.K, up.N, up.r, up.B), dtype=torch.uint8, device=DEV)
+        P = hsq._ptr
+        args = (P(up.lam), P(up.packed), P(up.sw), P(up.L1), P(up.L2), up.r, P(up.bias), P(out),
+                hsq.F32, P(ws), ws.numel(), 0, hsq._stream())
+        st = (lib.hsq_w4a4_lowrank_linear_g(P(up.X), up.M, up.K, up.N, up.B, 64, *args) if fn == "g"
+              else lib.hsq_w4a4_lowrank_linear_ex(P(up.X), up.M, up.K, up.N, up.B, *args))
+        assert st == 0
+        torch.cuda.synchronize()
+        outs.append(out.view(torch.int32).cpu().numpy())
+    assert np.array_equal(outs[0], outs[1])

@@ -65,6 +65,11 @@ def _load():
             "hsq_w4a4_group_partials": ([P, I, I, I, P, P, I, I, I, I, P, P, S, I, P], I),
             "hsq_w4a4_quantize_stage": ([P, I, I, I, I, P, P, I, P, S, P], I),
             "hsq_w4a4_contract_stage": ([I, I, I, I, P, P, P, I, P, P, I, P, S, I, P], I),
+            "hsq_workspace_bytes_g": ([I, I, I, I, I, I], S),
+            "hsq_w4a4_lowrank_linear_g": ([P, I, I, I, I, I, P, P, P, P, P, I, P, P, I, P, S, I, P], I),
+            "hsq_w4a4_quantize_stage_g": ([P, I, I, I, I, I, P, P, I, P, S, P], I),
+            "hsq_w4a4_contract_stage_g": ([I, I, I, I, I, P, P, P, I, P, P, I, P, S, I, P], I),
+            "hsq_w4a4_group_partials_g": ([P, I, I, I, I, P, P, I, I, I, I, P, P, S, I, P], I),
         }
         for name, (args, res) in sig.items():
             fn = getattr(lib, name)
@@ -131,8 +136,11 @@ def packed_weight_bytes(K: int, N: int) -> int:
     return int(_load().hsq_packed_weight_bytes(K, N))
 
 
-def workspace_bytes(M: int, K: int, N: int, r: int, batch: int = 1) -> int:
-    return int(_load().hsq_workspace_bytes(M, K, N, r, batch))
+def workspace_bytes(M: int, K: int, N: int, r: int, batch: int = 1, group: int = 64) -> int:
+    lib = _load()
+    if group == 64:
+        return int(lib.hsq_workspace_bytes(M, K, N, r, batch))
+    return int(lib.hsq_workspace_bytes_g(M, K, N, r, batch, group))
 
 
 def pack_weights(codes, packed=None, status=None):
@@ -183,15 +191,16 @@ def quantize_act(X, lam, L1=None):
 
 def w4a4_lowrank_linear(X, lam, packed_w, sw, L1=None, L2=None, bias=None, *, N: int,
                         batch: int = 1, y_dtype: str = "bf16", out=None, workspace=None,
-                        kernel: str = "auto"):
+                        kernel: str = "auto", group: int = 64):
     """The fused layer.  Shapes: X (M, K); lam (K,); packed_w (batch * blob,);
-    sw (batch, K/64, N); L1 (batch, K, r); L2 (batch, r, N); bias (batch, N).
-    Returns Y (batch, M, N) as bf16 or fp32."""
+    sw (batch, K/group, N); L1 (batch, K, r); L2 (batch, r, N); bias (batch, N).
+    Returns Y (batch, M, N) as bf16 or fp32.  group 64 calls
+    hsq_w4a4_lowrank_linear_ex, other widths hsq_w4a4_lowrank_linear_g."""
     torch = _torch()
     lib = _load()
     _dev_tensor(X, "X", _half_types())
     M, K = X.shape
-    G = K // 64
+    G = K // group
     _dev_tensor(lam, "lambda", _half_types(), (K,))
     _dev_tensor(packed_w, "packed_w", (torch.uint8,), (batch * lib.hsq_packed_weight_bytes(K, N),))
     _dev_tensor(sw, "sw", _half_types(), (batch, G, N))
@@ -205,58 +214,65 @@ def w4a4_lowrank_linear(X, lam, packed_w, sw, L1=None, L2=None, bias=None, *, N:
     if out is None:
         out = torch.empty((batch, M, N), dtype=ydt[1], device=X.device)
     _dev_tensor(out, "out", (ydt[1],), (batch, M, N))
-    need = lib.hsq_workspace_bytes(M, K, N, r, batch)
+    need = workspace_bytes(M, K, N, r, batch, group)
     if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=X.device)
     _dev_tensor(workspace, "workspace", (torch.uint8,))
-    _check(lib.hsq_w4a4_lowrank_linear_ex(
-        _ptr(X), M, K, N, batch, _ptr(lam), _ptr(packed_w), _ptr(sw),
-        _ptr(L1) if r else None, _ptr(L2) if r else None, r, _ptr(bias), _ptr(out), ydt[0],
-        _ptr(workspace), workspace.numel(), _KERNELS[kernel], _stream()),
-        "hsq_w4a4_lowrank_linear")
+    args = (_ptr(lam), _ptr(packed_w), _ptr(sw), _ptr(L1) if r else None, _ptr(L2) if r else None,
+            r, _ptr(bias), _ptr(out), ydt[0], _ptr(workspace), workspace.numel(), _KERNELS[kernel],
+            _stream())
+    if group == 64:
+        _check(lib.hsq_w4a4_lowrank_linear_ex(_ptr(X), M, K, N, batch, *args), "hsq_w4a4_lowrank_linear")
+    else:
+        _check(lib.hsq_w4a4_lowrank_linear_g(_ptr(X), M, K, N, batch, group, *args),
+               "hsq_w4a4_lowrank_linear_g")
     return out
 
 
-def quantize_stage(X, lam, L1, *, N: int, batch: int, workspace):
+def quantize_stage(X, lam, L1, *, N: int, batch: int, workspace, group: int = 64):
     """First stage of the layer: quantize X and form U into ``workspace``."""
     lib = _load()
     M, K = X.shape
     r = 0 if L1 is None else int(L1.shape[-1])
-    _check(lib.hsq_w4a4_quantize_stage(_ptr(X), M, K, N, batch, _ptr(lam), _ptr(L1) if r else None,
-                                       r, _ptr(workspace), workspace.numel(), _stream()),
-           "hsq_w4a4_quantize_stage")
+    _check(lib.hsq_w4a4_quantize_stage_g(_ptr(X), M, K, N, batch, group, _ptr(lam),
+                                         _ptr(L1) if r else None, r, _ptr(workspace),
+                                         workspace.numel(), _stream()),
+           "hsq_w4a4_quantize_stage_g")
 
 
 def contract_stage(M: int, K: int, packed_w, sw, L2, bias, out, *, N: int, batch: int, r: int,
-                   workspace, kernel: str = "auto"):
+                   workspace, kernel: str = "auto", group: int = 64):
     """Second stage: contraction + epilogue from the workspace into ``out``."""
     torch = _torch()
     lib = _load()
     ydt = BF16 if out.dtype == torch.bfloat16 else F32
-    _check(lib.hsq_w4a4_contract_stage(M, K, N, batch, _ptr(packed_w), _ptr(sw),
-                                       _ptr(L2) if r else None, r, _ptr(bias), _ptr(out), ydt,
-                                       _ptr(workspace), workspace.numel(), _KERNELS[kernel],
-                                       _stream()),
-           "hsq_w4a4_contract_stage")
+    _check(lib.hsq_w4a4_contract_stage_g(M, K, N, batch, group, _ptr(packed_w), _ptr(sw),
+                                         _ptr(L2) if r else None, r, _ptr(bias), _ptr(out), ydt,
+                                         _ptr(workspace), workspace.numel(), _KERNELS[kernel],
+                                         _stream()),
+           "hsq_w4a4_contract_stage_g")
 
 
 def w4a4_group_partials(X, lam, packed_w, N: int, m0: int, mc: int, n0: int, nc: int,
-                        workspace=None, kernel: str = "auto"):
-    """int32 P (mc, nc, K/64) of the window, from the production kernels."""
+                        workspace=None, kernel: str = "auto", group: int = 64):
+    """int32 P (mc, nc, K/group) of the window, from the production kernels."""
     torch = _torch()
     lib = _load()
     _dev_tensor(X, "X", _half_types())
     M, K = X.shape
     _dev_tensor(lam, "lambda", _half_types(), (K,))
     _dev_tensor(packed_w, "packed_w", (torch.uint8,))
-    P = torch.empty((mc, nc, K // 64), dtype=torch.int32, device=X.device)
-    need = lib.hsq_workspace_bytes(M, K, N, 0, 1)
+    P = torch.empty((mc, nc, K // group), dtype=torch.int32, device=X.device)
+    need = workspace_bytes(M, K, N, 0, 1, group)
     if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=X.device)
-    _check(lib.hsq_w4a4_group_partials(_ptr(X), M, K, N, _ptr(lam), _ptr(packed_w), m0, mc, n0,
-                                       nc, _ptr(P), _ptr(workspace), workspace.numel(),
-                                       _KERNELS[kernel], _stream()),
-           "hsq_w4a4_group_partials")
+    args = (_ptr(lam), _ptr(packed_w), m0, mc, n0, nc, _ptr(P), _ptr(workspace), workspace.numel(),
+            _KERNELS[kernel], _stream())
+    if group == 64:
+        _check(lib.hsq_w4a4_group_partials(_ptr(X), M, K, N, *args), "hsq_w4a4_group_partials")
+    else:
+        _check(lib.hsq_w4a4_group_partials_g(_ptr(X), M, K, N, group, *args),
+               "hsq_w4a4_group_partials_g")
     return P
 
 
@@ -265,9 +281,11 @@ class Layer:
     residual blobs, the scales, the low-rank factors, the bias and a reusable
     workspace, and runs the fused call on the current stream."""
 
-    def __init__(self, lam, qw, sw, L1=None, L2=None, bias=None, max_tokens: int = 0):
+    def __init__(self, lam, qw, sw, L1=None, L2=None, bias=None, max_tokens: int = 0,
+                 group: int = 64):
         torch = _torch()
         self.batch, self.K, self.N = qw.shape
+        self.group = group
         self.r = 0 if L1 is None else int(L1.shape[-1])
         blobs = [pack_weights(qw[b].contiguous())[0] for b in range(self.batch)]
         self.packed = torch.cat(blobs) if self.batch > 1 else blobs[0]
@@ -275,14 +293,14 @@ class Layer:
         self.workspace = None
         if max_tokens:
             self.workspace = torch.empty(
-                workspace_bytes(max_tokens, self.K, self.N, self.r, self.batch),
+                workspace_bytes(max_tokens, self.K, self.N, self.r, self.batch, group),
                 dtype=torch.uint8, device=qw.device)
 
     def __call__(self, X, y_dtype: str = "bf16", out=None, kernel: str = "auto"):
         ws = self.workspace
-        need = workspace_bytes(X.shape[0], self.K, self.N, self.r, self.batch)
+        need = workspace_bytes(X.shape[0], self.K, self.N, self.r, self.batch, self.group)
         if ws is None or ws.numel() < need:
             ws = None
         return w4a4_lowrank_linear(X, self.lam, self.packed, self.sw, self.L1, self.L2, self.bias,
                                    N=self.N, batch=self.batch, y_dtype=y_dtype, out=out,
-                                   workspace=ws, kernel=kernel)
+                                   workspace=ws, kernel=kernel, group=self.group)

@@ -9,24 +9,27 @@
 
 namespace hsq {
 
-WsLayout plan_workspace(int M, int K, int N, int r, int batch) {
+WsLayout plan_workspace(int M, int K, int N, int r, int batch, int group) {
   WsLayout L;
   L.MT = ceil_div(M, kTile);
-  L.G = K / kGroup;
+  L.group = group;
+  L.bpg = group / kGroup;
+  L.G = K / group;
   L.Gp = padded_groups(K);
+  L.SG = scale_groups_stored(K, group);
   L.Mpad = L.MT * kTile;
   // Quantization pass: K is split into slices whose U partials are summed
   // by the contraction kernels.
-  L.u_slices = quant_slices(M, K, r, batch);
+  L.u_slices = quant_slices(M, K, r, batch, group);
   size_t off = 0;
   L.qa_off = off;
   off = align_up(off + (size_t)L.MT * L.Gp * 1024, 256);
   L.sxs_off = off;
-  off = align_up(off + (size_t)L.MT * L.Gp * 16 * sizeof(uint16_t), 256);
+  off = align_up(off + (size_t)L.MT * L.SG * 16 * sizeof(uint16_t), 256);
   L.uw_off = off;
   off = align_up(off + (size_t)L.u_slices * batch * r * L.Mpad * sizeof(float), 256);
   L.part_off = off;
-  off = align_up(off + tiled_partial_bytes(M, N, K, batch), 256);
+  off = align_up(off + tiled_partial_bytes(M, N, K, batch, group), 256);
   L.total = off;
   return L;
 }
@@ -57,20 +60,24 @@ int hip_status(hipError_t e) {
   return HSQ_E_HIP;
 }
 
-size_t workspace_bytes(int M, int K, int N, int r, int batch) {
-  if (check_sizes(M, K, N, r, batch) != HSQ_OK) return 0;
-  return plan_workspace(M, K, N, r, batch).total;
+bool group_ok(int group) { return group == 64 || group == 128; }
+
+size_t workspace_bytes(int M, int K, int N, int r, int batch, int group) {
+  if (check_sizes(M, K, N, r, batch) != HSQ_OK || !group_ok(group) || K % group != 0) return 0;
+  return plan_workspace(M, K, N, r, batch, group).total;
 }
 
 // Argument checks shared by every form of the linear.  `quant` / `contract`
 // select which stage's pointers must be present.
-int validate(const uint16_t *X, int M, int K, int N, int batch, const uint16_t *lambda,
-             const uint8_t *packed_w, const uint16_t *sw, const uint16_t *L1, const uint16_t *L2,
-             int r, const uint16_t *bias, const void *Y, int y_dtype, const void *workspace,
-             size_t ws_bytes, int *kernel, bool quant, bool contract, const int32_t *P, int m0,
-             int mc, int n0, int nc) {
+int validate(const uint16_t *X, int M, int K, int N, int batch, int group,
+             const uint16_t *lambda, const uint8_t *packed_w, const uint16_t *sw,
+             const uint16_t *L1, const uint16_t *L2, int r, const uint16_t *bias, const void *Y,
+             int y_dtype, const void *workspace, size_t ws_bytes, int *kernel, bool quant,
+             bool contract, const int32_t *P, int m0, int mc, int n0, int nc) {
   int st = check_sizes(M, K, N, r, batch);
   if (st != HSQ_OK) return st;
+  if (!group_ok(group)) return HSQ_E_INVAL;
+  if (K % group != 0) return HSQ_E_SHAPE;
   const bool dump = P != nullptr;
   if (!workspace) return HSQ_E_INVAL;
   if (quant && (!X || !lambda || (r > 0 && !L1))) return HSQ_E_INVAL;
@@ -86,19 +93,20 @@ int validate(const uint16_t *X, int M, int K, int N, int batch, const uint16_t *
     if (p && !aligned16(p)) return HSQ_E_ALIGN;
   if (*kernel == HSQ_KERNEL_AUTO) *kernel = M <= kSkinnyMaxM ? HSQ_KERNEL_SKINNY : HSQ_KERNEL_TILED;
   if (*kernel == HSQ_KERNEL_SKINNY && M > kSkinnyMaxM) return HSQ_E_INVAL;
-  if (ws_bytes < plan_workspace(M, K, N, r, batch).total) return HSQ_E_WORKSPACE;
+  if (ws_bytes < plan_workspace(M, K, N, r, batch, group).total) return HSQ_E_WORKSPACE;
   return HSQ_OK;
 }
 
-int quant_stage(const uint16_t *X, int M, int K, int N, int batch, const uint16_t *lambda,
-                const uint16_t *L1, int r, void *workspace, hipStream_t s) {
-  const WsLayout L = plan_workspace(M, K, N, r, batch);
+int quant_stage(const uint16_t *X, int M, int K, int N, int batch, int group,
+                const uint16_t *lambda, const uint16_t *L1, int r, void *workspace, hipStream_t s) {
+  const WsLayout L = plan_workspace(M, K, N, r, batch, group);
   char *ws = (char *)workspace;
   QuantArgs q{};
   q.X = X;
   q.lam = lambda;
   q.L1 = r > 0 ? L1 : nullptr;
-  q.M = M; q.K = K; q.G = L.G;
+  q.M = M; q.K = K; q.G = K / kGroup;
+  q.bpg = L.bpg; q.SG = L.SG;
   q.r = r; q.batch = batch;
   q.kend = L.Gp * kGroup;
   q.qa = (int8_t *)(ws + L.qa_off);
@@ -108,11 +116,11 @@ int quant_stage(const uint16_t *X, int M, int K, int N, int batch, const uint16_
   return hip_status(launch_quant_tiles(q, s));
 }
 
-int contract_stage(int M, int K, int N, int batch, const uint8_t *packed_w, const uint16_t *sw,
-                   const uint16_t *L2, int r, const uint16_t *bias, void *Y, int y_dtype,
-                   void *workspace, int kernel, hipStream_t s, int32_t *P, int m0, int mc,
-                   int n0, int nc) {
-  const WsLayout L = plan_workspace(M, K, N, r, batch);
+int contract_stage(int M, int K, int N, int batch, int group, const uint8_t *packed_w,
+                   const uint16_t *sw, const uint16_t *L2, int r, const uint16_t *bias, void *Y,
+                   int y_dtype, void *workspace, int kernel, hipStream_t s, int32_t *P, int m0,
+                   int mc, int n0, int nc) {
+  const WsLayout L = plan_workspace(M, K, N, r, batch, group);
   char *ws = (char *)workspace;
   GemmArgs g{};
   g.qa = (const int8_t *)(ws + L.qa_off);
@@ -127,6 +135,7 @@ int contract_stage(int M, int K, int N, int batch, const uint8_t *packed_w, cons
   g.Y = Y;
   g.y_bf16 = y_dtype == HSQ_BF16;
   g.M = M; g.N = N; g.G = L.G; g.Gp = L.Gp; g.Mpad = L.Mpad; g.r = r; g.ucols = batch * r;
+  g.bpg = L.bpg; g.SG = L.SG;
   g.P = P; g.m0 = m0; g.mc = mc; g.n0 = n0; g.nc = nc;
   g.part = (float *)(ws + L.part_off);
   const bool dump = P != nullptr;
@@ -134,20 +143,48 @@ int contract_stage(int M, int K, int N, int batch, const uint8_t *packed_w, cons
                                                 : launch_gemm_tiled(g, batch, dump, s));
 }
 
-int run_linear(const uint16_t *X, int M, int K, int N, int batch, const uint16_t *lambda,
-               const uint8_t *packed_w, const uint16_t *sw, const uint16_t *L1,
-               const uint16_t *L2, int r, const uint16_t *bias, void *Y, int y_dtype,
-               void *workspace, size_t ws_bytes, int kernel, void *stream,
+int run_linear(const uint16_t *X, int M, int K, int N, int batch, int group,
+               const uint16_t *lambda, const uint8_t *packed_w, const uint16_t *sw,
+               const uint16_t *L1, const uint16_t *L2, int r, const uint16_t *bias, void *Y,
+               int y_dtype, void *workspace, size_t ws_bytes, int kernel, void *stream,
                // partial-sum dump (test export); P == nullptr for the linear
                int32_t *P, int m0, int mc, int n0, int nc) {
-  int st = validate(X, M, K, N, batch, lambda, packed_w, sw, L1, L2, r, bias, Y, y_dtype,
+  int st = validate(X, M, K, N, batch, group, lambda, packed_w, sw, L1, L2, r, bias, Y, y_dtype,
                     workspace, ws_bytes, &kernel, true, true, P, m0, mc, n0, nc);
   if (st != HSQ_OK) return st;
   hipStream_t s = (hipStream_t)stream;
-  st = quant_stage(X, M, K, N, batch, lambda, L1, r, workspace, s);
+  st = quant_stage(X, M, K, N, batch, group, lambda, L1, r, workspace, s);
   if (st != HSQ_OK) return st;
-  return contract_stage(M, K, N, batch, packed_w, sw, L2, r, bias, Y, y_dtype, workspace, kernel,
-                        s, P, m0, mc, n0, nc);
+  return contract_stage(M, K, N, batch, group, packed_w, sw, L2, r, bias, Y, y_dtype, workspace,
+                        kernel, s, P, m0, mc, n0, nc);
+}
+
+int quantize_stage_g(const uint16_t *X, int M, int K, int N, int batch, int group,
+                     const uint16_t *lambda, const uint16_t *L1, int r, void *workspace,
+                     size_t ws_bytes, void *stream) {
+  int kernel = HSQ_KERNEL_AUTO;
+  int st = validate(X, M, K, N, batch, group, lambda, nullptr, nullptr, L1, nullptr, r, nullptr,
+                    nullptr, HSQ_F32, workspace, ws_bytes, &kernel, true, false, nullptr, 0, 0, 0, 0);
+  if (st != HSQ_OK) return st;
+  return quant_stage(X, M, K, N, batch, group, lambda, L1, r, workspace, (hipStream_t)stream);
+}
+
+int contract_stage_g(int M, int K, int N, int batch, int group, const uint8_t *packed_w,
+                     const uint16_t *sw, const uint16_t *L2, int r, const uint16_t *bias, void *Y,
+                     int y_dtype, void *workspace, size_t ws_bytes, int kernel, void *stream) {
+  int st = validate(nullptr, M, K, N, batch, group, nullptr, packed_w, sw, nullptr, L2, r, bias, Y,
+                    y_dtype, workspace, ws_bytes, &kernel, false, true, nullptr, 0, 0, 0, 0);
+  if (st != HSQ_OK) return st;
+  return contract_stage(M, K, N, batch, group, packed_w, sw, L2, r, bias, Y, y_dtype, workspace,
+                        kernel, (hipStream_t)stream, nullptr, 0, 0, 0, 0);
+}
+
+int group_partials_g(const uint16_t *X, int M, int K, int N, int group, const uint16_t *lambda,
+                     const uint8_t *packed_w, int m0, int mc, int n0, int nc, int32_t *P,
+                     void *workspace, size_t ws_bytes, int kernel, void *stream) {
+  if (!P) return HSQ_E_INVAL;
+  return run_linear(X, M, K, N, 1, group, lambda, packed_w, nullptr, nullptr, nullptr, 0, nullptr,
+                    nullptr, HSQ_F32, workspace, ws_bytes, kernel, stream, P, m0, mc, n0, nc);
 }
 
 }  // namespace
@@ -217,7 +254,11 @@ int hsq_quantize_act(const uint16_t *X, int M, int K, const uint16_t *lambda,
 }
 
 size_t hsq_workspace_bytes(int M, int K, int N, int r, int batch) {
-  return workspace_bytes(M, K, N, r, batch);
+  return workspace_bytes(M, K, N, r, batch, kGroup);
+}
+
+size_t hsq_workspace_bytes_g(int M, int K, int N, int r, int batch, int group) {
+  return workspace_bytes(M, K, N, r, batch, group);
 }
 
 int hsq_w4a4_lowrank_linear(const uint16_t *X, int M, int K, int N, int batch,
@@ -225,7 +266,7 @@ int hsq_w4a4_lowrank_linear(const uint16_t *X, int M, int K, int N, int batch,
                             const uint16_t *sw, const uint16_t *L1, const uint16_t *L2, int r,
                             const uint16_t *bias, void *Y, int y_dtype, void *workspace,
                             size_t ws_bytes, void *stream) {
-  return run_linear(X, M, K, N, batch, lambda, packed_w, sw, L1, L2, r, bias, Y, y_dtype,
+  return run_linear(X, M, K, N, batch, kGroup, lambda, packed_w, sw, L1, L2, r, bias, Y, y_dtype,
                     workspace, ws_bytes, HSQ_KERNEL_AUTO, stream, nullptr, 0, 0, 0, 0);
 }
 
@@ -234,38 +275,61 @@ int hsq_w4a4_lowrank_linear_ex(const uint16_t *X, int M, int K, int N, int batch
                                const uint16_t *sw, const uint16_t *L1, const uint16_t *L2,
                                int r, const uint16_t *bias, void *Y, int y_dtype,
                                void *workspace, size_t ws_bytes, int kernel, void *stream) {
-  return run_linear(X, M, K, N, batch, lambda, packed_w, sw, L1, L2, r, bias, Y, y_dtype,
+  return run_linear(X, M, K, N, batch, kGroup, lambda, packed_w, sw, L1, L2, r, bias, Y, y_dtype,
+                    workspace, ws_bytes, kernel, stream, nullptr, 0, 0, 0, 0);
+}
+
+int hsq_w4a4_lowrank_linear_g(const uint16_t *X, int M, int K, int N, int batch, int group,
+                              const uint16_t *lambda, const uint8_t *packed_w,
+                              const uint16_t *sw, const uint16_t *L1, const uint16_t *L2,
+                              int r, const uint16_t *bias, void *Y, int y_dtype,
+                              void *workspace, size_t ws_bytes, int kernel, void *stream) {
+  return run_linear(X, M, K, N, batch, group, lambda, packed_w, sw, L1, L2, r, bias, Y, y_dtype,
                     workspace, ws_bytes, kernel, stream, nullptr, 0, 0, 0, 0);
 }
 
 int hsq_w4a4_quantize_stage(const uint16_t *X, int M, int K, int N, int batch,
                             const uint16_t *lambda, const uint16_t *L1, int r, void *workspace,
                             size_t ws_bytes, void *stream) {
-  int kernel = HSQ_KERNEL_AUTO;
-  int st = validate(X, M, K, N, batch, lambda, nullptr, nullptr, L1, nullptr, r, nullptr, nullptr,
-                    HSQ_F32, workspace, ws_bytes, &kernel, true, false, nullptr, 0, 0, 0, 0);
-  if (st != HSQ_OK) return st;
-  return quant_stage(X, M, K, N, batch, lambda, L1, r, workspace, (hipStream_t)stream);
+  return quantize_stage_g(X, M, K, N, batch, kGroup, lambda, L1, r, workspace, ws_bytes, stream);
+}
+
+int hsq_w4a4_quantize_stage_g(const uint16_t *X, int M, int K, int N, int batch, int group,
+                              const uint16_t *lambda, const uint16_t *L1, int r, void *workspace,
+                              size_t ws_bytes, void *stream) {
+  return quantize_stage_g(X, M, K, N, batch, group, lambda, L1, r, workspace, ws_bytes, stream);
 }
 
 int hsq_w4a4_contract_stage(int M, int K, int N, int batch, const uint8_t *packed_w,
                             const uint16_t *sw, const uint16_t *L2, int r, const uint16_t *bias,
                             void *Y, int y_dtype, void *workspace, size_t ws_bytes, int kernel,
                             void *stream) {
-  int st = validate(nullptr, M, K, N, batch, nullptr, packed_w, sw, nullptr, L2, r, bias, Y,
-                    y_dtype, workspace, ws_bytes, &kernel, false, true, nullptr, 0, 0, 0, 0);
-  if (st != HSQ_OK) return st;
-  return contract_stage(M, K, N, batch, packed_w, sw, L2, r, bias, Y, y_dtype, workspace, kernel,
-                        (hipStream_t)stream, nullptr, 0, 0, 0, 0);
+  return contract_stage_g(M, K, N, batch, kGroup, packed_w, sw, L2, r, bias, Y, y_dtype, workspace,
+                          ws_bytes, kernel, stream);
+}
+
+int hsq_w4a4_contract_stage_g(int M, int K, int N, int batch, int group, const uint8_t *packed_w,
+                              const uint16_t *sw, const uint16_t *L2, int r, const uint16_t *bias,
+                              void *Y, int y_dtype, void *workspace, size_t ws_bytes, int kernel,
+                              void *stream) {
+  return contract_stage_g(M, K, N, batch, group, packed_w, sw, L2, r, bias, Y, y_dtype, workspace,
+                          ws_bytes, kernel, stream);
 }
 
 int hsq_w4a4_group_partials(const uint16_t *X, int M, int K, int N, const uint16_t *lambda,
                             const uint8_t *packed_w, int m0, int mc, int n0, int nc,
                             int32_t *P, void *workspace, size_t ws_bytes, int kernel,
                             void *stream) {
-  if (!P) return HSQ_E_INVAL;
-  return run_linear(X, M, K, N, 1, lambda, packed_w, nullptr, nullptr, nullptr, 0, nullptr,
-                    nullptr, HSQ_F32, workspace, ws_bytes, kernel, stream, P, m0, mc, n0, nc);
+  return group_partials_g(X, M, K, N, kGroup, lambda, packed_w, m0, mc, n0, nc, P, workspace,
+                          ws_bytes, kernel, stream);
+}
+
+int hsq_w4a4_group_partials_g(const uint16_t *X, int M, int K, int N, int group,
+                              const uint16_t *lambda, const uint8_t *packed_w, int m0, int mc,
+                              int n0, int nc, int32_t *P, void *workspace, size_t ws_bytes,
+                              int kernel, void *stream) {
+  return group_partials_g(X, M, K, N, group, lambda, packed_w, m0, mc, n0, nc, P, workspace,
+                          ws_bytes, kernel, stream);
 }
 
 }  // extern "C"

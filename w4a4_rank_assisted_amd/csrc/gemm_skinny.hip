@@ -27,8 +27,12 @@ constexpr int kStreamLoad = 2;
 // registers need the larger per-wave budget)
 constexpr int max_waves(int mt) { return mt <= 2 ? 16 : 8; }
 
-template <int MT, int P, int CT, bool DUMP>
+template <int MT, int P, int CT, bool DUMP, int BPG>
 __global__ __launch_bounds__(64 * max_waves(MT)) void k_gemm_skinny(GemmArgs a, int W) {
+  // a block pair of the packed residual is two 64-channel groups (BPG = 1)
+  // or one 128-channel group (BPG = 2: its two MFMAs accumulate in int32,
+  // then one rescale)
+  constexpr int NS = BPG == 1 ? 2 : 1;              // scale groups per block pair
   // dynamic LDS: partial tiles [W][CT][MT][4][64], then U [r][16*MT]
   // (slices summed), L2 [r][16*CT], bias [16*CT]
   extern __shared__ float red[];
@@ -47,7 +51,7 @@ __global__ __launch_bounds__(64 * max_waves(MT)) void k_gemm_skinny(GemmArgs a, 
   const __amdgpu_buffer_rsrc_t rs_w =
       buffer_rsrc(a.w + (size_t)proj * a.w_stride, (uint32_t)NT * GP * 1024);
   const __amdgpu_buffer_rsrc_t rs_a = buffer_rsrc(a.qa, (uint32_t)MT * a.Gp * 1024);
-  const __amdgpu_buffer_rsrc_t rs_x = buffer_rsrc(a.sxs, (uint32_t)MT * a.Gp * 32);
+  const __amdgpu_buffer_rsrc_t rs_x = buffer_rsrc(a.sxs, (uint32_t)MT * a.SG * 32);
   const __amdgpu_buffer_rsrc_t rs_s =
       buffer_rsrc(DUMP ? nullptr : a.sw + (size_t)proj * G * a.N, DUMP ? 0u : (uint32_t)G * a.N * 2);
   uint32_t offw[CT], offsw[CT];
@@ -72,30 +76,33 @@ __global__ __launch_bounds__(64 * max_waves(MT)) void k_gemm_skinny(GemmArgs a, 
   // CT column tiles
   struct Act {
     v4i av[MT][2];
-    v4h sx[MT][2];
-    v2h sw[CT];                         // the pair's two groups, fp16
+    v4h sx[MT][NS];
+    _Float16 sw[CT][NS];
   };
   auto load_act = [&](int gp, Act &t) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < MT; ++i)
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int g = 2 * gp + h;
+      for (int h = 0; h < 2; ++h)
         t.av[i][h] = __builtin_bit_cast(
-            v4i, __builtin_amdgcn_raw_buffer_load_b128(rs_a, (uint32_t)(i * a.Gp * 64 + lane) * 16, g * 1024, 0));
-        if (!DUMP)
-          t.sx[i][h] = __builtin_bit_cast(
-              v4h, __builtin_amdgcn_raw_buffer_load_b64(rs_x, (uint32_t)(i * a.Gp * 16 + rowq) * 2, g * 32, 0));
-      }
+            v4i, __builtin_amdgcn_raw_buffer_load_b128(rs_a, (uint32_t)(i * a.Gp * 64 + lane) * 16,
+                                                       (2 * gp + h) * 1024, 0));
     if (!DUMP) {
-      // a pad group (g = G) reads group G-1: its codes are zero, so it adds
+      // scale group sg of the pair: 2gp + h (group 64) or gp (group 128).
+      // A pad group (sg = G) reads group G-1: its codes are zero, so it adds
       // fma(1.5*2^23, sw, -1.5*2^23*sw) = 0 exactly whatever sw is
 #pragma unroll
-      for (int c = 0; c < CT; ++c)
+      for (int h = 0; h < NS; ++h) {
+        const int sg = NS * gp + h;
 #pragma unroll
-        for (int h = 0; h < 2; ++h)
+        for (int i = 0; i < MT; ++i)
+          t.sx[i][h] = __builtin_bit_cast(
+              v4h, __builtin_amdgcn_raw_buffer_load_b64(rs_x, (uint32_t)(i * a.SG * 16 + rowq) * 2, sg * 32, 0));
+#pragma unroll
+        for (int c = 0; c < CT; ++c)
           t.sw[c][h] = __builtin_bit_cast(
-              _Float16, __builtin_amdgcn_raw_buffer_load_b16(rs_s, offsw[c], min(2 * gp + h, G - 1) * a.N * 2, 0));
+              _Float16, __builtin_amdgcn_raw_buffer_load_b16(rs_s, offsw[c], min(sg, G - 1) * a.N * 2, 0));
+      }
     }
   };
 
@@ -123,19 +130,25 @@ __global__ __launch_bounds__(64 * max_waves(MT)) void k_gemm_skinny(GemmArgs a, 
     for (int p = 0; p < P; ++p) {
       const int gp = c0 + p;
 #pragma unroll
-      for (int c = 0; c < CT; ++c)
+      for (int c = 0; c < CT; ++c) {
+        v4i bb[2];
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
-          const int g = 2 * gp + h;
           const uint32_t w0 = h ? wv[p][c].z : wv[p][c].x, w1 = h ? wv[p][c].w : wv[p][c].y;
-          const v4i b = {(int)(w0 & kNibMask), (int)((w0 << 4) & kNibMask), (int)(w1 & kNibMask),
-                         (int)((w1 << 4) & kNibMask)};
+          bb[h] = (v4i){(int)(w0 & kNibMask), (int)((w0 << 4) & kNibMask), (int)(w1 & kNibMask),
+                        (int)((w1 << 4) & kNibMask)};
+        }
+#pragma unroll
+        for (int h = 0; h < NS; ++h) {
+          const int g = NS * gp + h;                // scale group
           // sw / 16: the MFMA yields 16 * P
           const float swf = (DUMP || p >= pn) ? 0.0f : (float)t[p].sw[c][h] * 0.0625f;
           const float nsw = -kMagic * swf;
 #pragma unroll
           for (int i = 0; i < MT; ++i) {
-            const v4i d = __builtin_amdgcn_mfma_i32_16x16x64_i8(t[p].av[i][h], b, magic, 0, 0, 0);
+            v4i d = __builtin_amdgcn_mfma_i32_16x16x64_i8(t[p].av[i][h], bb[h], magic, 0, 0, 0);
+            if constexpr (BPG == 2)                 // the group's second block, accumulated
+              d = __builtin_amdgcn_mfma_i32_16x16x64_i8(t[p].av[i][1], bb[1], d, 0, 0, 0);
             if (DUMP) {
               const int n = (nt0 + c) * 16 + colq;
 #pragma unroll
@@ -161,6 +174,7 @@ __global__ __launch_bounds__(64 * max_waves(MT)) void k_gemm_skinny(GemmArgs a, 
             }
           }
         }
+      }
     }
   }
   if (DUMP) return;
@@ -211,17 +225,17 @@ __global__ __launch_bounds__(64 * max_waves(MT)) void k_gemm_skinny(GemmArgs a, 
   }
 }
 
-template <int MT, int P, int CT>
+template <int MT, int P, int CT, int BPG>
 hipError_t launch_cfg(const GemmArgs &a, int batch, bool dump, int W, hipStream_t s) {
   const int NT = ceil_div(a.N, kTile);
   const size_t lds = ((size_t)W * CT * MT * 4 * 64 + (size_t)a.r * MT * 16 + (size_t)a.r * 16 * CT +
                       16 * CT) * sizeof(float);
   if (dump) {
     const int g0 = a.n0 / (16 * CT), g1 = (a.n0 + a.nc - 1) / (16 * CT);
-    hipLaunchKernelGGL((k_gemm_skinny<MT, P, CT, true>), dim3((unsigned)(g1 - g0 + 1), 1u),
+    hipLaunchKernelGGL((k_gemm_skinny<MT, P, CT, true, BPG>), dim3((unsigned)(g1 - g0 + 1), 1u),
                        dim3((unsigned)(64 * W)), 0, s, a, W);
   } else {
-    hipLaunchKernelGGL((k_gemm_skinny<MT, P, CT, false>), dim3((unsigned)ceil_div(NT, CT), (unsigned)batch),
+    hipLaunchKernelGGL((k_gemm_skinny<MT, P, CT, false, BPG>), dim3((unsigned)ceil_div(NT, CT), (unsigned)batch),
                        dim3((unsigned)(64 * W)), lds, s, a, W);
   }
   return hipGetLastError();
@@ -239,6 +253,7 @@ int waves_for(int GP, int P, int mt) {
 // Cost = sequential runs per wave x rounds of 4096 waves (about what the
 // chip holds at this register use), with a penalty when fewer workgroups
 // than CUs stream; the cheapest shape wins, wider CT on ties.
+template <int BPG>
 hipError_t launch_mt1(const GemmArgs &a, int batch, bool dump, hipStream_t s) {
   const int NT = ceil_div(a.N, kTile), GP = a.Gp / 2;
   auto cost = [&](int P, int CT) {
@@ -249,33 +264,43 @@ hipError_t launch_mt1(const GemmArgs &a, int batch, bool dump, hipStream_t s) {
     if (wgs < 256) c += (256 - wgs) * 4 / 256 + 1;   // idle CUs
     return c;
   };
+  // (group 128 keeps both blocks of a pair unpacked at once: four column
+  // tiles would not fit the register budget, so it stops at three)
+  constexpr int kShapes = BPG == 1 ? 4 : 3;
   int best = 0;
   const long long cs[4] = {cost(4, 1), cost(2, 2), cost(2, 3), cost(2, 4)};
-  for (int k = 1; k < 4; ++k)
+  for (int k = 1; k < kShapes; ++k)
     if (cs[k] <= cs[best]) best = k;
   switch (best) {
-    case 3: return launch_cfg<1, 2, 4>(a, batch, dump, waves_for(GP, 2, 1), s);
-    case 2: return launch_cfg<1, 2, 3>(a, batch, dump, waves_for(GP, 2, 1), s);
-    case 1: return launch_cfg<1, 2, 2>(a, batch, dump, waves_for(GP, 2, 1), s);
-    default: return launch_cfg<1, 4, 1>(a, batch, dump, waves_for(GP, 4, 1), s);
+    case 3:
+      if constexpr (BPG == 1) return launch_cfg<1, 2, 4, BPG>(a, batch, dump, waves_for(GP, 2, 1), s);
+      [[fallthrough]];
+    case 2: return launch_cfg<1, 2, 3, BPG>(a, batch, dump, waves_for(GP, 2, 1), s);
+    case 1: return launch_cfg<1, 2, 2, BPG>(a, batch, dump, waves_for(GP, 2, 1), s);
+    default: return launch_cfg<1, 4, 1, BPG>(a, batch, dump, waves_for(GP, 4, 1), s);
   }
 }
 
-template <int MT>
+template <int MT, int BPG>
 hipError_t launch_mt(const GemmArgs &a, int batch, bool dump, hipStream_t s) {
-  return launch_cfg<MT, 2, 1>(a, batch, dump, waves_for(a.Gp / 2, 2, MT), s);
+  return launch_cfg<MT, 2, 1, BPG>(a, batch, dump, waves_for(a.Gp / 2, 2, MT), s);
+}
+
+template <int BPG>
+hipError_t launch_bpg(const GemmArgs &a, int batch, bool dump, hipStream_t s) {
+  switch (ceil_div(a.M, kTile)) {
+    case 1: return launch_mt1<BPG>(a, batch, dump, s);
+    case 2: return launch_mt<2, BPG>(a, batch, dump, s);
+    case 3: return launch_mt<3, BPG>(a, batch, dump, s);
+    case 4: return launch_mt<4, BPG>(a, batch, dump, s);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 }  // namespace
 
 hipError_t launch_gemm_skinny(const GemmArgs &a, int batch, bool dump, hipStream_t s) {
-  switch (ceil_div(a.M, kTile)) {
-    case 1: return launch_mt1(a, batch, dump, s);
-    case 2: return launch_mt<2>(a, batch, dump, s);
-    case 3: return launch_mt<3>(a, batch, dump, s);
-    case 4: return launch_mt<4>(a, batch, dump, s);
-    default: return hipErrorInvalidValue;
-  }
+  return a.bpg == 2 ? launch_bpg<2>(a, batch, dump, s) : launch_bpg<1>(a, batch, dump, s);
 }
 
 }  // namespace hsq

@@ -37,6 +37,8 @@
 // tile in split order (deterministic) and runs the epilogue.
 #include "hsq_internal.h"
 
+#include <type_traits>
+
 namespace hsq {
 
 namespace {
@@ -59,10 +61,13 @@ constexpr int kAccPerThread = TM * TN * 4;
 static_assert(TMB * 64 == NTH && TNB * 64 == NTH, "one A chunk and one B slot per thread");
 static_assert(TMB * 16 <= NTH / 2 && BN <= NTH / 2, "scale loads: sx in the first half, sw in the second");
 
+// One stage is one scale group: one 64-channel block (BPG = 1) or a block
+// pair (BPG = 2, group 128).
+template <int BPG>
 struct alignas(16) Stages {
-  int8_t a[2][TMB][64][16];           // [buf][m-tile][lane][bytes]          16 KB
-  int8_t b[2][TNB][64][16];           // [buf][n-tile][lane][bytes]          16 KB
-  float2 sw[2][BN];                   // [buf][col] = (sw, -magic*sw)         2 KB
+  int8_t a[2][BPG][TMB][64][16];      // [buf][block][m-tile][lane][bytes]   16 KB per block
+  int8_t b[2][BPG][TNB][64][16];      // [buf][block][n-tile][lane][bytes]   16 KB per block
+  float2 sw[2][BN];                   // [buf][col] = (sw, -magic*sw)/16      2 KB
   uint16_t sx[2][TMB][16];            // [buf][m-tile][row] fp16             512 B
 };
 
@@ -79,9 +84,9 @@ struct alignas(16) EpiSmem<0> {
   float bias[BN];
 };
 
-template <int RPT>
+template <int RPT, int BPG>
 struct alignas(16) Smem {
-  Stages st;
+  Stages<BPG> st;
   EpiSmem<RPT> ep;
 };
 
@@ -117,12 +122,12 @@ __device__ __forceinline__ void tile_of(int bid, int nblk, int mblk, int &mb, in
   nb = w / gsz;
 }
 
-template <bool DUMP, int RPT, int MODE>
+template <bool DUMP, int RPT, int MODE, int BPG>
 __global__ __launch_bounds__(NTH, 2) void k_gemm_tiled(GemmArgs a, int nblk, int mblk) {
   static_assert(MODE != kSplit || RPT == 0, "a split pass has no epilogue");
   constexpr bool EPI = !DUMP && MODE != kSplit;   // this pass writes Y
-  __shared__ Smem<RPT> smem;
-  Stages &sm = smem.st;
+  __shared__ Smem<RPT, BPG> smem;
+  Stages<BPG> &sm = smem.st;
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -138,10 +143,14 @@ __global__ __launch_bounds__(NTH, 2) void k_gemm_tiled(GemmArgs a, int nblk, int
   if (DUMP && ((mt0 + TMB) * 16 <= a.m0 || mt0 * 16 >= a.m0 + a.mc ||
                (nt0 + TNB) * 16 <= a.n0 || nt0 * 16 >= a.n0 + a.nc))
     return;  // whole block outside the window (uniform: before any barrier)
-  // stages [g0, g1): every (padded) group, or one split's group pairs
-  int g0 = 0, g1 = a.Gp;
+  // stages: one per scale group, padded to even (a pad stage has weight
+  // scale 0: it adds exactly 0); [g0, g1): all of them, or one split's
+  // stage pairs
+  const int nstg = BPG == 1 ? a.Gp : (a.G + 1) / 2 * 2;
+  const int last = (BPG == 1 ? a.Gp : a.G) - 1;  // last stage with data (loads clamp to it)
+  int g0 = 0, g1 = nstg;
   if (MODE == kSplit) {
-    const int S = (int)gridDim.z, z = (int)blockIdx.z, pairs = a.Gp / 2;
+    const int S = (int)gridDim.z, z = (int)blockIdx.z, pairs = nstg / 2;
     g0 = 2 * (z * pairs / S);
     g1 = 2 * ((z + 1) * pairs / S);
   }
@@ -153,9 +162,10 @@ __global__ __launch_bounds__(NTH, 2) void k_gemm_tiled(GemmArgs a, int nblk, int
   // Loads past the matrix edges read the last valid block (clamped
   // addresses, straight-line code); the edge masks are applied on the way
   // into LDS, where only masked rows / columns see those values.
-  const int G = a.G;
-  v4u ra[kSlots];
-  v2u rb[kSlots];
+  const int G = a.G;                  // scale groups
+  using RB = std::conditional_t<BPG == 1, v2u, v4u>;
+  v4u ra[kSlots][BPG];
+  RB rb[kSlots];
   uint32_t rsx[kSlots];
   uint32_t rsw[kSlots];
   // Addresses: buffer resources over the operands, a fixed 32-bit byte
@@ -163,32 +173,40 @@ __global__ __launch_bounds__(NTH, 2) void k_gemm_tiled(GemmArgs a, int nblk, int
   // stage costs no vector address math.
   const __amdgpu_buffer_rsrc_t rs_a = buffer_rsrc(a.qa, (uint32_t)MT * a.Gp * 1024);
   const __amdgpu_buffer_rsrc_t rs_w = buffer_rsrc(w, (uint32_t)NT * GP * 1024);
-  const __amdgpu_buffer_rsrc_t rs_x = buffer_rsrc(a.sxs, (uint32_t)MT * a.Gp * 32);
+  const __amdgpu_buffer_rsrc_t rs_x = buffer_rsrc(a.sxs, (uint32_t)MT * a.SG * 32);
   const __amdgpu_buffer_rsrc_t rs_s = buffer_rsrc(sw, DUMP ? 0u : (uint32_t)G * a.N * 2);
   // thread t: 16-byte chunk t of the A tile, lane slot t of the B tile;
   // the first half also one activation scale, the second one weight scale
   const uint32_t offa = ((uint32_t)min(mt0 + (tid >> 6), MT - 1) * a.Gp * 64 + (tid & 63)) * 16;
   const uint32_t offb = ((uint32_t)min(nt0 + (tid >> 6), NT - 1) * GP * 64 + (tid & 63)) * 16;
-  const uint32_t offsx = ((uint32_t)min(mt0 + ((tid >> 4) & (TMB - 1)), MT - 1) * a.Gp * 16 + (tid & 15)) * 2;
+  const uint32_t offsx = ((uint32_t)min(mt0 + ((tid >> 4) & (TMB - 1)), MT - 1) * a.SG * 16 + (tid & 15)) * 2;
   const uint32_t offsw = (uint32_t)min(nt0 * 16 + (tid & (BN - 1)), a.N - 1) * 2;
   // Straight-line code with a fixed number of loads per stage (the stage
   // index is clamped near the end instead of skipping the loads), so the
   // compiler's wait counting stays exact and waits only for the older slot.
   auto load_stage = [&](int g, auto slotc) __attribute__((always_inline)) {
     constexpr int SL = decltype(slotc)::value;
-    g = min(g, a.Gp - 1);
-    ra[SL] = __builtin_amdgcn_raw_buffer_load_b128(rs_a, offa, g * 1024, 0);
-    rb[SL] = __builtin_amdgcn_raw_buffer_load_b64(rs_w, offb, (g >> 1) * 1024 + 8 * (g & 1), 0);
-    rsx[SL] = __builtin_amdgcn_raw_buffer_load_b16(rs_x, offsx, g * 32, 0);
+    const int gl = min(g, last);
+#pragma unroll
+    for (int b = 0; b < BPG; ++b)
+      ra[SL][b] = __builtin_amdgcn_raw_buffer_load_b128(rs_a, offa, (gl * BPG + b) * 1024, 0);
+    if constexpr (BPG == 1)           // half a block pair: this group's 16 columns x 64 channels
+      rb[SL] = __builtin_amdgcn_raw_buffer_load_b64(rs_w, offb, (gl >> 1) * 1024 + 8 * (gl & 1), 0);
+    else                              // the whole pair: one 128-channel group
+      rb[SL] = __builtin_amdgcn_raw_buffer_load_b128(rs_w, offb, gl * 1024, 0);
+    rsx[SL] = __builtin_amdgcn_raw_buffer_load_b16(rs_x, offsx, gl * 32, 0);
     if (!DUMP) rsw[SL] = __builtin_amdgcn_raw_buffer_load_b16(rs_s, offsw, min(g, G - 1) * a.N * 2, 0);
   };
   auto store_stage = [&](int g, auto slotc, int buf) __attribute__((always_inline)) {
     constexpr int SL = decltype(slotc)::value;
-    *reinterpret_cast<v4u *>(&sm.a[buf][tid >> 6][tid & 63][0]) = ra[SL];
-    {
-      const v2u v = rb[SL];
-      *reinterpret_cast<v4u *>(&sm.b[buf][tid >> 6][tid & 63][0]) =
-          (v4u){v.x & kNibMask, (v.x << 4) & kNibMask, v.y & kNibMask, (v.y << 4) & kNibMask};
+#pragma unroll
+    for (int b = 0; b < BPG; ++b)
+      *reinterpret_cast<v4u *>(&sm.a[buf][b][tid >> 6][tid & 63][0]) = ra[SL][b];
+#pragma unroll
+    for (int b = 0; b < BPG; ++b) {
+      const uint32_t w0 = rb[SL][2 * b], w1 = rb[SL][2 * b + 1];
+      *reinterpret_cast<v4u *>(&sm.b[buf][b][tid >> 6][tid & 63][0]) =
+          (v4u){w0 & kNibMask, (w0 << 4) & kNibMask, w1 & kNibMask, (w1 << 4) & kNibMask};
     }
     if (tid < TMB * 16) {
       const int mi = tid >> 4, row = tid & 15;
@@ -320,16 +338,30 @@ __global__ __launch_bounds__(NTH, 2) void k_gemm_tiled(GemmArgs a, int nblk, int
     constexpr int BUF = SL & 1;                   // LDS buffer == g & 1
     load_stage(g + kSlots, slotc);    // past the end: a clamped, unused reload
 
-    v4i bv[TN];
-    v4i av[TM];
+    v4i bv[TN][BPG];
+    v4i av[TM][BPG];
 #pragma unroll
     for (int j = 0; j < TN; ++j) {
-      bv[j] = *reinterpret_cast<const v4i *>(&sm.b[BUF][wn * TN + j][lane][0]);
+#pragma unroll
+      for (int b = 0; b < BPG; ++b)
+        bv[j][b] = *reinterpret_cast<const v4i *>(&sm.b[BUF][b][wn * TN + j][lane][0]);
       swv[BUF][j] = sm.sw[BUF][(wn * TN + j) * 16 + colq];
     }
     auto read_a = [&](int i) __attribute__((always_inline)) {
-      av[i] = *reinterpret_cast<const v4i *>(&sm.a[BUF][wm * TM + i][lane][0]);
+#pragma unroll
+      for (int b = 0; b < BPG; ++b)
+        av[i][b] = *reinterpret_cast<const v4i *>(&sm.a[BUF][b][wm * TM + i][lane][0]);
       sxv[i] = *reinterpret_cast<const v4h *>(&sm.sx[BUF][wm * TM + i][rowq]);
+    };
+    // one row tile's MFMAs: a group's blocks accumulate in int32 (the
+    // second block's MFMA takes the first one's result as its input)
+    auto mfma_row = [&](int s) __attribute__((always_inline)) {
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        d[s][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(av[s][0], bv[j][0], magic, 0, 0, 0);
+        if constexpr (BPG == 2)
+          d[s][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(av[s][1], bv[j][1], d[s][j], 0, 0, 0);
+      }
     };
     read_a(0);
 #pragma unroll
@@ -342,27 +374,23 @@ __global__ __launch_bounds__(NTH, 2) void k_gemm_tiled(GemmArgs a, int nblk, int
         if (TM > 1) read_a(1);
         rescale(TM - 1, swv[BUF ^ 1], sx_carry, g - 1);
         __builtin_amdgcn_sched_barrier(0);
-        pin(av[0]);
 #pragma unroll
-        for (int j = 0; j < TN; ++j)
-          d[0][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(av[0], bv[j], magic, 0, 0, 0);
+        for (int b = 0; b < BPG; ++b) pin(av[0][b]);
+        mfma_row(0);
         continue;
       }
-      pin(av[s]);
-      if (s + 1 < TM) read_a(s + 1);
-      {
 #pragma unroll
-        for (int j = 0; j < TN; ++j)
-          d[s][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(av[s], bv[j], magic, 0, 0, 0);
-        rescale(s - 1, swv[BUF], sxv[s - 1], g);
-      }
-      // issue order within the step: one MFMA, then the eight rescale FMAs
-      // of one tile, and so on, so the matrix core works while the VALU
-      // rescales
+      for (int b = 0; b < BPG; ++b) pin(av[s][b]);
+      if (s + 1 < TM) read_a(s + 1);
+      mfma_row(s);
+      rescale(s - 1, swv[BUF], sxv[s - 1], g);
+      // issue order within the step: one tile's MFMAs, then the eight
+      // rescale FMAs of one tile, and so on, so the matrix core works while
+      // the VALU rescales
       if (!DUMP) {
 #pragma unroll
         for (int j = 0; j < TN; ++j) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x008, BPG, 0);
           __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
         }
       }
@@ -495,20 +523,20 @@ __global__ __launch_bounds__(NTH, 2) void k_gemm_tiled(GemmArgs a, int nblk, int
   }
 }
 
-template <int RPT, int MODE>
+template <int RPT, int MODE, int BPG>
 hipError_t launch_rpt(const GemmArgs &a, int batch, int nblk, int mblk, hipStream_t s) {
-  hipLaunchKernelGGL((k_gemm_tiled<false, RPT, MODE>), dim3((unsigned)(nblk * mblk), (unsigned)batch),
+  hipLaunchKernelGGL((k_gemm_tiled<false, RPT, MODE, BPG>), dim3((unsigned)(nblk * mblk), (unsigned)batch),
                      dim3(NTH), 0, s, a, nblk, mblk);
   return hipGetLastError();
 }
 
-template <int MODE>
+template <int MODE, int BPG>
 hipError_t launch_epi(const GemmArgs &a, int batch, int nblk, int mblk, hipStream_t s) {
-  if (a.r == 0) return launch_rpt<0, MODE>(a, batch, nblk, mblk, s);
-  if (a.r <= 4) return launch_rpt<4, MODE>(a, batch, nblk, mblk, s);
-  if (a.r <= 8) return launch_rpt<8, MODE>(a, batch, nblk, mblk, s);
-  if (a.r <= 16) return launch_rpt<16, MODE>(a, batch, nblk, mblk, s);
-  return launch_rpt<32, MODE>(a, batch, nblk, mblk, s);
+  if (a.r == 0) return launch_rpt<0, MODE, BPG>(a, batch, nblk, mblk, s);
+  if (a.r <= 4) return launch_rpt<4, MODE, BPG>(a, batch, nblk, mblk, s);
+  if (a.r <= 8) return launch_rpt<8, MODE, BPG>(a, batch, nblk, mblk, s);
+  if (a.r <= 16) return launch_rpt<16, MODE, BPG>(a, batch, nblk, mblk, s);
+  return launch_rpt<32, MODE, BPG>(a, batch, nblk, mblk, s);
 }
 
 }  // namespace
@@ -518,9 +546,11 @@ hipError_t launch_epi(const GemmArgs &a, int batch, int nblk, int mblk, hipStrea
 // busiest CU's work; the cheapest S wins, and on a tie a larger S only while
 // fewer than two workgroups per CU run (one leaves each SIMD two waves).
 // Each split keeps at least kMinSplitPairs group pairs.
-int tiled_splits(int M, int N, int K, int batch) {
+// Work is counted in stage pairs (two scale groups: two 64-channel blocks
+// for group 64, four for group 128).
+int tiled_splits(int M, int N, int K, int batch, int group) {
   const long long tiles = (long long)ceil_div(N, BN) * ceil_div(M, BM) * batch;
-  const int pairs = padded_groups(K) / 2;
+  const int pairs = group == kGroup ? padded_groups(K) / 2 : (K / group + 1) / 2;
   if (tiles >= kCUs) return 1;
   int best = 1;
   long long best_cost = -1;
@@ -534,30 +564,35 @@ int tiled_splits(int M, int N, int K, int batch) {
   return best;
 }
 
-size_t tiled_partial_bytes(int M, int N, int K, int batch) {
-  const int S = tiled_splits(M, N, K, batch);
+size_t tiled_partial_bytes(int M, int N, int K, int batch, int group) {
+  const int S = tiled_splits(M, N, K, batch, group);
   if (S <= 1) return 0;
   return (size_t)S * ceil_div(N, BN) * ceil_div(M, BM) * batch * NTH * kAccPerThread * sizeof(float);
 }
 
-hipError_t launch_gemm_tiled(const GemmArgs &a, int batch, bool dump, hipStream_t s) {
+template <int BPG>
+hipError_t launch_tiled_bpg(const GemmArgs &a, int batch, bool dump, hipStream_t s) {
   const int nblk = ceil_div(a.N, BN), mblk = ceil_div(a.M, BM);
   if (dump) {
     // every tile of one projection; blocks outside the window exit at once
-    hipLaunchKernelGGL((k_gemm_tiled<true, 0, kFull>), dim3((unsigned)(nblk * mblk), 1u), dim3(NTH), 0,
-                       s, a, nblk, mblk);
+    hipLaunchKernelGGL((k_gemm_tiled<true, 0, kFull, BPG>), dim3((unsigned)(nblk * mblk), 1u), dim3(NTH),
+                       0, s, a, nblk, mblk);
     return hipGetLastError();
   }
-  const int S = tiled_splits(a.M, a.N, a.G * kGroup, batch);
-  if (S <= 1) return launch_epi<kFull>(a, batch, nblk, mblk, s);
+  const int S = tiled_splits(a.M, a.N, a.G * kGroup * BPG, batch, kGroup * BPG);
+  if (S <= 1) return launch_epi<kFull, BPG>(a, batch, nblk, mblk, s);
   GemmArgs b = a;
   b.splits = S;
-  hipLaunchKernelGGL((k_gemm_tiled<false, 0, kSplit>),
+  hipLaunchKernelGGL((k_gemm_tiled<false, 0, kSplit, BPG>),
                      dim3((unsigned)(nblk * mblk), (unsigned)batch, (unsigned)S), dim3(NTH), 0, s, b,
                      nblk, mblk);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  return launch_epi<kReduce>(b, batch, nblk, mblk, s);
+  return launch_epi<kReduce, BPG>(b, batch, nblk, mblk, s);
+}
+
+hipError_t launch_gemm_tiled(const GemmArgs &a, int batch, bool dump, hipStream_t s) {
+  return a.bpg == 2 ? launch_tiled_bpg<2>(a, batch, dump, s) : launch_tiled_bpg<1>(a, batch, dump, s);
 }
 
 }  // namespace hsq

@@ -42,6 +42,11 @@ inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 // endian dwords give the 16 int8 MFMA operand bytes 16*code in order p.
 // ---------------------------------------------------------------------------
 inline int padded_groups(int K) { return ceil_div(K / kGroup, 2) * 2; }
+// Scale groups of `group` channels (64 or 128): one scale per (row or
+// column, group).  A group-128 scale covers two 64-channel blocks, which is
+// one block pair of the packed residual.  The activation scales are stored
+// per row tile for every padded 64-block (group 64) or every group (128).
+inline int scale_groups_stored(int K, int group) { return group == kGroup ? padded_groups(K) : K / group; }
 inline size_t packed_bytes(int K, int N) {
   return (size_t)ceil_div(N, kTile) * (size_t)(padded_groups(K) / 2) * 1024u;
 }
@@ -51,8 +56,9 @@ inline size_t packed_bytes(int K, int N) {
 //   qa  : MT x Gp x 64 lanes x 16 int8 codes   (MFMA A-operand order:
 //         lane l of block (mt, g) holds row 16mt + l%16, channels
 //         64g + 16(l/16) + p, p = 0..15; pad rows / groups are zero)
-//   sxs : MT x Gp x 16 fp16, the activation scale of (row, group), zero for
-//         pad rows / groups (read straight into v_fma_mix_f32)
+//   sxs : MT x SG x 16 fp16, the activation scale of (row, scale group),
+//         zero for pad rows / groups (read straight into v_fma_mix_f32);
+//         SG = scale_groups_stored(K, group)
 //   uw  : S_u x (batch*r) x (16*MT) fp32, one slice of U per K-slice of the
 //         quantization pass, summed in slice order by the consumer
 //   part: split-K partial tiles of the tiled contraction when its grid is
@@ -60,12 +66,13 @@ inline size_t packed_bytes(int K, int N) {
 // ---------------------------------------------------------------------------
 struct WsLayout {
   int MT = 0, G = 0, Gp = 0, Mpad = 0;
+  int group = kGroup, bpg = 1, SG = 0;  // G = K/group scale groups; bpg = group/64 blocks each
   int u_slices = 0;      // S_u: K-slices of the quantization pass
   size_t qa_off = 0, sxs_off = 0, uw_off = 0, part_off = 0, total = 0;
 };
 
-// Plans the workspace for (M, K, N, r, batch).  Pure host arithmetic.
-WsLayout plan_workspace(int M, int K, int N, int r, int batch);
+// Plans the workspace for (M, K, N, r, batch, group).  Pure host arithmetic.
+WsLayout plan_workspace(int M, int K, int N, int r, int batch, int group);
 
 // Largest token count the skinny kernel accepts (4 row tiles).
 constexpr int kSkinnyMaxM = 64;
@@ -77,7 +84,8 @@ struct QuantArgs {
   const uint16_t *X;       // M x K bf16
   const uint16_t *lam;     // K fp16
   const uint16_t *L1;      // batch x K x r bf16 (or null)
-  int M, K, G;
+  int M, K, G;             // G = K/64 real 64-channel blocks
+  int bpg, SG;             // blocks per scale group (1 or 2); scale groups stored per row tile
   int r, batch;
   int c0, cb;              // rank columns [c0, c0 + cb) of the batch*r columns
   int kend;                // channels processed: K (public) or 64*Gp (internal)
@@ -105,7 +113,8 @@ struct GemmArgs {
   const uint16_t *bias;    // batch x N bf16 or null
   void *Y;                 // batch x M x N
   int y_bf16;
-  int M, N, G, Gp, Mpad, r, ucols;
+  int M, N, G, Gp, Mpad, r, ucols;  // G = K/group scale groups; Gp = padded 64-blocks
+  int bpg, SG;             // blocks per scale group (1 or 2); scale groups stored per row tile
   // partial-sum dump window (test export)
   int32_t *P;
   int m0, mc, n0, nc;
@@ -123,12 +132,12 @@ hipError_t launch_unpack(const uint8_t *packed, int K, int N, int8_t *codes, hip
 // is the number of K-slices (U partials) of the internal pass.
 hipError_t launch_quant_act(const QuantArgs &a, hipStream_t s);
 hipError_t launch_quant_tiles(const QuantArgs &a, hipStream_t s);
-int quant_slices(int M, int K, int r, int batch);
+int quant_slices(int M, int K, int r, int batch, int group);
 hipError_t launch_gemm_tiled(const GemmArgs &a, int batch, bool dump, hipStream_t s);
 // Split-K factor of the tiled contraction for this shape (1: no split) and
 // the workspace bytes of its partial tiles.
-int tiled_splits(int M, int N, int K, int batch);
-size_t tiled_partial_bytes(int M, int N, int K, int batch);
+int tiled_splits(int M, int N, int K, int batch, int group);
+size_t tiled_partial_bytes(int M, int N, int K, int batch, int group);
 hipError_t launch_gemm_skinny(const GemmArgs &a, int batch, bool dump, hipStream_t s);
 
 }  // namespace hsq

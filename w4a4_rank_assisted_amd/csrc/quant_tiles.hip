@@ -9,12 +9,14 @@
 // activations (Deflating the Hessian, Table 1 caption), high-precision
 // branch on unquantized inputs (DiRotQ notes, key design 2).
 //
-// Mapping: a workgroup owns one 16-row tile and a K-slice of groups; its
-// waves take the slice's groups round-robin.  For a group, lane l holds row
-// l%16 and channels 16*(l/16) .. +15 -- exactly lane l's 16-byte slot of the
-// int8 MFMA operand block (row tile, group) -- so X arrives as two 16-byte
-// loads per lane (64 contiguous bytes per row and load) and the codes leave
-// as one contiguous 1 KB store per wave.  The group absmax is a 4-lane
+// Mapping: a workgroup owns one 16-row tile and a K-slice of scale groups
+// (64 channels, or 128 -- two 64-channel blocks -- for group-128, Deflating
+// the Hessian, Table 3 caption); its waves take the slice's groups
+// round-robin.  For a 64-channel block, lane l holds row l%16 and channels
+// 16*(l/16) .. +15 -- exactly lane l's 16-byte slot of the int8 MFMA operand
+// block (row tile, block) -- so X arrives as two 16-byte loads per lane and
+// block (64 contiguous bytes per row and load) and the codes leave as one
+// contiguous 1 KB store per wave and block.  The group absmax is a 4-lane
 // exchange (lanes l, l^16, l^32, l^48 hold the row's four channel blocks).
 // 1/lambda (exact IEEE division, once per channel) and L1 (fp32) of the
 // slice are staged in LDS, padded so that the four channel blocks of a
@@ -43,21 +45,24 @@ struct TilePlan {
   int slices, gpb, waves, nr;
 };
 
-// the U shares reuse the tables' LDS once every wave has left the loop
-size_t plan_lds(int gpb, int nr, int waves) {
-  const size_t tables = (size_t)gpb * 4 * (kLamKq + kqs(nr)), shares = (size_t)waves * 64 * nr;
+// the U shares reuse the tables' LDS once every wave has left the loop;
+// gpb units of bpg blocks each
+size_t plan_lds(int gpb, int bpg, int nr, int waves) {
+  const size_t tables = (size_t)gpb * bpg * 4 * (kLamKq + kqs(nr)), shares = (size_t)waves * 64 * nr;
   return sizeof(float) * (tables > shares ? tables : shares);
 }
 
-// K-slices: enough for the staged tables to fit kSliceLdsBytes and, up to
-// kMaxUSlices, for about kTargetWaves waves of 4; few row tiles get wider
-// workgroups (up to 16 waves, at most one per group of the slice).
-TilePlan tile_plan(int M, int K, int r, int batch) {
+// Work units: scale groups of bpg 64-channel blocks (every padded block for
+// group 64, every 128-channel group for group 128).  K-slices: enough for
+// the staged tables to fit kSliceLdsBytes and, up to kMaxUSlices, for about
+// kTargetWaves waves of 4; few row tiles get wider workgroups (up to 16
+// waves, at most one per unit of the slice).
+TilePlan tile_plan(int M, int K, int r, int batch, int group) {
   TilePlan p{};
-  const int MT = ceil_div(M, kTile), Gp = padded_groups(K);
+  const int MT = ceil_div(M, kTile), Gp = scale_groups_stored(K, group), bpg = group / kGroup;
   const int total = r * batch;
   p.nr = pass_width(total < kRankPass ? total : kRankPass);
-  const size_t per_group = sizeof(float) * (4 * kLamKq + 4 * kqs(p.nr));
+  const size_t per_group = sizeof(float) * bpg * (4 * kLamKq + 4 * kqs(p.nr));
   int fit = (int)(kSliceLdsBytes / per_group);
   if (fit < 1) fit = 1;
   int S = ceil_div(Gp, fit);
@@ -74,52 +79,60 @@ TilePlan tile_plan(int M, int K, int r, int batch) {
   return p;
 }
 
-template <int NR, bool CODES>
+template <int NR, bool CODES, int BPG>
 __global__ __launch_bounds__(1024) void k_quant_tiles(QuantArgs a, int gpb) {
-  // dynamic LDS: 1/lambda [gpb][4][kLamKq], L1 [gpb][4][kqs(NR)] (channel
-  // block: 16 channels x NR columns); after the loop, U shares [waves][NR][64]
+  // dynamic LDS: 1/lambda [gpb*BPG][4][kLamKq], L1 [gpb*BPG][4][kqs(NR)]
+  // (per 64-block and channel block: 16 channels x NR columns); after the
+  // loop, U shares [waves][NR][64]
   extern __shared__ float lds[];
   float *ilam = lds;
-  float *l1s = ilam + gpb * 4 * kLamKq;
+  float *l1s = ilam + gpb * BPG * 4 * kLamKq;
   float *upart = lds;
 
   const int nthr = (int)blockDim.x, W = nthr >> 6;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int mt = blockIdx.x;
+  const int nunits = a.SG;                    // scale groups per row tile (the units)
   const int gs = blockIdx.y * gpb;
-  const int ge = min(gs + gpb, a.Gp), ngb = ge - gs;
+  const int ge = min(gs + gpb, nunits), ngb = ge - gs;
+  const int nblk = ngb * BPG;                 // 64-blocks of the slice
   const int row = lane & 15, kq = lane >> 4;
   const int m = mt * kTile + row;
 
   // X through a resource of exactly M*K bf16 (M*K < 2^31): rows past M get
   // the offset at its end and read zero (the range check covers the lane
-  // offset); the group offset is scalar and clamped to the last real group
-  // (a pad group reads that one and zeroes it through its zero 1/lambda)
+  // offset); the block offset is scalar and clamped to the last real block
+  // (a pad block reads that one and zeroes it through its zero 1/lambda)
   const uint32_t xbytes = (uint32_t)((size_t)a.M * a.K * 2);
   const __amdgpu_buffer_rsrc_t rs_x = buffer_rsrc(a.X, xbytes);
   const uint32_t offx = m < a.M ? ((uint32_t)m * (uint32_t)a.K + 16u * kq) * 2u : xbytes;
-  auto load_x = [&](int g, v4u &x0, v4u &x1) __attribute__((always_inline)) {
-    const int gc = min(g, a.G - 1);
-    x0 = __builtin_amdgcn_raw_buffer_load_b128(rs_x, offx, gc * 128, 0);
-    x1 = __builtin_amdgcn_raw_buffer_load_b128(rs_x, offx, gc * 128 + 16, 0);
+  // the unit's BPG blocks, two 16-byte loads each
+  auto load_x = [&](int g, v4u (&x)[2 * BPG]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int b = 0; b < BPG; ++b) {
+      const int bc = min(g * BPG + b, a.G - 1);
+      x[2 * b] = __builtin_amdgcn_raw_buffer_load_b128(rs_x, offx, bc * 128, 0);
+      x[2 * b + 1] = __builtin_amdgcn_raw_buffer_load_b128(rs_x, offx, bc * 128 + 16, 0);
+    }
   };
   int g = gs + wave;
-  v4u x0, x1;
-  load_x(min(g, ge - 1), x0, x1);             // in flight during the staging (unused past the slice)
+  v4u x[2 * BPG];
+  load_x(min(g, ge - 1), x);                  // in flight during the staging (unused past the slice)
 
   // ---- slice tables: 1/lambda, 8 channels per item ----
-  for (int p = tid; p < ngb * 8; p += nthr) {
-    const int gl = p >> 3, c = 8 * (p & 7);
-    const bool real = gs + gl < a.G;
-    const v4u lv = *reinterpret_cast<const v4u *>(a.lam + (size_t)min(gs + gl, a.G - 1) * kGroup + c);
+  const int bs = gs * BPG;                    // first 64-block of the slice
+  for (int p = tid; p < nblk * 8; p += nthr) {
+    const int bl = p >> 3, c = 8 * (p & 7);
+    const bool real = bs + bl < a.G;
+    const v4u lv = *reinterpret_cast<const v4u *>(a.lam + (size_t)min(bs + bl, a.G - 1) * kGroup + c);
     float f[8];
 #pragma unroll
     for (int h = 0; h < 4; ++h) {
       f[2 * h] = real ? 1.0f / f16_to_f32((uint16_t)(lv[h] & 0xFFFFu)) : 0.0f;
       f[2 * h + 1] = real ? 1.0f / f16_to_f32((uint16_t)(lv[h] >> 16)) : 0.0f;
     }
-    v4f *dst = reinterpret_cast<v4f *>(ilam + (gl * 4 + (c >> 4)) * kLamKq + (c & 15));
+    v4f *dst = reinterpret_cast<v4f *>(ilam + (bl * 4 + (c >> 4)) * kLamKq + (c & 15));
     dst[0] = (v4f){f[0], f[1], f[2], f[3]};
     dst[1] = (v4f){f[4], f[5], f[6], f[7]};
   }
@@ -128,9 +141,9 @@ __global__ __launch_bounds__(1024) void k_quant_tiles(QuantArgs a, int gpb) {
     if ((a.r & 3) == 0) {
       // four columns of one projection per item (cb and c0 are multiples of 4)
       constexpr int Q = NR / 4;
-      for (int p = tid; p < ngb * kGroup * Q; p += nthr) {
-        const int q4 = p % Q, chl = p / Q, gl = chl >> 6, c = chl & 63;
-        const int gg = gs + gl, jj = 4 * q4;
+      for (int p = tid; p < nblk * kGroup * Q; p += nthr) {
+        const int q4 = p % Q, chl = p / Q, bl = chl >> 6, c = chl & 63;
+        const int gg = bs + bl, jj = 4 * q4;
         v4f v = {0.f, 0.f, 0.f, 0.f};
         if (gg < a.G && jj < a.cb) {
           const int cc = a.c0 + jj, b = cc / a.r, j = cc % a.r;
@@ -138,18 +151,18 @@ __global__ __launch_bounds__(1024) void k_quant_tiles(QuantArgs a, int gpb) {
           v = (v4f){bf16_to_f32(w.x & 0xFFFFu), bf16_to_f32(w.x >> 16), bf16_to_f32(w.y & 0xFFFFu),
                     bf16_to_f32(w.y >> 16)};
         }
-        *reinterpret_cast<v4f *>(l1s + (gl * 4 + (c >> 4)) * kqs(NR) + (c & 15) * NR + jj) = v;
+        *reinterpret_cast<v4f *>(l1s + (bl * 4 + (c >> 4)) * kqs(NR) + (c & 15) * NR + jj) = v;
       }
     } else {
-      for (int p = tid; p < ngb * kGroup * NR; p += nthr) {
-        const int jj = p % NR, chl = p / NR, gl = chl >> 6, c = chl & 63;
-        const int gg = gs + gl;
+      for (int p = tid; p < nblk * kGroup * NR; p += nthr) {
+        const int jj = p % NR, chl = p / NR, bl = chl >> 6, c = chl & 63;
+        const int gg = bs + bl;
         float v = 0.0f;
         if (gg < a.G && jj < a.cb) {
           const int cc = a.c0 + jj, b = cc / a.r, j = cc % a.r;
           v = bf16_to_f32(a.L1[((size_t)b * a.K + (size_t)gg * kGroup + c) * a.r + j]);
         }
-        l1s[(gl * 4 + (c >> 4)) * kqs(NR) + (c & 15) * NR + jj] = v;
+        l1s[(bl * 4 + (c >> 4)) * kqs(NR) + (c & 15) * NR + jj] = v;
       }
     }
   }
@@ -160,35 +173,40 @@ __global__ __launch_bounds__(1024) void k_quant_tiles(QuantArgs a, int gpb) {
   for (int j = 0; j < (NR > 0 ? NR : 1); ++j) u[j] = 0.0f;
 
   for (; g < ge; g += W) {
-    // next group of this wave in flight (past the slice: a clamped, unused
+    // next unit of this wave in flight (past the slice: a clamped, unused
     // load, so that the code stays straight-line and the waits exact)
-    v4u n0, n1;
-    load_x(min(g + W, ge - 1), n0, n1);
+    v4u nx[2 * BPG];
+    load_x(min(g + W, ge - 1), nx);
     const int gl = g - gs;
-    const v4f *il = reinterpret_cast<const v4f *>(ilam + (gl * 4 + kq) * kLamKq);
-    const v4f l0 = il[0], l1 = il[1], l2 = il[2], l3 = il[3];
-    float xh[16];
-    xh[0] = bf16_to_f32(x0.x & 0xFFFFu) * l0.x;
-    xh[1] = bf16_to_f32(x0.x >> 16) * l0.y;
-    xh[2] = bf16_to_f32(x0.y & 0xFFFFu) * l0.z;
-    xh[3] = bf16_to_f32(x0.y >> 16) * l0.w;
-    xh[4] = bf16_to_f32(x0.z & 0xFFFFu) * l1.x;
-    xh[5] = bf16_to_f32(x0.z >> 16) * l1.y;
-    xh[6] = bf16_to_f32(x0.w & 0xFFFFu) * l1.z;
-    xh[7] = bf16_to_f32(x0.w >> 16) * l1.w;
-    xh[8] = bf16_to_f32(x1.x & 0xFFFFu) * l2.x;
-    xh[9] = bf16_to_f32(x1.x >> 16) * l2.y;
-    xh[10] = bf16_to_f32(x1.y & 0xFFFFu) * l2.z;
-    xh[11] = bf16_to_f32(x1.y >> 16) * l2.w;
-    xh[12] = bf16_to_f32(x1.z & 0xFFFFu) * l3.x;
-    xh[13] = bf16_to_f32(x1.z >> 16) * l3.y;
-    xh[14] = bf16_to_f32(x1.w & 0xFFFFu) * l3.z;
-    xh[15] = bf16_to_f32(x1.w >> 16) * l3.w;
+    float xh[16 * BPG];
+#pragma unroll
+    for (int b = 0; b < BPG; ++b) {
+      const v4f *il = reinterpret_cast<const v4f *>(ilam + ((gl * BPG + b) * 4 + kq) * kLamKq);
+      const v4f l0 = il[0], l1 = il[1], l2 = il[2], l3 = il[3];
+      const v4u x0 = x[2 * b], x1 = x[2 * b + 1];
+      float *h = xh + 16 * b;
+      h[0] = bf16_to_f32(x0.x & 0xFFFFu) * l0.x;
+      h[1] = bf16_to_f32(x0.x >> 16) * l0.y;
+      h[2] = bf16_to_f32(x0.y & 0xFFFFu) * l0.z;
+      h[3] = bf16_to_f32(x0.y >> 16) * l0.w;
+      h[4] = bf16_to_f32(x0.z & 0xFFFFu) * l1.x;
+      h[5] = bf16_to_f32(x0.z >> 16) * l1.y;
+      h[6] = bf16_to_f32(x0.w & 0xFFFFu) * l1.z;
+      h[7] = bf16_to_f32(x0.w >> 16) * l1.w;
+      h[8] = bf16_to_f32(x1.x & 0xFFFFu) * l2.x;
+      h[9] = bf16_to_f32(x1.x >> 16) * l2.y;
+      h[10] = bf16_to_f32(x1.y & 0xFFFFu) * l2.z;
+      h[11] = bf16_to_f32(x1.y >> 16) * l2.w;
+      h[12] = bf16_to_f32(x1.z & 0xFFFFu) * l3.x;
+      h[13] = bf16_to_f32(x1.z >> 16) * l3.y;
+      h[14] = bf16_to_f32(x1.w & 0xFFFFu) * l3.z;
+      h[15] = bf16_to_f32(x1.w >> 16) * l3.w;
+    }
 
     if constexpr (CODES) {
       float amax = 0.0f;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(xh[i]));
+      for (int i = 0; i < 16 * BPG; ++i) amax = fmaxf(amax, fabsf(xh[i]));
       amax = fmaxf(amax, __shfl_xor(amax, 16));
       amax = fmaxf(amax, __shfl_xor(amax, 32));
       uint16_t s16 = 0;
@@ -203,39 +221,45 @@ __global__ __launch_bounds__(1024) void k_quant_tiles(QuantArgs a, int gpb) {
       // the clamp works on those bits (a quotient beyond +-2^22 lands outside
       // the clamp window on the right side).  The low byte of the clamped
       // bits is the two's-complement code.
-      int c[16];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int b = __float_as_int(xh[i] * inv_s + kMagic);
-        c[i] = min(max(b, kMagicBits - 8), kMagicBits + 7);
-      }
-      v4u w;
+      for (int b = 0; b < BPG; ++b) {
+        int c[16];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const uint32_t lo = __builtin_amdgcn_perm((uint32_t)c[4 * j + 1], (uint32_t)c[4 * j], 0x0c0c0400u);
-        const uint32_t hi = __builtin_amdgcn_perm((uint32_t)c[4 * j + 3], (uint32_t)c[4 * j + 2], 0x0c0c0400u);
-        w[j] = __builtin_amdgcn_perm(hi, lo, 0x05040100u);
+        for (int i = 0; i < 16; ++i) {
+          const int v = __float_as_int(xh[16 * b + i] * inv_s + kMagic);
+          c[i] = min(max(v, kMagicBits - 8), kMagicBits + 7);
+        }
+        v4u w;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const uint32_t lo = __builtin_amdgcn_perm((uint32_t)c[4 * j + 1], (uint32_t)c[4 * j], 0x0c0c0400u);
+          const uint32_t hi = __builtin_amdgcn_perm((uint32_t)c[4 * j + 3], (uint32_t)c[4 * j + 2], 0x0c0c0400u);
+          w[j] = __builtin_amdgcn_perm(hi, lo, 0x05040100u);
+        }
+        const size_t blk = (size_t)mt * a.Gp + (size_t)g * BPG + b;
+        *reinterpret_cast<v4u *>(a.qa + blk * 1024 + (size_t)lane * 16) = w;
       }
-      const size_t blk = (size_t)mt * a.Gp + g;
-      *reinterpret_cast<v4u *>(a.qa + blk * 1024 + (size_t)lane * 16) = w;
-      if (kq == 0) a.sxs[blk * 16 + row] = s16;
+      if (kq == 0) a.sxs[((size_t)mt * a.SG + g) * 16 + row] = s16;
     }
 
     if constexpr (NR > 0) {
-      const float *lr = l1s + (gl * 4 + kq) * kqs(NR);
 #pragma unroll
-      for (int i = 0; i < 16; ++i)
+      for (int b = 0; b < BPG; ++b) {
+        const float *lr = l1s + ((gl * BPG + b) * 4 + kq) * kqs(NR);
 #pragma unroll
-        for (int j4 = 0; j4 < NR; j4 += 4) {
-          const v4f l = *reinterpret_cast<const v4f *>(lr + i * NR + j4);
-          u[j4 + 0] = __builtin_fmaf(xh[i], l.x, u[j4 + 0]);
-          u[j4 + 1] = __builtin_fmaf(xh[i], l.y, u[j4 + 1]);
-          u[j4 + 2] = __builtin_fmaf(xh[i], l.z, u[j4 + 2]);
-          u[j4 + 3] = __builtin_fmaf(xh[i], l.w, u[j4 + 3]);
-        }
+        for (int i = 0; i < 16; ++i)
+#pragma unroll
+          for (int j4 = 0; j4 < NR; j4 += 4) {
+            const v4f l = *reinterpret_cast<const v4f *>(lr + i * NR + j4);
+            u[j4 + 0] = __builtin_fmaf(xh[16 * b + i], l.x, u[j4 + 0]);
+            u[j4 + 1] = __builtin_fmaf(xh[16 * b + i], l.y, u[j4 + 1]);
+            u[j4 + 2] = __builtin_fmaf(xh[16 * b + i], l.z, u[j4 + 2]);
+            u[j4 + 3] = __builtin_fmaf(xh[16 * b + i], l.w, u[j4 + 3]);
+          }
+      }
     }
-    x0 = n0;
-    x1 = n1;
+#pragma unroll
+    for (int t = 0; t < 2 * BPG; ++t) x[t] = nx[t];
   }
 
   // ---- U of the slice: shares of (wave, channel block) summed in that
@@ -256,28 +280,42 @@ __global__ __launch_bounds__(1024) void k_quant_tiles(QuantArgs a, int gpb) {
   }
 }
 
-template <int NR>
+template <int NR, int BPG>
 hipError_t launch_pass(const QuantArgs &a, const TilePlan &p, bool codes, hipStream_t s) {
   const dim3 grid((unsigned)(a.Mpad / kTile), (unsigned)p.slices);
   const dim3 block((unsigned)(64 * p.waves));
-  const size_t lds = plan_lds(p.gpb, NR, p.waves);
+  const size_t lds = plan_lds(p.gpb, BPG, NR, p.waves);
   if (codes)
-    hipLaunchKernelGGL((k_quant_tiles<NR, true>), grid, block, lds, s, a, p.gpb);
+    hipLaunchKernelGGL((k_quant_tiles<NR, true, BPG>), grid, block, lds, s, a, p.gpb);
   else
-    hipLaunchKernelGGL((k_quant_tiles<NR, false>), grid, block, lds, s, a, p.gpb);
+    hipLaunchKernelGGL((k_quant_tiles<NR, false, BPG>), grid, block, lds, s, a, p.gpb);
   return hipGetLastError();
+}
+
+template <int BPG>
+hipError_t launch_width(const QuantArgs &a, const TilePlan &p, bool codes, hipStream_t s) {
+  switch (pass_width(a.cb)) {
+    case 0: return launch_pass<0, BPG>(a, p, codes, s);
+    case 4: return launch_pass<4, BPG>(a, p, codes, s);
+    case 8: return launch_pass<8, BPG>(a, p, codes, s);
+    case 12: return launch_pass<12, BPG>(a, p, codes, s);
+    default: return launch_pass<16, BPG>(a, p, codes, s);
+  }
 }
 
 }  // namespace
 
-int quant_slices(int M, int K, int r, int batch) { return tile_plan(M, K, r, batch).slices; }
+int quant_slices(int M, int K, int r, int batch, int group) {
+  return tile_plan(M, K, r, batch, group).slices;
+}
 
 // One launch per pass of up to 16 rank columns; the first also writes codes
 // and scales.  Every pass uses the first pass's grid (same K-slices, so the
 // U partials line up).
 hipError_t launch_quant_tiles(const QuantArgs &a0, hipStream_t s) {
-  const TilePlan p = tile_plan(a0.M, a0.K, a0.r, a0.batch);
-  if (plan_lds(p.gpb, p.nr, p.waves) > 64 * 1024) return hipErrorInvalidValue;
+  const int group = a0.bpg * kGroup;
+  const TilePlan p = tile_plan(a0.M, a0.K, a0.r, a0.batch, group);
+  if (plan_lds(p.gpb, a0.bpg, p.nr, p.waves) > 64 * 1024) return hipErrorInvalidValue;
   const int total = a0.r * a0.batch;
   int c0 = 0;
   do {
@@ -285,14 +323,7 @@ hipError_t launch_quant_tiles(const QuantArgs &a0, hipStream_t s) {
     a.c0 = c0;
     a.cb = total - c0 < kRankPass ? total - c0 : kRankPass;
     const bool codes = c0 == 0;
-    hipError_t e;
-    switch (pass_width(a.cb)) {
-      case 0: e = launch_pass<0>(a, p, codes, s); break;
-      case 4: e = launch_pass<4>(a, p, codes, s); break;
-      case 8: e = launch_pass<8>(a, p, codes, s); break;
-      case 12: e = launch_pass<12>(a, p, codes, s); break;
-      default: e = launch_pass<16>(a, p, codes, s); break;
-    }
+    const hipError_t e = a.bpg == 2 ? launch_width<2>(a, p, codes, s) : launch_width<1>(a, p, codes, s);
     if (e != hipSuccess) return e;
     c0 += kRankPass;
   } while (c0 < total);
