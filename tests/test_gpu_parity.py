@@ -211,6 +211,7 @@ def test_full_size_outputs_sampled_rows(oracle, name, M):
     (130, 4096, 130, 4, 1),   # few tiles, long K: 8 K splits, ragged M and N
     (100, 2240, 200, 4, 3),   # 4 K splits, a pad group, three projections
     (40, 20480, 45, 4, 1),    # long K, odd N: more skinny weight scales than its threads hold
+    (70, 1024, 24000, 4, 1),  # 188 tiles: two K halves per tiled workgroup
 ])
 def test_ragged_shapes_match_oracle(oracle, M, K, N, r, batch):
     lay = make_random_layer(M * 31 + N, M, K, N, r=r, batch=batch, outlier_channels=2)

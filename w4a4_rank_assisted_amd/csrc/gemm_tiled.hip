@@ -35,6 +35,13 @@
 // group pairs, and store their fp32 accumulators as partial tiles in the
 // workspace; a second launch of the same kernel sums the S partials of a
 // tile in split order (deterministic) and runs the epilogue.
+//
+// K halves: with a few hundred tiles or fewer, a workgroup of 16 waves may
+// own a tile instead, as two 8-wave halves over the two halves of its K
+// range, each with its own stage buffers; they share the stage barriers,
+// and half 1 hands its accumulators to half 0 through LDS at the end (a
+// fixed order, no workspace traffic).  tiled_plan picks halves and splits
+// from a cost model fitted to measured times.
 #include "hsq_internal.h"
 
 #include <type_traits>
@@ -84,9 +91,17 @@ struct alignas(16) EpiSmem<0> {
   float bias[BN];
 };
 
-template <int RPT, int BPG>
+// KH = 2: two halves of 8 waves share the tile, each with its own stage
+// buffers and half of the K range; half 1 parks its accumulators at
+// kRedOff (past the output-transpose area of half 0's waves) once the
+// stage loop is over.
+constexpr int kRedOff = WM * WN * 16 * (TN * 16) * 4;   // bytes
+template <int RPT, int BPG, int KH>
 struct alignas(16) Smem {
-  Stages<BPG> st;
+  union {
+    Stages<BPG> st[KH];
+    float red[KH == 2 ? kRedOff / 4 + NTH * TM * TN * 4 : 1];
+  };
   EpiSmem<RPT> ep;
 };
 
@@ -122,15 +137,19 @@ __device__ __forceinline__ void tile_of(int bid, int nblk, int mblk, int &mb, in
   nb = w / gsz;
 }
 
-template <bool DUMP, int RPT, int MODE, int BPG>
-__global__ __launch_bounds__(NTH, 2) void k_gemm_tiled(GemmArgs a, int nblk, int mblk) {
+template <bool DUMP, int RPT, int MODE, int BPG, int KH>
+__global__ __launch_bounds__(NTH * KH, 2) void k_gemm_tiled(GemmArgs a, int nblk, int mblk) {
   static_assert(MODE != kSplit || RPT == 0, "a split pass has no epilogue");
+  static_assert(KH == 1 || (!DUMP && MODE != kReduce), "the K halves serve the stage loop");
   constexpr bool EPI = !DUMP && MODE != kSplit;   // this pass writes Y
-  __shared__ Smem<RPT, BPG> smem;
-  Stages<BPG> &sm = smem.st;
+  __shared__ Smem<RPT, BPG, KH> smem;
 
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = threadIdx.x & 63;
+  const int wave0 = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+  const int half = KH == 1 ? 0 : wave0 / (WM * WN);   // K half of this wave
+  const int tid = (int)threadIdx.x - half * NTH;     // thread index within the half
+  const int wave = wave0 - half * (WM * WN);
+  Stages<BPG> &sm = smem.st[half];
   const int wm = wave / WN, wn = wave % WN;
   const int proj = blockIdx.y;
   int mb, nb;
@@ -153,6 +172,16 @@ __global__ __launch_bounds__(NTH, 2) void k_gemm_tiled(GemmArgs a, int nblk, int
     const int S = (int)gridDim.z, z = (int)blockIdx.z, pairs = nstg / 2;
     g0 = 2 * (z * pairs / S);
     g1 = 2 * ((z + 1) * pairs / S);
+  }
+  // stages with data for this workgroup: [g0, gend); with two K halves,
+  // half h runs [g0 + h*L, g0 + (h+1)*L), L even, so both make the same
+  // number of steps (barriers); stages of half 1 past gend get weight
+  // scale 0 and add exactly 0
+  const int gend = min(g1, a.G);
+  if constexpr (KH == 2) {
+    const int L = ((g1 - g0) / 2 + 1) & ~1;
+    g0 += half * L;
+    g1 = g0 + L;
   }
   // this tile's partial tiles: [proj][tile][split][chunk][thread] float4
   float *part_tile = a.part + (((size_t)proj * nblk * mblk + (size_t)mb * nblk + nb) * a.splits) *
@@ -213,7 +242,7 @@ __global__ __launch_bounds__(NTH, 2) void k_gemm_tiled(GemmArgs a, int nblk, int
       sm.sx[buf][mi][row] = (mt0 + mi < MT) ? (uint16_t)rsx[SL] : (uint16_t)0;
     } else if (!DUMP && tid >= NTH / 2 && tid < NTH / 2 + BN) {
       const int col = tid - NTH / 2, n = nt0 * 16 + col;
-      const float sv = (g < G && n < a.N) ? f16_to_f32((uint16_t)rsw[SL]) : 0.0f;
+      const float sv = (g < gend && n < a.N) ? f16_to_f32((uint16_t)rsw[SL]) : 0.0f;
       sm.sw[buf][col] = make_float2(sv * 0.0625f, -kMagic * 0.0625f * sv);
     }
   };
@@ -235,7 +264,7 @@ __global__ __launch_bounds__(NTH, 2) void k_gemm_tiled(GemmArgs a, int nblk, int
   constexpr int EU = RPT * BM / NTH;  // (rank column, row) pairs per thread
   constexpr int US = RPT <= 8 ? kMaxUSlices : kMaxUSlices / 2;  // U slices prefetched
   float eu[EU > 0 ? EU : 1][US], el2[EU > 0 ? EU : 1], ebias = 0.0f;
-  if (EPI) {
+  if (EPI && half == 0) {
     const uint16_t *L2 = a.L2 + (size_t)proj * a.r * a.N;
 #pragma unroll
     for (int e = 0; e < EU; ++e) {
@@ -258,7 +287,7 @@ __global__ __launch_bounds__(NTH, 2) void k_gemm_tiled(GemmArgs a, int nblk, int
       load_stage(g0 + 3, int_c<3 % kSlots>{});
     }
   }
-  if (EPI) {
+  if (EPI && half == 0) {
 #pragma unroll
     for (int e = 0; e < EU; ++e) {
       const int idx = e * NTH + tid, c = idx / BM, rr = idx % BM;
@@ -423,6 +452,29 @@ __global__ __launch_bounds__(NTH, 2) void k_gemm_tiled(GemmArgs a, int nblk, int
 
   if (DUMP) return;
 
+  if constexpr (KH == 2) {
+    // half 1's accumulators to LDS (the stage loop ended with a barrier, so
+    // the stage buffers are free), added by half 0 in a fixed order
+    float *red = smem.red + kRedOff / 4;
+    if (half == 1) {
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+          *reinterpret_cast<v4f *>(red + ((i * TN + j) * NTH + tid) * 4) =
+              (v4f){acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]};
+    }
+    __syncthreads();
+    if (half == 1) return;            // no barrier follows
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        const v4f v = *reinterpret_cast<const v4f *>(red + ((i * TN + j) * NTH + tid) * 4);
+        acc[i][j][0] += v[0]; acc[i][j][1] += v[1]; acc[i][j][2] += v[2]; acc[i][j][3] += v[3];
+      }
+  }
+
   if constexpr (MODE == kSplit) {
     // this split's partial tile: chunk c = (i, j) as one float4 per thread,
     // 1 KB contiguous per wave and chunk
@@ -523,46 +575,67 @@ __global__ __launch_bounds__(NTH, 2) void k_gemm_tiled(GemmArgs a, int nblk, int
   }
 }
 
-template <int RPT, int MODE, int BPG>
+template <int RPT, int MODE, int BPG, int KH>
 hipError_t launch_rpt(const GemmArgs &a, int batch, int nblk, int mblk, hipStream_t s) {
-  hipLaunchKernelGGL((k_gemm_tiled<false, RPT, MODE, BPG>), dim3((unsigned)(nblk * mblk), (unsigned)batch),
-                     dim3(NTH), 0, s, a, nblk, mblk);
+  hipLaunchKernelGGL((k_gemm_tiled<false, RPT, MODE, BPG, KH>), dim3((unsigned)(nblk * mblk), (unsigned)batch),
+                     dim3(NTH * KH), 0, s, a, nblk, mblk);
   return hipGetLastError();
 }
 
-template <int MODE, int BPG>
+template <int MODE, int BPG, int KH>
 hipError_t launch_epi(const GemmArgs &a, int batch, int nblk, int mblk, hipStream_t s) {
-  if (a.r == 0) return launch_rpt<0, MODE, BPG>(a, batch, nblk, mblk, s);
-  if (a.r <= 4) return launch_rpt<4, MODE, BPG>(a, batch, nblk, mblk, s);
-  if (a.r <= 8) return launch_rpt<8, MODE, BPG>(a, batch, nblk, mblk, s);
-  if (a.r <= 16) return launch_rpt<16, MODE, BPG>(a, batch, nblk, mblk, s);
-  return launch_rpt<32, MODE, BPG>(a, batch, nblk, mblk, s);
+  if (a.r == 0) return launch_rpt<0, MODE, BPG, KH>(a, batch, nblk, mblk, s);
+  if (a.r <= 4) return launch_rpt<4, MODE, BPG, KH>(a, batch, nblk, mblk, s);
+  if (a.r <= 8) return launch_rpt<8, MODE, BPG, KH>(a, batch, nblk, mblk, s);
+  if (a.r <= 16) return launch_rpt<16, MODE, BPG, KH>(a, batch, nblk, mblk, s);
+  return launch_rpt<32, MODE, BPG, KH>(a, batch, nblk, mblk, s);
+}
+
+struct TiledPlan {
+  int splits;   // workgroups per output tile (partial tiles in the workspace when > 1)
+  int kh;       // K halves inside a workgroup (1: 8 waves, 2: 16 waves)
+};
+
+// Plan of the tiled contraction: the (K halves, splits) pair with the
+// least modelled time.  Units: the time a CU running two eight-wave
+// workgroups takes for one tile and one stage pair (about 1 us on the
+// MI355X); each of the two then advances at half that rate.  The other
+// constants are fitted to measured contraction times: one eight-wave
+// workgroup alone on a CU needs 1.4 units per stage pair plus 1.2 for its
+// prologue and epilogue (nothing else hides them); a sixteen-wave
+// workgroup (two K halves, one per CU) needs 1.2 per stage pair, its
+// pairs rounded up to even so the halves match, plus 2.3 (its halves
+// share every barrier, and half 0 alone runs the epilogue).  It therefore
+// pays only where the alternative is a split: each split tile beyond the
+// first writes and reads a 64 KB fp32 partial tile, about 0.03 units at
+// the HBM rate such traffic reaches.  Group 128 keeps eight waves: its
+// block-pair stage needs more registers than sixteen waves per CU leave.
+TiledPlan tiled_plan(int M, int N, int K, int batch, int group) {
+  const long long tiles = (long long)ceil_div(N, BN) * ceil_div(M, BM) * batch;
+  const int pairs = group == kGroup ? padded_groups(K) / 2 : (K / group + 1) / 2;
+  TiledPlan best{1, 1};
+  double best_t = -1.0;
+  for (int kh = 1; kh <= (group == kGroup ? 2 : 1); ++kh)
+    for (int S = 1; S <= kMaxSplits && (S == 1 || S * kMinSplitPairs <= pairs); ++S) {
+      const long long wgs = tiles * S;
+      const double per = (double)ceil_div(pairs, S);
+      double t;
+      if (kh == 1)
+        t = wgs <= kCUs ? 1.4 * per + 1.2 : 2.0 * (double)((wgs + 2 * kCUs - 1) / (2 * kCUs)) * per;
+      else
+        t = (double)((wgs + kCUs - 1) / kCUs) * (1.2 * (double)(2 * ceil_div((int)per, 2)) + 2.3);
+      if (S > 1) t += 0.03 * (double)wgs;
+      if (best_t < 0.0 || t < best_t - 1e-9) {
+        best = {S, kh};
+        best_t = t;
+      }
+    }
+  return best;
 }
 
 }  // namespace
 
-// Split K when the tiles alone leave compute units idle.  Cost of S splits:
-// workgroups per CU (rounded up) x group pairs per workgroup, i.e. the
-// busiest CU's work; the cheapest S wins, and on a tie a larger S only while
-// fewer than two workgroups per CU run (one leaves each SIMD two waves).
-// Each split keeps at least kMinSplitPairs group pairs.
-// Work is counted in stage pairs (two scale groups: two 64-channel blocks
-// for group 64, four for group 128).
-int tiled_splits(int M, int N, int K, int batch, int group) {
-  const long long tiles = (long long)ceil_div(N, BN) * ceil_div(M, BM) * batch;
-  const int pairs = group == kGroup ? padded_groups(K) / 2 : (K / group + 1) / 2;
-  if (tiles >= kCUs) return 1;
-  int best = 1;
-  long long best_cost = -1;
-  for (int S = 1; S <= kMaxSplits && S * kMinSplitPairs <= pairs; ++S) {
-    const long long c = (tiles * S + kCUs - 1) / kCUs * ceil_div(pairs, S);
-    if (best_cost < 0 || c < best_cost || (c == best_cost && tiles * best < 2 * kCUs)) {
-      best = S;
-      best_cost = c;
-    }
-  }
-  return best;
-}
+int tiled_splits(int M, int N, int K, int batch, int group) { return tiled_plan(M, N, K, batch, group).splits; }
 
 size_t tiled_partial_bytes(int M, int N, int K, int batch, int group) {
   const int S = tiled_splits(M, N, K, batch, group);
@@ -570,25 +643,32 @@ size_t tiled_partial_bytes(int M, int N, int K, int batch, int group) {
   return (size_t)S * ceil_div(N, BN) * ceil_div(M, BM) * batch * NTH * kAccPerThread * sizeof(float);
 }
 
+template <int BPG, int KH>
+hipError_t launch_tiled_kh(const GemmArgs &a, int batch, int S, int nblk, int mblk, hipStream_t s) {
+  if (S <= 1) return launch_epi<kFull, BPG, KH>(a, batch, nblk, mblk, s);
+  GemmArgs b = a;
+  b.splits = S;
+  hipLaunchKernelGGL((k_gemm_tiled<false, 0, kSplit, BPG, KH>),
+                     dim3((unsigned)(nblk * mblk), (unsigned)batch, (unsigned)S), dim3(NTH * KH), 0, s, b,
+                     nblk, mblk);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return launch_epi<kReduce, BPG, 1>(b, batch, nblk, mblk, s);
+}
+
 template <int BPG>
 hipError_t launch_tiled_bpg(const GemmArgs &a, int batch, bool dump, hipStream_t s) {
   const int nblk = ceil_div(a.N, BN), mblk = ceil_div(a.M, BM);
   if (dump) {
     // every tile of one projection; blocks outside the window exit at once
-    hipLaunchKernelGGL((k_gemm_tiled<true, 0, kFull, BPG>), dim3((unsigned)(nblk * mblk), 1u), dim3(NTH),
+    hipLaunchKernelGGL((k_gemm_tiled<true, 0, kFull, BPG, 1>), dim3((unsigned)(nblk * mblk), 1u), dim3(NTH),
                        0, s, a, nblk, mblk);
     return hipGetLastError();
   }
-  const int S = tiled_splits(a.M, a.N, a.G * kGroup * BPG, batch, kGroup * BPG);
-  if (S <= 1) return launch_epi<kFull, BPG>(a, batch, nblk, mblk, s);
-  GemmArgs b = a;
-  b.splits = S;
-  hipLaunchKernelGGL((k_gemm_tiled<false, 0, kSplit, BPG>),
-                     dim3((unsigned)(nblk * mblk), (unsigned)batch, (unsigned)S), dim3(NTH), 0, s, b,
-                     nblk, mblk);
-  const hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  return launch_epi<kReduce, BPG>(b, batch, nblk, mblk, s);
+  const TiledPlan p = tiled_plan(a.M, a.N, a.G * kGroup * BPG, batch, kGroup * BPG);
+  if constexpr (BPG == 1)
+    if (p.kh == 2) return launch_tiled_kh<BPG, 2>(a, batch, p.splits, nblk, mblk, s);
+  return launch_tiled_kh<BPG, 1>(a, batch, p.splits, nblk, mblk, s);
 }
 
 hipError_t launch_gemm_tiled(const GemmArgs &a, int batch, bool dump, hipStream_t s) {
