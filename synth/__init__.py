@@ -14,6 +14,7 @@ from .generators import (  # noqa: F401
     f64_to_bf16_bits,
     f64_to_f16_bits,
     layer_spec,
+    make_full_weight,
     make_layer,
     make_random_layer,
 )

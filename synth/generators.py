@@ -25,6 +25,7 @@ Layer dictionaries hold, with ``B`` = number of projections sharing X:
 from __future__ import annotations
 
 import dataclasses
+import zlib
 from typing import Dict, Optional
 
 import numpy as np
@@ -258,3 +259,23 @@ def make_random_layer(seed: int, M: int, K: int, N: int, r: int = 4, batch: int 
     spec = LayerSpec(f"random{seed}", 0, 0, M, K, N, r=r, batch=batch, x_recipe="random", group=group)
     return dict(spec=spec, X=f64_to_bf16_bits(x), lam=lam, qw=qw, sw=sw, L1=L1, L2=L2, bias=bias,
                 group=group)
+
+
+def make_full_weight(layer: dict, b: int = 0, noise: float = 1.0) -> np.ndarray:
+    """A full-precision (smoothed) weight for projection `b` of `layer`, the
+    input of the calibration steps: bf16 bits, shape (K, N), drawn as
+    qw * sw + L1 * L2 + e with e uniform in [-noise/2, noise/2] * sw of its
+    group, i.e. a weight whose residual codes round it within `noise` steps
+    and whose low-rank factor is the layer's own.  A sampling recipe only:
+    the calibration arithmetic itself is not done here."""
+    spec = layer["spec"]
+    K, N = layer["qw"].shape[1:]
+    group = layer["group"]
+    rng = np.random.default_rng(np.random.SeedSequence(
+        [ROOT_SEED, 3000 + spec.cfg, spec.layer, K, N, b, zlib.crc32(spec.name.encode())]))
+    swf = np.repeat(f16_bits_to_f32(layer["sw"][b]).astype(np.float64), group, axis=0)   # (K, N)
+    base = layer["qw"][b].astype(np.float64) * swf
+    low = bf16_bits_to_f32(layer["L1"][b]).astype(np.float64) @ bf16_bits_to_f32(layer["L2"][b]).astype(np.float64)
+    e = rng.uniform(-0.5, 0.5, (K, N)) * noise * swf
+    return f64_to_bf16_bits(base + low + e)
+
