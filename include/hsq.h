@@ -218,6 +218,68 @@ int hsq_w4a4_group_partials_g(const uint16_t *X, int M, int K, int N, int group,
                               int n0, int nc, int32_t *P, void *workspace, size_t ws_bytes,
                               int kernel, void *stream);
 
+/* ---- calibration: the Hessian, its deflation, the closed-form L2 ----
+ * The steps that produce a layer's factors (Deflating the Hessian, paper
+ * page: abstract and Figure 1 caption; H-SVDQuant explainer, rit.work,
+ * section on Hessian deflation).  The pages give no formulas; these follow
+ * the plainest reading (the activation-noise surrogate term is left out):
+ *
+ *   H      = Xh^T Xh                     Xh[m,k] = X[m,k] * fl32(1/lambda[k]) (as above)
+ *   C      = L1^T H L1                   r x r
+ *   Hperp  = H - (H L1) C^-1 (H L1)^T     deflated Hessian: Hperp L1 = 0
+ *   E      = W - deq(Q(R))               deq(Q(R))[k,n] = code[k,n] * sw[k/group, n]
+ *   L2*    = C^-1 (H L1)^T E             the output-side factor minimising
+ *                                        || Xh E - Xh L1 L2 ||_F
+ *
+ * Sizes: K a multiple of 64 with 64 <= K <= 16384 (HSQ_E_SHAPE / _INVAL),
+ * 1 <= r <= 32.  H, Hperp are K x K fp32 row-major.  Pointers are device
+ * pointers, 16-byte aligned; buffers are the caller's.  All arithmetic is
+ * fp32 except C and its inverse (fp64); results are deterministic. */
+
+/* Workspace of hsq_hessian_accumulate (0: none needed; also 0 for invalid
+ * sizes).  Few 128 x 128 blocks of H (small K) split the tokens across
+ * workgroups, whose fp32 partial blocks live here. */
+size_t hsq_hessian_workspace_bytes(int M, int K);
+
+/* H = Xh^T Xh (accumulate = 0) or H += Xh^T Xh (accumulate = 1), over the
+ * M calibration tokens of X (M x K bf16, row-major) with the layer's
+ * smoothing lambda (K fp16).  Both triangles of H are written.  Stream the
+ * calibration set through several calls with accumulate = 1.
+ * M * K < 2^30.  Errors: HSQ_E_INVAL (null pointer, sizes, accumulate not
+ * 0/1), HSQ_E_SHAPE, HSQ_E_ALIGN, HSQ_E_WORKSPACE, HSQ_E_HIP. */
+int hsq_hessian_accumulate(const uint16_t *X, int M, int K, const uint16_t *lambda, float *H,
+                           int accumulate, void *workspace, size_t ws_bytes, void *stream);
+
+/* Workspace of hsq_deflate_hessian (0 for invalid sizes). */
+size_t hsq_deflate_workspace_bytes(int K, int r);
+
+/* Deflates H by span(L1) (L1: K x r bf16, the layer's input-side factor):
+ *   HL1   out: K x r fp32, H L1
+ *   Cinv  out: r x r fp64, (L1^T H L1)^-1 (Gauss-Jordan, partial pivoting;
+ *         a singular C gives NaN)
+ *   Hperp out: K x K fp32; may be H itself (in place), must not otherwise
+ *         overlap it.
+ * Errors: HSQ_E_INVAL, HSQ_E_SHAPE, HSQ_E_ALIGN, HSQ_E_WORKSPACE,
+ * HSQ_E_HIP. */
+int hsq_deflate_hessian(const float *H, int K, const uint16_t *L1, int r, float *Hperp, float *HL1,
+                        double *Cinv, void *workspace, size_t ws_bytes, void *stream);
+
+/* Workspace of hsq_closed_form_l2 (0 for invalid sizes). */
+size_t hsq_closed_form_l2_workspace_bytes(int K, int N, int r);
+
+/* The closed-form output-side factor L2* = Cinv (HL1)^T E (r x N fp32 out)
+ * from the outputs of hsq_deflate_hessian and one projection's weight:
+ *   W        K x N bf16, the full-precision (smoothed) weight
+ *   packed_w the packed residual codes of its quantized residual
+ *            (hsq_pack_weights layout), sw its (K/group) x N fp16 scales
+ *   group    HSQ_GROUP_64 or HSQ_GROUP_128 (must divide K)
+ * E is decoded on the fly and never stored.  K * N < 2^31.
+ * Errors: HSQ_E_INVAL, HSQ_E_SHAPE, HSQ_E_ALIGN, HSQ_E_WORKSPACE,
+ * HSQ_E_HIP. */
+int hsq_closed_form_l2(const float *HL1, const double *Cinv, int K, int N, int r, int group,
+                       const uint16_t *W, const uint8_t *packed_w, const uint16_t *sw, float *L2,
+                       void *workspace, size_t ws_bytes, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

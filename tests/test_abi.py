@@ -195,3 +195,33 @@ def test_group_width_entry_points_validate():
     assert c(64, 256, 256, 1, 32, A, A, A, 4, A, A, hsq.BF16, A, 1 << 30, 0, None) == hsq.E_INVAL
     pg = lib.hsq_w4a4_group_partials_g
     assert pg(A, 64, 256, 256, 128, A, A, 0, 65, 0, 256, A, A, 1 << 30, 0, None) == hsq.E_SHAPE
+
+
+def test_calibration_entry_points_validate():
+    ws = lib.hsq_hessian_workspace_bytes
+    assert ws(4096, 1152) > 0            # 45 blocks of H: token splits with partial blocks
+    assert ws(2048, 4096) == 0           # 528 blocks: none
+    assert ws(10, 100) == 0 and ws(0, 128) == 0
+    h = lib.hsq_hessian_accumulate
+    assert h(None, 64, 128, A, A, 0, None, 0, None) == hsq.E_INVAL
+    assert h(A, 64, 96, A, A, 0, None, 0, None) == hsq.E_SHAPE
+    assert h(A, 64, 32768, A, A, 0, None, 0, None) == hsq.E_INVAL
+    assert h(A, 64, 128, A, A, 2, None, 0, None) == hsq.E_INVAL
+    assert h(A, 64, 128, A, A + 4, 0, None, 0, None) == hsq.E_ALIGN
+    assert h(A, 1 << 17, 1 << 13, A, A, 0, A, 1 << 40, None) == hsq.E_INVAL   # M * K >= 2^30
+    assert h(A, 4096, 1152, A, A, 0, A, 16, None) == hsq.E_WORKSPACE
+    d = lib.hsq_deflate_hessian
+    assert lib.hsq_deflate_workspace_bytes(1024, 4) > 1024 * 4 * 4
+    assert lib.hsq_deflate_workspace_bytes(1024, 0) == 0
+    assert d(A, 128, A, 0, A, A, A, A, 1 << 20, None) == hsq.E_INVAL
+    assert d(A, 128, A, 33, A, A, A, A, 1 << 20, None) == hsq.E_INVAL
+    assert d(A, 96, A, 4, A, A, A, A, 1 << 20, None) == hsq.E_SHAPE
+    assert d(A, 128, A, 4, A, A + 8, A, A, 1 << 20, None) == hsq.E_ALIGN
+    assert d(A, 128, A, 4, A, A, A, A, 16, None) == hsq.E_WORKSPACE
+    l2 = lib.hsq_closed_form_l2
+    assert lib.hsq_closed_form_l2_workspace_bytes(1152, 4608, 4) > 0
+    assert l2(A, A, 256, 64, 4, 96, A, A, A, A, A, 1 << 20, None) == hsq.E_INVAL
+    assert l2(A, A, 192, 64, 4, 128, A, A, A, A, A, 1 << 20, None) == hsq.E_SHAPE
+    assert l2(A, A, 256, 0, 4, 64, A, A, A, A, A, 1 << 20, None) == hsq.E_INVAL
+    assert l2(A, A, 256, 64, 4, 64, None, A, A, A, A, 1 << 20, None) == hsq.E_INVAL
+    assert l2(A, A, 256, 64, 4, 64, A, A, A, A, A, 0, None) == hsq.E_WORKSPACE

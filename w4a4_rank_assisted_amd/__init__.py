@@ -70,6 +70,12 @@ def _load():
             "hsq_w4a4_quantize_stage_g": ([P, I, I, I, I, I, P, P, I, P, S, P], I),
             "hsq_w4a4_contract_stage_g": ([I, I, I, I, I, P, P, P, I, P, P, I, P, S, I, P], I),
             "hsq_w4a4_group_partials_g": ([P, I, I, I, I, P, P, I, I, I, I, P, P, S, I, P], I),
+            "hsq_hessian_workspace_bytes": ([I, I], S),
+            "hsq_hessian_accumulate": ([P, I, I, P, P, I, P, S, P], I),
+            "hsq_deflate_workspace_bytes": ([I, I], S),
+            "hsq_deflate_hessian": ([P, I, P, I, P, P, P, P, S, P], I),
+            "hsq_closed_form_l2_workspace_bytes": ([I, I, I], S),
+            "hsq_closed_form_l2": ([P, P, I, I, I, I, P, P, P, P, P, S, P], I),
         }
         for name, (args, res) in sig.items():
             fn = getattr(lib, name)
@@ -304,3 +310,76 @@ class Layer:
         return w4a4_lowrank_linear(X, self.lam, self.packed, self.sw, self.L1, self.L2, self.bias,
                                    N=self.N, batch=self.batch, y_dtype=y_dtype, out=out,
                                    workspace=ws, kernel=kernel, group=self.group)
+
+
+# ------------------------------------------------------------- calibration
+def _workspace(nbytes: int, device):
+    torch = _torch()
+    return torch.empty(max(int(nbytes), 16), dtype=torch.uint8, device=device)
+
+
+def hessian_accumulate(X, lam, H=None, accumulate: bool = False, workspace=None):
+    """H = Xh^T Xh (or H += it): X (M, K) bf16, lam (K,) fp16 -> H (K, K) fp32."""
+    torch = _torch()
+    lib = _load()
+    _dev_tensor(X, "X", _half_types())
+    M, K = X.shape
+    _dev_tensor(lam, "lambda", _half_types(), (K,))
+    if H is None:
+        H = torch.empty((K, K), dtype=torch.float32, device=X.device)
+    _dev_tensor(H, "H", (torch.float32,), (K, K))
+    need = int(lib.hsq_hessian_workspace_bytes(M, K))
+    if workspace is None:
+        workspace = _workspace(need, X.device)
+    _check(lib.hsq_hessian_accumulate(_ptr(X), M, K, _ptr(lam), _ptr(H), int(bool(accumulate)),
+                                      _ptr(workspace), workspace.numel(), _stream()),
+           "hsq_hessian_accumulate")
+    return H
+
+
+def deflate_hessian(H, L1, Hperp=None, workspace=None):
+    """Deflation of H (K, K) fp32 by span(L1), L1 (K, r) bf16 ->
+    (Hperp (K, K) fp32, HL1 (K, r) fp32, Cinv (r, r) fp64).  Pass Hperp=H
+    to deflate in place."""
+    torch = _torch()
+    lib = _load()
+    K = H.shape[0]
+    _dev_tensor(H, "H", (torch.float32,), (K, K))
+    r = int(L1.shape[1])
+    _dev_tensor(L1, "L1", _half_types(), (K, r))
+    if Hperp is None:
+        Hperp = torch.empty_like(H)
+    _dev_tensor(Hperp, "Hperp", (torch.float32,), (K, K))
+    HL1 = torch.empty((K, r), dtype=torch.float32, device=H.device)
+    Cinv = torch.empty((r, r), dtype=torch.float64, device=H.device)
+    if workspace is None:
+        workspace = _workspace(lib.hsq_deflate_workspace_bytes(K, r), H.device)
+    _check(lib.hsq_deflate_hessian(_ptr(H), K, _ptr(L1), r, _ptr(Hperp), _ptr(HL1), _ptr(Cinv),
+                                   _ptr(workspace), workspace.numel(), _stream()),
+           "hsq_deflate_hessian")
+    return Hperp, HL1, Cinv
+
+
+def closed_form_l2(HL1, Cinv, W, packed_w, sw, group: int = 64, out=None, workspace=None):
+    """L2* (r, N) fp32 from HL1 (K, r), Cinv (r, r) fp64, W (K, N) bf16 and the
+    packed residual (codes + sw (K/group, N) fp16) of the same projection."""
+    torch = _torch()
+    lib = _load()
+    K, r = HL1.shape
+    _dev_tensor(HL1, "HL1", (torch.float32,), (K, r))
+    _dev_tensor(Cinv, "Cinv", (torch.float64,), (r, r))
+    _dev_tensor(W, "W", _half_types())
+    N = int(W.shape[1])
+    _dev_tensor(W, "W", _half_types(), (K, N))
+    _dev_tensor(packed_w, "packed_w", (torch.uint8,), (lib.hsq_packed_weight_bytes(K, N),))
+    _dev_tensor(sw, "sw", _half_types(), (K // group, N))
+    if out is None:
+        out = torch.empty((r, N), dtype=torch.float32, device=W.device)
+    _dev_tensor(out, "L2", (torch.float32,), (r, N))
+    if workspace is None:
+        workspace = _workspace(lib.hsq_closed_form_l2_workspace_bytes(K, N, r), W.device)
+    _check(lib.hsq_closed_form_l2(_ptr(HL1), _ptr(Cinv), K, N, r, group, _ptr(W), _ptr(packed_w),
+                                  _ptr(sw), _ptr(out), _ptr(workspace), workspace.numel(), _stream()),
+           "hsq_closed_form_l2")
+    return out
+

@@ -62,6 +62,17 @@ int hip_status(hipError_t e) {
 
 bool group_ok(int group) { return group == 64 || group == 128; }
 
+// Calibration sizes: K a positive multiple of 64 up to kCalibMaxK (H is
+// K x K fp32, up to 1 GiB); the Hessian's token x channel count below 2^30.
+constexpr int kCalibMaxK = 16384;
+constexpr long long kCalibMaxMK = 1LL << 30;
+
+int calib_sizes(int K) {
+  if (K < kGroup || K > kCalibMaxK) return HSQ_E_INVAL;
+  if (K % kGroup != 0) return HSQ_E_SHAPE;
+  return HSQ_OK;
+}
+
 size_t workspace_bytes(int M, int K, int N, int r, int batch, int group) {
   if (check_sizes(M, K, N, r, batch) != HSQ_OK || !group_ok(group) || K % group != 0) return 0;
   return plan_workspace(M, K, N, r, batch, group).total;
@@ -330,6 +341,76 @@ int hsq_w4a4_group_partials_g(const uint16_t *X, int M, int K, int N, int group,
                               int kernel, void *stream) {
   return group_partials_g(X, M, K, N, group, lambda, packed_w, m0, mc, n0, nc, P, workspace,
                           ws_bytes, kernel, stream);
+}
+
+// ---------------------------------------------------------------- calibration
+
+size_t hsq_hessian_workspace_bytes(int M, int K) {
+  if (calib_sizes(K) != HSQ_OK || M < 1 || (long long)M * K >= kCalibMaxMK) return 0;
+  return hessian_workspace_bytes(M, K);
+}
+
+int hsq_hessian_accumulate(const uint16_t *X, int M, int K, const uint16_t *lambda, float *H,
+                           int accumulate, void *workspace, size_t ws_bytes, void *stream) {
+  int st = calib_sizes(K);
+  if (st != HSQ_OK) return st;
+  if (M < 1 || (long long)M * K >= kCalibMaxMK || (accumulate != 0 && accumulate != 1)) return HSQ_E_INVAL;
+  if (!X || !lambda || !H) return HSQ_E_INVAL;
+  const void *ptrs[] = {X, lambda, H, workspace};
+  for (const void *p : ptrs)
+    if (p && !aligned16(p)) return HSQ_E_ALIGN;
+  const size_t need = hessian_workspace_bytes(M, K);
+  if (need > 0 && (!workspace || ws_bytes < need)) return HSQ_E_WORKSPACE;
+  HessArgs a{};
+  a.X = X; a.lam = lambda; a.H = H; a.M = M; a.K = K; a.accumulate = accumulate;
+  a.part = (float *)workspace;
+  return hip_status(launch_hessian(a, (hipStream_t)stream));
+}
+
+size_t hsq_deflate_workspace_bytes(int K, int r) {
+  if (calib_sizes(K) != HSQ_OK || r < 1 || r > kMaxRank) return 0;
+  return deflate_workspace_bytes(K, r);
+}
+
+int hsq_deflate_hessian(const float *H, int K, const uint16_t *L1, int r, float *Hperp, float *HL1,
+                        double *Cinv, void *workspace, size_t ws_bytes, void *stream) {
+  int st = calib_sizes(K);
+  if (st != HSQ_OK) return st;
+  if (r < 1 || r > kMaxRank || !H || !L1 || !Hperp || !HL1 || !Cinv || !workspace) return HSQ_E_INVAL;
+  const void *ptrs[] = {H, L1, Hperp, HL1, Cinv, workspace};
+  for (const void *p : ptrs)
+    if (!aligned16(p)) return HSQ_E_ALIGN;
+  if (ws_bytes < deflate_workspace_bytes(K, r)) return HSQ_E_WORKSPACE;
+  DeflArgs a{};
+  a.H = H; a.Hperp = Hperp; a.L1 = L1; a.HL1 = HL1; a.Cinv = Cinv; a.K = K; a.r = r;
+  a.L1f = (float *)workspace;
+  a.Cpart = (double *)((char *)workspace + align_up((size_t)K * rank_pad(r) * sizeof(float), 256));
+  return hip_status(launch_deflate(a, (hipStream_t)stream));
+}
+
+size_t hsq_closed_form_l2_workspace_bytes(int K, int N, int r) {
+  if (calib_sizes(K) != HSQ_OK || r < 1 || r > kMaxRank || N < 1 || (long long)K * N >= INT_MAX) return 0;
+  return l2_workspace_bytes(K, N, r);
+}
+
+int hsq_closed_form_l2(const float *HL1, const double *Cinv, int K, int N, int r, int group,
+                       const uint16_t *W, const uint8_t *packed_w, const uint16_t *sw, float *L2,
+                       void *workspace, size_t ws_bytes, void *stream) {
+  int st = calib_sizes(K);
+  if (st != HSQ_OK) return st;
+  if (!group_ok(group)) return HSQ_E_INVAL;
+  if (K % group != 0) return HSQ_E_SHAPE;
+  if (r < 1 || r > kMaxRank || N < 1 || (long long)K * N >= INT_MAX) return HSQ_E_INVAL;
+  if (!HL1 || !Cinv || !W || !packed_w || !sw || !L2 || !workspace) return HSQ_E_INVAL;
+  const void *ptrs[] = {HL1, Cinv, W, packed_w, sw, L2, workspace};
+  for (const void *p : ptrs)
+    if (!aligned16(p)) return HSQ_E_ALIGN;
+  if (ws_bytes < l2_workspace_bytes(K, N, r)) return HSQ_E_WORKSPACE;
+  L2Args a{};
+  a.HL1 = HL1; a.Cinv = Cinv; a.W = W; a.packed = packed_w; a.sw = sw; a.L2 = L2;
+  a.Tpart = (float *)workspace;
+  a.K = K; a.N = N; a.r = r; a.group = group;
+  return hip_status(launch_l2(a, (hipStream_t)stream));
 }
 
 }  // extern "C"

@@ -140,6 +140,52 @@ int tiled_splits(int M, int N, int K, int batch, int group);
 size_t tiled_partial_bytes(int M, int N, int K, int batch, int group);
 hipError_t launch_gemm_skinny(const GemmArgs &a, int batch, bool dump, hipStream_t s);
 
+// ---------------------------------------------------------------------------
+// Calibration (calib.hip)
+// ---------------------------------------------------------------------------
+struct HessArgs {
+  const uint16_t *X;       // M x K bf16 calibration activations (row-major)
+  const uint16_t *lam;     // K fp16 smoothing factors
+  float *H;                // K x K fp32
+  int M, K;
+  int accumulate;          // 0: H = Xh^T Xh; 1: H += Xh^T Xh
+  float *part;             // token-split partial blocks (workspace)
+  int splits;
+};
+
+struct DeflArgs {
+  const float *H;          // K x K fp32
+  float *Hperp;            // K x K fp32 (may equal H)
+  const uint16_t *L1;      // K x r bf16
+  float *HL1;              // K x r fp32 (output)
+  double *Cinv;            // r x r fp64 (output)
+  float *L1f;              // workspace: K x RP fp32, L1 padded to the rank template
+  double *Cpart;           // workspace: per-workgroup shares of C
+  int K, r;
+};
+
+struct L2Args {
+  const float *HL1;        // K x r fp32
+  const double *Cinv;      // r x r fp64
+  const uint16_t *W;       // K x N bf16 full-precision (smoothed) weight
+  const uint8_t *packed;   // packed residual codes of W's quantized residual
+  const uint16_t *sw;      // (K / group) x N fp16 residual scales
+  float *L2;               // r x N fp32 (output)
+  float *Tpart;            // workspace: slices x r x N fp32
+  int K, N, r, group;
+};
+
+int rank_pad(int r);
+int hessian_splits(int M, int K);
+size_t hessian_workspace_bytes(int M, int K);
+hipError_t launch_hessian(const HessArgs &a, hipStream_t s);
+int deflate_hl1_wgs(int K);
+size_t deflate_workspace_bytes(int K, int r);
+hipError_t launch_deflate(const DeflArgs &a, hipStream_t s);
+int l2_slices(int K, int N, int r);
+size_t l2_workspace_bytes(int K, int N, int r);
+hipError_t launch_l2(const L2Args &a, hipStream_t s);
+
 }  // namespace hsq
 
 // ---------------------------------------------------------------------------
