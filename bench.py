@@ -31,6 +31,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "effective TOPS of fused W4A4+rank-4 linear; % of int8 MFMA / HBM roofline"
 PEAK_INT8_TOPS = 5000.0      # MI355X dense int8 MFMA, 5.0 POP/s
+PEAK_BF16_TFLOPS = 2500.0    # MI355X dense bf16 MFMA, 2.5 PFLOP/s
 PEAK_HBM_GBS = 8000.0        # MI355X HBM3E, 8 TB/s
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 KERNEL_SOURCES = {
@@ -219,6 +220,168 @@ def summarize_profiles(args):
     return 0
 
 
+def calib_cpu_baseline(lay, W, seconds: float):
+    """The calibration oracle (NumPy fp64) on the same projection: H, the
+    deflation and the closed-form L2, repeated until `seconds` have passed."""
+    from oracle import calibration as cal
+
+    L1 = cal.bf16_matrix(lay["L1"][0])
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        H = cal.hessian(lay["X"], lay["lam"])
+        cal.deflate(H, L1)
+        E = cal.residual_error(W, lay["qw"][0], lay["sw"][0], lay["group"])
+        cal.closed_form_l2(H, L1, E)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= seconds or reps >= 20:
+            break
+    M, K = lay["X"].shape
+    N = W.shape[1]
+    return {"value": round(el / reps * 1e3, 2), "unit": "ms per calibration step",
+            "cores": os.cpu_count(), "kind": "oracle",
+            "sample": (f"Hessian of {M} tokens x {K} channels, deflation, closed-form L2 of one "
+                       f"{K}x{N} projection, NumPy float64 (threaded BLAS), {reps} repetition(s), "
+                       f"{el:.1f} s")}
+
+
+def calib_main(args):
+    """One calibration step of one projection: H = Xh^T Xh over the layer's
+    tokens, its deflation by span(L1), and the closed-form L2 from the
+    projection's full weight and packed residual.  Each kernel's inputs
+    rotate through copies larger than the 256 MB Infinity Cache where they
+    are HBM-bound.  Prints one JSON line with a roofline per kernel."""
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU; use --gpus 1", file=sys.stderr)
+        return 2
+    import numpy as np
+    import torch
+
+    import w4a4_rank_assisted_amd as hsq
+    from synth import layer_spec, make_full_weight, make_layer
+
+    dev = torch.device("cuda:0")
+    spec = layer_spec(args.layer, args.tokens, args.group)
+    lay = make_layer(args.layer, args.tokens, args.group)
+    W = make_full_weight(lay, 0)
+    M, K, N, r = spec.M, spec.K, spec.N, spec.r
+
+    def d16(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev)
+
+    X, lam, L1 = d16(lay["X"]), d16(lay["lam"]), d16(lay["L1"][0])
+    Wd, sw = d16(W), d16(lay["sw"][0])
+    packed = hsq.pack_weights(torch.from_numpy(lay["qw"][0]).to(dev))[0]
+    hbytes = K * K * 4
+    nh = max(1, math.ceil(args.rotate_mb * 1e6 / (2 * hbytes)))
+    Hs = [torch.empty((K, K), dtype=torch.float32, device=dev) for _ in range(nh)]
+    Hp = [torch.empty((K, K), dtype=torch.float32, device=dev) for _ in range(nh)]
+    wbytes = W.size * 2 + packed.numel()
+    nw = max(1, math.ceil(args.rotate_mb * 1e6 / wbytes))
+    Ws = [(Wd.clone(), packed.clone()) for _ in range(nw)]
+    hws = torch.empty(max(16, hsq._load().hsq_hessian_workspace_bytes(M, K)), dtype=torch.uint8, device=dev)
+    dws = torch.empty(hsq._load().hsq_deflate_workspace_bytes(K, r), dtype=torch.uint8, device=dev)
+    lws = torch.empty(hsq._load().hsq_closed_form_l2_workspace_bytes(K, N, r), dtype=torch.uint8,
+                      device=dev)
+    HL1 = torch.empty((K, r), dtype=torch.float32, device=dev)
+    Cinv = torch.empty((r, r), dtype=torch.float64, device=dev)
+    L2 = torch.empty((r, N), dtype=torch.float32, device=dev)
+    lib = hsq._load()
+
+    def stream():
+        return hsq._stream()
+
+    def hess(i):
+        H = Hs[i % nh]
+        assert lib.hsq_hessian_accumulate(X.data_ptr(), M, K, lam.data_ptr(), H.data_ptr(), 0,
+                                          hws.data_ptr(), hws.numel(), stream()) == 0
+
+    def defl(i):
+        assert lib.hsq_deflate_hessian(Hs[i % nh].data_ptr(), K, L1.data_ptr(), r, Hp[i % nh].data_ptr(),
+                                       HL1.data_ptr(), Cinv.data_ptr(), dws.data_ptr(), dws.numel(),
+                                       stream()) == 0
+
+    def l2(i):
+        w, pk = Ws[i % nw]
+        assert lib.hsq_closed_form_l2(HL1.data_ptr(), Cinv.data_ptr(), K, N, r, args.group, w.data_ptr(),
+                                      pk.data_ptr(), sw.data_ptr(), L2.data_ptr(), lws.data_ptr(),
+                                      lws.numel(), stream()) == 0
+
+    def step(i):
+        hess(i)
+        defl(i)
+        l2(i)
+
+    for i in range(max(args.warmup, nh)):
+        step(i)
+    torch.cuda.synchronize()
+    steps = args.steps
+    cap = torch.cuda.Stream()
+    graphs = {}
+    for name, fn in (("step", step), ("hessian", hess), ("deflate", defl), ("l2", l2)):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(cap):
+            with torch.cuda.graph(g, stream=cap):
+                for i in range(steps):
+                    fn(args.warmup + i)
+        graphs[name] = g
+    torch.cuda.synchronize()
+    for g in graphs.values():
+        g.replay()
+    torch.cuda.synchronize()
+
+    def timed(name):
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        with torch.cuda.stream(cap):
+            t0.record(cap)
+            graphs[name].replay()
+            t1.record(cap)
+        torch.cuda.synchronize()
+        return t0.elapsed_time(t1) / steps
+
+    ms = {k: timed(k) for k in ("step", "hessian", "deflate", "l2")}
+    # algorithmic work: the symmetric product needs M*K*(K+1) flops (one
+    # triangle); the deflation reads H twice (H L1 must be complete before
+    # any entry of Hperp) and writes Hperp; the L2 pass reads the bf16
+    # weight, the packed codes and their scales once
+    hflops = M * K * (K + 1)
+    dbytes = 3 * hbytes + 2 * K * r * 2 + K * r * 4
+    lbytes = K * N * 2 + K * N // 2 + (K // args.group) * N * 2 + K * r * 4 + r * N * 4
+    roofs = {
+        "hessian": {"bound": "mfma", "achieved": round(hflops / (ms["hessian"] * 1e-3) / 1e12, 2),
+                    "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "flops_per_launch": hflops},
+        "deflate": {"bound": "hbm", "achieved": round(dbytes / (ms["deflate"] * 1e-3) / 1e9, 1),
+                    "peak": PEAK_HBM_GBS, "unit": "GB/s", "bytes_per_launch": dbytes},
+        "l2": {"bound": "hbm", "achieved": round(lbytes / (ms["l2"] * 1e-3) / 1e9, 1),
+               "peak": PEAK_HBM_GBS, "unit": "GB/s", "bytes_per_launch": lbytes},
+    }
+    for k, v in roofs.items():
+        v["frac"] = round(v["achieved"] / v["peak"], 4)
+        v["ms"] = round(ms[k], 5)
+        v["traffic"] = None
+    dom = max(roofs, key=lambda k: ms[k])
+    out = {
+        "metric": "calibration step (Hessian + deflation + closed-form L2) per projection",
+        "value": round(ms["step"], 5), "unit": "ms", "n_gpus": 1, "steps": steps,
+        "warmup": args.warmup, "ms_per_step": round(ms["step"], 5), "higher_is_better": False,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16 MFMA / fp32 / fp64",
+        "data": "synthetic",
+        "config": {"workload": f"{spec.name} calibration: {M} tokens, {K} -> {N}, rank {r}",
+                   "M": M, "K": K, "N": N, "rank": r, "group": args.group,
+                   "rotated_H": nh, "rotated_W": nw},
+        "kernels": roofs,
+        "roofline": dict(roofs[dom], kernel=dom),
+        "device": device_info(torch),
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = calib_cpu_baseline(lay, W, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -243,9 +406,14 @@ def main(argv=None):
                          "(see summarize_profiles)")
     ap.add_argument("--write-traffic", action="store_true",
                     help="with --summarize: record the measured HBM bytes in profiles/traffic.json")
+    ap.add_argument("--calib", action="store_true",
+                    help="time the calibration kernels (Hessian, deflation, closed-form L2) on the "
+                         "layer instead of the inference path")
     args = ap.parse_args(argv)
     if args.summarize:
         return summarize_profiles(args)
+    if args.calib:
+        return calib_main(args)
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:

@@ -52,16 +52,49 @@ struct alignas(16) HessSmem {
   uint16_t t[2][2][HB][HLD];       // [buffer][A, B][channel in block][token in stage]
 };
 
-// upper-triangle block index -> (row block, column block), bi <= bj
-__device__ __forceinline__ void tri_block(int t, int nb, int &bi, int &bj) {
-  int i = 0, rowlen = nb;
-  while (t >= rowlen) {
-    t -= rowlen;
-    ++i;
-    --rowlen;
+template <int V>
+struct int_c {
+  static constexpr int value = V;
+};
+
+constexpr int kSuper = 8;          // blocks per side of a super-block
+
+// workgroup id -> (row block, column block), bi <= bj.  Consecutive ids go
+// to different XCDs (id % 8), each with its own L2; regroup them so that
+// XCD x owns a contiguous range of an order that walks the upper triangle
+// in kSuper x kSuper super-blocks (row-major over super-blocks, row-major
+// inside).  The workgroups an XCD runs at once then share a few row and
+// column strips of X per stage instead of touching every strip.
+__device__ __forceinline__ void hess_block(int bid, int nb, int &bi, int &bj) {
+  const int T = nb * (nb + 1) / 2;
+  const int per = T / 8, rem = T % 8, x = bid % 8, loc = bid / 8;
+  int t = x * per + min(x, rem) + loc;
+  const int nsb = (nb + kSuper - 1) / kSuper;
+  for (int I = 0; I < nsb; ++I) {
+    const int rows = min(kSuper, nb - I * kSuper);
+    for (int J = I; J < nsb; ++J) {
+      const int cols = min(kSuper, nb - J * kSuper);
+      const int cnt = I == J ? rows * (rows + 1) / 2 : rows * cols;
+      if (t < cnt) {
+        if (I != J) {
+          bi = I * kSuper + t / cols;
+          bj = J * kSuper + t % cols;
+        } else {
+          int i = 0, len = rows;
+          while (t >= len) {
+            t -= len;
+            ++i;
+            --len;
+          }
+          bi = I * kSuper + i;
+          bj = I * kSuper + i + t;
+        }
+        return;
+      }
+      t -= cnt;
+    }
   }
-  bi = i;
-  bj = i + t;
+  bi = bj = 0;                    // unreachable: bid < T
 }
 
 template <int MODE>
@@ -72,7 +105,7 @@ __global__ __launch_bounds__(HNT, 2) void k_hessian(HessArgs a) {
   const int wr = wave >> 1, wc = wave & 1;
   const int nb = (a.K + HB - 1) / HB;
   int bi, bj;
-  tri_block(blockIdx.x, nb, bi, bj);
+  hess_block(blockIdx.x, nb, bi, bj);
   const bool diag = bi == bj;
   const int I0 = bi * HB, J0 = bj * HB;
   const int nblk = nb * (nb + 1) / 2;
@@ -98,42 +131,38 @@ __global__ __launch_bounds__(HNT, 2) void k_hessian(HessArgs a) {
     const __amdgpu_buffer_rsrc_t rx = buffer_rsrc(a.X, (uint32_t)((size_t)a.M * a.K * 2));
     const uint32_t kBad = 0x80000000u;                // past the buffer: the load returns 0
     const int ca = I0 + 8 * c8, cb = J0 + 8 * c8;
-    v4u ra[4], rb[4];
-    auto load = [&](int s) __attribute__((always_inline)) {
+    // two register slots: a stage's loads are issued two stages before its
+    // tiles are consumed (slot = stage parity, fixed by unrolling by two);
+    // tokens past the split's end load as zeros
+    v4u ra[2][4], rb[2][4];
+    auto load = [&](int s, auto slotc) __attribute__((always_inline)) {
+      constexpr int SL = decltype(slotc)::value;
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         const int m = s * HKC + 4 * r4 + u;
         const bool mok = m < m_end;
         const uint32_t rowoff = (uint32_t)m * (uint32_t)a.K * 2u;
-        ra[u] = __builtin_amdgcn_raw_buffer_load_b128(rx, (mok && ca < a.K) ? rowoff + ca * 2 : kBad, 0, 0);
-        if (!diag)
-          rb[u] = __builtin_amdgcn_raw_buffer_load_b128(rx, (mok && cb < a.K) ? rowoff + cb * 2 : kBad, 0, 0);
+        ra[SL][u] = __builtin_amdgcn_raw_buffer_load_b128(rx, (mok && ca < a.K) ? rowoff + ca * 2 : kBad, 0, 0);
+        rb[SL][u] = __builtin_amdgcn_raw_buffer_load_b128(rx, (mok && cb < a.K) ? rowoff + cb * 2 : kBad, 0, 0);
       }
     };
-    auto store = [&](int buf) __attribute__((always_inline)) {
+    auto store = [&](auto slotc, int buf) __attribute__((always_inline)) {
+      constexpr int SL = decltype(slotc)::value;
 #pragma unroll
       for (int c = 0; c < 8; ++c) {
         const int k = c >> 1;
         const uint32_t sel = (c & 1) ? 0x07060302u : 0x05040100u;
-        const uint32_t lo = __builtin_amdgcn_perm(ra[1][k], ra[0][k], sel);
-        const uint32_t hi = __builtin_amdgcn_perm(ra[3][k], ra[2][k], sel);
+        const uint32_t lo = __builtin_amdgcn_perm(ra[SL][1][k], ra[SL][0][k], sel);
+        const uint32_t hi = __builtin_amdgcn_perm(ra[SL][3][k], ra[SL][2][k], sel);
         *reinterpret_cast<v2u *>(&sm.t[buf][0][8 * c8 + c][4 * r4]) = (v2u){lo, hi};
-        if (!diag) {
-          const uint32_t lo2 = __builtin_amdgcn_perm(rb[1][k], rb[0][k], sel);
-          const uint32_t hi2 = __builtin_amdgcn_perm(rb[3][k], rb[2][k], sel);
-          *reinterpret_cast<v2u *>(&sm.t[buf][1][8 * c8 + c][4 * r4]) = (v2u){lo2, hi2};
-        }
+        const uint32_t lo2 = __builtin_amdgcn_perm(rb[SL][1][k], rb[SL][0][k], sel);
+        const uint32_t hi2 = __builtin_amdgcn_perm(rb[SL][3][k], rb[SL][2][k], sel);
+        *reinterpret_cast<v2u *>(&sm.t[buf][1][8 * c8 + c][4 * r4]) = (v2u){lo2, hi2};
       }
     };
-    const int ob = diag ? 0 : 1;      // operand B's tile
-    if (s0 < s1) {
-      load(s0);
-      store(0);
-    }
-    __syncthreads();
-    for (int s = s0; s < s1; ++s) {
-      const int buf = (s - s0) & 1;
-      if (s + 1 < s1) load(s + 1);
+    // (a diagonal block loads its one strip twice: branch-free loads keep
+    // the compiler's wait counting exact, so every load stays in flight)
+    auto compute = [&](int buf) __attribute__((always_inline)) {
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
         v8bf av[4], bv[4];
@@ -143,7 +172,7 @@ __global__ __launch_bounds__(HNT, 2) void k_hessian(HessArgs a) {
           av[i] = *reinterpret_cast<const v8bf *>(&sm.t[buf][0][64 * wr + 16 * i + (lane & 15)][tk]);
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-          bv[j] = *reinterpret_cast<const v8bf *>(&sm.t[buf][ob][64 * wc + 16 * j + (lane & 15)][tk]);
+          bv[j] = *reinterpret_cast<const v8bf *>(&sm.t[buf][1][64 * wc + 16 * j + (lane & 15)][tk]);
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -153,8 +182,24 @@ __global__ __launch_bounds__(HNT, 2) void k_hessian(HessArgs a) {
             acc[i][j][0] = c4[0]; acc[i][j][1] = c4[1]; acc[i][j][2] = c4[2]; acc[i][j][3] = c4[3];
           }
       }
-      if (s + 1 < s1) store(buf ^ 1);
+    };
+    if (s0 < s1) {
+      load(s0, int_c<0>{});
+      load(s0 + 1, int_c<1>{});
+      store(int_c<0>{}, 0);
+    }
+    __syncthreads();
+    for (int s = s0; s < s1; s += 2) {
+      load(s + 2, int_c<0>{});
+      compute(0);
+      if (s + 1 < s1) store(int_c<1>{}, 1);
       __syncthreads();
+      if (s + 1 < s1) {
+        load(s + 3, int_c<1>{});
+        compute(1);
+        if (s + 2 < s1) store(int_c<0>{}, 0);
+        __syncthreads();
+      }
     }
   }
 
@@ -257,7 +302,7 @@ namespace {
 // ---------------------------------------------------------------- deflation
 constexpr int DNT = 256;           // threads of the deflation kernels
 constexpr int kHl1Waves = DNT / 64;
-constexpr int kHl1MaxWgs = 256;
+constexpr int kHl1MaxWgs = 1024;
 constexpr int kDefRows = 16;       // rows of H per deflation workgroup
 constexpr int kDefCols = 4 * DNT;  // columns per deflation workgroup
 
@@ -339,7 +384,7 @@ __global__ __launch_bounds__(DNT) void k_hl1(DeflArgs a) {
     double v = 0.0;
 #pragma unroll
     for (int w = 0; w < kHl1Waves; ++w) v += cs[w][p];
-    a.Cpart[(size_t)blockIdx.x * RP * RP + p] = v;
+    a.Cpart[(size_t)p * gridDim.x + blockIdx.x] = v;   // entry-major: the sum reads rows
   }
 }
 
@@ -351,14 +396,18 @@ __global__ __launch_bounds__(DNT) void k_cinv(DeflArgs a, int nparts) {
   __shared__ double m[RP][2 * RP];
   __shared__ double f[RP];
   __shared__ int piv;
-  const int tid = threadIdx.x, r = a.r;
-  for (int p = tid; p < RP * RP; p += DNT) {
-    const int i = p / RP, j = p % RP;
+  const int tid = threadIdx.x, r = a.r, lane = tid & 63, wave = tid >> 6;
+  // entry p of C by wave p % 4: lane l adds shares l, l + 64, ... in order,
+  // then a butterfly over the lanes (the same order in every lane)
+  for (int p = wave; p < RP * RP; p += DNT / 64) {
     double v = 0.0;
-    for (int w = 0; w < nparts; ++w) v += a.Cpart[(size_t)w * RP * RP + p];
-    m[i][j] = v;
-    m[i][RP + j] = i == j ? 1.0 : 0.0;
+#pragma unroll 16
+    for (int w = lane; w < nparts; w += 64) v += a.Cpart[(size_t)p * nparts + w];
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+    if (lane == 0) m[p / RP][p % RP] = v;
   }
+  for (int p = tid; p < RP * RP; p += DNT) m[p / RP][RP + p % RP] = (p / RP == p % RP) ? 1.0 : 0.0;
   __syncthreads();
   for (int c = 0; c < r; ++c) {
     if (tid == 0) {
@@ -484,27 +533,28 @@ __global__ __launch_bounds__(LNT) void k_l2_part(L2Args a) {
     if (c < a.r) a.Tpart[((size_t)z * a.r + c) * a.N + n] = t[c];
 }
 
-// L2[c][n] = sum_b C^-1[c][b] * sum_s T_s[b][n] (slices in order, fp64)
+// L2[c][n] = sum_b C^-1[c][b] * sum_s T_s[b][n] (slices in order, fp64).
+// Thread (column, rank row b) sums T_s[b][n] over the slices; the
+// workgroup's columns then meet in LDS for the r x r product.
 template <int RP>
 __global__ __launch_bounds__(LNT) void k_l2_final(L2Args a, int S) {
-  const int n = blockIdx.x * LNT + threadIdx.x;
-  if (n >= a.N) return;
-  double tb[RP];
-#pragma unroll
-  for (int b = 0; b < RP; ++b) {
-    double v = 0.0;
-    if (b < a.r)
-      for (int z = 0; z < S; ++z) v += (double)a.Tpart[((size_t)z * a.r + b) * a.N + n];
-    tb[b] = v;
+  constexpr int CPW = LNT / RP;                   // columns per workgroup
+  __shared__ double tb[RP][CPW];
+  const int b = threadIdx.x / CPW, cl = threadIdx.x % CPW;
+  const int n = blockIdx.x * CPW + cl;
+  double v = 0.0;
+  if (b < a.r && n < a.N) {
+    const float *src = a.Tpart + (size_t)b * a.N + n;
+#pragma unroll 8
+    for (int z = 0; z < S; ++z) v += (double)src[(size_t)z * a.r * a.N];
   }
-#pragma unroll
-  for (int c = 0; c < RP; ++c) {
-    if (c >= a.r) break;
-    double v = 0.0;
-#pragma unroll
-    for (int b = 0; b < RP; ++b)
-      if (b < a.r) v += a.Cinv[c * a.r + b] * tb[b];
-    a.L2[(size_t)c * a.N + n] = (float)v;
+  tb[b][cl] = v;
+  __syncthreads();
+  const int c = b;
+  if (c < a.r && n < a.N) {
+    double y = 0.0;
+    for (int k = 0; k < a.r; ++k) y += a.Cinv[c * a.r + k] * tb[k][cl];
+    a.L2[(size_t)c * a.N + n] = (float)y;
   }
 }
 
@@ -533,7 +583,7 @@ hipError_t launch_l2_rp(const L2Args &a, hipStream_t s) {
                      (size_t)maxk * RP * sizeof(float), s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_l2_final<RP>, dim3((unsigned)ceil_div(a.N, LNT)), dim3(LNT), 0, s, a, S);
+  hipLaunchKernelGGL(k_l2_final<RP>, dim3((unsigned)ceil_div(a.N, LNT / RP)), dim3(LNT), 0, s, a, S);
   return hipGetLastError();
 }
 
@@ -558,12 +608,13 @@ hipError_t launch_deflate(const DeflArgs &a, hipStream_t s) {
   }
 }
 
-// K slices of the L2 pass: about 512 workgroups, at most one per 64-channel
-// block, and enough that a slice's HL1 rows fit 64 KB of LDS (at most
-// 256 / RP blocks per slice).
+// K slices of the L2 pass: about 2048 workgroups (8 per CU: each thread
+// walks its column's channels one after the other, so the pass needs many
+// waves in flight), at most one per 64-channel block, and enough that a
+// slice's HL1 rows fit 64 KB of LDS (at most 256 / RP blocks per slice).
 int l2_slices(int K, int N, int r) {
   const int cols = ceil_div(N, LNT), blocks = K / kGroup;
-  const int S = std::max(ceil_div(512, cols), ceil_div(blocks * rank_pad(r), 256));
+  const int S = std::max(ceil_div(2048, cols), ceil_div(blocks * rank_pad(r), 256));
   return std::max(1, std::min(S, blocks));
 }
 
