@@ -218,6 +218,45 @@ int hsq_w4a4_group_partials_g(const uint16_t *X, int M, int K, int N, int group,
                               int n0, int nc, int32_t *P, void *workspace, size_t ws_bytes,
                               int kernel, void *stream);
 
+/* ---- fused two-layer chain: Y = down(act(up(X))) ----
+ * Two linears of the kind above (group 64, one projection each, ranks r_up
+ * and r_down) with an elementwise activation between them, as in the MLP
+ * of a diffusion transformer block (FLUX.1: an up-projection of width H,
+ * GELU, a down-projection; 3072 -> 12288 -> 3072 at its model width).  The
+ * up layer's contraction does not write its output:
+ * its epilogue applies the activation in fp32 and forms, from that fp32
+ * value, the down layer's smoothed input, its group-64 scales and int4
+ * codes (the quantizer of the formula block above, applied to
+ * a[m,k] = act(Y_up[m,k]) instead of a bf16 X) and the partial sums of the
+ * down layer's rank branch U_down = (a * fl32(1/lambda_down)) L1_down.
+ * The down layer then runs its contraction on them: the hidden activation
+ * never travels through HBM as a bf16 tensor and the down layer has no
+ * quantization pass.
+ *   act   HSQ_ACT_IDENTITY, or HSQ_ACT_GELU_TANH: the tanh form of GELU,
+ *         0.5 y (1 + tanh(z)), z = 0.7978845608 (y + 0.044715 y^3), computed
+ *         in fp32 as y / (1 + e(-2z)) with e(x) = p(r) * 2^n, n = rint(x *
+ *         1.44269504), r = (x - n * 0.693145751953125) - n *
+ *         1.428606765330187e-6, p the degree-6 Taylor polynomial of exp
+ *         in Horner form, x clamped to [-87, 88], every operation rounded
+ *         once (no fused multiply-add)
+ *   Y          out: M x N, HSQ_F32 or HSQ_BF16
+ *   Y_hidden   optional out (NULL: not written): M x H fp32, the up
+ *              layer's output before the activation (a test export)
+ *   r_down     0 .. 8; the up layer runs the tiled contraction unsplit
+ * All other arguments as for hsq_w4a4_lowrank_linear, per layer.
+ * Errors: HSQ_E_INVAL, HSQ_E_SHAPE (K or H not a multiple of 64),
+ * HSQ_E_ALIGN, HSQ_E_WORKSPACE, HSQ_E_HIP. */
+#define HSQ_ACT_IDENTITY   0
+#define HSQ_ACT_GELU_TANH  1
+size_t hsq_mlp_workspace_bytes(int M, int K, int H, int N, int r_up, int r_down);
+int hsq_w4a4_lowrank_mlp(const uint16_t *X, int M, int K, int H, int N, const uint16_t *lambda_up,
+                         const uint8_t *packed_up, const uint16_t *sw_up, const uint16_t *L1_up,
+                         const uint16_t *L2_up, int r_up, const uint16_t *bias_up, int act,
+                         const uint16_t *lambda_down, const uint8_t *packed_down,
+                         const uint16_t *sw_down, const uint16_t *L1_down, const uint16_t *L2_down,
+                         int r_down, const uint16_t *bias_down, void *Y, int y_dtype, float *Y_hidden,
+                         void *workspace, size_t ws_bytes, void *stream);
+
 /* ---- calibration: the Hessian, its deflation, the closed-form L2 ----
  * The steps that produce a layer's factors (Deflating the Hessian, paper
  * page: abstract and Figure 1 caption; H-SVDQuant explainer, rit.work,

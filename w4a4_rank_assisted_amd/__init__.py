@@ -24,6 +24,8 @@ HEADER = os.path.join(os.path.dirname(_HERE), "include", "hsq.h")
 OK, E_INVAL, E_SHAPE, E_ALIGN, E_WORKSPACE, E_HIP = 0, -1, -2, -3, -4, -5
 F32, BF16 = 0, 1
 KERNEL_AUTO, KERNEL_TILED, KERNEL_SKINNY = 0, 1, 2
+ACT_IDENTITY, ACT_GELU_TANH = 0, 1
+_ACTS = {"identity": ACT_IDENTITY, "gelu_tanh": ACT_GELU_TANH}
 _KERNELS = {"auto": KERNEL_AUTO, "tiled": KERNEL_TILED, "skinny": KERNEL_SKINNY}
 
 _lib = None
@@ -70,6 +72,9 @@ def _load():
             "hsq_w4a4_quantize_stage_g": ([P, I, I, I, I, I, P, P, I, P, S, P], I),
             "hsq_w4a4_contract_stage_g": ([I, I, I, I, I, P, P, P, I, P, P, I, P, S, I, P], I),
             "hsq_w4a4_group_partials_g": ([P, I, I, I, I, P, P, I, I, I, I, P, P, S, I, P], I),
+            "hsq_mlp_workspace_bytes": ([I, I, I, I, I, I], S),
+            "hsq_w4a4_lowrank_mlp": ([P, I, I, I, I, P, P, P, P, P, I, P, I, P, P, P, P, P, I, P, P, I, P,
+                                      P, S, P], I),
             "hsq_hessian_workspace_bytes": ([I, I], S),
             "hsq_hessian_accumulate": ([P, I, I, P, P, I, P, S, P], I),
             "hsq_deflate_workspace_bytes": ([I, I], S),
@@ -310,6 +315,54 @@ class Layer:
         return w4a4_lowrank_linear(X, self.lam, self.packed, self.sw, self.L1, self.L2, self.bias,
                                    N=self.N, batch=self.batch, y_dtype=y_dtype, out=out,
                                    workspace=ws, kernel=kernel, group=self.group)
+
+
+# ------------------------------------------------------------- fused chain
+def mlp_workspace_bytes(M: int, K: int, H: int, N: int, r_up: int, r_down: int) -> int:
+    return int(_load().hsq_mlp_workspace_bytes(M, K, H, N, r_up, r_down))
+
+
+def w4a4_lowrank_mlp(X, up, down, *, H: int, N: int, act: str = "gelu_tanh", y_dtype: str = "bf16",
+                     out=None, hidden_out=None, workspace=None):
+    """Y = down(act(up(X))) with the down layer's quantized input formed in the
+    up layer's epilogue.  ``up`` / ``down`` are dicts with lam, packed, sw,
+    L1, L2, bias (shapes as for one projection of w4a4_lowrank_linear; L1,
+    L2 may be None for rank 0).  hidden_out: optional (M, H) fp32 tensor that
+    receives the up layer's output before the activation."""
+    torch = _torch()
+    lib = _load()
+    _dev_tensor(X, "X", _half_types())
+    M, K = X.shape
+    r1 = 0 if up.get("L1") is None else int(up["L1"].shape[-1])
+    r2 = 0 if down.get("L1") is None else int(down["L1"].shape[-1])
+    for name, d, kk, nn, r in (("up", up, K, H, r1), ("down", down, H, N, r2)):
+        _dev_tensor(d["lam"], f"{name}.lam", _half_types(), (kk,))
+        _dev_tensor(d["packed"], f"{name}.packed", (torch.uint8,), (lib.hsq_packed_weight_bytes(kk, nn),))
+        _dev_tensor(d["sw"], f"{name}.sw", _half_types(), (kk // 64, nn))
+        if r:
+            _dev_tensor(d["L1"], f"{name}.L1", _half_types(), (kk, r))
+            _dev_tensor(d["L2"], f"{name}.L2", _half_types(), (r, nn))
+        if d.get("bias") is not None:
+            _dev_tensor(d["bias"], f"{name}.bias", _half_types(), (nn,))
+    ydt = {"bf16": (BF16, torch.bfloat16), "f32": (F32, torch.float32)}[y_dtype]
+    if out is None:
+        out = torch.empty((M, N), dtype=ydt[1], device=X.device)
+    _dev_tensor(out, "out", (ydt[1],), (M, N))
+    if hidden_out is not None:
+        _dev_tensor(hidden_out, "hidden_out", (torch.float32,), (M, H))
+    if workspace is None:
+        workspace = torch.empty(mlp_workspace_bytes(M, K, H, N, r1, r2), dtype=torch.uint8, device=X.device)
+    _dev_tensor(workspace, "workspace", (torch.uint8,))
+
+    def layer_args(d, r):
+        return (_ptr(d["lam"]), _ptr(d["packed"]), _ptr(d["sw"]), _ptr(d["L1"]) if r else None,
+                _ptr(d["L2"]) if r else None, r, _ptr(d.get("bias")))
+
+    _check(lib.hsq_w4a4_lowrank_mlp(_ptr(X), M, K, H, N, *layer_args(up, r1), _ACTS[act],
+                                    *layer_args(down, r2), _ptr(out), ydt[0], _ptr(hidden_out),
+                                    _ptr(workspace), workspace.numel(), _stream()),
+           "hsq_w4a4_lowrank_mlp")
+    return out
 
 
 # ------------------------------------------------------------- calibration

@@ -130,7 +130,7 @@ int quant_stage(const uint16_t *X, int M, int K, int N, int batch, int group,
 int contract_stage(int M, int K, int N, int batch, int group, const uint8_t *packed_w,
                    const uint16_t *sw, const uint16_t *L2, int r, const uint16_t *bias, void *Y,
                    int y_dtype, void *workspace, int kernel, hipStream_t s, int32_t *P, int m0,
-                   int mc, int n0, int nc) {
+                   int mc, int n0, int nc, int u_slices = -1) {
   const WsLayout L = plan_workspace(M, K, N, r, batch, group);
   char *ws = (char *)workspace;
   GemmArgs g{};
@@ -140,7 +140,7 @@ int contract_stage(int M, int K, int N, int batch, int group, const uint8_t *pac
   g.w_stride = packed_bytes(K, N);
   g.sw = sw;
   g.uw = (const float *)(ws + L.uw_off);
-  g.u_slices = L.u_slices;
+  g.u_slices = u_slices >= 0 ? u_slices : L.u_slices;
   g.L2 = r > 0 ? L2 : nullptr;
   g.bias = bias;
   g.Y = Y;
@@ -188,6 +188,98 @@ int contract_stage_g(int M, int K, int N, int batch, int group, const uint8_t *p
   if (st != HSQ_OK) return st;
   return contract_stage(M, K, N, batch, group, packed_w, sw, L2, r, bias, Y, y_dtype, workspace,
                         kernel, (hipStream_t)stream, nullptr, 0, 0, 0, 0);
+}
+
+// Fused two-layer chain (group 64, one projection each): workspace of the
+// up layer, of the down layer, and the down layer's U shares per 128-column
+// block of the hidden width.
+struct ChainLayout {
+  WsLayout up, dn;
+  size_t up_off = 0, dn_off = 0, upart_off = 0, total = 0;
+  int nblk = 0;
+};
+
+ChainLayout plan_chain(int M, int K, int H, int N, int r1, int r2) {
+  ChainLayout c;
+  c.up = plan_workspace(M, K, H, r1, 1, kGroup);
+  c.dn = plan_workspace(M, H, N, r2, 1, kGroup);
+  c.nblk = ceil_div(H, 128);
+  c.up_off = 0;
+  c.dn_off = align_up(c.up.total, 256);
+  c.upart_off = align_up(c.dn_off + c.dn.total, 256);
+  c.total = align_up(c.upart_off + (size_t)c.nblk * r2 * c.up.Mpad * sizeof(float), 256);
+  return c;
+}
+
+int chain_sizes(int M, int K, int H, int N, int r1, int r2) {
+  int st = check_sizes(M, K, H, r1, 1);
+  if (st != HSQ_OK) return st;
+  st = check_sizes(M, H, N, r2, 1);
+  if (st != HSQ_OK) return st;
+  if (r2 > kChainMaxRank) return HSQ_E_INVAL;
+  return HSQ_OK;
+}
+
+int run_chain(const uint16_t *X, int M, int K, int H, int N, const uint16_t *lam_up,
+              const uint8_t *packed_up, const uint16_t *sw_up, const uint16_t *L1_up,
+              const uint16_t *L2_up, int r1, const uint16_t *bias_up, int act,
+              const uint16_t *lam_dn, const uint8_t *packed_dn, const uint16_t *sw_dn,
+              const uint16_t *L1_dn, const uint16_t *L2_dn, int r2, const uint16_t *bias_dn, void *Y,
+              int y_dtype, float *yhid, void *workspace, size_t ws_bytes, void *stream) {
+  int st = chain_sizes(M, K, H, N, r1, r2);
+  if (st != HSQ_OK) return st;
+  if (act != HSQ_ACT_IDENTITY && act != HSQ_ACT_GELU_TANH) return HSQ_E_INVAL;
+  if (y_dtype != HSQ_F32 && y_dtype != HSQ_BF16) return HSQ_E_INVAL;
+  if (!X || !lam_up || !packed_up || !sw_up || !lam_dn || !packed_dn || !sw_dn || !Y || !workspace)
+    return HSQ_E_INVAL;
+  if ((r1 > 0 && (!L1_up || !L2_up)) || (r2 > 0 && (!L1_dn || !L2_dn))) return HSQ_E_INVAL;
+  const void *ptrs[] = {X, lam_up, packed_up, sw_up, L1_up, L2_up, bias_up, lam_dn, packed_dn,
+                        sw_dn, L1_dn, L2_dn, bias_dn, Y, yhid, workspace};
+  for (const void *p : ptrs)
+    if (p && !aligned16(p)) return HSQ_E_ALIGN;
+  const ChainLayout c = plan_chain(M, K, H, N, r1, r2);
+  if (ws_bytes < c.total) return HSQ_E_WORKSPACE;
+  hipStream_t s = (hipStream_t)stream;
+  char *ws = (char *)workspace;
+  char *wup = ws + c.up_off, *wdn = ws + c.dn_off;
+  // 1. the up layer's quantization pass
+  st = quant_stage(X, M, K, H, 1, kGroup, lam_up, L1_up, r1, wup, s);
+  if (st != HSQ_OK) return st;
+  // 2. its contraction, whose epilogue quantizes act(Y) into the down
+  //    layer's workspace
+  GemmArgs g{};
+  g.qa = (const int8_t *)(wup + c.up.qa_off);
+  g.sxs = (const uint16_t *)(wup + c.up.sxs_off);
+  g.w = packed_up;
+  g.w_stride = packed_bytes(K, H);
+  g.sw = sw_up;
+  g.uw = (const float *)(wup + c.up.uw_off);
+  g.u_slices = c.up.u_slices;
+  g.L2 = r1 > 0 ? L2_up : nullptr;
+  g.bias = bias_up;
+  g.M = M; g.N = H; g.G = c.up.G; g.Gp = c.up.Gp; g.Mpad = c.up.Mpad; g.r = r1; g.ucols = r1;
+  g.bpg = 1; g.SG = c.up.SG;
+  g.splits = 1;
+  g.act = act;
+  g.lam2 = lam_dn;
+  g.L1n = r2 > 0 ? L1_dn : nullptr;
+  g.r2 = r2;
+  g.Gp2 = c.dn.Gp;
+  g.qa2 = (int8_t *)(wdn + c.dn.qa_off);
+  g.sxs2 = (uint16_t *)(wdn + c.dn.sxs_off);
+  g.upart2 = (float *)(ws + c.upart_off);
+  g.yhid = yhid;
+  st = hip_status(launch_gemm_tiled_chain(g, s));
+  if (st != HSQ_OK) return st;
+  // 3. the down layer's U: the column-block shares summed in order
+  if (r2 > 0) {
+    st = hip_status(launch_chain_ureduce(g.upart2, c.nblk, r2, c.up.Mpad, (float *)(wdn + c.dn.uw_off), s));
+    if (st != HSQ_OK) return st;
+  }
+  // 4. the down layer's contraction from that workspace (one U slice)
+  const int kernel = M <= kSkinnyMaxM ? HSQ_KERNEL_SKINNY : HSQ_KERNEL_TILED;
+  return contract_stage(M, H, N, 1, kGroup, packed_dn, sw_dn, L2_dn, r2, bias_dn, Y, y_dtype, wdn,
+                        kernel, s, nullptr, 0, 0, 0, 0, 1);
 }
 
 int group_partials_g(const uint16_t *X, int M, int K, int N, int group, const uint16_t *lambda,
@@ -341,6 +433,25 @@ int hsq_w4a4_group_partials_g(const uint16_t *X, int M, int K, int N, int group,
                               int kernel, void *stream) {
   return group_partials_g(X, M, K, N, group, lambda, packed_w, m0, mc, n0, nc, P, workspace,
                           ws_bytes, kernel, stream);
+}
+
+// ---------------------------------------------------------------- fused chain
+
+size_t hsq_mlp_workspace_bytes(int M, int K, int H, int N, int r1, int r2) {
+  if (chain_sizes(M, K, H, N, r1, r2) != HSQ_OK) return 0;
+  return plan_chain(M, K, H, N, r1, r2).total;
+}
+
+int hsq_w4a4_lowrank_mlp(const uint16_t *X, int M, int K, int H, int N, const uint16_t *lambda_up,
+                         const uint8_t *packed_up, const uint16_t *sw_up, const uint16_t *L1_up,
+                         const uint16_t *L2_up, int r_up, const uint16_t *bias_up, int act,
+                         const uint16_t *lambda_down, const uint8_t *packed_down,
+                         const uint16_t *sw_down, const uint16_t *L1_down, const uint16_t *L2_down,
+                         int r_down, const uint16_t *bias_down, void *Y, int y_dtype, float *Y_hidden,
+                         void *workspace, size_t ws_bytes, void *stream) {
+  return run_chain(X, M, K, H, N, lambda_up, packed_up, sw_up, L1_up, L2_up, r_up, bias_up, act,
+                   lambda_down, packed_down, sw_down, L1_down, L2_down, r_down, bias_down, Y, y_dtype,
+                   Y_hidden, workspace, ws_bytes, stream);
 }
 
 // ---------------------------------------------------------------- calibration

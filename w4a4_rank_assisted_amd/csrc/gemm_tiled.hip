@@ -137,10 +137,11 @@ __device__ __forceinline__ void tile_of(int bid, int nblk, int mblk, int &mb, in
   nb = w / gsz;
 }
 
-template <bool DUMP, int RPT, int MODE, int BPG, int KH>
+template <bool DUMP, int RPT, int MODE, int BPG, int KH, bool CHAIN = false>
 __global__ __launch_bounds__(NTH * KH, 2) void k_gemm_tiled(GemmArgs a, int nblk, int mblk) {
   static_assert(MODE != kSplit || RPT == 0, "a split pass has no epilogue");
   static_assert(KH == 1 || (!DUMP && MODE != kReduce), "the K halves serve the stage loop");
+  static_assert(!CHAIN || (MODE == kFull && KH == 1 && BPG == 1 && !DUMP), "the chain epilogue: one unsplit pass");
   constexpr bool EPI = !DUMP && MODE != kSplit;   // this pass writes Y
   __shared__ Smem<RPT, BPG, KH> smem;
 
@@ -529,6 +530,112 @@ __global__ __launch_bounds__(NTH * KH, 2) void k_gemm_tiled(GemmArgs a, int nblk
 #pragma unroll
   for (int j = 0; j < TN; ++j) bj[j] = smem.ep.bias[(wn * TN + j) * 16 + colq];
 
+  if constexpr (CHAIN) {
+    // ---- fused chain: the next layer's input instead of Y ----
+    // x = act(Y) * fl32(1 / lam2[n]) (0 past M or N); per row and 64-column
+    // group (the columns of a pair of waves) the scale and codes exactly as
+    // the quantization pass forms them, the codes written to the next
+    // layer's workspace in MFMA operand order; the partial sums of the next
+    // layer's rank-r2 down projection over this tile's 128 columns.  The
+    // stage buffers are free (the stage loop ended with a barrier):
+    //   [0, 16 KiB)        codes, [wave][row][column] int8
+    //   [16, 18 KiB)       row absmax, [wave][row]
+    //   [18, 34 KiB)       U shares, [column quarter][tile row][8]
+    constexpr int WR = TM * 16, WC = TN * 16;          // 64 rows x 32 columns per wave
+    constexpr int R2 = kChainMaxRank;
+    static_assert(WC == 32 && WN == 4 && BN == 128, "a 64-column group is the columns of two waves");
+    static_assert(8 * WR * WC + 8 * WR * 4 + WN * BM * R2 * 4 <= (int)sizeof(Stages<BPG>), "chain LDS");
+    char *lb = reinterpret_cast<char *>(&sm);
+    int8_t *cbuf = reinterpret_cast<int8_t *>(lb) + wave * (WR * WC);
+    float *amx = reinterpret_cast<float *>(lb + 8 * WR * WC);
+    float *uex = amx + 8 * WR;
+    float il[TN], l1n[TN][R2];
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      const int n = (nt0 + wn * TN + j) * 16 + colq;
+      il[j] = n < a.N ? 1.0f / f16_to_f32(a.lam2[n]) : 0.0f;
+#pragma unroll
+      for (int c = 0; c < R2; ++c)
+        l1n[j][c] = (n < a.N && c < a.r2) ? bf16_to_f32(a.L1n[(size_t)n * a.r2 + c]) : 0.0f;
+    }
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int tr = (wm * TM + i) * 16 + rowq + q;   // row within the tile
+        const int m = mt0 * 16 + tr;
+        float mx = 0.0f;
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+          const float y = acc[i][j][q] + bj[j];
+          const int n = (nt0 + wn * TN + j) * 16 + colq;
+          if (a.yhid && m < a.M && n < a.N) a.yhid[(size_t)m * a.N + n] = y;
+          const float v = a.act == kActGeluTanh ? gelu_tanh_f32(y) : y;
+          const float x = m < a.M ? v * il[j] : 0.0f;
+          acc[i][j][q] = x;
+          mx = fmaxf(mx, fabsf(x));
+        }
+        // over the 16 lanes holding this row's columns
+#pragma unroll
+        for (int o = 1; o < 16; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
+        if (colq == 0) amx[wave * WR + i * 16 + rowq + q] = mx;
+#pragma unroll
+        for (int c = 0; c < R2; ++c) {
+          if (c >= a.r2) break;
+          float p = acc[i][0][q] * l1n[0][c];
+#pragma unroll
+          for (int j = 1; j < TN; ++j) p = __builtin_fmaf(acc[i][j][q], l1n[j][c], p);
+#pragma unroll
+          for (int o = 1; o < 16; o <<= 1) p += __shfl_xor(p, o, 64);
+          if (colq == 0) uex[(wn * BM + tr) * R2 + c] = p;
+        }
+      }
+    __syncthreads();
+    const int grp = 2 * nb + (wn >> 1);                 // 64-column group of the next layer
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int wr = i * 16 + rowq + q;
+        const float gmax = fmaxf(amx[wave * WR + wr], amx[(wave ^ 1) * WR + wr]);
+        const uint16_t s16 = act_scale16(gmax);
+        const float inv_s = s16 != 0 ? 1.0f / f16_to_f32(s16) : 0.0f;
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+          cbuf[wr * WC + j * 16 + colq] = (int8_t)(act_code_bits(acc[i][j][q], inv_s) & 0xFF);
+        const int m = mt0 * 16 + wm * WR + wr;
+        if ((wn & 1) == 0 && colq == 0 && m < a.Mpad && grp < a.Gp2)
+          a.sxs2[((size_t)(m >> 4) * a.Gp2 + grp) * 16 + (m & 15)] = s16;
+      }
+    // codes: per row of the wave, two 16-channel chunks (channels
+    // 32 * (wn & 1) + 16 * ch .. + 15 of the group) -> lane slot
+    // (row % 16) + 16 * kq of the block (row tile, group)
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int t = lane + 64 * k, wr = t & 63, ch = t >> 6;
+      const int m = mt0 * 16 + wm * WR + wr;
+      const v4u v = *reinterpret_cast<const v4u *>(cbuf + wr * WC + 16 * ch);
+      if (m < a.Mpad && grp < a.Gp2) {
+        const int kq = 2 * (wn & 1) + ch;
+        *reinterpret_cast<v4u *>(a.qa2 + (((size_t)(m >> 4) * a.Gp2 + grp) * 64 + (m & 15) + 16 * kq) * 16) = v;
+      }
+    }
+    // U shares of the tile: the four column quarters summed in order
+    if (wn == 0) {
+      for (int t = lane; t < WR * R2; t += 64) {
+        const int wr = t / R2, c = t % R2;
+        const int tr = wm * WR + wr, m = mt0 * 16 + tr;
+        if (c < a.r2 && m < a.Mpad) {
+          float u = uex[tr * R2 + c];
+#pragma unroll
+          for (int w = 1; w < WN; ++w) u += uex[(w * BM + tr) * R2 + c];
+          a.upart2[((size_t)nb * a.r2 + c) * a.Mpad + m] = u;
+        }
+      }
+    }
+    return;
+  }
+
   // output: per row tile, transpose the wave's 16 x 64 values through a
   // wave-private LDS region and store 16 bytes per lane
   constexpr int WC = TN * 16;                         // columns of the wave
@@ -669,6 +776,38 @@ hipError_t launch_tiled_bpg(const GemmArgs &a, int batch, bool dump, hipStream_t
   if constexpr (BPG == 1)
     if (p.kh == 2) return launch_tiled_kh<BPG, 2>(a, batch, p.splits, nblk, mblk, s);
   return launch_tiled_kh<BPG, 1>(a, batch, p.splits, nblk, mblk, s);
+}
+
+template <int RPT>
+hipError_t launch_chain_rpt(const GemmArgs &a, int nblk, int mblk, hipStream_t s) {
+  hipLaunchKernelGGL((k_gemm_tiled<false, RPT, kFull, 1, 1, true>), dim3((unsigned)(nblk * mblk), 1u), dim3(NTH),
+                     0, s, a, nblk, mblk);
+  return hipGetLastError();
+}
+
+__global__ __launch_bounds__(256) void k_chain_ureduce(const float *upart, int nblk, int r2, int Mpad, float *uw) {
+  const int i = blockIdx.x * 256 + threadIdx.x;     // (rank column, row) of the next layer's U
+  if (i >= r2 * Mpad) return;
+  float u = 0.0f;
+#pragma unroll 8
+  for (int b = 0; b < nblk; ++b) u += upart[(size_t)b * r2 * Mpad + i];
+  uw[i] = u;
+}
+
+hipError_t launch_gemm_tiled_chain(const GemmArgs &a, hipStream_t s) {
+  if (a.bpg != 1 || a.r2 < 1 || a.r2 > kChainMaxRank) return hipErrorInvalidValue;
+  const int nblk = ceil_div(a.N, BN), mblk = ceil_div(a.M, BM);
+  if (a.r == 0) return launch_chain_rpt<0>(a, nblk, mblk, s);
+  if (a.r <= 4) return launch_chain_rpt<4>(a, nblk, mblk, s);
+  if (a.r <= 8) return launch_chain_rpt<8>(a, nblk, mblk, s);
+  if (a.r <= 16) return launch_chain_rpt<16>(a, nblk, mblk, s);
+  return launch_chain_rpt<32>(a, nblk, mblk, s);
+}
+
+hipError_t launch_chain_ureduce(const float *upart, int nblk, int r2, int Mpad, float *uw, hipStream_t s) {
+  hipLaunchKernelGGL(k_chain_ureduce, dim3((unsigned)ceil_div(r2 * Mpad, 256)), dim3(256), 0, s, upart, nblk, r2,
+                     Mpad, uw);
+  return hipGetLastError();
 }
 
 hipError_t launch_gemm_tiled(const GemmArgs &a, int batch, bool dump, hipStream_t s) {

@@ -122,7 +122,24 @@ struct GemmArgs {
   // number per output tile
   float *part;
   int splits;
+  // fused chain (tiled contraction, CHAIN mode): instead of Y, the epilogue
+  // writes the next layer's input: act(Y) smoothed by lam2 and quantized
+  // into that layer's workspace (codes qa2, scales sxs2), and the partial
+  // sums of its rank-r2 down projection per 128-column block (upart2:
+  // [column block][r2][Mpad]); optionally Y itself before the activation
+  // (yhid, M x N fp32, a test export)
+  int act;
+  const uint16_t *lam2;
+  const uint16_t *L1n;
+  int r2, Gp2;
+  int8_t *qa2;
+  uint16_t *sxs2;
+  float *upart2;
+  float *yhid;
 };
+
+constexpr int kActIdentity = 0, kActGeluTanh = 1;
+constexpr int kChainMaxRank = 8;   // rank of the next layer in a fused chain
 
 hipError_t launch_pack(const int8_t *codes, int K, int N, uint8_t *packed, int *status,
                        hipStream_t s);
@@ -139,6 +156,11 @@ hipError_t launch_gemm_tiled(const GemmArgs &a, int batch, bool dump, hipStream_
 int tiled_splits(int M, int N, int K, int batch, int group);
 size_t tiled_partial_bytes(int M, int N, int K, int batch, int group);
 hipError_t launch_gemm_skinny(const GemmArgs &a, int batch, bool dump, hipStream_t s);
+// The tiled contraction with the CHAIN epilogue (one projection, unsplit,
+// 8-wave workgroups), and the sum of its U partials into the next layer's
+// single U slice: uw[j][m] = sum over column blocks of upart[blk][j][m].
+hipError_t launch_gemm_tiled_chain(const GemmArgs &a, hipStream_t s);
+hipError_t launch_chain_ureduce(const float *upart, int nblk, int r2, int Mpad, float *uw, hipStream_t s);
 
 // ---------------------------------------------------------------------------
 // Calibration (calib.hip)
@@ -226,6 +248,48 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
   uint32_t u = __float_as_uint(f);
   u += 0x7FFFu + ((u >> 16) & 1u);
   return (uint16_t)(u >> 16);
+}
+
+// The activation quantizer's two roundings (the same arithmetic as the
+// quantization pass): the fp16 scale of a group from its absmax (0 for a
+// zero group, saturating at 65504), and a code clamp(rint(fl32(xh / s)),
+// -8, 7) as the bits of 1.5 * 2^23 + code.
+__device__ __forceinline__ uint16_t act_scale16(float amax) {
+  if (amax == 0.0f) return 0;
+  uint16_t s16 = f32_to_f16(amax / 7.0f);
+  return s16 == 0x7C00u ? (uint16_t)0x7BFFu : s16;
+}
+__device__ __forceinline__ int act_code_bits(float xh, float inv_s) {
+  const int v = __float_as_int(xh * inv_s + kMagic);
+  return min(max(v, kMagicBits - 8), kMagicBits + 7);
+}
+
+// exp(x) in fp32 from basic operations only (each rounded once, no fused
+// multiply-add), so that a plain fp32 implementation reproduces it bit for
+// bit: x clamped to [-87, 88]; n = rint(x log2 e); Cody-Waite reduction
+// r = x - n ln2 (ln2 split into 0.693145751953125 + 1.428606765330187e-6);
+// the degree-6 Taylor polynomial of e^r in Horner form; times 2^n built
+// from its exponent bits.  Relative error below 2^-21 on the range.
+__device__ __forceinline__ float exp_f32_basic(float x) {
+  x = fminf(fmaxf(x, -87.0f), 88.0f);
+  const float n = __builtin_rintf(x * 1.44269504f);
+  const float r = (x - n * 0.693145751953125f) - n * 1.428606765330187e-06f;
+  float p = 1.388888888888889e-03f;              // 1/720
+  p = p * r + 8.333333333333333e-03f;            // 1/120
+  p = p * r + 4.166666666666666e-02f;            // 1/24
+  p = p * r + 1.666666666666667e-01f;            // 1/6
+  p = p * r + 0.5f;
+  p = p * r + 1.0f;
+  p = p * r + 1.0f;
+  return p * __int_as_float(((int)n + 127) << 23);
+}
+
+// GELU in its tanh form, 0.5 y (1 + tanh(sqrt(2/pi) (y + 0.044715 y^3))),
+// evaluated as y / (1 + exp(-2z)) with z = sqrt(2/pi) (y + 0.044715 y^3).
+__device__ __forceinline__ float gelu_tanh_f32(float y) {
+  const float y3 = (y * y) * y;
+  const float z = 0.7978845608f * (y + 0.044715f * y3);
+  return y / (1.0f + exp_f32_basic(-2.0f * z));
 }
 
 }  // namespace hsq
