@@ -382,6 +382,114 @@ def calib_main(args):
     return 0
 
 
+def chain_main(args):
+    """The FLUX.1 MLP as one fused call (up layer, GELU and the down layer's
+    quantization in the up contraction's epilogue, then the down
+    contraction) vs the two layers as separate calls (the up layer writing
+    bf16 Y, the down layer quantizing it again; no activation pass, so a
+    lower bound on the unfused time).  Inputs and outputs rotate past the
+    Infinity Cache.  Prints one JSON line."""
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU; use --gpus 1", file=sys.stderr)
+        return 2
+    import numpy as np
+    import torch
+
+    import w4a4_rank_assisted_amd as hsq
+    from synth import make_layer
+
+    dev = torch.device("cuda:0")
+    up_l, dn_l = make_layer("flux_up"), make_layer("flux_down")
+    M, K = up_l["X"].shape
+    H, N = up_l["qw"].shape[2], dn_l["qw"].shape[2]
+    r1, r2 = up_l["L1"].shape[2], dn_l["L1"].shape[2]
+
+    def d16(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev)
+
+    def upload(lay):
+        return dict(lam=d16(lay["lam"]), packed=hsq.pack_weights(torch.from_numpy(lay["qw"][0]).to(dev))[0],
+                    sw=d16(lay["sw"][0]), L1=d16(lay["L1"][0]), L2=d16(lay["L2"][0]), bias=d16(lay["bias"][0]))
+
+    up0, dn0 = upload(up_l), upload(dn_l)
+    X0 = d16(up_l["X"])
+    set_bytes = X0.numel() * 2 + up0["packed"].numel() + dn0["packed"].numel() + M * N * 2 + M * H * 2
+    nsets = max(1, math.ceil(args.rotate_mb * 1e6 / set_bytes))
+    sets = []
+    for _ in range(nsets):
+        up = dict(up0, packed=up0["packed"].clone())
+        dn = dict(dn0, packed=dn0["packed"].clone())
+        sets.append(dict(X=X0.clone(), up=up, dn=dn, Y=torch.empty((M, N), dtype=torch.bfloat16, device=dev),
+                         Yh=torch.empty((1, M, H), dtype=torch.bfloat16, device=dev)))
+    wsc = torch.empty(hsq.mlp_workspace_bytes(M, K, H, N, r1, r2), dtype=torch.uint8, device=dev)
+    wsu = torch.empty(hsq.workspace_bytes(M, K, H, r1, 1), dtype=torch.uint8, device=dev)
+    wsd = torch.empty(hsq.workspace_bytes(M, H, N, r2, 1), dtype=torch.uint8, device=dev)
+
+    def fused(i):
+        st = sets[i % nsets]
+        hsq.w4a4_lowrank_mlp(st["X"], st["up"], st["dn"], H=H, N=N, act="gelu_tanh", y_dtype="bf16",
+                             out=st["Y"], workspace=wsc)
+
+    def separate(i):
+        st = sets[i % nsets]
+        u, d = st["up"], st["dn"]
+        hsq.w4a4_lowrank_linear(st["X"], u["lam"], u["packed"], u["sw"][None], u["L1"][None], u["L2"][None],
+                                u["bias"][None], N=H, y_dtype="bf16", out=st["Yh"], workspace=wsu)
+        hsq.w4a4_lowrank_linear(st["Yh"][0], d["lam"], d["packed"], d["sw"][None], d["L1"][None],
+                                d["L2"][None], d["bias"][None], N=N, y_dtype="bf16", out=st["Y"][None],
+                                workspace=wsd)
+
+    for i in range(args.warmup):
+        fused(i)
+        separate(i)
+    torch.cuda.synchronize()
+    cap = torch.cuda.Stream()
+    graphs = {}
+    for name, fn in (("fused", fused), ("separate", separate)):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(cap):
+            with torch.cuda.graph(g, stream=cap):
+                for i in range(args.steps):
+                    fn(args.warmup + i)
+        graphs[name] = g
+    torch.cuda.synchronize()
+    for g in graphs.values():
+        g.replay()
+    torch.cuda.synchronize()
+
+    def timed(name):
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        with torch.cuda.stream(cap):
+            t0.record(cap)
+            graphs[name].replay()
+            t1.record(cap)
+        torch.cuda.synchronize()
+        return t0.elapsed_time(t1) / args.steps
+
+    ms_f, ms_s = timed("fused"), timed("separate")
+    ops = 2 * M * (K * H + H * N)
+    ach = ops / (ms_f * 1e-3) / 1e12
+    out = {
+        "metric": "effective TOPS of the fused W4A4+rank-4 MLP chain (up, GELU, down)",
+        "value": round(ach, 3), "unit": "TOPS", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_f, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "int8", "data": "synthetic",
+        "config": {"workload": f"FLUX.1 MLP: {M} tokens, {K} -> {H} (GELU) -> {N}, rank {r1}/{r2}",
+                   "M": M, "K": K, "H": H, "N": N, "rotated_sets": nsets},
+        "separate_ms_per_step": round(ms_s, 5),
+        "speedup_vs_separate": round(ms_s / ms_f, 4),
+        "roofline": {"bound": "mfma", "achieved": round(ach, 2), "peak": PEAK_INT8_TOPS, "unit": "TFLOP/s",
+                     "frac": round(ach / PEAK_INT8_TOPS, 4), "traffic": None,
+                     "kernel": "whole chain (both contractions dominate)", "ops_per_launch": ops},
+        "device": device_info(torch),
+        "cpu_baseline": None,
+    }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -406,6 +514,9 @@ def main(argv=None):
                          "(see summarize_profiles)")
     ap.add_argument("--write-traffic", action="store_true",
                     help="with --summarize: record the measured HBM bytes in profiles/traffic.json")
+    ap.add_argument("--chain", action="store_true",
+                    help="time the fused two-layer chain (FLUX.1 MLP: flux_up, GELU, flux_down) against "
+                         "the two layers run one after the other")
     ap.add_argument("--calib", action="store_true",
                     help="time the calibration kernels (Hessian, deflation, closed-form L2) on the "
                          "layer instead of the inference path")
@@ -414,6 +525,8 @@ def main(argv=None):
         return summarize_profiles(args)
     if args.calib:
         return calib_main(args)
+    if args.chain:
+        return chain_main(args)
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:

@@ -575,9 +575,7 @@ __global__ __launch_bounds__(NTH * KH, 2) void k_gemm_tiled(GemmArgs a, int nblk
           acc[i][j][q] = x;
           mx = fmaxf(mx, fabsf(x));
         }
-        // over the 16 lanes holding this row's columns
-#pragma unroll
-        for (int o = 1; o < 16; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
+        mx = row16_max(mx);                             // over the 16 lanes holding this row's columns
         if (colq == 0) amx[wave * WR + i * 16 + rowq + q] = mx;
 #pragma unroll
         for (int c = 0; c < R2; ++c) {
@@ -585,8 +583,7 @@ __global__ __launch_bounds__(NTH * KH, 2) void k_gemm_tiled(GemmArgs a, int nblk
           float p = acc[i][0][q] * l1n[0][c];
 #pragma unroll
           for (int j = 1; j < TN; ++j) p = __builtin_fmaf(acc[i][j][q], l1n[j][c], p);
-#pragma unroll
-          for (int o = 1; o < 16; o <<= 1) p += __shfl_xor(p, o, 64);
+          p = row16_sum(p);
           if (colq == 0) uex[(wn * BM + tr) * R2 + c] = p;
         }
       }

@@ -250,6 +250,27 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
   return (uint16_t)(u >> 16);
 }
 
+// Reductions over a row of 16 lanes through DPP (no LDS traffic): the
+// butterfly quad-xor-1, quad-xor-2, half-row mirror, row mirror leaves the
+// row's maximum / sum in every lane of the row, and since each step adds a
+// value to its partner's in both orders, every lane holds the same bits.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float row16_max(float v) {
+  v = fmaxf(v, dpp_f32<0xB1>(v));    // quad_perm [1,0,3,2]
+  v = fmaxf(v, dpp_f32<0x4E>(v));    // quad_perm [2,3,0,1]
+  v = fmaxf(v, dpp_f32<0x141>(v));   // row_half_mirror
+  return fmaxf(v, dpp_f32<0x140>(v));  // row_mirror
+}
+__device__ __forceinline__ float row16_sum(float v) {
+  v += dpp_f32<0xB1>(v);
+  v += dpp_f32<0x4E>(v);
+  v += dpp_f32<0x141>(v);
+  return v + dpp_f32<0x140>(v);
+}
+
 // The activation quantizer's two roundings (the same arithmetic as the
 // quantization pass): the fp16 scale of a group from its absmax (0 for a
 // zero group, saturating at 65504), and a code clamp(rint(fl32(xh / s)),
