@@ -218,6 +218,33 @@ int hsq_w4a4_group_partials_g(const uint16_t *X, int M, int K, int N, int group,
                               int n0, int nc, int32_t *P, void *workspace, size_t ws_bytes,
                               int kernel, void *stream);
 
+/* ---- MX-fp4 format variant of the layer ----
+ * The same layer (smoothing, rank-r branch on the smoothed activations,
+ * bias) with both 4-bit operands of the residual product in MX-fp4 (OCP
+ * Microscaling Formats v1.0) instead of int4 with fp16 group-64 scales: per
+ * 32 consecutive values along K one e8m0 scale 2^X, X = floor(log2 amax) - 2
+ * (stored as X + 127, clamped to [0, 254]; a zero block stores 127), and
+ * e2m1 elements {0, 0.5, 1, 1.5, 2, 3, 4, 6} rounded to nearest (ties to the
+ * even mantissa), magnitudes above 6 saturating.  The activations are
+ * blocked per token, the residual per output column.  The product runs on
+ * gfx950's scaled fp4 MFMA, which applies both scales.
+ * hsq_mx_pack_weights: R (K x N fp32, the residual, row-major) -> packed
+ *   (hsq_mx_packed_weight_bytes(K, N) bytes: codes in MFMA operand order,
+ *   then the scales).
+ * hsq_mx_lowrank_linear: Y (M x N, HSQ_F32 or HSQ_BF16) = Q(Xh) Q(R) +
+ *   (Xh L1) L2 + bias; X, lambda, L1 (K x r), L2 (r x N), bias (N) as for
+ *   hsq_w4a4_lowrank_linear with batch 1; workspace of
+ *   hsq_mx_workspace_bytes(M, K, r) bytes.
+ * Errors: HSQ_E_INVAL, HSQ_E_SHAPE (K not a multiple of 64), HSQ_E_ALIGN,
+ * HSQ_E_WORKSPACE, HSQ_E_HIP. */
+size_t hsq_mx_packed_weight_bytes(int K, int N);
+int hsq_mx_pack_weights(const float *R, int K, int N, uint8_t *packed, void *stream);
+size_t hsq_mx_workspace_bytes(int M, int K, int r);
+int hsq_mx_lowrank_linear(const uint16_t *X, int M, int K, int N, const uint16_t *lambda,
+                          const uint8_t *packed_mx, const uint16_t *L1, const uint16_t *L2, int r,
+                          const uint16_t *bias, void *Y, int y_dtype, void *workspace, size_t ws_bytes,
+                          void *stream);
+
 /* ---- fused two-layer chain: Y = down(act(up(X))) ----
  * Two linears of the kind above (group 64, one projection each, ranks r_up
  * and r_down) with an elementwise activation between them, as in the MLP

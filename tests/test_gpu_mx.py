@@ -1,0 +1,121 @@
+"""MX-fp4 variant of the layer (hsq_mx_pack_weights, hsq_mx_lowrank_linear)
+vs the CPU oracle (oracle/mx.py), through the C ABI, on seeded inputs.
+
+Bars: the packed weight codes and e8m0 scales, and the activation codes and
+scales (decoded from the workspace), bit-exact; U relative Frobenius
+<= 1e-5; Y fp32 within 1e-3 relative Frobenius of the oracle's fp64 result,
+bf16 within 1e-3 of that result rounded to bf16.  The residual is the int4
+layer's own dequantized residual qw * sw (exact in fp32), re-quantized to
+MX-fp4.
+"""
+
+import numpy as np
+import pytest
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():  # collected on CPU-only hosts, never run there
+    pytest.skip("needs a GPU", allow_module_level=True)
+
+import w4a4_rank_assisted_amd as hsq  # noqa: E402
+from oracle import mx  # noqa: E402
+from synth import bf16_bits_to_f32, f64_to_bf16_bits, make_layer, make_random_layer  # noqa: E402
+
+DEV = torch.device("cuda:0")
+TOL = 1e-3
+
+
+def say(msg):
+    print(msg, flush=True)
+
+
+def dev16(a):
+    return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(DEV)
+
+
+def rel(a, b):
+    return float(np.linalg.norm(a - b) / max(np.linalg.norm(b), 1e-300))
+
+
+def align(v, a=256):
+    return -(-v // a) * a
+
+
+def residual(lay):
+    sw = lay["sw"][0].view(np.float16).astype(np.float32)
+    return (lay["qw"][0].astype(np.float32) * np.repeat(sw, lay["group"], axis=0)).astype(np.float32)
+
+
+def decode_blob(raw, tiles, KS, rows, K):
+    """codes [tiles*16 rows][4*KS*32 channels] -> [:rows, :K] and scales
+    [rows][K/32] from a blob (codes, then scales)."""
+    KS4 = -(-KS // 4)
+    b = raw[: tiles * KS * 1024].reshape(tiles, KS, 4, 16, 16)          # t, ks, kb, r, byte
+    lo, hi = b & 15, b >> 4
+    nib = np.stack([lo, hi], axis=-1).reshape(tiles, KS, 4, 16, 32)      # element 2i low, 2i+1 high
+    codes = nib.transpose(0, 3, 1, 2, 4).reshape(tiles * 16, KS * 128)[:rows, :K]
+    s = raw[tiles * KS * 1024: tiles * KS * 1024 + tiles * KS4 * 256].reshape(tiles, KS4, 4, 16, 4)  # t, ks4, kb, r, j
+    sc = s.transpose(0, 3, 1, 4, 2).reshape(tiles * 16, KS4 * 16)[:rows, : K // 32]
+    return codes, sc
+
+
+def run_case(lay, rows=None):
+    M, K = lay["X"].shape
+    N = lay["qw"].shape[2]
+    r = lay["L1"].shape[2]
+    say(f"[mx] M={M} K={K} N={N} r={r}")
+    R = residual(lay)
+    packed = hsq.mx_pack_weights(torch.from_numpy(R).to(DEV))
+    torch.cuda.synchronize()
+    KS, NT, MT = -(-K // 128), -(-N // 16), -(-M // 16)
+    wc, ws = decode_blob(packed.cpu().numpy(), NT, KS, N, K)
+    oc, osc = mx.quantize_weight(R)
+    assert np.array_equal(wc, oc.T) and np.array_equal(ws, osc.T)
+    X, lam = dev16(lay["X"]), dev16(lay["lam"])
+    L1 = dev16(lay["L1"][0]) if r else None
+    L2 = dev16(lay["L2"][0]) if r else None
+    bias = dev16(lay["bias"][0])
+    wsp = torch.zeros(hsq._load().hsq_mx_workspace_bytes(M, K, r), dtype=torch.uint8, device=DEV)
+    Y = hsq.mx_lowrank_linear(X, lam, packed, L1, L2, bias, N=N, y_dtype="f32", workspace=wsp)
+    Yb = hsq.mx_lowrank_linear(X, lam, packed, L1, L2, bias, N=N, y_dtype="bf16").float()
+    torch.cuda.synchronize()
+    raw = wsp.cpu().numpy()
+    qa_off = align(K * 4)
+    blob = raw[qa_off: qa_off + MT * KS * 1024]
+    sa_off = align(qa_off + MT * KS * 1024)
+    sc = raw[sa_off: sa_off + MT * (-(-KS // 4)) * 256]
+    ac, asc = decode_blob(np.concatenate([blob, sc]), MT, KS, M, K)
+    oac, oas = mx.quantize_act(lay["X"], lay["lam"])
+    assert np.array_equal(ac, oac) and np.array_equal(asc, oas)
+    rows = np.arange(M) if rows is None else rows
+    if r:
+        u_off = align(sa_off + MT * (-(-KS // 4)) * 256)
+        Mpad = MT * 16
+        U = raw[u_off: u_off + r * Mpad * 4].view(np.float32).reshape(r, Mpad)[:, :M].T
+        xh = mx.smoothed(lay["X"], lay["lam"]).astype(np.float64)
+        L1f = (lay["L1"][0].astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+        assert rel(U.astype(np.float64), xh @ L1f) <= 1e-5
+    ref = mx.linear(lay["X"], lay["lam"], R, lay["L1"][0] if r else None, lay["L2"][0] if r else None,
+                    lay["bias"][0], rows=rows)
+    e32 = rel(Y.cpu().numpy()[rows].astype(np.float64), ref)
+    ref_b = bf16_bits_to_f32(f64_to_bf16_bits(ref)).astype(np.float64)
+    e16 = rel(Yb.cpu().numpy()[rows].astype(np.float64), ref_b)
+    say(f"    codes/scales exact; Y fp32 rel {e32:.3e}, bf16 rel {e16:.3e}")
+    assert e32 <= TOL and e16 <= TOL
+
+
+@pytest.mark.parametrize("M,K,N,r", [
+    (5, 192, 33, 0),          # rank 0, ragged N, one row tile, a k-step of one 64-block pad
+    (70, 576, 300, 4),        # 18 blocks: the last k-step half padded
+    (130, 1024, 130, 7),      # odd rank (scalar L1 reads), ragged rows and columns
+    (200, 2048, 256, 32),     # largest rank
+])
+def test_mx_matches_oracle(M, K, N, r):
+    run_case(make_random_layer(700 + M, M, K, N, r=r, outlier_channels=3))
+
+
+def test_mx_pixart_full_size_sampled_rows():
+    lay = make_layer("pixart_up")
+    rows = np.array(sorted(set([0, 4095]) | set(np.random.default_rng(5).choice(4096, 30, replace=False).tolist())))
+    run_case(lay, rows)

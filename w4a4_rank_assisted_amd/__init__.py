@@ -72,6 +72,10 @@ def _load():
             "hsq_w4a4_quantize_stage_g": ([P, I, I, I, I, I, P, P, I, P, S, P], I),
             "hsq_w4a4_contract_stage_g": ([I, I, I, I, I, P, P, P, I, P, P, I, P, S, I, P], I),
             "hsq_w4a4_group_partials_g": ([P, I, I, I, I, P, P, I, I, I, I, P, P, S, I, P], I),
+            "hsq_mx_packed_weight_bytes": ([I, I], S),
+            "hsq_mx_pack_weights": ([P, I, I, P, P], I),
+            "hsq_mx_workspace_bytes": ([I, I, I], S),
+            "hsq_mx_lowrank_linear": ([P, I, I, I, P, P, P, P, I, P, P, I, P, S, P], I),
             "hsq_mlp_workspace_bytes": ([I, I, I, I, I, I], S),
             "hsq_w4a4_lowrank_mlp": ([P, I, I, I, I, P, P, P, P, P, I, P, I, P, P, P, P, P, I, P, P, I, P,
                                       P, S, P], I),
@@ -315,6 +319,47 @@ class Layer:
         return w4a4_lowrank_linear(X, self.lam, self.packed, self.sw, self.L1, self.L2, self.bias,
                                    N=self.N, batch=self.batch, y_dtype=y_dtype, out=out,
                                    workspace=ws, kernel=kernel, group=self.group)
+
+
+# ------------------------------------------------------------- MX-fp4 variant
+def mx_pack_weights(R):
+    """R (K, N) fp32 device tensor -> packed MX-fp4 blob (uint8)."""
+    torch = _torch()
+    lib = _load()
+    _dev_tensor(R, "R", (torch.float32,))
+    K, N = R.shape
+    packed = torch.empty(lib.hsq_mx_packed_weight_bytes(K, N), dtype=torch.uint8, device=R.device)
+    _check(lib.hsq_mx_pack_weights(_ptr(R), K, N, _ptr(packed), _stream()), "hsq_mx_pack_weights")
+    return packed
+
+
+def mx_lowrank_linear(X, lam, packed, L1=None, L2=None, bias=None, *, N: int, y_dtype: str = "bf16",
+                      out=None, workspace=None):
+    """The MX-fp4 layer: X (M, K) bf16, lam (K,), packed (from mx_pack_weights),
+    L1 (K, r), L2 (r, N), bias (N,) -> Y (M, N)."""
+    torch = _torch()
+    lib = _load()
+    _dev_tensor(X, "X", _half_types())
+    M, K = X.shape
+    _dev_tensor(lam, "lambda", _half_types(), (K,))
+    _dev_tensor(packed, "packed", (torch.uint8,), (lib.hsq_mx_packed_weight_bytes(K, N),))
+    r = 0 if L1 is None else int(L1.shape[-1])
+    if r:
+        _dev_tensor(L1, "L1", _half_types(), (K, r))
+        _dev_tensor(L2, "L2", _half_types(), (r, N))
+    if bias is not None:
+        _dev_tensor(bias, "bias", _half_types(), (N,))
+    ydt = {"bf16": (BF16, torch.bfloat16), "f32": (F32, torch.float32)}[y_dtype]
+    if out is None:
+        out = torch.empty((M, N), dtype=ydt[1], device=X.device)
+    _dev_tensor(out, "out", (ydt[1],), (M, N))
+    if workspace is None:
+        workspace = torch.empty(lib.hsq_mx_workspace_bytes(M, K, r), dtype=torch.uint8, device=X.device)
+    _check(lib.hsq_mx_lowrank_linear(_ptr(X), M, K, N, _ptr(lam), _ptr(packed), _ptr(L1) if r else None,
+                                     _ptr(L2) if r else None, r, _ptr(bias), _ptr(out), ydt[0],
+                                     _ptr(workspace), workspace.numel(), _stream()),
+           "hsq_mx_lowrank_linear")
+    return out
 
 
 # ------------------------------------------------------------- fused chain

@@ -22,7 +22,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_DIR = os.path.join(HERE, "_lib")
 LIB = os.path.join(LIB_DIR, "libhsq.so")
-SOURCES = ["api.hip", "pack.hip", "quant.hip", "quant_tiles.hip", "gemm_tiled.hip", "gemm_skinny.hip", "calib.hip"]
+SOURCES = ["api.hip", "pack.hip", "quant.hip", "quant_tiles.hip", "gemm_tiled.hip", "gemm_skinny.hip", "calib.hip", "mx.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 

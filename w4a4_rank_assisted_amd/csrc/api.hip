@@ -435,6 +435,53 @@ int hsq_w4a4_group_partials_g(const uint16_t *X, int M, int K, int N, int group,
                           ws_bytes, kernel, stream);
 }
 
+// ---------------------------------------------------------------- MX-fp4 variant
+
+size_t hsq_mx_packed_weight_bytes(int K, int N) {
+  if (K < kGroup || K % kGroup != 0 || N < 1 || (long long)K * N >= INT_MAX) return 0;
+  return mx_packed_bytes(K, N);
+}
+
+int hsq_mx_pack_weights(const float *R, int K, int N, uint8_t *packed, void *stream) {
+  if (!R || !packed || N < 1 || K < 1) return HSQ_E_INVAL;
+  if (K % kGroup != 0) return HSQ_E_SHAPE;
+  if ((long long)K * N >= INT_MAX) return HSQ_E_INVAL;
+  if (!aligned16(R) || !aligned16(packed)) return HSQ_E_ALIGN;
+  return hip_status(launch_mx_pack(R, K, N, packed, (hipStream_t)stream));
+}
+
+size_t hsq_mx_workspace_bytes(int M, int K, int r) {
+  if (check_sizes(M, K, 1, r, 1) != HSQ_OK) return 0;
+  return plan_mx(M, K, r).total;
+}
+
+int hsq_mx_lowrank_linear(const uint16_t *X, int M, int K, int N, const uint16_t *lambda,
+                          const uint8_t *packed_mx, const uint16_t *L1, const uint16_t *L2, int r,
+                          const uint16_t *bias, void *Y, int y_dtype, void *workspace, size_t ws_bytes,
+                          void *stream) {
+  int st = check_sizes(M, K, N, r, 1);
+  if (st != HSQ_OK) return st;
+  if (!X || !lambda || !packed_mx || !Y || !workspace || (r > 0 && (!L1 || !L2))) return HSQ_E_INVAL;
+  if (y_dtype != HSQ_F32 && y_dtype != HSQ_BF16) return HSQ_E_INVAL;
+  const void *ptrs[] = {X, lambda, packed_mx, L1, L2, bias, Y, workspace};
+  for (const void *p : ptrs)
+    if (p && !aligned16(p)) return HSQ_E_ALIGN;
+  const MxLayout L = plan_mx(M, K, r);
+  if (ws_bytes < L.total) return HSQ_E_WORKSPACE;
+  char *ws = (char *)workspace;
+  MxArgs a{};
+  a.X = X; a.lam = lambda; a.L1 = r > 0 ? L1 : nullptr; a.L2 = r > 0 ? L2 : nullptr; a.bias = bias;
+  a.invlam = (float *)(ws + L.invlam_off);
+  a.qa = (uint8_t *)(ws + L.qa_off);
+  a.sa = (uint8_t *)(ws + L.sa_off);
+  a.U = (float *)(ws + L.u_off);
+  a.wq = packed_mx;
+  a.ws = packed_mx + (size_t)ceil_div(N, 16) * L.KS * 1024;
+  a.Y = Y; a.y_bf16 = y_dtype == HSQ_BF16;
+  a.M = M; a.K = K; a.N = N; a.r = r; a.KS = L.KS; a.KS4 = L.KS4; a.Mpad = L.Mpad;
+  return hip_status(launch_mx_linear(a, (hipStream_t)stream));
+}
+
 // ---------------------------------------------------------------- fused chain
 
 size_t hsq_mlp_workspace_bytes(int M, int K, int H, int N, int r1, int r2) {

@@ -163,6 +163,30 @@ hipError_t launch_gemm_tiled_chain(const GemmArgs &a, hipStream_t s);
 hipError_t launch_chain_ureduce(const float *upart, int nblk, int r2, int Mpad, float *uw, hipStream_t s);
 
 // ---------------------------------------------------------------------------
+// MX-fp4 variant (mx.hip)
+// ---------------------------------------------------------------------------
+struct MxLayout {
+  int KS = 0, KS4 = 0, Mpad = 0;   // k-steps of 128 channels, groups of four k-steps, padded rows
+  size_t invlam_off = 0, qa_off = 0, sa_off = 0, u_off = 0, total = 0;
+};
+
+struct MxArgs {
+  const uint16_t *X, *lam, *L1, *L2, *bias;
+  float *invlam;           // workspace: fl32(1/lambda)
+  uint8_t *qa, *sa;        // workspace: activation codes and scales (blob layout)
+  float *U;                // workspace: r x Mpad
+  const uint8_t *wq, *ws;  // packed weights: codes, scales
+  void *Y;
+  int y_bf16;
+  int M, K, N, r, KS, KS4, Mpad;
+};
+
+size_t mx_packed_bytes(int K, int N);
+MxLayout plan_mx(int M, int K, int r);
+hipError_t launch_mx_pack(const float *R, int K, int N, uint8_t *packed, hipStream_t s);
+hipError_t launch_mx_linear(const MxArgs &a, hipStream_t s);
+
+// ---------------------------------------------------------------------------
 // Calibration (calib.hip)
 // ---------------------------------------------------------------------------
 struct HessArgs {
