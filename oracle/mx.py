@@ -16,7 +16,10 @@ scales.  Per block of 32 consecutive values along the reduction dimension:
   * elements: v = value / 2^X rounded to the nearest e2m1 value
     {0, 0.5, 1, 1.5, 2, 3, 4, 6} (ties to the even mantissa), magnitudes
     above 6 saturating to 6; the 4-bit code is the index of the magnitude in
-    that list plus 8 for a negative value.
+    that list plus 8 when v's sign bit is set.  e2m1 is sign-magnitude, so a
+    negative value whose magnitude rounds to 0 becomes -0 (code 8), as an
+    IEEE-754 round-to-nearest-even conversion keeps the sign of a zero
+    result; -0 and +0 contribute the same 0 to every product.
 
 The activations are blocked along K per token, the residual along K per
 output column.  The product is sum over blocks of 2^(Xa + Xw) times the
@@ -33,15 +36,16 @@ BLOCK = 32
 
 def e2m1_round(v):
     """Nearest e2m1 magnitude of |v| (ties to even mantissa), saturating at
-    6; returns (code 0..15, value)."""
+    6, with v's sign bit; returns (code 0..15, value)."""
     v = np.asarray(v, dtype=np.float64)
     m = np.abs(v)
     q = np.where(m < 2.0, np.rint(m * 2.0) / 2.0,
                  np.where(m < 4.0, np.rint(m), np.rint(m / 2.0) * 2.0))
     q = np.minimum(q, 6.0)
     idx = np.searchsorted(E2M1, q)
-    code = idx + np.where((v < 0) & (q > 0), 8, 0)
-    return code.astype(np.uint8), np.where(v < 0, -q, q)
+    neg = np.signbit(v)                      # the sign bit is kept, also when the magnitude rounds to 0
+    code = idx + np.where(neg, 8, 0)
+    return code.astype(np.uint8), np.where(neg, -q, q)
 
 
 def quantize_blocks(x):

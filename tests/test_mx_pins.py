@@ -27,10 +27,11 @@ pytestmark = pytest.mark.filterwarnings("ignore::RuntimeWarning")
     (0.0, 0.0, 0), (0.25, 0.0, 0), (0.3, 0.5, 1), (0.75, 1.0, 2), (1.25, 1.0, 2), (1.3, 1.5, 3),
     (1.75, 2.0, 4), (2.5, 2.0, 4), (2.6, 3.0, 5), (3.5, 4.0, 6), (5.0, 4.0, 6), (5.5, 6.0, 7),
     (6.9, 6.0, 7), (7.99, 6.0, 7), (-0.75, -1.0, 10), (-5.0, -4.0, 14), (-7.0, -6.0, 15),
+    (-0.2, -0.0, 8), (-0.25, -0.0, 8), (-0.0, -0.0, 8), (-0.26, -0.5, 9),   # sign kept at zero
 ])
 def test_e2m1_hand_cases(v, val, code):
     c, q = mx.e2m1_round(np.array([v]))
-    assert q[0] == val and c[0] == code
+    assert q[0] == val and np.signbit(q[0]) == np.signbit(val) and c[0] == code
 
 
 def test_e2m1_rounding_matches_brute_force():
@@ -45,8 +46,9 @@ def test_e2m1_rounding_matches_brute_force():
         i = best[1]
         if m > 6.0:
             i = 7
-        return mx.E2M1[i] * (-1 if v < 0 else 1), i + (8 if v < 0 and i > 0 else 0)
-    grid = np.arange(-8.0, 8.0, 1.0 / 64)
+        neg = math.copysign(1.0, v) < 0
+        return mx.E2M1[i] * (-1 if neg else 1), i + (8 if neg else 0)
+    grid = np.concatenate([np.arange(-8.0, 8.0, 1.0 / 64), [-0.0]])
     c, q = mx.e2m1_round(grid)
     for v, cc, qq in zip(grid, c, q):
         rv, rc = ref(float(v))
