@@ -32,6 +32,7 @@ sys.path.insert(0, ROOT)
 METRIC = "effective TOPS of fused W4A4+rank-4 linear; % of int8 MFMA / HBM roofline"
 PEAK_INT8_TOPS = 5000.0      # MI355X dense int8 MFMA, 5.0 POP/s
 PEAK_BF16_TFLOPS = 2500.0    # MI355X dense bf16 MFMA, 2.5 PFLOP/s
+PEAK_FP4_TFLOPS = 10100.0    # MI355X dense fp4 / fp6 MFMA, 10.1 PFLOP/s
 PEAK_HBM_GBS = 8000.0        # MI355X HBM3E, 8 TB/s
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 KERNEL_SOURCES = {
@@ -382,6 +383,87 @@ def calib_main(args):
     return 0
 
 
+def mx_main(args):
+    """The MX-fp4 variant of one layer (one projection): one step = the whole
+    hsq_mx_lowrank_linear call (1/lambda table, quantization pass with the
+    rank branch, scaled-fp4 MFMA contraction with the epilogue).  The
+    residual is the int4 layer's dequantized residual re-quantized to
+    MX-fp4.  Inputs rotate past the Infinity Cache.  The roofline is that
+    of the whole call against the fp4 MFMA peak (the quantization pass
+    included)."""
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU; use --gpus 1", file=sys.stderr)
+        return 2
+    import numpy as np
+    import torch
+
+    import w4a4_rank_assisted_amd as hsq
+    from synth import layer_spec, make_layer
+
+    dev = torch.device("cuda:0")
+    spec = layer_spec(args.layer, args.tokens)
+    lay = make_layer(args.layer, args.tokens)
+    M, K, N, r = spec.M, spec.K, spec.N, spec.r
+
+    def d16(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev)
+
+    swf = lay["sw"][0].view(np.float16).astype(np.float32)
+    R = (lay["qw"][0].astype(np.float32) * np.repeat(swf, lay["group"], axis=0)).astype(np.float32)
+    packed0 = hsq.mx_pack_weights(torch.from_numpy(R).to(dev))
+    lam, L1, L2, bias = d16(lay["lam"]), d16(lay["L1"][0]), d16(lay["L2"][0]), d16(lay["bias"][0])
+    X0 = d16(lay["X"])
+    set_bytes = X0.numel() * 2 + packed0.numel() + M * N * 2
+    nsets = max(1, math.ceil(args.rotate_mb * 1e6 / set_bytes))
+    sets = [dict(X=X0.clone(), P=packed0.clone(), Y=torch.empty((M, N), dtype=torch.bfloat16, device=dev))
+            for _ in range(nsets)]
+    ws = torch.empty(hsq._load().hsq_mx_workspace_bytes(M, K, r), dtype=torch.uint8, device=dev)
+
+    def step(i):
+        st = sets[i % nsets]
+        hsq.mx_lowrank_linear(st["X"], lam, st["P"], L1, L2, bias, N=N, y_dtype="bf16", out=st["Y"],
+                              workspace=ws)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    cap = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(cap):
+        with torch.cuda.graph(g, stream=cap):
+            for i in range(args.steps):
+                step(args.warmup + i)
+    torch.cuda.synchronize()
+    g.replay()
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(cap):
+        t0.record(cap)
+        g.replay()
+        t1.record(cap)
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / args.steps
+    ops = 2 * M * N * K
+    ach = ops / (ms * 1e-3) / 1e12
+    out = {
+        "metric": "effective TOPS of the MX-fp4 W4A4+rank-4 linear (scaled fp4 MFMA)",
+        "value": round(ach, 3), "unit": "TOPS", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "fp4 (e2m1, e8m0 block-32 scales)", "data": "synthetic",
+        "config": {"workload": f"{spec.name}: {spec.description} (MX-fp4 residual)", "M": M, "K": K, "N": N,
+                   "rank": r, "rotated_sets": nsets},
+        "roofline": {"bound": "mfma", "achieved": round(ach, 2), "peak": PEAK_FP4_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(ach / PEAK_FP4_TFLOPS, 4), "traffic": None,
+                     "kernel": "whole call (quantization pass + scaled fp4 MFMA contraction)",
+                     "ops_per_launch": ops},
+        "device": device_info(torch),
+        "cpu_baseline": None,
+    }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
 def chain_main(args):
     """The FLUX.1 MLP as one fused call (up layer, GELU and the down layer's
     quantization in the up contraction's epilogue, then the down
@@ -514,6 +596,8 @@ def main(argv=None):
                          "(see summarize_profiles)")
     ap.add_argument("--write-traffic", action="store_true",
                     help="with --summarize: record the measured HBM bytes in profiles/traffic.json")
+    ap.add_argument("--mx", action="store_true",
+                    help="time the MX-fp4 variant of the layer (scaled fp4 MFMA) on --layer")
     ap.add_argument("--chain", action="store_true",
                     help="time the fused two-layer chain (FLUX.1 MLP: flux_up, GELU, flux_down) against "
                          "the two layers run one after the other")
@@ -527,6 +611,8 @@ def main(argv=None):
         return calib_main(args)
     if args.chain:
         return chain_main(args)
+    if args.mx:
+        return mx_main(args)
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:

@@ -81,7 +81,7 @@ def run_case(lay, rows=None):
     Yb = hsq.mx_lowrank_linear(X, lam, packed, L1, L2, bias, N=N, y_dtype="bf16").float()
     torch.cuda.synchronize()
     raw = wsp.cpu().numpy()
-    qa_off = align(K * 4)
+    qa_off = 0
     blob = raw[qa_off: qa_off + MT * KS * 1024]
     sa_off = align(qa_off + MT * KS * 1024)
     sc = raw[sa_off: sa_off + MT * (-(-KS // 4)) * 256]
@@ -92,7 +92,12 @@ def run_case(lay, rows=None):
     if r:
         u_off = align(sa_off + MT * (-(-KS // 4)) * 256)
         Mpad = MT * 16
-        U = raw[u_off: u_off + r * Mpad * 4].view(np.float32).reshape(r, Mpad)[:, :M].T
+        S = -(-KS // 4)                        # U partials: one per four k-steps, summed in order
+        Us = raw[u_off: u_off + S * r * Mpad * 4].view(np.float32).reshape(S, r, Mpad)
+        U = Us[0].astype(np.float32)
+        for sl in range(1, S):
+            U = (U + Us[sl]).astype(np.float32)
+        U = U[:, :M].T
         xh = mx.smoothed(lay["X"], lay["lam"]).astype(np.float64)
         L1f = (lay["L1"][0].astype(np.uint32) << 16).view(np.float32).astype(np.float64)
         assert rel(U.astype(np.float64), xh @ L1f) <= 1e-5

@@ -471,7 +471,6 @@ int hsq_mx_lowrank_linear(const uint16_t *X, int M, int K, int N, const uint16_t
   char *ws = (char *)workspace;
   MxArgs a{};
   a.X = X; a.lam = lambda; a.L1 = r > 0 ? L1 : nullptr; a.L2 = r > 0 ? L2 : nullptr; a.bias = bias;
-  a.invlam = (float *)(ws + L.invlam_off);
   a.qa = (uint8_t *)(ws + L.qa_off);
   a.sa = (uint8_t *)(ws + L.sa_off);
   a.U = (float *)(ws + L.u_off);
@@ -479,6 +478,8 @@ int hsq_mx_lowrank_linear(const uint16_t *X, int M, int K, int N, const uint16_t
   a.ws = packed_mx + (size_t)ceil_div(N, 16) * L.KS * 1024;
   a.Y = Y; a.y_bf16 = y_dtype == HSQ_BF16;
   a.M = M; a.K = K; a.N = N; a.r = r; a.KS = L.KS; a.KS4 = L.KS4; a.Mpad = L.Mpad;
+  a.u_slices = L.KS4;
+  a.wide = 0;
   return hip_status(launch_mx_linear(a, (hipStream_t)stream));
 }
 

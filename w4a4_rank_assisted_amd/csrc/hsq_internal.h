@@ -167,18 +167,19 @@ hipError_t launch_chain_ureduce(const float *upart, int nblk, int r2, int Mpad, 
 // ---------------------------------------------------------------------------
 struct MxLayout {
   int KS = 0, KS4 = 0, Mpad = 0;   // k-steps of 128 channels, groups of four k-steps, padded rows
-  size_t invlam_off = 0, qa_off = 0, sa_off = 0, u_off = 0, total = 0;
+  size_t qa_off = 0, sa_off = 0, u_off = 0, total = 0;
 };
 
 struct MxArgs {
   const uint16_t *X, *lam, *L1, *L2, *bias;
-  float *invlam;           // workspace: fl32(1/lambda)
   uint8_t *qa, *sa;        // workspace: activation codes and scales (blob layout)
   float *U;                // workspace: r x Mpad
   const uint8_t *wq, *ws;  // packed weights: codes, scales
   void *Y;
   int y_bf16;
   int M, K, N, r, KS, KS4, Mpad;
+  int u_slices;            // U partials, one per four k-steps (= KS4)
+  int wide;                // contraction workgroup: 0 -> 128 x 128, 1 -> 256 x 128
 };
 
 size_t mx_packed_bytes(int K, int N);

@@ -26,12 +26,6 @@ namespace hsq {
 
 namespace {
 
-constexpr int MB = 128, NB = 128;                 // output tile
-constexpr int MTB = MB / 16, NTB = NB / 16;      // MFMA tiles per output tile
-constexpr int MWM = 2, MWN = 4;                   // waves along M and N
-constexpr int MNT = 64 * MWM * MWN;               // 512 threads
-constexpr int MTM = MTB / MWM, MTN = NTB / MWN;   // 4 x 2 MFMA tiles per wave
-static_assert(MTB * 64 == MNT && NTB * 64 == MNT, "one A and one B 16-byte slot per thread and stage");
 
 typedef int v8i __attribute__((ext_vector_type(8)));
 
@@ -43,20 +37,12 @@ __device__ __forceinline__ int mx_scale_byte(float amax) {
   return e - 2 < 0 ? 0 : e - 2;
 }
 
-// e2m1 code (0..15) of v = x / 2^X: nearest magnitude, ties to the even
-// mantissa, saturating at 6
-__device__ __forceinline__ uint32_t e2m1_code(float v) {
-  const float m = fabsf(v);
-  float q;
-  if (m < 2.0f) q = __builtin_rintf(m * 2.0f) * 0.5f;
-  else if (m < 4.0f) q = __builtin_rintf(m);
-  else q = __builtin_rintf(m * 0.5f) * 2.0f;
-  q = fminf(q, 6.0f);
-  const uint32_t idx = q < 2.0f ? (uint32_t)(q * 2.0f) : (q < 4.0f ? (uint32_t)q + 2u : (uint32_t)(q * 0.5f) + 4u);
-  return idx | ((v < 0.0f && q > 0.0f) ? 8u : 0u);
-}
-
-// 32 values -> 16 bytes of codes (four dwords) and the scale byte
+// 32 values -> 16 bytes of codes (four dwords) and the scale byte.  v =
+// x * 2^-X is exact (a power-of-two product whose result stays below 8); the
+// packed fp4 down-conversion of gfx950 (divisor 1) rounds v to the nearest
+// e2m1 value, ties to the even mantissa, saturates at 6 and keeps the sign
+// bit; the first value of each pair goes to the low nibble of the byte
+// selected by the last operand.
 __device__ __forceinline__ int mx_block(const float (&x)[32], v4u &packed) {
   float amax = 0.0f;
 #pragma unroll
@@ -66,8 +52,10 @@ __device__ __forceinline__ int mx_block(const float (&x)[32], v4u &packed) {
 #pragma unroll
   for (int w = 0; w < 4; ++w) {
     uint32_t d = 0;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) d |= e2m1_code(x[8 * w + e] * inv) << (4 * e);
+    d = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(d, x[8 * w + 0] * inv, x[8 * w + 1] * inv, 1.0f, 0);
+    d = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(d, x[8 * w + 2] * inv, x[8 * w + 3] * inv, 1.0f, 1);
+    d = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(d, x[8 * w + 4] * inv, x[8 * w + 5] * inv, 1.0f, 2);
+    d = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(d, x[8 * w + 6] * inv, x[8 * w + 7] * inv, 1.0f, 3);
     packed[w] = d;
   }
   return sb;
@@ -91,29 +79,39 @@ __global__ void k_mx_pack_w(const float *R, int K, int N, int KS, uint8_t *blob,
   scales[(((size_t)nt * KS4 + (ks >> 2)) * 64 + lane) * 4 + (ks & 3)] = (uint8_t)sb;
 }
 
-__global__ void k_mx_invlam(const uint16_t *lam, int K, float *inv) {
-  const int k = blockIdx.x * 256 + threadIdx.x;
-  if (k < K) inv[k] = 1.0f / f16_to_f32(lam[k]);
-}
-
-// Activations of one 16-row tile: thread t takes row t % 16 and the
-// 32-blocks t / 16, t / 16 + 16, ...; its share of U (its blocks, in
-// order) is summed over the 16 threads of its row in order through LDS.
+// Activations: a workgroup takes one 16-row tile and 16 consecutive 32-blocks
+// (four k-steps); thread t takes row t % 16 and block t / 16.  Its share of
+// U is summed over the 16 threads of its row in block order through LDS and
+// written as this slice's U partial (the contraction sums the slices in
+// order).
 template <int RP>
 __global__ __launch_bounds__(256) void k_mx_quant(MxArgs a) {
+  constexpr bool STAGE = RP > 0 && RP <= 8;      // L1 rows of the slice in LDS
   __shared__ float us[16][16][RP > 0 ? RP : 1];
+  __shared__ float l1s[STAGE ? 16 * 32 * RP : 1];
+  __shared__ alignas(16) float ils[512];           // fl32(1 / lambda) of the slice's channels
   const int tid = threadIdx.x, row = tid & 15, q = tid >> 4;
   const int mt = blockIdx.x, m = mt * 16 + row;
   const int nb = 4 * a.KS;                        // 32-blocks incl. the pad of the last k-step
   float u[RP > 0 ? RP : 1];
 #pragma unroll
   for (int c = 0; c < (RP > 0 ? RP : 1); ++c) u[c] = 0.0f;
-  for (int b = q; b < nb; b += 16) {
+  const int k0 = 512 * blockIdx.y;
+  for (int p = tid; p < 512; p += 256) ils[p] = k0 + p < a.K ? 1.0f / f16_to_f32(a.lam[k0 + p]) : 0.0f;
+  if constexpr (STAGE) {
+    for (int p = tid; p < 512 * RP; p += 256) {
+      const int kk = p / RP, c = p % RP, k = k0 + kk;
+      l1s[p] = (c < a.r && k < a.K) ? bf16_to_f32(a.L1[(size_t)k * a.r + c]) : 0.0f;
+    }
+  }
+  __syncthreads();
+  // this workgroup's slice: 16 blocks (one k-step group), one per thread row
+  for (int b = 16 * blockIdx.y + q; b < min(nb, 16 * blockIdx.y + 16); b += 16) {
     float x[32];
     const bool live = m < a.M && 32 * b < a.K;
     if (live) {
       const v4u *src = reinterpret_cast<const v4u *>(a.X + (size_t)m * a.K + 32 * b);
-      const v4f *il = reinterpret_cast<const v4f *>(a.invlam + 32 * b);
+      const v4f *il = reinterpret_cast<const v4f *>(ils + 32 * (b - 16 * (int)blockIdx.y));
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
         const v4u v = src[w];
@@ -136,7 +134,15 @@ __global__ __launch_bounds__(256) void k_mx_quant(MxArgs a) {
     const int ks = b >> 2, lane = row + 16 * (b & 3);
     *reinterpret_cast<v4u *>(a.qa + (((size_t)mt * a.KS + ks) * 64 + lane) * 16) = p;
     a.sa[(((size_t)mt * a.KS4 + (ks >> 2)) * 64 + lane) * 4 + (ks & 3)] = (uint8_t)sb;
-    if constexpr (RP > 0) {
+    if constexpr (STAGE) {
+      if (live) {
+        const float *lr = l1s + (32 * (b - 16 * (int)blockIdx.y)) * RP;
+#pragma unroll
+        for (int e = 0; e < 32; ++e)
+#pragma unroll
+          for (int c = 0; c < RP; ++c) u[c] = __builtin_fmaf(x[e], lr[e * RP + c], u[c]);
+      }
+    } else if constexpr (RP > 0) {
       if (live && (a.r & 3) == 0) {
         // four rank columns per 8-byte load
 #pragma unroll 4
@@ -171,7 +177,7 @@ __global__ __launch_bounds__(256) void k_mx_quant(MxArgs a) {
       const int rr = it & 15, c = it >> 4;
       float s = 0.0f;
       for (int j = 0; j < 16; ++j) s += us[rr][j][c];
-      if (c < a.r) a.U[(size_t)c * a.Mpad + mt * 16 + rr] = s;
+      if (c < a.r) a.U[((size_t)blockIdx.y * a.r + c) * a.Mpad + mt * 16 + rr] = s;
     }
   }
 }
@@ -181,97 +187,123 @@ struct int_c {
   static constexpr int value = V;
 };
 
-// The residual contraction with the epilogue: 8 waves in 2 x 4, each 64 x
-// 32 outputs (4 x 2 MFMA tiles); one k-step (128 channels) per stage, two
-// LDS buffers, the next stage's operands loaded into registers one stage
-// ahead; scales straight from memory, one dword per tile and lane for four
-// k-steps (byte j picked by a shift).
-template <int RPT>
-__global__ __launch_bounds__(MNT, 2) void k_mx_gemm(MxArgs a) {
-  __shared__ alignas(16) uint8_t sa_[2][MTB][64][16];
-  __shared__ alignas(16) uint8_t sb_[2][NTB][64][16];
-  __shared__ float eu[RPT > 0 ? RPT : 1][MB];
-  __shared__ float el2[RPT > 0 ? RPT : 1][NB];
-  __shared__ float ebias[NB];
+// The residual contraction with the epilogue.  A workgroup of WGM x WGN
+// waves owns (TMW * WGM) x (TNW * WGN) MFMA tiles; each wave TMW x TNW of
+// them.  One k-step (128 channels) per stage; the operand blocks go
+// global -> registers -> LDS with the loads of stage s + 2 issued at the
+// start of stage s into one of two register slots (slot = stage parity,
+// fixed at compile time by unrolling), two LDS buffers, one barrier per
+// stage.  The e8m0 scales come straight from memory, one dword per tile
+// and lane for four k-steps (byte j picked by a shift).
+template <int TMW, int TNW, int WGM, int WGN, int RPT>
+__global__ __launch_bounds__(64 * WGM * WGN) void k_mx_gemm(MxArgs a) {
+  constexpr int NTHR = 64 * WGM * WGN;
+  constexpr int AT = TMW * WGM, BT = TNW * WGN;          // tiles of the workgroup
+  constexpr int LA = AT * 64 / NTHR, LB = BT * 64 / NTHR; // 16-byte slots per thread and stage
+  static_assert(AT * 64 % NTHR == 0 && BT * 64 % NTHR == 0, "whole slots per thread");
+  constexpr int BMR = AT * 16, BNC = BT * 16;            // rows, columns of the workgroup
+  __shared__ alignas(16) uint8_t opa[2][AT][64][16];
+  __shared__ alignas(16) uint8_t opb[2][BT][64][16];
+  __shared__ float eu[RPT > 0 ? RPT : 1][BMR];
+  __shared__ float el2[RPT > 0 ? RPT : 1][BNC];
+  __shared__ float ebias[BNC];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave / MWN, wn = wave % MWN;
-  const int nblk = (a.N + NB - 1) / NB;
+  const int wm = wave / WGN, wn = wave % WGN;
+  const int nblk = (a.N + BNC - 1) / BNC;
   const int mb = blockIdx.x / nblk, nb = blockIdx.x % nblk;
-  const int mt0 = mb * MTB, nt0 = nb * NTB;
+  const int mt0 = mb * AT, nt0 = nb * BT;
   const int MT = a.Mpad / 16, NT = (a.N + 15) / 16;
   const int KS = a.KS, KS4 = a.KS4;
-  // operand slot of this thread: tile tid / 64, lane tid % 64
-  const int tA = min(mt0 + (tid >> 6), MT - 1), tB = min(nt0 + (tid >> 6), NT - 1);
-  const v4u *gA = reinterpret_cast<const v4u *>(a.qa) + ((size_t)tA * KS) * 64 + lane;
-  const v4u *gB = reinterpret_cast<const v4u *>(a.wq) + ((size_t)tB * KS) * 64 + lane;
-  // scale dwords of this lane's tiles
+  const v4u *gA[LA];
+  const v4u *gB[LB];
+#pragma unroll
+  for (int u = 0; u < LA; ++u)
+    gA[u] = reinterpret_cast<const v4u *>(a.qa) + ((size_t)min(mt0 + (tid >> 6) + u * (NTHR / 64), MT - 1) * KS) * 64 + lane;
+#pragma unroll
+  for (int u = 0; u < LB; ++u)
+    gB[u] = reinterpret_cast<const v4u *>(a.wq) + ((size_t)min(nt0 + (tid >> 6) + u * (NTHR / 64), NT - 1) * KS) * 64 + lane;
   const uint32_t *sA = reinterpret_cast<const uint32_t *>(a.sa);
   const uint32_t *sB = reinterpret_cast<const uint32_t *>(a.ws);
 
-  // epilogue operands
-  for (int p = tid; p < RPT * MB; p += MNT) {
-    const int c = p / MB, rr = p % MB, m = mt0 * 16 + rr;
-    eu[c][rr] = (c < a.r && m < a.M) ? a.U[(size_t)c * a.Mpad + m] : 0.0f;
+  // epilogue operands: U (its K-slices summed in order), L2, bias
+  for (int p = tid; p < RPT * BMR; p += NTHR) {
+    const int c = p / BMR, rr = p % BMR, m = mt0 * 16 + rr;
+    float u = 0.0f;
+    if (c < a.r && m < a.M)
+      for (int sl = 0; sl < a.u_slices; ++sl) u += a.U[((size_t)sl * a.r + c) * a.Mpad + m];
+    eu[c][rr] = u;
   }
-  for (int p = tid; p < RPT * NB; p += MNT) {
-    const int c = p / NB, cc = p % NB, n = nt0 * 16 + cc;
+  for (int p = tid; p < RPT * BNC; p += NTHR) {
+    const int c = p / BNC, cc = p % BNC, n = nt0 * 16 + cc;
     el2[c][cc] = (c < a.r && n < a.N) ? bf16_to_f32(a.L2[(size_t)c * a.N + n]) : 0.0f;
   }
-  if (tid < NB) {
-    const int n = nt0 * 16 + tid;
-    ebias[tid] = (a.bias && n < a.N) ? bf16_to_f32(a.bias[n]) : 0.0f;
+  for (int p = tid; p < BNC; p += NTHR) {
+    const int n = nt0 * 16 + p;
+    ebias[p] = (a.bias && n < a.N) ? bf16_to_f32(a.bias[n]) : 0.0f;
   }
 
-  v4f acc[MTM][MTN];
+  v4f acc[TMW][TNW];
 #pragma unroll
-  for (int i = 0; i < MTM; ++i)
+  for (int i = 0; i < TMW; ++i)
 #pragma unroll
-    for (int j = 0; j < MTN; ++j) acc[i][j] = (v4f){0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < TNW; ++j) acc[i][j] = (v4f){0.f, 0.f, 0.f, 0.f};
 
-  v4u ra = gA[0], rb = gB[0];
-  *reinterpret_cast<v4u *>(&sa_[0][tid >> 6][lane][0]) = ra;
-  *reinterpret_cast<v4u *>(&sb_[0][tid >> 6][lane][0]) = rb;
+  v4u ra[2][LA], rb[2][LB];
+  auto load = [&](int ks, auto sc) __attribute__((always_inline)) {
+    constexpr int SL = decltype(sc)::value;
+    const int k = min(ks, KS - 1);                   // past the end: a clamped, unused reload
+#pragma unroll
+    for (int u = 0; u < LA; ++u) ra[SL][u] = gA[u][(size_t)k * 64];
+#pragma unroll
+    for (int u = 0; u < LB; ++u) rb[SL][u] = gB[u][(size_t)k * 64];
+  };
+  auto store = [&](int buf, auto sc) __attribute__((always_inline)) {
+    constexpr int SL = decltype(sc)::value;
+#pragma unroll
+    for (int u = 0; u < LA; ++u)
+      *reinterpret_cast<v4u *>(&opa[buf][(tid >> 6) + u * (NTHR / 64)][lane][0]) = ra[SL][u];
+#pragma unroll
+    for (int u = 0; u < LB; ++u)
+      *reinterpret_cast<v4u *>(&opb[buf][(tid >> 6) + u * (NTHR / 64)][lane][0]) = rb[SL][u];
+  };
+
+  load(0, int_c<0>{});
+  load(1, int_c<1>{});
+  store(0, int_c<0>{});
   __syncthreads();
 
-  uint32_t scA[MTM], scB[MTN];
+  uint32_t scA[TMW], scB[TNW];
+  // stage ks: J = ks % 4 (scale byte), slot and buffer = ks % 2
   auto stage = [&](int ks, auto jc) __attribute__((always_inline)) {
-    constexpr int J = decltype(jc)::value;          // byte of the scale dwords
-    const int buf = ks & 1;
+    constexpr int J = decltype(jc)::value;
+    constexpr int SL = J & 1;
     if (J == 0) {
 #pragma unroll
-      for (int i = 0; i < MTM; ++i)
-        scA[i] = sA[(((size_t)min(mt0 + wm * MTM + i, MT - 1) * KS4 + (ks >> 2)) * 64 + lane)];
+      for (int i = 0; i < TMW; ++i)
+        scA[i] = sA[(((size_t)min(mt0 + wm * TMW + i, MT - 1) * KS4 + (ks >> 2)) * 64 + lane)];
 #pragma unroll
-      for (int j = 0; j < MTN; ++j)
-        scB[j] = sB[(((size_t)min(nt0 + wn * MTN + j, NT - 1) * KS4 + (ks >> 2)) * 64 + lane)];
+      for (int j = 0; j < TNW; ++j)
+        scB[j] = sB[(((size_t)min(nt0 + wn * TNW + j, NT - 1) * KS4 + (ks >> 2)) * 64 + lane)];
     }
-    if (ks + 1 < KS) {
-      ra = gA[(size_t)(ks + 1) * 64];
-      rb = gB[(size_t)(ks + 1) * 64];
-    }
-    v8i av[MTM], bv[MTN];
+    load(ks + 2, int_c<SL>{});                        // this slot's data went to LDS a stage ago
+    v8i bv[TNW];
 #pragma unroll
-    for (int i = 0; i < MTM; ++i) {
-      const v4u v = *reinterpret_cast<const v4u *>(&sa_[buf][wm * MTM + i][lane][0]);
-      av[i] = (v8i){(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
-    }
-#pragma unroll
-    for (int j = 0; j < MTN; ++j) {
-      const v4u v = *reinterpret_cast<const v4u *>(&sb_[buf][wn * MTN + j][lane][0]);
+    for (int j = 0; j < TNW; ++j) {
+      const v4u v = *reinterpret_cast<const v4u *>(&opb[SL][wn * TNW + j][lane][0]);
       bv[j] = (v8i){(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
     }
 #pragma unroll
-    for (int i = 0; i < MTM; ++i)
+    for (int i = 0; i < TMW; ++i) {
+      const v4u v = *reinterpret_cast<const v4u *>(&opa[SL][wm * TMW + i][lane][0]);
+      const v8i av = (v8i){(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
+      const int sa_b = (int)((scA[i] >> (8 * J)) & 0xFFu);
 #pragma unroll
-      for (int j = 0; j < MTN; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-            av[i], bv[j], acc[i][j], 4, 4, 0, (int)((scA[i] >> (8 * J)) & 0xFFu), 0,
-            (int)((scB[j] >> (8 * J)) & 0xFFu));
-    if (ks + 1 < KS) {
-      *reinterpret_cast<v4u *>(&sa_[buf ^ 1][tid >> 6][lane][0]) = ra;
-      *reinterpret_cast<v4u *>(&sb_[buf ^ 1][tid >> 6][lane][0]) = rb;
+      for (int j = 0; j < TNW; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv[j], acc[i][j], 4, 4, 0, sa_b, 0,
+                                                                     (int)((scB[j] >> (8 * J)) & 0xFFu));
     }
+    if (ks + 1 < KS) store(SL ^ 1, int_c<SL ^ 1>{});
     __syncthreads();
   };
   int ks = 0;
@@ -285,39 +317,73 @@ __global__ __launch_bounds__(MNT, 2) void k_mx_gemm(MxArgs a) {
   if (ks + 1 < KS) stage(ks + 1, int_c<1>{});
   if (ks + 2 < KS) stage(ks + 2, int_c<2>{});
 
-  // epilogue: Y = acc + U L2 + bias
+  // epilogue: Y = acc + U L2 + bias; per row tile the wave's 16 x WCOL
+  // values go through a wave-private LDS region (the operand buffers are
+  // free after the last barrier) and leave as 16-byte row-contiguous stores
+  constexpr int WCOL = TNW * 16;
+  static_assert(WGM * WGN * 16 * WCOL * 4 <= (int)sizeof(opa), "transpose region");
+  char *tb = reinterpret_cast<char *>(&opa[0][0][0][0]) + wave * (16 * WCOL * 4);
   const int rowq = 4 * (lane >> 4), colq = lane & 15;
+  const int yb = a.y_bf16 ? 2 : 4, per16 = 16 / yb, cpr = WCOL / per16;
+  const bool vec_ok = (a.N % per16) == 0;
+  const int ncol0 = (nt0 + wn * TNW) * 16;
 #pragma unroll
-  for (int i = 0; i < MTM; ++i)
+  for (int i = 0; i < TMW; ++i) {
 #pragma unroll
-    for (int j = 0; j < MTN; ++j) {
-      const int cc = (wn * MTN + j) * 16 + colq, n = nt0 * 16 + cc;
+    for (int j = 0; j < TNW; ++j) {
+      const int cc = (wn * TNW + j) * 16 + colq;
 #pragma unroll
       for (int qq = 0; qq < 4; ++qq) {
-        const int rr = (wm * MTM + i) * 16 + rowq + qq, m = mt0 * 16 + rr;
+        const int rr = (wm * TMW + i) * 16 + rowq + qq;
         float y = acc[i][j][qq];
 #pragma unroll
         for (int c = 0; c < RPT; ++c) y = __builtin_fmaf(eu[c][rr], el2[c][cc], y);
         y += ebias[cc];
-        if (m < a.M && n < a.N) {
-          const size_t off = (size_t)m * a.N + n;
-          if (a.y_bf16)
-            reinterpret_cast<uint16_t *>(a.Y)[off] = f32_to_bf16(y);
-          else
-            reinterpret_cast<float *>(a.Y)[off] = y;
-        }
+        const int off = (rowq + qq) * WCOL + j * 16 + colq;
+        if (a.y_bf16)
+          reinterpret_cast<uint16_t *>(tb)[off] = f32_to_bf16(y);
+        else
+          reinterpret_cast<float *>(tb)[off] = y;
       }
     }
+    const int mrow0 = (mt0 + wm * TMW + i) * 16;
+    for (int k = lane; k < 16 * cpr; k += 64) {
+      const int row = k / cpr, ch = k % cpr;
+      const int m = mrow0 + row, n = ncol0 + ch * per16;
+      if (m >= a.M || n >= a.N) continue;
+      const v4u v = *reinterpret_cast<const v4u *>(tb + (row * WCOL + ch * per16) * yb);
+      char *dst = reinterpret_cast<char *>(a.Y) + ((size_t)m * a.N + n) * yb;
+      if (vec_ok && n + per16 <= a.N) {
+        *reinterpret_cast<v4u *>(dst) = v;
+      } else if (a.y_bf16) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          if (n + e < a.N) reinterpret_cast<uint16_t *>(dst)[e] = (uint16_t)(v[e >> 1] >> (16 * (e & 1)));
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (n + e < a.N) reinterpret_cast<uint32_t *>(dst)[e] = v[e];
+      }
+    }
+  }
+}
+
+// workgroup shapes: 128 x 128 (4 waves of 64 x 64) and 256 x 128 (4 waves of
+// 128 x 64)
+template <int RP, int TMW>
+hipError_t launch_mx_gemm(const MxArgs &a, hipStream_t s) {
+  constexpr int TNW = 4, WGM = 2, WGN = 2;
+  const int tiles = ceil_div(a.N, 16 * TNW * WGN) * ceil_div(a.M, 16 * TMW * WGM);
+  hipLaunchKernelGGL((k_mx_gemm<TMW, TNW, WGM, WGN, RP>), dim3((unsigned)tiles), dim3(64 * WGM * WGN), 0, s, a);
+  return hipGetLastError();
 }
 
 template <int RP>
 hipError_t launch_mx_rp(const MxArgs &a, hipStream_t s) {
-  hipLaunchKernelGGL(k_mx_quant<RP>, dim3((unsigned)(a.Mpad / 16)), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(k_mx_quant<RP>, dim3((unsigned)(a.Mpad / 16), (unsigned)a.u_slices), dim3(256), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int tiles = ceil_div(a.N, NB) * ceil_div(a.M, MB);
-  hipLaunchKernelGGL(k_mx_gemm<RP>, dim3((unsigned)tiles), dim3(MNT), 0, s, a);
-  return hipGetLastError();
+  return a.wide ? launch_mx_gemm<RP, 8>(a, s) : launch_mx_gemm<RP, 4>(a, s);
 }
 
 }  // namespace
@@ -333,14 +399,12 @@ MxLayout plan_mx(int M, int K, int r) {
   L.KS4 = ceil_div(L.KS, 4);
   L.Mpad = ceil_div(M, 16) * 16;
   size_t off = 0;
-  L.invlam_off = off;
-  off = align_up(off + (size_t)K * sizeof(float), 256);
   L.qa_off = off;
   off = align_up(off + (size_t)(L.Mpad / 16) * L.KS * 1024, 256);
   L.sa_off = off;
   off = align_up(off + (size_t)(L.Mpad / 16) * L.KS4 * 256, 256);
   L.u_off = off;
-  off = align_up(off + (size_t)r * L.Mpad * sizeof(float), 256);
+  off = align_up(off + (size_t)L.KS4 * r * L.Mpad * sizeof(float), 256);
   L.total = off;
   return L;
 }
@@ -353,9 +417,6 @@ hipError_t launch_mx_pack(const float *R, int K, int N, uint8_t *packed, hipStre
 }
 
 hipError_t launch_mx_linear(const MxArgs &a, hipStream_t s) {
-  hipLaunchKernelGGL(k_mx_invlam, dim3((unsigned)ceil_div(a.K, 256)), dim3(256), 0, s, a.lam, a.K, a.invlam);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
   if (a.r == 0) return launch_mx_rp<0>(a, s);
   if (a.r <= 4) return launch_mx_rp<4>(a, s);
   if (a.r <= 8) return launch_mx_rp<8>(a, s);
