@@ -479,7 +479,6 @@ int hsq_mx_lowrank_linear(const uint16_t *X, int M, int K, int N, const uint16_t
   a.Y = Y; a.y_bf16 = y_dtype == HSQ_BF16;
   a.M = M; a.K = K; a.N = N; a.r = r; a.KS = L.KS; a.KS4 = L.KS4; a.Mpad = L.Mpad;
   a.u_slices = L.KS4;
-  a.wide = 0;
   return hip_status(launch_mx_linear(a, (hipStream_t)stream));
 }
 

@@ -118,25 +118,6 @@ struct int_c {
 __device__ __forceinline__ void pin(v4i &x) { asm volatile("" : "+v"(x)); }
 __device__ __forceinline__ void pin(float &x) { asm volatile("" : "+v"(x)); }
 
-// block index -> (m-block, n-block).  Consecutive workgroup ids go to
-// different XCDs (id % 8); regroup them so that XCD x owns a contiguous
-// range of the tile order, and walk that order in groups of kGroupM
-// m-blocks so concurrently running tiles share rows of A and columns of B.
-__device__ __forceinline__ void tile_of(int bid, int nblk, int mblk, int &mb, int &nb) {
-  const int T = nblk * mblk;
-  const int per = T / 8, rem = T % 8;
-  const int x = bid % 8, loc = bid / 8;
-  // XCD x owns [start(x), start(x) + per + (x < rem)); ids with loc == per
-  // exist only for x < rem.
-  const int t = x * per + min(x, rem) + loc;
-  const int span = kGroupM * nblk;
-  const int grp = t / span, first = grp * kGroupM;
-  const int gsz = min(mblk - first, kGroupM);
-  const int w = t % span;
-  mb = first + w % gsz;
-  nb = w / gsz;
-}
-
 template <bool DUMP, int RPT, int MODE, int BPG, int KH, bool CHAIN = false>
 __global__ __launch_bounds__(NTH * KH, 2) void k_gemm_tiled(GemmArgs a, int nblk, int mblk) {
   static_assert(MODE != kSplit || RPT == 0, "a split pass has no epilogue");
@@ -154,7 +135,7 @@ __global__ __launch_bounds__(NTH * KH, 2) void k_gemm_tiled(GemmArgs a, int nblk
   const int wm = wave / WN, wn = wave % WN;
   const int proj = blockIdx.y;
   int mb, nb;
-  tile_of(blockIdx.x, nblk, mblk, mb, nb);
+  xcd_tile_of(blockIdx.x, nblk, mblk, kGroupM, mb, nb);
   const int mt0 = mb * TMB, nt0 = nb * TNB;
   const int MT = a.Mpad / 16, NT = (a.N + 15) / 16;
   const int GP = a.Gp / 2;            // group pairs in the packed residual

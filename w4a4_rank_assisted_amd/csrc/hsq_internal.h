@@ -162,6 +162,25 @@ hipError_t launch_gemm_skinny(const GemmArgs &a, int batch, bool dump, hipStream
 hipError_t launch_gemm_tiled_chain(const GemmArgs &a, hipStream_t s);
 hipError_t launch_chain_ureduce(const float *upart, int nblk, int r2, int Mpad, float *uw, hipStream_t s);
 
+// block index -> (m-block, n-block).  Consecutive workgroup ids go to
+// different XCDs (id % 8); regroup them so that XCD x owns a contiguous
+// range of the tile order, and walk that order in groups of group_m
+// m-blocks so concurrently running tiles share rows of A and columns of B.
+__device__ __forceinline__ void xcd_tile_of(int bid, int nblk, int mblk, int group_m, int &mb, int &nb) {
+  const int T = nblk * mblk;
+  const int per = T / 8, rem = T % 8;
+  const int x = bid % 8, loc = bid / 8;
+  // XCD x owns [start(x), start(x) + per + (x < rem)); ids with loc == per
+  // exist only for x < rem.
+  const int t = x * per + min(x, rem) + loc;
+  const int span = group_m * nblk;
+  const int grp = t / span, first = grp * group_m;
+  const int gsz = min(mblk - first, group_m);
+  const int w = t % span;
+  mb = first + w % gsz;
+  nb = w / gsz;
+}
+
 // ---------------------------------------------------------------------------
 // MX-fp4 variant (mx.hip)
 // ---------------------------------------------------------------------------
@@ -179,7 +198,6 @@ struct MxArgs {
   int y_bf16;
   int M, K, N, r, KS, KS4, Mpad;
   int u_slices;            // U partials, one per four k-steps (= KS4)
-  int wide;                // contraction workgroup: 0 -> 128 x 128, 1 -> 256 x 128
 };
 
 size_t mx_packed_bytes(int K, int N);

@@ -194,8 +194,9 @@ struct int_c {
 // start of stage s into one of two register slots (slot = stage parity,
 // fixed at compile time by unrolling), two LDS buffers, one barrier per
 // stage.  The e8m0 scales come straight from memory, one dword per tile
-// and lane for four k-steps (byte j picked by a shift).
-template <int TMW, int TNW, int WGM, int WGN, int RPT>
+// and lane for four k-steps (byte j picked by a shift).  Workgroups walk
+// the tiles in the XCD-grouped order of xcd_tile_of.
+template <int TMW, int TNW, int WGM, int WGN, int RPT, int GROUPM = 8>
 __global__ __launch_bounds__(64 * WGM * WGN) void k_mx_gemm(MxArgs a) {
   constexpr int NTHR = 64 * WGM * WGN;
   constexpr int AT = TMW * WGM, BT = TNW * WGN;          // tiles of the workgroup
@@ -210,8 +211,9 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_mx_gemm(MxArgs a) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / WGN, wn = wave % WGN;
-  const int nblk = (a.N + BNC - 1) / BNC;
-  const int mb = blockIdx.x / nblk, nb = blockIdx.x % nblk;
+  const int nblk = (a.N + BNC - 1) / BNC, mblk = (a.Mpad / 16 + AT - 1) / AT;
+  int mb, nb;
+  xcd_tile_of(blockIdx.x, nblk, mblk, GROUPM, mb, nb);
   const int mt0 = mb * AT, nt0 = nb * BT;
   const int MT = a.Mpad / 16, NT = (a.N + 15) / 16;
   const int KS = a.KS, KS4 = a.KS4;
@@ -383,7 +385,7 @@ hipError_t launch_mx_rp(const MxArgs &a, hipStream_t s) {
   hipLaunchKernelGGL(k_mx_quant<RP>, dim3((unsigned)(a.Mpad / 16), (unsigned)a.u_slices), dim3(256), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  return a.wide ? launch_mx_gemm<RP, 8>(a, s) : launch_mx_gemm<RP, 4>(a, s);
+  return launch_mx_gemm<RP, 4>(a, s);
 }
 
 }  // namespace
