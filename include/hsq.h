@@ -218,6 +218,38 @@ int hsq_w4a4_group_partials_g(const uint16_t *X, int M, int K, int N, int group,
                               int n0, int nc, int32_t *P, void *workspace, size_t ws_bytes,
                               int kernel, void *stream);
 
+/* ---- asymmetric activations ----
+ * The activation format of the INT W4A4 setting in the DiRotQ notes
+ * (papernotes.org, experimental setup): activations quantized per token and
+ * group asymmetrically, weights symmetrically as above.  The notes print no
+ * formula; this library reads it as the min-max quantizer with 16 levels
+ * whose range is widened to contain 0 (so that 0 is a level):
+ *   lo[m,g]  = min(0, min_{k in g} xh[m,k]),  hi[m,g] = max(0, max_{k in g} xh[m,k])
+ *   sx[m,g]  = fp16_rne(fl32(fl32(hi - lo) / 15))   (0 if hi == lo; saturates at 65504)
+ *   z[m,g]   = clamp(rint(fl32(-lo * fl32(1 / sx))), 0, 15)      zero point
+ *   q[m,k]   = clamp(rint(fl32(xh * fl32(1 / sx))) + z, 0, 15)  (all 0 if sx = 0)
+ *   qx[m,k]  = q[m,k] - z[m,g]                      in [-15, 15]
+ * and P, U, Y as in the formula block (with this qx).  qx fits the int8
+ * operand of the contraction, so both contraction kernels run unchanged.
+ * act_quant is HSQ_AQ_SYMMETRIC (the formula block; each function then
+ * equals its _g counterpart) or HSQ_AQ_ASYMMETRIC; anything else is
+ * HSQ_E_INVAL.  Arguments, workspace and errors otherwise as for the _g
+ * functions. */
+#define HSQ_AQ_SYMMETRIC   0
+#define HSQ_AQ_ASYMMETRIC  1
+int hsq_w4a4_lowrank_linear_aq(const uint16_t *X, int M, int K, int N, int batch, int group,
+                               int act_quant, const uint16_t *lambda, const uint8_t *packed_w,
+                               const uint16_t *sw, const uint16_t *L1, const uint16_t *L2, int r,
+                               const uint16_t *bias, void *Y, int y_dtype, void *workspace,
+                               size_t ws_bytes, int kernel, void *stream);
+int hsq_w4a4_quantize_stage_aq(const uint16_t *X, int M, int K, int N, int batch, int group,
+                               int act_quant, const uint16_t *lambda, const uint16_t *L1, int r,
+                               void *workspace, size_t ws_bytes, void *stream);
+int hsq_w4a4_group_partials_aq(const uint16_t *X, int M, int K, int N, int group, int act_quant,
+                               const uint16_t *lambda, const uint8_t *packed_w, int m0, int mc,
+                               int n0, int nc, int32_t *P, void *workspace, size_t ws_bytes,
+                               int kernel, void *stream);
+
 /* ---- MX-fp4 format variant of the layer ----
  * The same layer (smoothing, rank-r branch on the smoothed activations,
  * bias) with both 4-bit operands of the residual product in MX-fp4 (OCP
@@ -225,7 +257,8 @@ int hsq_w4a4_group_partials_g(const uint16_t *X, int M, int K, int N, int group,
  * 32 consecutive values along K one e8m0 scale 2^X, X = floor(log2 amax) - 2
  * (stored as X + 127, clamped to [0, 254]; a zero block stores 127), and
  * e2m1 elements {0, 0.5, 1, 1.5, 2, 3, 4, 6} rounded to nearest (ties to the
- * even mantissa), magnitudes above 6 saturating.  The activations are
+ * even mantissa), magnitudes above 6 saturating; the code keeps the value's
+ * sign bit, also where the magnitude rounds to 0 (-0, code 8).  The activations are
  * blocked per token, the residual per output column.  The product runs on
  * gfx950's scaled fp4 MFMA, which applies both scales.
  * hsq_mx_pack_weights: R (K x N fp32, the residual, row-major) -> packed

@@ -72,6 +72,9 @@ def _load():
             "hsq_w4a4_quantize_stage_g": ([P, I, I, I, I, I, P, P, I, P, S, P], I),
             "hsq_w4a4_contract_stage_g": ([I, I, I, I, I, P, P, P, I, P, P, I, P, S, I, P], I),
             "hsq_w4a4_group_partials_g": ([P, I, I, I, I, P, P, I, I, I, I, P, P, S, I, P], I),
+            "hsq_w4a4_lowrank_linear_aq": ([P, I, I, I, I, I, I, P, P, P, P, P, I, P, P, I, P, S, I, P], I),
+            "hsq_w4a4_quantize_stage_aq": ([P, I, I, I, I, I, I, P, P, I, P, S, P], I),
+            "hsq_w4a4_group_partials_aq": ([P, I, I, I, I, I, P, P, I, I, I, I, P, P, S, I, P], I),
             "hsq_mx_packed_weight_bytes": ([I, I], S),
             "hsq_mx_pack_weights": ([P, I, I, P, P], I),
             "hsq_mx_workspace_bytes": ([I, I, I], S),
@@ -204,13 +207,17 @@ def quantize_act(X, lam, L1=None):
     return qx, sx, U[:, :r]
 
 
+_ACT_QUANT = {"sym": 0, "asym": 1}
+
+
 def w4a4_lowrank_linear(X, lam, packed_w, sw, L1=None, L2=None, bias=None, *, N: int,
                         batch: int = 1, y_dtype: str = "bf16", out=None, workspace=None,
-                        kernel: str = "auto", group: int = 64):
+                        kernel: str = "auto", group: int = 64, act_quant: str = "sym"):
     """The fused layer.  Shapes: X (M, K); lam (K,); packed_w (batch * blob,);
     sw (batch, K/group, N); L1 (batch, K, r); L2 (batch, r, N); bias (batch, N).
-    Returns Y (batch, M, N) as bf16 or fp32.  group 64 calls
-    hsq_w4a4_lowrank_linear_ex, other widths hsq_w4a4_lowrank_linear_g."""
+    Returns Y (batch, M, N) as bf16 or fp32.  Symmetric group-64 activations
+    call hsq_w4a4_lowrank_linear_ex, other widths hsq_w4a4_lowrank_linear_g,
+    asymmetric activations (act_quant="asym") hsq_w4a4_lowrank_linear_aq."""
     torch = _torch()
     lib = _load()
     _dev_tensor(X, "X", _half_types())
@@ -236,7 +243,10 @@ def w4a4_lowrank_linear(X, lam, packed_w, sw, L1=None, L2=None, bias=None, *, N:
     args = (_ptr(lam), _ptr(packed_w), _ptr(sw), _ptr(L1) if r else None, _ptr(L2) if r else None,
             r, _ptr(bias), _ptr(out), ydt[0], _ptr(workspace), workspace.numel(), _KERNELS[kernel],
             _stream())
-    if group == 64:
+    if act_quant != "sym":
+        _check(lib.hsq_w4a4_lowrank_linear_aq(_ptr(X), M, K, N, batch, group, _ACT_QUANT[act_quant], *args),
+               "hsq_w4a4_lowrank_linear_aq")
+    elif group == 64:
         _check(lib.hsq_w4a4_lowrank_linear_ex(_ptr(X), M, K, N, batch, *args), "hsq_w4a4_lowrank_linear")
     else:
         _check(lib.hsq_w4a4_lowrank_linear_g(_ptr(X), M, K, N, batch, group, *args),
@@ -244,15 +254,16 @@ def w4a4_lowrank_linear(X, lam, packed_w, sw, L1=None, L2=None, bias=None, *, N:
     return out
 
 
-def quantize_stage(X, lam, L1, *, N: int, batch: int, workspace, group: int = 64):
+def quantize_stage(X, lam, L1, *, N: int, batch: int, workspace, group: int = 64,
+                   act_quant: str = "sym"):
     """First stage of the layer: quantize X and form U into ``workspace``."""
     lib = _load()
     M, K = X.shape
     r = 0 if L1 is None else int(L1.shape[-1])
-    _check(lib.hsq_w4a4_quantize_stage_g(_ptr(X), M, K, N, batch, group, _ptr(lam),
-                                         _ptr(L1) if r else None, r, _ptr(workspace),
-                                         workspace.numel(), _stream()),
-           "hsq_w4a4_quantize_stage_g")
+    _check(lib.hsq_w4a4_quantize_stage_aq(_ptr(X), M, K, N, batch, group, _ACT_QUANT[act_quant],
+                                          _ptr(lam), _ptr(L1) if r else None, r, _ptr(workspace),
+                                          workspace.numel(), _stream()),
+           "hsq_w4a4_quantize_stage_aq")
 
 
 def contract_stage(M: int, K: int, packed_w, sw, L2, bias, out, *, N: int, batch: int, r: int,
@@ -269,7 +280,7 @@ def contract_stage(M: int, K: int, packed_w, sw, L2, bias, out, *, N: int, batch
 
 
 def w4a4_group_partials(X, lam, packed_w, N: int, m0: int, mc: int, n0: int, nc: int,
-                        workspace=None, kernel: str = "auto", group: int = 64):
+                        workspace=None, kernel: str = "auto", group: int = 64, act_quant: str = "sym"):
     """int32 P (mc, nc, K/group) of the window, from the production kernels."""
     torch = _torch()
     lib = _load()
@@ -283,7 +294,10 @@ def w4a4_group_partials(X, lam, packed_w, N: int, m0: int, mc: int, n0: int, nc:
         workspace = torch.empty(need, dtype=torch.uint8, device=X.device)
     args = (_ptr(lam), _ptr(packed_w), m0, mc, n0, nc, _ptr(P), _ptr(workspace), workspace.numel(),
             _KERNELS[kernel], _stream())
-    if group == 64:
+    if act_quant != "sym":
+        _check(lib.hsq_w4a4_group_partials_aq(_ptr(X), M, K, N, group, _ACT_QUANT[act_quant], *args),
+               "hsq_w4a4_group_partials_aq")
+    elif group == 64:
         _check(lib.hsq_w4a4_group_partials(_ptr(X), M, K, N, *args), "hsq_w4a4_group_partials")
     else:
         _check(lib.hsq_w4a4_group_partials_g(_ptr(X), M, K, N, group, *args),

@@ -109,7 +109,8 @@ int validate(const uint16_t *X, int M, int K, int N, int batch, int group,
 }
 
 int quant_stage(const uint16_t *X, int M, int K, int N, int batch, int group,
-                const uint16_t *lambda, const uint16_t *L1, int r, void *workspace, hipStream_t s) {
+                const uint16_t *lambda, const uint16_t *L1, int r, void *workspace, hipStream_t s,
+                int aq = HSQ_AQ_SYMMETRIC) {
   const WsLayout L = plan_workspace(M, K, N, r, batch, group);
   char *ws = (char *)workspace;
   QuantArgs q{};
@@ -124,6 +125,7 @@ int quant_stage(const uint16_t *X, int M, int K, int N, int batch, int group,
   q.sxs = (uint16_t *)(ws + L.sxs_off);
   q.uw = (float *)(ws + L.uw_off);
   q.Gp = L.Gp; q.Mpad = L.Mpad; q.ucols = batch * r;
+  q.asym = aq == HSQ_AQ_ASYMMETRIC;
   return hip_status(launch_quant_tiles(q, s));
 }
 
@@ -159,12 +161,12 @@ int run_linear(const uint16_t *X, int M, int K, int N, int batch, int group,
                const uint16_t *L1, const uint16_t *L2, int r, const uint16_t *bias, void *Y,
                int y_dtype, void *workspace, size_t ws_bytes, int kernel, void *stream,
                // partial-sum dump (test export); P == nullptr for the linear
-               int32_t *P, int m0, int mc, int n0, int nc) {
+               int32_t *P, int m0, int mc, int n0, int nc, int aq = HSQ_AQ_SYMMETRIC) {
   int st = validate(X, M, K, N, batch, group, lambda, packed_w, sw, L1, L2, r, bias, Y, y_dtype,
                     workspace, ws_bytes, &kernel, true, true, P, m0, mc, n0, nc);
   if (st != HSQ_OK) return st;
   hipStream_t s = (hipStream_t)stream;
-  st = quant_stage(X, M, K, N, batch, group, lambda, L1, r, workspace, s);
+  st = quant_stage(X, M, K, N, batch, group, lambda, L1, r, workspace, s, aq);
   if (st != HSQ_OK) return st;
   return contract_stage(M, K, N, batch, group, packed_w, sw, L2, r, bias, Y, y_dtype, workspace,
                         kernel, s, P, m0, mc, n0, nc);
@@ -172,12 +174,12 @@ int run_linear(const uint16_t *X, int M, int K, int N, int batch, int group,
 
 int quantize_stage_g(const uint16_t *X, int M, int K, int N, int batch, int group,
                      const uint16_t *lambda, const uint16_t *L1, int r, void *workspace,
-                     size_t ws_bytes, void *stream) {
+                     size_t ws_bytes, void *stream, int aq = HSQ_AQ_SYMMETRIC) {
   int kernel = HSQ_KERNEL_AUTO;
   int st = validate(X, M, K, N, batch, group, lambda, nullptr, nullptr, L1, nullptr, r, nullptr,
                     nullptr, HSQ_F32, workspace, ws_bytes, &kernel, true, false, nullptr, 0, 0, 0, 0);
   if (st != HSQ_OK) return st;
-  return quant_stage(X, M, K, N, batch, group, lambda, L1, r, workspace, (hipStream_t)stream);
+  return quant_stage(X, M, K, N, batch, group, lambda, L1, r, workspace, (hipStream_t)stream, aq);
 }
 
 int contract_stage_g(int M, int K, int N, int batch, int group, const uint8_t *packed_w,
@@ -284,11 +286,14 @@ int run_chain(const uint16_t *X, int M, int K, int H, int N, const uint16_t *lam
 
 int group_partials_g(const uint16_t *X, int M, int K, int N, int group, const uint16_t *lambda,
                      const uint8_t *packed_w, int m0, int mc, int n0, int nc, int32_t *P,
-                     void *workspace, size_t ws_bytes, int kernel, void *stream) {
+                     void *workspace, size_t ws_bytes, int kernel, void *stream,
+                     int aq = HSQ_AQ_SYMMETRIC) {
   if (!P) return HSQ_E_INVAL;
   return run_linear(X, M, K, N, 1, group, lambda, packed_w, nullptr, nullptr, nullptr, 0, nullptr,
-                    nullptr, HSQ_F32, workspace, ws_bytes, kernel, stream, P, m0, mc, n0, nc);
+                    nullptr, HSQ_F32, workspace, ws_bytes, kernel, stream, P, m0, mc, n0, nc, aq);
 }
+
+bool aq_ok(int aq) { return aq == HSQ_AQ_SYMMETRIC || aq == HSQ_AQ_ASYMMETRIC; }
 
 }  // namespace
 
@@ -433,6 +438,33 @@ int hsq_w4a4_group_partials_g(const uint16_t *X, int M, int K, int N, int group,
                               int kernel, void *stream) {
   return group_partials_g(X, M, K, N, group, lambda, packed_w, m0, mc, n0, nc, P, workspace,
                           ws_bytes, kernel, stream);
+}
+
+int hsq_w4a4_lowrank_linear_aq(const uint16_t *X, int M, int K, int N, int batch, int group,
+                               int act_quant, const uint16_t *lambda, const uint8_t *packed_w,
+                               const uint16_t *sw, const uint16_t *L1, const uint16_t *L2, int r,
+                               const uint16_t *bias, void *Y, int y_dtype, void *workspace,
+                               size_t ws_bytes, int kernel, void *stream) {
+  if (!aq_ok(act_quant)) return HSQ_E_INVAL;
+  return run_linear(X, M, K, N, batch, group, lambda, packed_w, sw, L1, L2, r, bias, Y, y_dtype,
+                    workspace, ws_bytes, kernel, stream, nullptr, 0, 0, 0, 0, act_quant);
+}
+
+int hsq_w4a4_quantize_stage_aq(const uint16_t *X, int M, int K, int N, int batch, int group,
+                               int act_quant, const uint16_t *lambda, const uint16_t *L1, int r,
+                               void *workspace, size_t ws_bytes, void *stream) {
+  if (!aq_ok(act_quant)) return HSQ_E_INVAL;
+  return quantize_stage_g(X, M, K, N, batch, group, lambda, L1, r, workspace, ws_bytes, stream,
+                          act_quant);
+}
+
+int hsq_w4a4_group_partials_aq(const uint16_t *X, int M, int K, int N, int group, int act_quant,
+                               const uint16_t *lambda, const uint8_t *packed_w, int m0, int mc,
+                               int n0, int nc, int32_t *P, void *workspace, size_t ws_bytes,
+                               int kernel, void *stream) {
+  if (!aq_ok(act_quant)) return HSQ_E_INVAL;
+  return group_partials_g(X, M, K, N, group, lambda, packed_w, m0, mc, n0, nc, P, workspace,
+                          ws_bytes, kernel, stream, act_quant);
 }
 
 // ---------------------------------------------------------------- MX-fp4 variant

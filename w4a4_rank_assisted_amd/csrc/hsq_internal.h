@@ -90,6 +90,7 @@ struct QuantArgs {
   int c0, cb;              // rank columns [c0, c0 + cb) of the batch*r columns
   int kend;                // channels processed: K (public) or 64*Gp (internal)
   int write_codes;         // 0: rank pass only
+  int asym;                // 1: asymmetric codes (q - z, zero point z per group)
   // public outputs (packed codes, fp16 scales, U as M x r)
   uint8_t *qx;
   uint16_t *sx;

@@ -79,7 +79,10 @@ TilePlan tile_plan(int M, int K, int r, int batch, int group) {
   return p;
 }
 
-template <int NR, bool CODES, int BPG>
+// code modes: rank pass only, symmetric codes, asymmetric codes
+constexpr int kNoCodes = 0, kSymCodes = 1, kAsymCodes = 2;
+
+template <int NR, int CM, int BPG>
 __global__ __launch_bounds__(1024) void k_quant_tiles(QuantArgs a, int gpb) {
   // dynamic LDS: 1/lambda [gpb*BPG][4][kLamKq], L1 [gpb*BPG][4][kqs(NR)]
   // (per 64-block and channel block: 16 channels x NR columns); after the
@@ -203,16 +206,37 @@ __global__ __launch_bounds__(1024) void k_quant_tiles(QuantArgs a, int gpb) {
       h[15] = bf16_to_f32(x1.w >> 16) * l3.w;
     }
 
-    if constexpr (CODES) {
-      float amax = 0.0f;
-#pragma unroll
-      for (int i = 0; i < 16 * BPG; ++i) amax = fmaxf(amax, fabsf(xh[i]));
-      amax = fmaxf(amax, __shfl_xor(amax, 16));
-      amax = fmaxf(amax, __shfl_xor(amax, 32));
+    if constexpr (CM != kNoCodes) {
       uint16_t s16 = 0;
-      if (amax != 0.0f) {
-        s16 = f32_to_f16(amax / 7.0f);
-        if (s16 == 0x7C00u) s16 = 0x7BFFu;        // saturate at 65504
+      int zq = 0;                                 // zero point (asymmetric codes)
+      float gmin = 0.0f;                          // group minimum, widened to 0 (asymmetric)
+      if constexpr (CM == kSymCodes) {
+        float amax = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 16 * BPG; ++i) amax = fmaxf(amax, fabsf(xh[i]));
+        amax = fmaxf(amax, __shfl_xor(amax, 16));
+        amax = fmaxf(amax, __shfl_xor(amax, 32));
+        if (amax != 0.0f) {
+          s16 = f32_to_f16(amax / 7.0f);
+          if (s16 == 0x7C00u) s16 = 0x7BFFu;      // saturate at 65504
+        }
+      } else {
+        // asymmetric: the group's range widened to contain 0, 16 levels
+        float gmax = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 16 * BPG; ++i) {
+          gmin = fminf(gmin, xh[i]);
+          gmax = fmaxf(gmax, xh[i]);
+        }
+        gmin = fminf(gmin, __shfl_xor(gmin, 16));
+        gmin = fminf(gmin, __shfl_xor(gmin, 32));
+        gmax = fmaxf(gmax, __shfl_xor(gmax, 16));
+        gmax = fmaxf(gmax, __shfl_xor(gmax, 32));
+        const float range = gmax - gmin;
+        if (range != 0.0f) {
+          s16 = f32_to_f16(range / 15.0f);
+          if (s16 == 0x7C00u) s16 = 0x7BFFu;      // saturate at 65504
+        }
       }
       const float s = f16_to_f32(s16);
       const float inv_s = (s16 != 0) ? 1.0f / s : 0.0f;
@@ -220,14 +244,20 @@ __global__ __launch_bounds__(1024) void k_quant_tiles(QuantArgs a, int gpb) {
       // fp32 quotient to an integer (ties to even) in the low mantissa bits;
       // the clamp works on those bits (a quotient beyond +-2^22 lands outside
       // the clamp window on the right side).  The low byte of the clamped
-      // bits is the two's-complement code.
+      // bits is the two's-complement code.  Asymmetric: zero point z =
+      // clamp(rint(fl32(-gmin / s)), 0, 15), code q = clamp(rint(fl32(xh / s))
+      // + z, 0, 15), and the operand holds q - z (in [-15, 15]).
+      if constexpr (CM == kAsymCodes) zq = min(max(__float_as_int(-gmin * inv_s + kMagic) - kMagicBits, 0), 15);
 #pragma unroll
       for (int b = 0; b < BPG; ++b) {
         int c[16];
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int v = __float_as_int(xh[16 * b + i] * inv_s + kMagic);
-          c[i] = min(max(v, kMagicBits - 8), kMagicBits + 7);
+          if constexpr (CM == kSymCodes)
+            c[i] = min(max(v, kMagicBits - 8), kMagicBits + 7);
+          else
+            c[i] = min(max(v + zq, kMagicBits), kMagicBits + 15) - zq;
         }
         v4u w;
 #pragma unroll
@@ -281,25 +311,27 @@ __global__ __launch_bounds__(1024) void k_quant_tiles(QuantArgs a, int gpb) {
 }
 
 template <int NR, int BPG>
-hipError_t launch_pass(const QuantArgs &a, const TilePlan &p, bool codes, hipStream_t s) {
+hipError_t launch_pass(const QuantArgs &a, const TilePlan &p, int cm, hipStream_t s) {
   const dim3 grid((unsigned)(a.Mpad / kTile), (unsigned)p.slices);
   const dim3 block((unsigned)(64 * p.waves));
   const size_t lds = plan_lds(p.gpb, BPG, NR, p.waves);
-  if (codes)
-    hipLaunchKernelGGL((k_quant_tiles<NR, true, BPG>), grid, block, lds, s, a, p.gpb);
+  if (cm == kSymCodes)
+    hipLaunchKernelGGL((k_quant_tiles<NR, kSymCodes, BPG>), grid, block, lds, s, a, p.gpb);
+  else if (cm == kAsymCodes)
+    hipLaunchKernelGGL((k_quant_tiles<NR, kAsymCodes, BPG>), grid, block, lds, s, a, p.gpb);
   else
-    hipLaunchKernelGGL((k_quant_tiles<NR, false, BPG>), grid, block, lds, s, a, p.gpb);
+    hipLaunchKernelGGL((k_quant_tiles<NR, kNoCodes, BPG>), grid, block, lds, s, a, p.gpb);
   return hipGetLastError();
 }
 
 template <int BPG>
-hipError_t launch_width(const QuantArgs &a, const TilePlan &p, bool codes, hipStream_t s) {
+hipError_t launch_width(const QuantArgs &a, const TilePlan &p, int cm, hipStream_t s) {
   switch (pass_width(a.cb)) {
-    case 0: return launch_pass<0, BPG>(a, p, codes, s);
-    case 4: return launch_pass<4, BPG>(a, p, codes, s);
-    case 8: return launch_pass<8, BPG>(a, p, codes, s);
-    case 12: return launch_pass<12, BPG>(a, p, codes, s);
-    default: return launch_pass<16, BPG>(a, p, codes, s);
+    case 0: return launch_pass<0, BPG>(a, p, cm, s);
+    case 4: return launch_pass<4, BPG>(a, p, cm, s);
+    case 8: return launch_pass<8, BPG>(a, p, cm, s);
+    case 12: return launch_pass<12, BPG>(a, p, cm, s);
+    default: return launch_pass<16, BPG>(a, p, cm, s);
   }
 }
 
@@ -322,8 +354,8 @@ hipError_t launch_quant_tiles(const QuantArgs &a0, hipStream_t s) {
     QuantArgs a = a0;
     a.c0 = c0;
     a.cb = total - c0 < kRankPass ? total - c0 : kRankPass;
-    const bool codes = c0 == 0;
-    const hipError_t e = a.bpg == 2 ? launch_width<2>(a, p, codes, s) : launch_width<1>(a, p, codes, s);
+    const int cm = c0 != 0 ? kNoCodes : a.asym ? kAsymCodes : kSymCodes;
+    const hipError_t e = a.bpg == 2 ? launch_width<2>(a, p, cm, s) : launch_width<1>(a, p, cm, s);
     if (e != hipSuccess) return e;
     c0 += kRankPass;
   } while (c0 < total);
