@@ -583,6 +583,8 @@ def main(argv=None):
     ap.add_argument("--group", type=int, default=64, choices=[64, 128],
                     help="quantization group width (the pages' Qwen3-8B runs use 128)")
     ap.add_argument("--kernel", default="auto", choices=["auto", "tiled", "skinny"])
+    ap.add_argument("--act-quant", default="sym", choices=["sym", "asym"],
+                    help="activation format: symmetric int4 (the layer's) or the asymmetric variant")
     ap.add_argument("--y-dtype", default="bf16", choices=["bf16", "f32"])
     ap.add_argument("--rotate-mb", type=float, default=640.0,
                     help="total bytes of rotated input/output copies (defeats the 256 MB MALL)")
@@ -656,7 +658,8 @@ def main(argv=None):
         kernel = "skinny" if M <= 64 else "tiled"
 
     def quant(i):
-        hsq.quantize_stage(sets[i % nsets]["X"], lam, L1, N=N, batch=B, workspace=ws, group=args.group)
+        hsq.quantize_stage(sets[i % nsets]["X"], lam, L1, N=N, batch=B, workspace=ws, group=args.group,
+                           act_quant=args.act_quant)
 
     def contract(i):
         s = sets[i % nsets]
@@ -774,7 +777,7 @@ def main(argv=None):
         "config": {
             "workload": f"{spec.name}: {spec.description}",
             "M": M, "K": K, "N": N, "rank": r, "batch": B, "group": args.group,
-            "y_dtype": args.y_dtype, "contract_kernel": kernel,
+            "y_dtype": args.y_dtype, "contract_kernel": kernel, "act_quant": args.act_quant,
             "rotated_sets": nsets,
         },
         "stages_ms": {"quantize": round(q_avg, 5), "contract": round(c_avg, 5),
@@ -787,7 +790,7 @@ def main(argv=None):
         "roofline": roof,
         "cpu_baseline": None,
     }
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and args.act_quant == "sym":
         out["cpu_baseline"] = cpu_baseline(lay, spec, args.cpu_seconds)
     print(json.dumps(out), flush=True)
     return 0
