@@ -385,8 +385,8 @@ def calib_main(args):
 
 def mx_main(args):
     """The MX-fp4 variant of one layer (one projection): one step = the whole
-    hsq_mx_lowrank_linear call (1/lambda table, quantization pass with the
-    rank branch, scaled-fp4 MFMA contraction with the epilogue).  The
+    hsq_mx_lowrank_linear call (quantization pass with 1/lambda and the rank
+    branch, scaled-fp4 MFMA contraction with the epilogue).  The
     residual is the int4 layer's dequantized residual re-quantized to
     MX-fp4.  Inputs rotate past the Infinity Cache.  The roofline is that
     of the whole call against the fp4 MFMA peak (the quantization pass
