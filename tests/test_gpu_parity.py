@@ -225,6 +225,17 @@ def test_ragged_shapes_match_oracle(oracle, M, K, N, r, batch):
         assert np.array_equal(got, oracle.group_partials(q, lay["qw"][0]))
 
 
+@pytest.mark.parametrize("M,K,N,r", [
+    (2100, 256, 4100, 4),     # 17 x 33 = 561 tiles (more than two rounds of workgroups), ragged rows and columns
+    (2100, 192, 4100, 0),     # rank 0, a pad group
+])
+def test_many_tiles_ragged_full_output(oracle, M, K, N, r):
+    lay = make_random_layer(M + N + r, M, K, N, r=r, outlier_channels=2)
+    up = Uploaded(lay)
+    say(f"[many tiles] M={M} K={K} N={N} r={r}")
+    check_linear_rows(oracle, up, np.arange(M), "tiled")
+
+
 def test_zero_groups_subnormal_and_saturated_scales(oracle):
     M, K, N = 48, 512, 64
     lay = make_random_layer(77, M, K, N, r=4)
