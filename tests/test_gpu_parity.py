@@ -226,14 +226,22 @@ def test_ragged_shapes_match_oracle(oracle, M, K, N, r, batch):
 
 
 @pytest.mark.parametrize("M,K,N,r", [
-    (2100, 256, 4100, 4),     # 17 x 33 = 561 tiles (more than two rounds of workgroups), ragged rows and columns
+    # more than a round of workgroups (two per CU): 17 x 33 = 561 tiles,
+    # the last column tile 4 columns wide; ragged rows
+    (2100, 256, 4100, 4),
     (2100, 192, 4100, 0),     # rank 0, a pad group
+    (2100, 256, 4600, 8),     # 612 tiles, the last one 120 columns wide; rank 8
+    (2100, 128, 3000, 4),     # 408 tiles: one round
 ])
 def test_many_tiles_ragged_full_output(oracle, M, K, N, r):
     lay = make_random_layer(M + N + r, M, K, N, r=r, outlier_channels=2)
     up = Uploaded(lay)
     say(f"[many tiles] M={M} K={K} N={N} r={r}")
     check_linear_rows(oracle, up, np.arange(M), "tiled")
+    q, _ = oracle.quantize(lay["X"], lay["lam"])
+    m0, n0 = M - 150, N - 200
+    got = up.partials(m0, 150, n0, 200, "tiled")
+    assert np.array_equal(got, oracle.group_partials(q, lay["qw"][0], m0, 150, n0, 200))
 
 
 def test_zero_groups_subnormal_and_saturated_scales(oracle):
