@@ -370,8 +370,9 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_mx_gemm(MxArgs a) {
   }
 }
 
-// workgroup shapes: 128 x 128 (4 waves of 64 x 64) and 256 x 128 (4 waves of
-// 128 x 64)
+// workgroup 128 x 128: 2 x 2 waves of 64 x 64 (a 256 x 128 shape with
+// 128 x 64 per wave ran at one wave per SIMD and was slower on every layer
+// measured)
 template <int RP, int TMW>
 hipError_t launch_mx_gemm(const MxArgs &a, hipStream_t s) {
   constexpr int TNW = 4, WGM = 2, WGN = 2;
