@@ -193,11 +193,15 @@ struct int_c {
 // global -> registers -> LDS with the loads of stage s + 2 issued at the
 // start of stage s into one of two register slots (slot = stage parity,
 // fixed at compile time by unrolling), two LDS buffers, one barrier per
-// stage.  The e8m0 scales come straight from memory, one dword per tile
-// and lane for four k-steps (byte j picked by a shift).  Workgroups walk
-// the tiles in the XCD-grouped order of xcd_tile_of.
+// stage.  The e8m0 scales (one dword per tile and lane for four k-steps,
+// byte j picked by a shift) ride the same pipeline: a group of four
+// k-steps needs (AT + BT) x 64 dwords, loaded a quarter per stage with the
+// operands of the group before and written into one of two LDS scale
+// buffers, so that the first stage of a group reads its scales from LDS
+// instead of waiting on memory.  Workgroups walk the tiles in the
+// XCD-grouped order of xcd_tile_of.
 template <int TMW, int TNW, int WGM, int WGN, int RPT, int GROUPM = 8>
-__global__ __launch_bounds__(64 * WGM * WGN) void k_mx_gemm(MxArgs a) {
+__global__ __launch_bounds__(64 * WGM * WGN, 2) void k_mx_gemm(MxArgs a) {
   constexpr int NTHR = 64 * WGM * WGN;
   constexpr int AT = TMW * WGM, BT = TNW * WGN;          // tiles of the workgroup
   constexpr int LA = AT * 64 / NTHR, LB = BT * 64 / NTHR; // 16-byte slots per thread and stage
@@ -205,6 +209,9 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_mx_gemm(MxArgs a) {
   constexpr int BMR = AT * 16, BNC = BT * 16;            // rows, columns of the workgroup
   __shared__ alignas(16) uint8_t opa[2][AT][64][16];
   __shared__ alignas(16) uint8_t opb[2][BT][64][16];
+  constexpr int SCW = (AT + BT) * 64;                     // scale dwords of a group of four k-steps
+  static_assert(SCW == 4 * NTHR && AT * 64 == 2 * NTHR, "a quarter of a group's scales per thread and stage");
+  __shared__ uint32_t ssc[2][SCW];                        // [group parity][A tiles, then B tiles][lane]
   __shared__ float eu[RPT > 0 ? RPT : 1][BMR];
   __shared__ float el2[RPT > 0 ? RPT : 1][BNC];
   __shared__ float ebias[BNC];
@@ -217,16 +224,13 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_mx_gemm(MxArgs a) {
   const int mt0 = mb * AT, nt0 = nb * BT;
   const int MT = a.Mpad / 16, NT = (a.N + 15) / 16;
   const int KS = a.KS, KS4 = a.KS4;
-  const v4u *gA[LA];
-  const v4u *gB[LB];
-#pragma unroll
-  for (int u = 0; u < LA; ++u)
-    gA[u] = reinterpret_cast<const v4u *>(a.qa) + ((size_t)min(mt0 + (tid >> 6) + u * (NTHR / 64), MT - 1) * KS) * 64 + lane;
-#pragma unroll
-  for (int u = 0; u < LB; ++u)
-    gB[u] = reinterpret_cast<const v4u *>(a.wq) + ((size_t)min(nt0 + (tid >> 6) + u * (NTHR / 64), NT - 1) * KS) * 64 + lane;
-  const uint32_t *sA = reinterpret_cast<const uint32_t *>(a.sa);
-  const uint32_t *sB = reinterpret_cast<const uint32_t *>(a.ws);
+  // buffer loads: one per-lane offset, the tile and k-step in a scalar
+  // offset (the tile a thread loads depends on its wave only)
+  const __amdgpu_buffer_rsrc_t rs_qa = buffer_rsrc(a.qa, (uint32_t)MT * KS * 1024);
+  const __amdgpu_buffer_rsrc_t rs_wq = buffer_rsrc(a.wq, (uint32_t)NT * KS * 1024);
+  const __amdgpu_buffer_rsrc_t rs_sa = buffer_rsrc(a.sa, (uint32_t)MT * KS4 * 256);
+  const __amdgpu_buffer_rsrc_t rs_sb = buffer_rsrc(a.ws, (uint32_t)NT * KS4 * 256);
+  const uint32_t vo16 = (uint32_t)lane * 16, vo4 = (uint32_t)lane * 4;
 
   // epilogue operands: U (its K-slices summed in order), L2, bias
   for (int p = tid; p < RPT * BMR; p += NTHR) {
@@ -251,28 +255,50 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_mx_gemm(MxArgs a) {
 #pragma unroll
     for (int j = 0; j < TNW; ++j) acc[i][j] = (v4f){0.f, 0.f, 0.f, 0.f};
 
+  // the scale dword of quarter P of a group: A tiles (P = 0, 1: tiles 4P ..
+  // 4P + 3) or B tiles (P = 2, 3), one lane slot per thread
+  auto scale_word = [&](int g, auto pc) __attribute__((always_inline)) -> uint32_t {
+    constexpr int P = decltype(pc)::value;
+    const int tile = (P & 1) * (NTHR / 64) + wave;
+    if constexpr (P < 2)
+      return __builtin_amdgcn_raw_buffer_load_b32(rs_sa, vo4, (min(mt0 + tile, MT - 1) * KS4 + g) * 256, 0);
+    else
+      return __builtin_amdgcn_raw_buffer_load_b32(rs_sb, vo4, (min(nt0 + tile, NT - 1) * KS4 + g) * 256, 0);
+  };
   v4u ra[2][LA], rb[2][LB];
-  auto load = [&](int ks, auto sc) __attribute__((always_inline)) {
+  uint32_t rs[2];
+  // operands of k-step ks and quarter P = ks % 4 of the next group's scales
+  auto load = [&](int ks, auto sc, auto pc) __attribute__((always_inline)) {
     constexpr int SL = decltype(sc)::value;
     const int k = min(ks, KS - 1);                   // past the end: a clamped, unused reload
 #pragma unroll
-    for (int u = 0; u < LA; ++u) ra[SL][u] = gA[u][(size_t)k * 64];
+    for (int u = 0; u < LA; ++u)
+      ra[SL][u] = __builtin_amdgcn_raw_buffer_load_b128(rs_qa, vo16, (min(mt0 + wave + u * (NTHR / 64), MT - 1) * KS + k) * 1024, 0);
 #pragma unroll
-    for (int u = 0; u < LB; ++u) rb[SL][u] = gB[u][(size_t)k * 64];
+    for (int u = 0; u < LB; ++u)
+      rb[SL][u] = __builtin_amdgcn_raw_buffer_load_b128(rs_wq, vo16, (min(nt0 + wave + u * (NTHR / 64), NT - 1) * KS + k) * 1024, 0);
+    rs[SL] = scale_word(min(ks / 4 + 1, KS4 - 1), pc);
   };
-  auto store = [&](int buf, auto sc) __attribute__((always_inline)) {
+  auto store = [&](int buf, int ks, auto sc, auto pc) __attribute__((always_inline)) {
     constexpr int SL = decltype(sc)::value;
+    constexpr int P = decltype(pc)::value;
 #pragma unroll
     for (int u = 0; u < LA; ++u)
       *reinterpret_cast<v4u *>(&opa[buf][(tid >> 6) + u * (NTHR / 64)][lane][0]) = ra[SL][u];
 #pragma unroll
     for (int u = 0; u < LB; ++u)
       *reinterpret_cast<v4u *>(&opb[buf][(tid >> 6) + u * (NTHR / 64)][lane][0]) = rb[SL][u];
+    ssc[(ks / 4 + 1) & 1][P * NTHR + tid] = rs[SL];
   };
 
-  load(0, int_c<0>{});
-  load(1, int_c<1>{});
-  store(0, int_c<0>{});
+  // group 0's scales straight into their buffer
+  ssc[0][tid] = scale_word(0, int_c<0>{});
+  ssc[0][NTHR + tid] = scale_word(0, int_c<1>{});
+  ssc[0][2 * NTHR + tid] = scale_word(0, int_c<2>{});
+  ssc[0][3 * NTHR + tid] = scale_word(0, int_c<3>{});
+  load(0, int_c<0>{}, int_c<0>{});
+  load(1, int_c<1>{}, int_c<1>{});
+  store(0, 0, int_c<0>{}, int_c<0>{});
   __syncthreads();
 
   uint32_t scA[TMW], scB[TNW];
@@ -281,14 +307,13 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_mx_gemm(MxArgs a) {
     constexpr int J = decltype(jc)::value;
     constexpr int SL = J & 1;
     if (J == 0) {
+      const uint32_t *sc = ssc[(ks >> 2) & 1];
 #pragma unroll
-      for (int i = 0; i < TMW; ++i)
-        scA[i] = sA[(((size_t)min(mt0 + wm * TMW + i, MT - 1) * KS4 + (ks >> 2)) * 64 + lane)];
+      for (int i = 0; i < TMW; ++i) scA[i] = sc[(wm * TMW + i) * 64 + lane];
 #pragma unroll
-      for (int j = 0; j < TNW; ++j)
-        scB[j] = sB[(((size_t)min(nt0 + wn * TNW + j, NT - 1) * KS4 + (ks >> 2)) * 64 + lane)];
+      for (int j = 0; j < TNW; ++j) scB[j] = sc[AT * 64 + (wn * TNW + j) * 64 + lane];
     }
-    load(ks + 2, int_c<SL>{});                        // this slot's data went to LDS a stage ago
+    load(ks + 2, int_c<SL>{}, int_c<(J + 2) & 3>{});  // this slot's data went to LDS a stage ago
     v8i bv[TNW];
 #pragma unroll
     for (int j = 0; j < TNW; ++j) {
@@ -305,7 +330,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_mx_gemm(MxArgs a) {
         acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv[j], acc[i][j], 4, 4, 0, sa_b, 0,
                                                                      (int)((scB[j] >> (8 * J)) & 0xFFu));
     }
-    if (ks + 1 < KS) store(SL ^ 1, int_c<SL ^ 1>{});
+    if (ks + 1 < KS) store(SL ^ 1, ks + 1, int_c<SL ^ 1>{}, int_c<(J + 1) & 3>{});
     __syncthreads();
   };
   int ks = 0;
