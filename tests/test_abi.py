@@ -225,3 +225,47 @@ def test_calibration_entry_points_validate():
     assert l2(A, A, 256, 0, 4, 64, A, A, A, A, A, 1 << 20, None) == hsq.E_INVAL
     assert l2(A, A, 256, 64, 4, 64, None, A, A, A, A, 1 << 20, None) == hsq.E_INVAL
     assert l2(A, A, 256, 64, 4, 64, A, A, A, A, A, 0, None) == hsq.E_WORKSPACE
+
+
+def test_format_variant_entry_points_validate():
+    # asymmetric activations: the _g checks plus the format argument
+    f = lib.hsq_w4a4_lowrank_linear_aq
+    args = (A, A, A, A, A, 4, A, A, hsq.BF16, A, 1 << 30, 0, None)
+    assert f(A, 64, 256, 256, 1, 64, 2, *args) == hsq.E_INVAL            # no such format
+    assert f(A, 64, 256, 256, 1, 64, -1, *args) == hsq.E_INVAL
+    assert f(A, 64, 320, 256, 1, 128, 1, *args) == hsq.E_SHAPE           # 128 does not divide K
+    assert f(A, 64, 256, 256, 1, 64, 1, A, A, A, A, A, 4, A, A, hsq.BF16, A, 0, 0, None) == hsq.E_WORKSPACE
+    assert f(A, 64, 256, 256, 1, 64, 1, A, A, A, None, A, 4, A, A, hsq.BF16, A, 1 << 30, 0, None) == hsq.E_INVAL
+    q = lib.hsq_w4a4_quantize_stage_aq
+    assert q(A, 64, 256, 256, 1, 64, 3, A, A, 4, A, 1 << 30, None) == hsq.E_INVAL
+    assert q(A, 64, 256, 256, 1, 64, 1, A + 8, A, 4, A, 1 << 30, None) == hsq.E_ALIGN
+    pq = lib.hsq_w4a4_group_partials_aq
+    assert pq(A, 64, 256, 256, 64, 1, A, A, 0, 65, 0, 256, A, A, 1 << 30, 0, None) == hsq.E_SHAPE
+    assert pq(A, 64, 256, 256, 64, 5, A, A, 0, 64, 0, 256, A, A, 1 << 30, 0, None) == hsq.E_INVAL
+    # MX-fp4
+    assert lib.hsq_mx_packed_weight_bytes(63, 16) == 0
+    assert lib.hsq_mx_packed_weight_bytes(128, 16) == 1024 + 256     # one code block, one scale block
+    assert lib.hsq_mx_packed_weight_bytes(192, 33) == 3 * 2 * 1024 + 3 * 256
+    assert lib.hsq_mx_workspace_bytes(64, 256, 4) > 0
+    assert lib.hsq_mx_workspace_bytes(64, 100, 4) == 0
+    mp = lib.hsq_mx_pack_weights
+    assert mp(A, 96, 16, A, None) == hsq.E_SHAPE
+    assert mp(None, 128, 16, A, None) == hsq.E_INVAL
+    assert mp(A + 4, 128, 16, A, None) == hsq.E_ALIGN
+    ml = lib.hsq_mx_lowrank_linear
+    assert ml(A, 64, 256, 256, A, A, A, A, 4, A, A, 7, A, 1 << 30, None) == hsq.E_INVAL      # y dtype
+    assert ml(A, 64, 256, 256, A, A, None, A, 4, A, A, hsq.BF16, A, 1 << 30, None) == hsq.E_INVAL
+    assert ml(A, 64, 250, 256, A, A, A, A, 4, A, A, hsq.BF16, A, 1 << 30, None) == hsq.E_SHAPE
+    assert ml(A, 64, 256, 256, A, A, A, A, 4, A, A, hsq.BF16, A, 16, None) == hsq.E_WORKSPACE
+    # fused two-layer chain
+    mw = lib.hsq_mlp_workspace_bytes
+    assert mw(64, 256, 512, 256, 4, 4) > lib.hsq_workspace_bytes(64, 256, 512, 4, 1)
+    assert mw(64, 256, 512, 256, 4, 9) == 0          # the down layer's rank is at most 8
+    assert mw(64, 256, 500, 256, 4, 4) == 0          # H must be a multiple of 64
+    mlp = lib.hsq_w4a4_lowrank_mlp
+    up = (A, A, A, A, A, 4, A)
+    dn = (A, A, A, A, A, 4, A)
+    assert mlp(A, 64, 256, 512, 256, *up[:6], up[6], 9, *dn, A, hsq.BF16, None, A, 1 << 30, None) == hsq.E_INVAL
+    assert mlp(A, 64, 256, 512, 256, *up, hsq.ACT_GELU_TANH, *dn, A, 9, None, A, 1 << 30, None) == hsq.E_INVAL
+    assert mlp(A, 64, 256, 512, 256, *up, hsq.ACT_GELU_TANH, *dn, A, hsq.BF16, None, A, 16, None) == hsq.E_WORKSPACE
+    assert mlp(A, 64, 256, 512, 256, *up, hsq.ACT_GELU_TANH, *dn, A, hsq.BF16, A + 4, A, 1 << 30, None) == hsq.E_ALIGN
