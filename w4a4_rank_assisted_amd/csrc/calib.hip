@@ -43,10 +43,11 @@ typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 // ---------------------------------------------------------------- Hessian
 constexpr int HB = 128;            // block of H (rows = columns)
 constexpr int HKC = 64;            // tokens per stage
-constexpr int HNT = 256;           // threads: 4 waves, 2 x 2, 64 x 64 each
+constexpr int HNT = 512;           // threads: 8 waves, 2 x 4, 64 x 32 each
 constexpr int HLD = HKC + 8;       // LDS pitch in bf16 (144 bytes: conflict-free 16-byte reads)
 constexpr int kHessFull = 0, kHessSplit = 1, kHessReduce = 2;
-constexpr int kHessAcc = 4 * 4 * 4;  // accumulators per thread
+constexpr int HTM = 4, HTN = 2;    // 16 x 16 tiles per wave
+constexpr int kHessAcc = HTM * HTN * 4;  // accumulators per thread
 
 struct alignas(16) HessSmem {
   uint16_t t[2][2][HB][HLD];       // [buffer][A, B][channel in block][token in stage]
@@ -102,7 +103,7 @@ __global__ __launch_bounds__(HNT, 2) void k_hessian(HessArgs a) {
   __shared__ HessSmem sm;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wr = wave >> 1, wc = wave & 1;
+  const int wr = wave >> 2, wc = wave & 3;
   const int nb = (a.K + HB - 1) / HB;
   int bi, bj;
   hess_block(blockIdx.x, nb, bi, bj);
@@ -112,11 +113,11 @@ __global__ __launch_bounds__(HNT, 2) void k_hessian(HessArgs a) {
   // partial blocks: [split][block][chunk][thread] float4
   float *part = a.part + ((size_t)blockIdx.y * nblk + blockIdx.x) * (HNT * kHessAcc);
 
-  float acc[4][4][4];
+  float acc[HTM][HTN][4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < HTM; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < HTN; ++j)
 #pragma unroll
       for (int q = 0; q < 4; ++q) acc[i][j][q] = 0.0f;
 
@@ -125,16 +126,18 @@ __global__ __launch_bounds__(HNT, 2) void k_hessian(HessArgs a) {
     const int nst = (a.M + HKC - 1) / HKC, S = (int)gridDim.y, z = (int)blockIdx.y;
     const int s0 = z * nst / S, s1 = (z + 1) * nst / S;
     const int m_end = min(a.M, s1 * HKC);
-    // thread t loads tokens 4*(t%16) .. +3 of channels 8*(t/16) .. +7 of
-    // each operand tile (four 16-byte loads), and writes them transposed
-    const int c8 = tid >> 4, r4 = tid & 15;
+    // the first half of the threads loads the row strip (channels I0 ..),
+    // the second the column strip (J0 ..): thread t of a half loads tokens
+    // 4*(t%16) .. +3 of channels 8*(t/16) .. +7 (four 16-byte loads) and
+    // writes them transposed
+    const int strip = tid >> 8, t8 = tid & 255, c8 = t8 >> 4, r4 = t8 & 15;
     const __amdgpu_buffer_rsrc_t rx = buffer_rsrc(a.X, (uint32_t)((size_t)a.M * a.K * 2));
     const uint32_t kBad = 0x80000000u;                // past the buffer: the load returns 0
-    const int ca = I0 + 8 * c8, cb = J0 + 8 * c8;
+    const int cs = (strip ? J0 : I0) + 8 * c8;
     // two register slots: a stage's loads are issued two stages before its
     // tiles are consumed (slot = stage parity, fixed by unrolling by two);
     // tokens past the split's end load as zeros
-    v4u ra[2][4], rb[2][4];
+    v4u ra[2][4];
     auto load = [&](int s, auto slotc) __attribute__((always_inline)) {
       constexpr int SL = decltype(slotc)::value;
 #pragma unroll
@@ -142,8 +145,7 @@ __global__ __launch_bounds__(HNT, 2) void k_hessian(HessArgs a) {
         const int m = s * HKC + 4 * r4 + u;
         const bool mok = m < m_end;
         const uint32_t rowoff = (uint32_t)m * (uint32_t)a.K * 2u;
-        ra[SL][u] = __builtin_amdgcn_raw_buffer_load_b128(rx, (mok && ca < a.K) ? rowoff + ca * 2 : kBad, 0, 0);
-        rb[SL][u] = __builtin_amdgcn_raw_buffer_load_b128(rx, (mok && cb < a.K) ? rowoff + cb * 2 : kBad, 0, 0);
+        ra[SL][u] = __builtin_amdgcn_raw_buffer_load_b128(rx, (mok && cs < a.K) ? rowoff + cs * 2 : kBad, 0, 0);
       }
     };
     auto store = [&](auto slotc, int buf) __attribute__((always_inline)) {
@@ -154,10 +156,7 @@ __global__ __launch_bounds__(HNT, 2) void k_hessian(HessArgs a) {
         const uint32_t sel = (c & 1) ? 0x07060302u : 0x05040100u;
         const uint32_t lo = __builtin_amdgcn_perm(ra[SL][1][k], ra[SL][0][k], sel);
         const uint32_t hi = __builtin_amdgcn_perm(ra[SL][3][k], ra[SL][2][k], sel);
-        *reinterpret_cast<v2u *>(&sm.t[buf][0][8 * c8 + c][4 * r4]) = (v2u){lo, hi};
-        const uint32_t lo2 = __builtin_amdgcn_perm(rb[SL][1][k], rb[SL][0][k], sel);
-        const uint32_t hi2 = __builtin_amdgcn_perm(rb[SL][3][k], rb[SL][2][k], sel);
-        *reinterpret_cast<v2u *>(&sm.t[buf][1][8 * c8 + c][4 * r4]) = (v2u){lo2, hi2};
+        *reinterpret_cast<v2u *>(&sm.t[buf][strip][8 * c8 + c][4 * r4]) = (v2u){lo, hi};
       }
     };
     // (a diagonal block loads its one strip twice: branch-free loads keep
@@ -165,18 +164,18 @@ __global__ __launch_bounds__(HNT, 2) void k_hessian(HessArgs a) {
     auto compute = [&](int buf) __attribute__((always_inline)) {
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
-        v8bf av[4], bv[4];
+        v8bf av[HTM], bv[HTN];
         const int tk = 32 * kk + 8 * (lane >> 4);
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < HTM; ++i)
           av[i] = *reinterpret_cast<const v8bf *>(&sm.t[buf][0][64 * wr + 16 * i + (lane & 15)][tk]);
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-          bv[j] = *reinterpret_cast<const v8bf *>(&sm.t[buf][1][64 * wc + 16 * j + (lane & 15)][tk]);
+        for (int j = 0; j < HTN; ++j)
+          bv[j] = *reinterpret_cast<const v8bf *>(&sm.t[buf][1][32 * wc + 16 * j + (lane & 15)][tk]);
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < HTM; ++i)
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
+          for (int j = 0; j < HTN; ++j) {
             v4f c4 = {acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]};
             c4 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[i], bv[j], c4, 0, 0, 0);
             acc[i][j][0] = c4[0]; acc[i][j][1] = c4[1]; acc[i][j][2] = c4[2]; acc[i][j][3] = c4[3];
@@ -205,10 +204,10 @@ __global__ __launch_bounds__(HNT, 2) void k_hessian(HessArgs a) {
 
   if constexpr (MODE == kHessSplit) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < HTM; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        *reinterpret_cast<v4f *>(part + ((i * 4 + j) * HNT + tid) * 4) =
+      for (int j = 0; j < HTN; ++j)
+        *reinterpret_cast<v4f *>(part + ((i * HTN + j) * HNT + tid) * 4) =
             (v4f){acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]};
     return;
   } else {
@@ -217,10 +216,10 @@ __global__ __launch_bounds__(HNT, 2) void k_hessian(HessArgs a) {
       for (int z = 0; z < a.splits; ++z) {
         const float *src = a.part + ((size_t)z * nblk + blockIdx.x) * (HNT * kHessAcc);
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < HTM; ++i)
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const v4f v = *reinterpret_cast<const v4f *>(src + ((i * 4 + j) * HNT + tid) * 4);
+          for (int j = 0; j < HTN; ++j) {
+            const v4f v = *reinterpret_cast<const v4f *>(src + ((i * HTN + j) * HNT + tid) * 4);
             acc[i][j][0] += v[0]; acc[i][j][1] += v[1]; acc[i][j][2] += v[2]; acc[i][j][3] += v[3];
           }
       }
@@ -231,15 +230,15 @@ __global__ __launch_bounds__(HNT, 2) void k_hessian(HessArgs a) {
     // values transposed (four consecutive columns of one row per lane: one
     // 16-byte store)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < HTM; ++i) {
       const int gi0 = I0 + 64 * wr + 16 * i + 4 * (lane >> 4);   // rows gi0 .. gi0 + 3
       if (gi0 >= a.K) continue;
       float di[4];
 #pragma unroll
       for (int q = 0; q < 4; ++q) di[q] = 1.0f / f16_to_f32(a.lam[gi0 + q]);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int gj = J0 + 64 * wc + 16 * j + (lane & 15);
+      for (int j = 0; j < HTN; ++j) {
+        const int gj = J0 + 32 * wc + 16 * j + (lane & 15);
         if (gj >= a.K) continue;
         const float dj = 1.0f / f16_to_f32(a.lam[gj]);
         float v[4];
