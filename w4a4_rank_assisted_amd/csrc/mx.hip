@@ -87,8 +87,11 @@ __global__ void k_mx_pack_w(const float *R, int K, int N, int KS, uint8_t *blob,
 template <int RP>
 __global__ __launch_bounds__(256) void k_mx_quant(MxArgs a) {
   constexpr bool STAGE = RP > 0 && RP <= 8;      // L1 rows of the slice in LDS
+  // one 32-channel block's L1 rows per LBS floats, padded by four so that
+  // the blocks a wave reads at once sit in different banks
+  constexpr int LBS = 32 * (RP > 0 ? RP : 1) + 4;
   __shared__ float us[16][16][RP > 0 ? RP : 1];
-  __shared__ float l1s[STAGE ? 16 * 32 * RP : 1];
+  __shared__ alignas(16) float l1s[STAGE ? 16 * LBS : 1];
   __shared__ alignas(16) float ils[512];           // fl32(1 / lambda) of the slice's channels
   const int tid = threadIdx.x, row = tid & 15, q = tid >> 4;
   const int mt = blockIdx.x, m = mt * 16 + row;
@@ -101,7 +104,7 @@ __global__ __launch_bounds__(256) void k_mx_quant(MxArgs a) {
   if constexpr (STAGE) {
     for (int p = tid; p < 512 * RP; p += 256) {
       const int kk = p / RP, c = p % RP, k = k0 + kk;
-      l1s[p] = (c < a.r && k < a.K) ? bf16_to_f32(a.L1[(size_t)k * a.r + c]) : 0.0f;
+      l1s[(kk >> 5) * LBS + (kk & 31) * RP + c] = (c < a.r && k < a.K) ? bf16_to_f32(a.L1[(size_t)k * a.r + c]) : 0.0f;
     }
   }
   __syncthreads();
@@ -136,7 +139,7 @@ __global__ __launch_bounds__(256) void k_mx_quant(MxArgs a) {
     a.sa[(((size_t)mt * a.KS4 + (ks >> 2)) * 64 + lane) * 4 + (ks & 3)] = (uint8_t)sb;
     if constexpr (STAGE) {
       if (live) {
-        const float *lr = l1s + (32 * (b - 16 * (int)blockIdx.y)) * RP;
+        const float *lr = l1s + (b - 16 * (int)blockIdx.y) * LBS;
 #pragma unroll
         for (int e = 0; e < 32; ++e)
 #pragma unroll
