@@ -35,6 +35,7 @@ namespace {
 constexpr int kRankPass = 16;              // rank columns one pass accumulates
 constexpr size_t kSliceLdsBytes = 40 * 1024;  // staged 1/lambda + L1 per workgroup
 constexpr int kTargetWaves = 2048;         // waves a launch aims for (8 per CU)
+constexpr int kOneUnitWaves = 20 * 256;    // one unit per wave up to this many waves
 constexpr int kLamKq = 16 + 4;             // LDS floats per (group, channel block) of 1/lambda
 
 constexpr int kqs(int nr) { return 16 * nr + 4; }  // LDS floats per (group, channel block) of L1
@@ -73,9 +74,13 @@ TilePlan tile_plan(int M, int K, int r, int batch, int group) {
   p.gpb = ceil_div(Gp, S);
   p.slices = ceil_div(Gp, p.gpb);
   // waves per workgroup: 8 when each gets two or more groups of the slice
-  // (more loads in flight per CU), else 4
+  // (more loads in flight per CU), else 4; one unit per wave (every load of
+  // the slice in flight at once) when the launch is small or still fits one
+  // round of the chip at that width (at most 20 waves per CU: pixart's 512
+  // workgroups of 9 waves, 7.1 -> 6.2 us; wider launches lose a round)
   p.waves = p.gpb >= 16 ? 8 : 4;
-  if ((long long)MT * p.slices * 4 < kTargetWaves / 2) p.waves = p.gpb < 4 ? 4 : (p.gpb > 16 ? 16 : p.gpb);
+  if ((long long)MT * p.slices * 4 < kTargetWaves / 2 || (long long)MT * p.slices * p.gpb <= kOneUnitWaves)
+    p.waves = p.gpb < 4 ? 4 : (p.gpb > 16 ? 16 : p.gpb);
   return p;
 }
 
