@@ -236,23 +236,6 @@ __global__ __launch_bounds__(64 * WGM * WGN, 2) void k_mx_gemm(MxArgs a) {
   const __amdgpu_buffer_rsrc_t rs_sb = buffer_rsrc(a.ws, (uint32_t)NT * KS4 * 256);
   const uint32_t vo16 = (uint32_t)lane * 16, vo4 = (uint32_t)lane * 4;
 
-  // epilogue operands: U (its K-slices summed in order), L2, bias
-  for (int p = tid; p < RPT * BMR; p += NTHR) {
-    const int c = p / BMR, rr = p % BMR, m = mt0 * 16 + rr;
-    float u = 0.0f;
-    if (c < a.r && m < a.M)
-      for (int sl = 0; sl < a.u_slices; ++sl) u += a.U[((size_t)sl * a.r + c) * a.Mpad + m];
-    eu[c][rr] = u;
-  }
-  for (int p = tid; p < RPT * BNC; p += NTHR) {
-    const int c = p / BNC, cc = p % BNC, n = nt0 * 16 + cc;
-    el2[c][cc] = (c < a.r && n < a.N) ? bf16_to_f32(a.L2[(size_t)c * a.N + n]) : 0.0f;
-  }
-  for (int p = tid; p < BNC; p += NTHR) {
-    const int n = nt0 * 16 + p;
-    ebias[p] = (a.bias && n < a.N) ? bf16_to_f32(a.bias[n]) : 0.0f;
-  }
-
   v4f acc[TMW][TNW];
 #pragma unroll
   for (int i = 0; i < TMW; ++i)
@@ -295,15 +278,48 @@ __global__ __launch_bounds__(64 * WGM * WGN, 2) void k_mx_gemm(MxArgs a) {
     if (SQ == NTHR || tid < SQ) ssc[(ks / 4 + 1) & 1][P * SQ + tid] = rs[SL];
   };
 
-  // group 0's scales straight into their buffer
+  // prologue: group 0's scales, the first two k-steps' operands and the
+  // epilogue operands all in flight together, so the first stores wait on
+  // one memory round trip
+  uint32_t s0[4] = {0u, 0u, 0u, 0u};
   if (SQ == NTHR || tid < SQ) {
-    ssc[0][tid] = scale_word(0, int_c<0>{});
-    ssc[0][SQ + tid] = scale_word(0, int_c<1>{});
-    ssc[0][2 * SQ + tid] = scale_word(0, int_c<2>{});
-    ssc[0][3 * SQ + tid] = scale_word(0, int_c<3>{});
+    s0[0] = scale_word(0, int_c<0>{});
+    s0[1] = scale_word(0, int_c<1>{});
+    s0[2] = scale_word(0, int_c<2>{});
+    s0[3] = scale_word(0, int_c<3>{});
   }
   load(0, int_c<0>{}, int_c<0>{});
   load(1, int_c<1>{}, int_c<1>{});
+  // epilogue operands: U (its K-slices summed in order; the first
+  // kMaxUSlices loaded together, clamped addresses), L2, bias
+  for (int p = tid; p < RPT * BMR; p += NTHR) {
+    const int c = p / BMR, rr = p % BMR, m = mt0 * 16 + rr;
+    const int cc = min(c, a.r - 1), mm = min(m, a.Mpad - 1);
+    float us[kMaxUSlices];
+#pragma unroll
+    for (int sl = 0; sl < kMaxUSlices; ++sl)
+      us[sl] = a.U[((size_t)min(sl, a.u_slices - 1) * a.r + cc) * a.Mpad + mm];
+    float u = 0.0f;
+#pragma unroll
+    for (int sl = 0; sl < kMaxUSlices; ++sl)
+      if (sl < a.u_slices) u += us[sl];
+    for (int sl = kMaxUSlices; sl < a.u_slices; ++sl) u += a.U[((size_t)sl * a.r + cc) * a.Mpad + mm];
+    eu[c][rr] = (c < a.r && m < a.M) ? u : 0.0f;
+  }
+  for (int p = tid; p < RPT * BNC; p += NTHR) {
+    const int c = p / BNC, cc = p % BNC, n = nt0 * 16 + cc;
+    el2[c][cc] = (c < a.r && n < a.N) ? bf16_to_f32(a.L2[(size_t)c * a.N + n]) : 0.0f;
+  }
+  for (int p = tid; p < BNC; p += NTHR) {
+    const int n = nt0 * 16 + p;
+    ebias[p] = (a.bias && n < a.N) ? bf16_to_f32(a.bias[n]) : 0.0f;
+  }
+  if (SQ == NTHR || tid < SQ) {
+    ssc[0][tid] = s0[0];
+    ssc[0][SQ + tid] = s0[1];
+    ssc[0][2 * SQ + tid] = s0[2];
+    ssc[0][3 * SQ + tid] = s0[3];
+  }
   store(0, 0, int_c<0>{}, int_c<0>{});
   __syncthreads();
 
