@@ -124,3 +124,21 @@ def test_mx_pixart_full_size_sampled_rows():
     lay = make_layer("pixart_up")
     rows = np.array(sorted(set([0, 4095]) | set(np.random.default_rng(5).choice(4096, 30, replace=False).tolist())))
     run_case(lay, rows)
+
+
+def test_mx_degenerate_blocks():
+    # a zero token, a zero 32-block, blocks whose scale clamps at the small
+    # end, a block of huge values, an all-negative block (signed zeros among
+    # its codes), a constant block
+    M, K, N = 48, 512, 64
+    lay = make_random_layer(711, M, K, N, r=4)
+    x = bf16_bits_to_f32(lay["X"]).astype(np.float64)
+    x[3, :] = 0.0
+    x[7, 32:64] = 0.0
+    x[9, 64:96] *= 2.0 ** -60
+    x[10, 96:128] *= 2.0 ** -120
+    x[11, 128:160] *= 1.0e30
+    x[12, 160:192] = -np.abs(x[12, 160:192]) * 0.01
+    x[13, 192:224] = 0.75
+    lay["X"] = f64_to_bf16_bits(x)
+    run_case(lay)
