@@ -84,35 +84,107 @@ def read_traffic(kernel: str, layer: str):
     return ent.get("bytes_per_launch")
 
 
-def cpu_baseline(layer_dict, spec, seconds: float):
-    """The CPU oracle, as it stands, on the whole layer (all rows, every
-    projection), repeated until `seconds` of wall time have accumulated."""
+def _sample_rows(M: int, n: int):
+    """n rows spread evenly over [0, M), always including the first and last."""
+    import numpy as np
+
+    n = max(2, min(n, M))
+    return np.unique(np.linspace(0, M - 1, n).round().astype(np.int32))
+
+
+def cpu_baseline(layers, specs, seconds: float, rows_per_layer: int):
+    """The CPU oracle, as it stands, on a bounded sample of the workload:
+    the same evenly spaced rows of every layer (all output columns, every
+    projection), repeated until `seconds` of wall time have accumulated.
+    Rows are independent (the quantizer is per token), so the sample's rate
+    is the oracle's rate on the whole workload."""
     import oracle
 
     o = oracle.Oracle()
-    reps, t0 = 0, time.perf_counter()
+    picks = [_sample_rows(sp.M, rows_per_layer) for sp in specs]
+    reps, ops, t0 = 0, 0, time.perf_counter()
     while True:
-        o.linear_batched(layer_dict)
+        for lay, sp, rows in zip(layers, specs, picks):
+            o.linear_batched(lay, rows=rows)
+            ops += 2 * rows.size * sp.K * sp.N * sp.batch
         reps += 1
         el = time.perf_counter() - t0
         if el >= seconds or reps >= 20:
             break
-    ops = spec.ops * reps
-    return {
+    sample = "; ".join(f"{rows.size} of {sp.M} rows of {sp.name} ({sp.K}->{sp.N}, batch {sp.batch})"
+                       for sp, rows in zip(specs, picks))
+    out = {
         "value": round(ops / el / 1e12, 6),
         "unit": "TOPS",
         "cores": o.num_threads(),
         "kind": "oracle",
-        "sample": (f"whole {spec.name} layer ({spec.M}x{spec.K}->{spec.N}, batch {spec.batch}, "
-                   f"r {spec.r}): quantize + brute-force int32 group sums + fp64 output, "
+        "sample": (f"{sample}: quantize + brute-force int32 group sums + fp64 output, "
                    f"{reps} repetition(s), {el:.1f} s"),
     }
+    return out
+
+
+def cpu_single_thread_tiny(seconds: float = 2.0):
+    """Seconds per call of the oracle on one thread for the tiny smoke layer
+    (64 x 256 -> 256), the whole layer."""
+    import oracle
+    from synth import make_layer
+
+    o = oracle.Oracle()
+    lay = make_layer("tiny")
+    threads = o.num_threads()
+    o.set_num_threads(1)
+    try:
+        reps, t0 = 0, time.perf_counter()
+        while True:
+            o.linear_batched(lay)
+            reps += 1
+            el = time.perf_counter() - t0
+            if el >= seconds:
+                break
+    finally:
+        o.set_num_threads(threads)
+    return {"layer": "tiny 64x256->256", "threads": 1, "s_per_call": round(el / reps, 6)}
+
+
+# hipDeviceAttribute_t values (hip_runtime_api.h, ROCm 7): peak engine clock
+# in kHz, LDS bytes per compute unit
+_HIP_ATTR_CLOCK_KHZ = 5
+_HIP_ATTR_LDS_PER_CU = 10002
+
+
+def _hip_attributes(dev: int = 0):
+    """Peak clock and LDS size from the HIP runtime already in the process
+    (found through /proc/self/maps; None where it cannot be read)."""
+    import ctypes
+
+    path = None
+    try:
+        with open("/proc/self/maps") as f:
+            for line in f:
+                if "libamdhip64.so" in line:
+                    path = line.split()[-1]
+                    break
+    except OSError:
+        pass
+    if path is None:
+        return None, None
+    hip = ctypes.CDLL(path)
+    vals = []
+    for attr in (_HIP_ATTR_CLOCK_KHZ, _HIP_ATTR_LDS_PER_CU):
+        v = ctypes.c_int(0)
+        ok = hip.hipDeviceGetAttribute(ctypes.byref(v), attr, dev) == 0
+        vals.append(v.value if ok else None)
+    return vals[0], vals[1]
 
 
 def device_info(torch):
     p = torch.cuda.get_device_properties(0)
+    clock_khz, lds = _hip_attributes(0)
     return {"name": p.name, "arch": getattr(p, "gcnArchName", ""), "cus": p.multi_processor_count,
-            "hbm_gib": round(p.total_memory / 2**30, 1), "hip": torch.version.hip}
+            "hbm_gib": round(p.total_memory / 2**30, 1), "hip": torch.version.hip,
+            "peak_clock_mhz": None if clock_khz is None else clock_khz / 1000.0,
+            "lds_bytes_per_cu": lds}
 
 
 def _csv_rows(path):
@@ -263,8 +335,9 @@ def calib_main(args):
     from synth import layer_spec, make_full_weight, make_layer
 
     dev = torch.device("cuda:0")
-    spec = layer_spec(args.layer, args.tokens, args.group)
-    lay = make_layer(args.layer, args.tokens, args.group)
+    name = WORKLOADS[args.layer][1][0] if args.layer in WORKLOADS else args.layer
+    spec = layer_spec(name, args.tokens, args.group)
+    lay = make_layer(name, args.tokens, args.group)
     W = make_full_weight(lay, 0)
     M, K, N, r = spec.M, spec.K, spec.N, spec.r
 
@@ -402,8 +475,9 @@ def mx_main(args):
     from synth import layer_spec, make_layer
 
     dev = torch.device("cuda:0")
-    spec = layer_spec(args.layer, args.tokens)
-    lay = make_layer(args.layer, args.tokens)
+    name = WORKLOADS[args.layer][1][0] if args.layer in WORKLOADS else args.layer
+    spec = layer_spec(name, args.tokens)
+    lay = make_layer(name, args.tokens)
     M, K, N, r = spec.M, spec.K, spec.N, spec.r
 
     def d16(a):
@@ -577,8 +651,9 @@ def main(argv=None):
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--layer", default="pixart_up",
-                    help="tiny | pixart_up | sana_qkv | flux_up | flux_down | qwen3_up | qwen3_down")
+    ap.add_argument("--layer", default="flux_mlp",
+                    help="flux_mlp (FLUX.1 MLP: flux_up then flux_down per step) | tiny | pixart_up | "
+                         "sana_qkv | flux_up | flux_down | qwen3_up | qwen3_down")
     ap.add_argument("--tokens", type=int, default=None, help="M for the qwen3 layers (16/256/2048)")
     ap.add_argument("--group", type=int, default=64, choices=[64, 128],
                     help="quantization group width (the pages' Qwen3-8B runs use 128)")
@@ -589,6 +664,8 @@ def main(argv=None):
     ap.add_argument("--rotate-mb", type=float, default=640.0,
                     help="total bytes of rotated input/output copies (defeats the 256 MB MALL)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--cpu-rows", type=int, default=192,
+                    help="rows per layer in the CPU oracle's sample (evenly spaced, all columns)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-mb", type=float, default=0.0,
                     help="after the timed region, run 3 device-to-device copies of this many MB "
@@ -616,6 +693,22 @@ def main(argv=None):
     if args.mx:
         return mx_main(args)
 
+    return linear_main(args)
+
+
+# Workloads made of several layers, each on its own seeded input (layers of a
+# block are checked and timed independently; the activation between them is
+# not part of the method).  A step runs every layer once.
+WORKLOADS = {
+    "flux_mlp": ("FLUX.1 joint-token MLP, 4608 tokens (4096 image + 512 text): up-projection "
+                 "3072 -> 12288, then down-projection 12288 -> 3072, each layer on its own seeded input",
+                 ["flux_up", "flux_down"]),
+}
+
+
+def linear_main(args):
+    """One step = the layer(s) of the workload, each as its quantization
+    pass + residual contraction with the rank-r epilogue."""
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py measures one GPU: this layer's hot path runs on a single MI355X "
@@ -629,46 +722,63 @@ def main(argv=None):
     from synth import layer_spec, make_layer
 
     dev = torch.device("cuda:0")
-    spec = layer_spec(args.layer, args.tokens, args.group)
-    lay = make_layer(args.layer, args.tokens, args.group)
-    M, K, N, r, B = spec.M, spec.K, spec.N, spec.r, spec.batch
+    if args.layer in WORKLOADS:
+        wl_desc, names = WORKLOADS[args.layer]
+        wl_name = args.layer
+    else:
+        names = [args.layer]
+        wl_name, wl_desc = args.layer, None
+    ydt = torch.bfloat16 if args.y_dtype == "bf16" else torch.float32
+    y_bytes = 2 if args.y_dtype == "bf16" else 4
 
     def d16(a):
         return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev)
 
-    lam = d16(lay["lam"])
-    L1 = d16(lay["L1"]) if r else None
-    L2 = d16(lay["L2"]) if r else None
-    bias = d16(lay["bias"])
-    X0 = d16(lay["X"])
-    sw0 = d16(lay["sw"])
-    packed0 = torch.cat([hsq.pack_weights(torch.from_numpy(lay["qw"][b]).to(dev))[0]
-                         for b in range(B)])
-    ydt = torch.bfloat16 if args.y_dtype == "bf16" else torch.float32
-    y_bytes = 2 if args.y_dtype == "bf16" else 4
-    set_bytes = (X0.numel() * 2 + packed0.numel() + sw0.numel() * 2 + B * M * N * y_bytes)
-    nsets = max(1, math.ceil(args.rotate_mb * 1e6 / set_bytes))
-    sets = []
-    for i in range(nsets):
-        sets.append(dict(X=X0.clone(), packed=packed0.clone(), sw=sw0.clone(),
-                         Y=torch.empty((B, M, N), dtype=ydt, device=dev)))
-    ws = torch.empty(hsq.workspace_bytes(M, K, N, r, B, args.group), dtype=torch.uint8, device=dev)
-    kernel = args.kernel
-    if kernel == "auto":
-        kernel = "skinny" if M <= 64 else "tiled"
+    # per layer: the seeded tensors on the device, rotated copies of what a
+    # step streams (X, packed W, sw, Y: more than the 256 MB MALL in total),
+    # and the layer's workspace
+    layers = []
+    for name in names:
+        spec = layer_spec(name, args.tokens, args.group)
+        lay = make_layer(name, args.tokens, args.group)
+        M, K, N, r, B = spec.M, spec.K, spec.N, spec.r, spec.batch
+        X0, sw0 = d16(lay["X"]), d16(lay["sw"])
+        packed0 = torch.cat([hsq.pack_weights(torch.from_numpy(lay["qw"][b]).to(dev))[0] for b in range(B)])
+        set_bytes = X0.numel() * 2 + packed0.numel() + sw0.numel() * 2 + B * M * N * y_bytes
+        nsets = max(1, math.ceil(args.rotate_mb * 1e6 / set_bytes))
+        sets = [dict(X=X0.clone(), packed=packed0.clone(), sw=sw0.clone(),
+                     Y=torch.empty((B, M, N), dtype=ydt, device=dev)) for _ in range(nsets)]
+        del X0, sw0, packed0
+        kernel = args.kernel
+        if kernel == "auto":
+            kernel = "skinny" if M <= 64 else "tiled"
+        layers.append(dict(
+            spec=spec, lay=lay, sets=sets, nsets=nsets, kernel=kernel,
+            lam=d16(lay["lam"]), L1=d16(lay["L1"]) if r else None, L2=d16(lay["L2"]) if r else None,
+            bias=d16(lay["bias"]),
+            ws=torch.empty(hsq.workspace_bytes(M, K, N, r, B, args.group), dtype=torch.uint8, device=dev)))
 
     def quant(i):
-        hsq.quantize_stage(sets[i % nsets]["X"], lam, L1, N=N, batch=B, workspace=ws, group=args.group,
-                           act_quant=args.act_quant)
+        for L in layers:
+            sp = L["spec"]
+            hsq.quantize_stage(L["sets"][i % L["nsets"]]["X"], L["lam"], L["L1"], N=sp.N, batch=sp.batch,
+                               workspace=L["ws"], group=args.group, act_quant=args.act_quant)
 
     def contract(i):
-        s = sets[i % nsets]
-        hsq.contract_stage(M, K, s["packed"], s["sw"], L2, bias, s["Y"], N=N, batch=B, r=r,
-                           workspace=ws, kernel=kernel, group=args.group)
+        for L in layers:
+            sp, st = L["spec"], L["sets"][i % L["nsets"]]
+            hsq.contract_stage(sp.M, sp.K, st["packed"], st["sw"], L["L2"], L["bias"], st["Y"], N=sp.N,
+                               batch=sp.batch, r=sp.r, workspace=L["ws"], kernel=L["kernel"],
+                               group=args.group)
 
     def step(i):
-        quant(i)
-        contract(i)
+        for L in layers:
+            sp, st = L["spec"], L["sets"][i % L["nsets"]]
+            hsq.quantize_stage(st["X"], L["lam"], L["L1"], N=sp.N, batch=sp.batch, workspace=L["ws"],
+                               group=args.group, act_quant=args.act_quant)
+            hsq.contract_stage(sp.M, sp.K, st["packed"], st["sw"], L["L2"], L["bias"], st["Y"], N=sp.N,
+                               batch=sp.batch, r=sp.r, workspace=L["ws"], kernel=L["kernel"],
+                               group=args.group)
 
     for i in range(args.warmup):
         step(i)
@@ -677,9 +787,9 @@ def main(argv=None):
     # The timed work is captured in HIP graphs and replayed, so the GPU runs
     # the kernels back to back without host launch gaps: one graph of the K
     # timed steps (rotating through the input sets), and, for the per-kernel
-    # durations, one graph of K quantization passes and one of K
-    # contractions.  Every graph is replayed once inside its own pair of
-    # events on the capture stream.
+    # durations, one graph of K steps' quantization passes and one of K
+    # steps' contractions.  Every graph is replayed once inside its own pair
+    # of events on the capture stream (the stream its kernels run on).
     cap = torch.cuda.Stream()
     graphs = {}
     for name, fn in (("step", step), ("quantize", quant), ("contract", contract)):
@@ -708,14 +818,15 @@ def main(argv=None):
     wall0 = time.perf_counter()
     total_ms = timed("step")
     wall = time.perf_counter() - wall0
-    q_avg = timed("quantize") / args.steps
-    c_avg = timed("contract") / args.steps
+    nl = len(layers)
+    q_avg = timed("quantize") / (args.steps * nl)
+    c_avg = timed("contract") / (args.steps * nl)
     ms_step = total_ms / args.steps
 
     # per-step spread: one-step graphs (one per input set), each replay
     # bracketed by events on the capture stream
     one = []
-    for k in range(min(nsets, args.steps)):
+    for k in range(min(max(L["nsets"] for L in layers), args.steps)):
         g = torch.cuda.CUDAGraph()
         with torch.cuda.stream(cap):
             with torch.cuda.graph(g, stream=cap):
@@ -740,27 +851,45 @@ def main(argv=None):
         for _ in range(3):
             dst.copy_(src)
         torch.cuda.synchronize()
-    ops = spec.ops
+
+    specs = [L["spec"] for L in layers]
+    ops = sum(sp.ops for sp in specs)
     value = ops / (ms_step * 1e-3) / 1e12
 
-    # roofline of the dominant kernel (the contraction): compute-bound at
-    # large M (int8 MFMA), HBM-bound when the weights dominate (small M)
-    cbytes = contract_bytes(M, K, N, r, B, y_bytes, args.group)
+    # roofline of the dominant kernel (the contraction, one launch per layer
+    # and step): compute-bound at large M (int8 MFMA), HBM-bound when the
+    # weights dominate (small M); achieved = algorithmic work per launch /
+    # the average launch duration
+    cbytes = sum(contract_bytes(sp.M, sp.K, sp.N, sp.r, sp.batch, y_bytes, args.group) for sp in specs)
     intensity = ops / cbytes
     ridge = PEAK_INT8_TOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
-    traffic = read_traffic(kernel, traffic_key(args.layer, args.tokens, M, args.group))
+    kernels = sorted(set(L["kernel"] for L in layers))
+    kname = f"contract ({'/'.join(kernels)})" + (f", {nl} launches per step ({', '.join(names)})" if nl > 1 else "")
+    # HBM bytes per launch from the counters (keyed by workload; for a
+    # several-layer workload, the average over its launches)
+    traffic = (read_traffic(kernels[0], traffic_key(args.layer, args.tokens, layers[0]["spec"].M, args.group))
+               if len(kernels) == 1 else None)
     if intensity >= ridge:
-        ach = ops / (c_avg * 1e-3) / 1e12
+        ach = ops / nl / (c_avg * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": round(ach, 2), "peak": PEAK_INT8_TOPS,
                 "unit": "TFLOP/s", "frac": round(ach / PEAK_INT8_TOPS, 4), "traffic": traffic,
-                "kernel": f"contract ({kernel})", "ops_per_launch": ops,
+                "kernel": kname, "ops_per_launch": ops // nl,
                 "note": "int8 MFMA operations (2 per multiply-accumulate) counted as FLOP"}
     else:
-        ach = cbytes / (c_avg * 1e-3) / 1e9
+        ach = cbytes / nl / (c_avg * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": traffic,
-                "kernel": f"contract ({kernel})", "bytes_per_launch": cbytes}
+                "kernel": kname, "bytes_per_launch": cbytes // nl}
 
+    sp0 = specs[0]
+    cfg = {"workload": f"{wl_name}: {wl_desc or sp0.description}"}
+    if nl == 1:
+        cfg.update(M=sp0.M, K=sp0.K, N=sp0.N, rank=sp0.r, batch=sp0.batch)
+    else:
+        cfg["layers"] = [dict(name=sp.name, M=sp.M, K=sp.K, N=sp.N, rank=sp.r, batch=sp.batch) for sp in specs]
+    cfg.update(group=args.group, y_dtype=args.y_dtype, contract_kernel="/".join(kernels),
+               act_quant=args.act_quant, rotated_sets=[L["nsets"] for L in layers])
+    abytes = sum(algorithmic_bytes(sp.M, sp.K, sp.N, sp.r, sp.batch, y_bytes, args.group) for sp in specs)
     out = {
         "metric": METRIC,
         "value": round(value, 3),
@@ -774,24 +903,21 @@ def main(argv=None):
         "vs_baseline": None,
         "dtype": "int8",
         "data": "synthetic",
-        "config": {
-            "workload": f"{spec.name}: {spec.description}",
-            "M": M, "K": K, "N": N, "rank": r, "batch": B, "group": args.group,
-            "y_dtype": args.y_dtype, "contract_kernel": kernel, "act_quant": args.act_quant,
-            "rotated_sets": nsets,
-        },
+        "config": cfg,
         "stages_ms": {"quantize": round(q_avg, 5), "contract": round(c_avg, 5),
+                      "per": "launch (average over the workload's layers)",
                       "timing": "HIP graph replay, events on the capture stream"},
         "step_us": spread,
         "device": device_info(torch),
-        "layer_hbm_frac": round(algorithmic_bytes(M, K, N, r, B, y_bytes, args.group) / (ms_step * 1e-3)
-                                / (PEAK_HBM_GBS * 1e9), 4),
+        "layer_hbm_frac": round(abytes / (ms_step * 1e-3) / (PEAK_HBM_GBS * 1e9), 4),
         "wall_s": round(wall, 4),
         "roofline": roof,
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline and args.act_quant == "sym":
-        out["cpu_baseline"] = cpu_baseline(lay, spec, args.cpu_seconds)
+        out["cpu_baseline"] = cpu_baseline([L["lay"] for L in layers], specs, args.cpu_seconds,
+                                           args.cpu_rows)
+        out["cpu_single_thread"] = cpu_single_thread_tiny()
     print(json.dumps(out), flush=True)
     return 0
 

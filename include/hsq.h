@@ -39,7 +39,10 @@
  *   - The library keeps no state between calls and is thread-safe; no C++
  *     exception crosses this interface.
  *   - Limits: K % 64 == 0 and K >= 64; M, N >= 1; 0 <= r <= 32;
- *     1 <= batch <= 16; M * K, M * N, K * N < 2^31.
+ *     1 <= batch <= 16; M * K, M * N, K * N < 2^31; and, for the linear,
+ *     16*ceil(M/16) * Kp < 2^32 and 16*ceil(N/16) * Kp / 2 < 2^32 with
+ *     Kp = K rounded up to 128 (the padded int8 activation codes and the
+ *     packed residual are addressed through 32-bit buffer resources).
  */
 #ifndef HSQ_H
 #define HSQ_H
@@ -93,9 +96,11 @@ size_t hsq_packed_weight_bytes(int K, int N);
  * Hessian, abstract), group-64 (Table 1 caption).
  *   codes   in : K x N int8 (input channel x output channel), values in [-8, 7]
  *   packed  out: hsq_packed_weight_bytes(K, N) bytes; padding is zero codes
- *   d_status out: one device int; set to 0, then to 1 if any code lies
- *                 outside [-8, 7] (that code's low nibble is stored).  The
- *                 caller reads it after synchronising.
+ *   d_status out: one device int; set to 0 (by a kernel: the call enqueues
+ *                 kernels only, so it can be captured in a HIP graph),
+ *                 then to 1 if any code lies outside [-8, 7] (that code's
+ *                 low nibble is stored).  The caller reads it after
+ *                 synchronising.
  * Errors: HSQ_E_INVAL, HSQ_E_SHAPE, HSQ_E_ALIGN, HSQ_E_HIP. */
 int hsq_pack_weights(const int8_t *codes, int K, int N, uint8_t *packed, int *d_status,
                      void *stream);
@@ -304,6 +309,14 @@ int hsq_mx_lowrank_linear(const uint16_t *X, int M, int K, int N, const uint16_t
  *              layer's output before the activation (a test export)
  *   r_down     0 .. 8; the up layer runs the tiled contraction unsplit
  * All other arguments as for hsq_w4a4_lowrank_linear, per layer.
+ * Performance: on an MI355X this call is SLOWER than the two layers run
+ * as separate hsq_w4a4_lowrank_linear calls (FLUX.1 MLP, 4608 tokens:
+ * 0.786 ms fused vs 0.701 ms separate, the separate path without any
+ * activation pass).  The up contraction is bound by its per-group VALU
+ * rescale, and the fused epilogue adds about 50 VALU instructions per
+ * output element (GELU, smoothing, absmax, codes, rank-r dot product) to
+ * it, more than the bf16 round trip and quantization pass it removes.  Use
+ * it where the hidden activation must not be materialised, not for speed.
  * Errors: HSQ_E_INVAL, HSQ_E_SHAPE (K or H not a multiple of 64),
  * HSQ_E_ALIGN, HSQ_E_WORKSPACE, HSQ_E_HIP. */
 #define HSQ_ACT_IDENTITY   0

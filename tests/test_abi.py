@@ -118,6 +118,12 @@ def _linear(**kw):
     (dict(wsb=0), hsq.E_WORKSPACE),
     (dict(wsb=1000), hsq.E_WORKSPACE),
     (dict(M=1 << 20, K=1 << 12), hsq.E_INVAL),  # M*K >= 2^31
+    # M*K < 2^31, but the int8 codes padded to 16 rows reach 2^32 bytes,
+    # past what the contraction's 32-bit buffer resources address
+    (dict(M=1, K=1 << 28, N=1), hsq.E_INVAL),
+    (dict(M=3, K=(1 << 28) - 64, N=1), hsq.E_INVAL),
+    # the largest token count the GPU limit tests run passes the size checks
+    (dict(M=32767, K=65536, N=16, wsb=0), hsq.E_WORKSPACE),
 ])
 def test_linear_rejects_before_launch(kw, code):
     assert _linear(**kw) == code

@@ -128,6 +128,17 @@ def test_chain_matches_oracle(M, K, H, N, act):
     run_case(up, dn, act)
 
 
+@pytest.mark.parametrize("M,K,H,N,r1,r2", [
+    (200, 256, 320, 200, 4, 0),      # rank-0 down layer: no U shares, no U reduction
+    (130, 512, 384, 72, 0, 4),       # rank-0 up layer
+    (40, 192, 256, 136, 0, 0),       # both rank 0, the down layer on the skinny contraction
+])
+def test_chain_rank_zero_layers(M, K, H, N, r1, r2):
+    up = make_random_layer(700 + M + r1, M, K, H, r=r1, outlier_channels=2)
+    dn = make_random_layer(800 + M + r2, M, H, N, r=r2, outlier_channels=0)
+    run_case(up, dn, "gelu_tanh")
+
+
 def test_chain_flux_mlp_sampled_rows():
     up = make_layer("flux_up")
     dn = make_layer("flux_down")

@@ -116,3 +116,45 @@ def test_graph_hessian(M, K):
     X2 = dev16(make_random_layer(79, M, K, 64, r=4)["X"])
     other = lambda: hsq.hessian_accumulate(X2, lam)
     replay_matches(run, H, other)
+
+
+def test_graph_pack_weights():
+    # the pack call (status clear + pack kernel) captured and replayed: the
+    # packed bytes and the status word equal the eager call's on every
+    # replay; a replay over codes that were made out of range in between
+    # sets the status, and the next clean replay clears it again
+    rng = np.random.default_rng(5)
+    K, N = 1152, 300
+    codes = dev8(rng.integers(-8, 8, (K, N), dtype=np.int8))
+    packed = torch.empty(hsq.packed_weight_bytes(K, N), dtype=torch.uint8, device=DEV)
+    status = torch.empty(4, dtype=torch.int32, device=DEV)
+    ref_packed, ref_status = hsq.pack_weights(codes)
+    torch.cuda.synchronize()
+    ref = ref_packed.cpu().numpy().copy()
+    assert int(ref_status[0].item()) == 0
+    g = torch.cuda.CUDAGraph()
+    cap = torch.cuda.Stream()
+    with torch.cuda.stream(cap):
+        with torch.cuda.graph(g, stream=cap):
+            hsq.pack_weights(codes, packed=packed, status=status)
+    torch.cuda.synchronize()
+    say(f"[graph] pack K={K} N={N}")
+    for rep in range(3):
+        packed.fill_(0xEE)
+        status.fill_(7)
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(packed.cpu().numpy(), ref), f"replay {rep}"
+        assert int(status[0].item()) == 0, f"replay {rep}"
+        hsq.pack_weights(codes)                 # eager work in between
+        torch.cuda.synchronize()
+    saved = codes[17, 5].item()
+    codes[17, 5] = 9                            # out of range: flagged
+    g.replay()
+    torch.cuda.synchronize()
+    assert int(status[0].item()) == 1
+    codes[17, 5] = saved
+    g.replay()
+    torch.cuda.synchronize()
+    assert int(status[0].item()) == 0
+    assert np.array_equal(packed.cpu().numpy(), ref)

@@ -344,6 +344,38 @@ def _workspace_codes_scales(up, ws):
     return codes, scales
 
 
+@pytest.mark.parametrize("name,M", [("tiny", None), ("pixart_up", None), ("sana_qkv", None),
+                                    ("flux_up", None), ("flux_down", None),
+                                    ("qwen3_up", 16), ("qwen3_down", 16), ("qwen3_up", 256),
+                                    ("qwen3_down", 256), ("qwen3_up", 2048), ("qwen3_down", 2048)])
+def test_linear_workspace_codes_scales_bit_exact(oracle, name, M):
+    # the codes and fp16 scales that the fused layer's own quantization pass
+    # writes for its contraction (group 64, symmetric), decoded from the
+    # workspace and compared with the oracle on every row and group; the
+    # pass is the one hsq_w4a4_lowrank_linear launches (same plan, same
+    # kernel), run here through the stage entry point so that the workspace
+    # holds its output
+    up = uploaded(name, M)
+    say(f"[codes ws g64] {name} M={up.M} K={up.K} N={up.N} batch={up.B}")
+    ws = torch.empty(hsq.workspace_bytes(up.M, up.K, up.N, up.r, up.B), dtype=torch.uint8, device=DEV)
+    ws.fill_(0x5A)                      # stale bytes: every byte the decode reads must be rewritten
+    hsq.quantize_stage(up.X, up.lam, up.L1, N=up.N, batch=up.B, workspace=ws)
+    torch.cuda.synchronize()
+    codes, scales = _workspace_codes_scales(up, ws)
+    q_ref, s_ref = oracle.quantize(up.lay["X"], up.lay["lam"])
+    assert np.array_equal(scales, s_ref)
+    assert np.array_equal(codes, q_ref)
+    # the same workspace after the whole layer (quantization pass + contraction)
+    ws2 = torch.empty_like(ws).fill_(0xA5)
+    out = torch.empty((up.B, up.M, up.N), dtype=torch.bfloat16, device=DEV)
+    hsq.w4a4_lowrank_linear(up.X, up.lam, up.packed, up.sw, up.L1, up.L2, up.bias, N=up.N, batch=up.B,
+                            out=out, workspace=ws2)
+    torch.cuda.synchronize()
+    codes2, scales2 = _workspace_codes_scales(up, ws2)
+    assert np.array_equal(scales2, s_ref)
+    assert np.array_equal(codes2, q_ref)
+
+
 @pytest.mark.parametrize("name,M", [("qwen3_up", 16), ("qwen3_down", 256), ("qwen3_up", 2048)])
 def test_group128_codes_scales_bit_exact(oracle, name, M):
     up = uploaded(name, M, 128)

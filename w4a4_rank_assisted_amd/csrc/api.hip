@@ -48,6 +48,14 @@ int check_sizes(int M, int K, int N, int r, int batch) {
   if (K % kGroup != 0) return HSQ_E_SHAPE;
   if ((long long)M * K >= INT_MAX || (long long)M * N >= INT_MAX || (long long)K * N >= INT_MAX)
     return HSQ_E_INVAL;
+  // The contraction kernels address the padded operand blobs through 32-bit
+  // buffer resources: the int8 activation codes (rows padded to 16, K to
+  // 128) and the packed residual (columns padded to 16) must each stay
+  // below 2^32 bytes, or the resource size would wrap and every load read 0.
+  const long long kpad = (long long)padded_groups(K) * kGroup;
+  if ((long long)ceil_div(M, kTile) * kTile * kpad >= (1LL << 32) ||
+      (long long)ceil_div(N, kTile) * kTile * kpad / 2 >= (1LL << 32))
+    return HSQ_E_INVAL;
   return HSQ_OK;
 }
 

@@ -773,7 +773,7 @@ __global__ __launch_bounds__(256) void k_chain_ureduce(const float *upart, int n
 }
 
 hipError_t launch_gemm_tiled_chain(const GemmArgs &a, hipStream_t s) {
-  if (a.bpg != 1 || a.r2 < 1 || a.r2 > kChainMaxRank) return hipErrorInvalidValue;
+  if (a.bpg != 1 || a.r2 < 0 || a.r2 > kChainMaxRank) return hipErrorInvalidValue;
   const int nblk = ceil_div(a.N, BN), mblk = ceil_div(a.M, BM);
   if (a.r == 0) return launch_chain_rpt<0>(a, nblk, mblk, s);
   if (a.r <= 4) return launch_chain_rpt<4>(a, nblk, mblk, s);

@@ -41,6 +41,8 @@ __global__ void k_pack(const int8_t *__restrict__ codes, int K, int N, int NT, i
   if (bad) *status = 1;  // benign race: every writer stores the same value
 }
 
+__global__ void k_clear_status(int *__restrict__ status) { *status = 0; }
+
 __global__ void k_unpack(const uint8_t *__restrict__ packed, int K, int N, int GP,
                          int8_t *__restrict__ codes) {
   size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x;  // one code
@@ -66,7 +68,10 @@ hipError_t launch_pack(const int8_t *codes, int K, int N, uint8_t *packed, int *
                        hipStream_t s) {
   int NT = ceil_div(N, kTile), GP = padded_groups(K) / 2;
   size_t nslots = (size_t)NT * GP * 64;
-  hipError_t e = hipMemsetAsync(status, 0, sizeof(int), s);
+  // the status word is cleared by a kernel, not a memset, so that the pack
+  // call can be captured in a HIP graph as kernel nodes only
+  hipLaunchKernelGGL(k_clear_status, dim3(1), dim3(1), 0, s, status);
+  hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   unsigned blocks = (unsigned)((nslots + 255) / 256);
   hipLaunchKernelGGL(k_pack, dim3(blocks), dim3(256), 0, s, codes, K, N, NT, GP, packed, status);
