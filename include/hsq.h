@@ -36,8 +36,9 @@
  *   - Arguments are validated before anything is enqueued; on an error the
  *     call returns a negative HSQ_E_* code and enqueues nothing.  Faults that
  *     happen while kernels run surface at the caller's next synchronisation.
- *   - The library keeps no state between calls and is thread-safe; no C++
- *     exception crosses this interface.
+ *   - The library keeps no state between calls (except the per-device
+ *     scratch of hsq_w4a4_lowrank_linear_noalloc) and is thread-safe; no
+ *     C++ exception crosses this interface.
  *   - Limits: K % 64 == 0 and K >= 64; M, N >= 1; 0 <= r <= 32;
  *     1 <= batch <= 16; M * K, M * N, K * N < 2^31; and, for the linear,
  *     16*ceil(M/16) * Kp < 2^32 and 16*ceil(N/16) * Kp / 2 < 2^32 with
@@ -61,6 +62,8 @@ extern "C" {
 #define HSQ_E_ALIGN      -3  /* a pointer is not 16-byte aligned */
 #define HSQ_E_WORKSPACE  -4  /* workspace missing or smaller than the size function returns */
 #define HSQ_E_HIP        -5  /* the HIP runtime refused a launch */
+#define HSQ_E_SCRATCH    -6  /* hsq_w4a4_lowrank_linear_noalloc: the sizes need more
+                                workspace than its static scratch holds */
 
 /* ---- output dtypes ---- */
 #define HSQ_F32   0
@@ -161,6 +164,32 @@ int hsq_w4a4_lowrank_linear_ex(const uint16_t *X, int M, int K, int N, int batch
                                const uint16_t *sw, const uint16_t *L1, const uint16_t *L2,
                                int r, const uint16_t *bias, void *Y, int y_dtype,
                                void *workspace, size_t ws_bytes, int kernel, void *stream);
+
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * layer as hsq_w4a4_lowrank_linear (group 64, contraction kernel chosen
+ * as for HSQ_KERNEL_AUTO), with its workspace in a static device array of
+ * HSQ_NOALLOC_SCRATCH_BYTES (64 MiB) inside the library instead of a caller
+ * buffer.  Every GPU the library runs on holds its own array until the
+ * process ends; the first call on a device looks up that device's address
+ * of it (no allocation).  The call uses the array of the CURRENT device
+ * (hipGetDevice); `stream` must belong to that device.  The call allocates
+ * and frees nothing.  All calls on one GPU share its array: calls that may
+ * overlap in time on one GPU (two streams, two host threads without
+ * ordering) race on it and must be serialised by the caller; calls in order
+ * on one stream are safe.  No part of the array needs to start zeroed (the
+ * quantization pass rewrites everything the contraction reads).
+ * Sizes whose workspace (hsq_workspace_bytes(M, K, N, r, batch)) exceeds
+ * the array return HSQ_E_SCRATCH before anything is enqueued; every
+ * configuration of the diffusion and LLM layers here fits (the largest,
+ * 4608 tokens x 12288 channels, needs about 59 MB).
+ * Other arguments and errors as for hsq_w4a4_lowrank_linear. */
+#define HSQ_NOALLOC_SCRATCH_BYTES (64u << 20)
+int hsq_w4a4_lowrank_linear_noalloc(const uint16_t *X, int M, int K, int N, int batch,
+                                    const uint16_t *lambda, const uint8_t *packed_w,
+                                    const uint16_t *sw, const uint16_t *L1, const uint16_t *L2,
+                                    int r, const uint16_t *bias, void *Y, int y_dtype,
+                                    void *stream);
 
 /* The same layer in two stages on one stream, for callers that time or
  * schedule them separately, or reuse one quantized input for several

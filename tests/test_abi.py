@@ -275,3 +275,20 @@ def test_format_variant_entry_points_validate():
     assert mlp(A, 64, 256, 512, 256, *up, hsq.ACT_GELU_TANH, *dn, A, 9, None, A, 1 << 30, None) == hsq.E_INVAL
     assert mlp(A, 64, 256, 512, 256, *up, hsq.ACT_GELU_TANH, *dn, A, hsq.BF16, None, A, 16, None) == hsq.E_WORKSPACE
     assert mlp(A, 64, 256, 512, 256, *up, hsq.ACT_GELU_TANH, *dn, A, hsq.BF16, A + 4, A, 1 << 30, None) == hsq.E_ALIGN
+
+
+def test_noalloc_entry_validates_before_any_device_call():
+    # every rejection happens before the scratch address is looked up, so
+    # none of these touches a GPU
+    f = lib.hsq_w4a4_lowrank_linear_noalloc
+    assert f(None, 64, 256, 256, 1, A, A, A, A, A, 4, A, A, hsq.BF16, None) == hsq.E_INVAL
+    assert f(A, 64, 100, 256, 1, A, A, A, A, A, 4, A, A, hsq.BF16, None) == hsq.E_SHAPE
+    assert f(A + 2, 64, 256, 256, 1, A, A, A, A, A, 4, A, A, hsq.BF16, None) == hsq.E_ALIGN
+    assert f(A, 64, 256, 256, 1, A, A, A, A, A, 4, A, A, 2, None) == hsq.E_INVAL
+    # codes alone need 2048 x 64 KiB = 128 MiB > the 64 MiB scratch
+    assert lib.hsq_workspace_bytes(32767, 4096, 16, 4, 1) > hsq.NOALLOC_SCRATCH_BYTES
+    assert f(A, 32767, 4096, 16, 1, A, A, A, A, A, 4, A, A, hsq.BF16, None) == hsq.E_SCRATCH
+    text = open(hsq.HEADER).read()
+    assert "#define HSQ_NOALLOC_SCRATCH_BYTES (64u << 20)" in text
+    assert "#define HSQ_E_SCRATCH    -6" in text
+    assert b"static scratch" in lib.hsq_status_string(hsq.E_SCRATCH)

@@ -21,7 +21,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "_lib", "libhsq.so")
 HEADER = os.path.join(os.path.dirname(_HERE), "include", "hsq.h")
 
-OK, E_INVAL, E_SHAPE, E_ALIGN, E_WORKSPACE, E_HIP = 0, -1, -2, -3, -4, -5
+OK, E_INVAL, E_SHAPE, E_ALIGN, E_WORKSPACE, E_HIP, E_SCRATCH = 0, -1, -2, -3, -4, -5, -6
+NOALLOC_SCRATCH_BYTES = 64 << 20
 F32, BF16 = 0, 1
 KERNEL_AUTO, KERNEL_TILED, KERNEL_SKINNY = 0, 1, 2
 ACT_IDENTITY, ACT_GELU_TANH = 0, 1
@@ -63,6 +64,7 @@ def _load():
             "hsq_quantize_act": ([P, I, I, P, P, I, P, P, P, P], I),
             "hsq_workspace_bytes": ([I, I, I, I, I], S),
             "hsq_w4a4_lowrank_linear": ([P, I, I, I, I, P, P, P, P, P, I, P, P, I, P, S, P], I),
+            "hsq_w4a4_lowrank_linear_noalloc": ([P, I, I, I, I, P, P, P, P, P, I, P, P, I, P], I),
             "hsq_w4a4_lowrank_linear_ex": ([P, I, I, I, I, P, P, P, P, P, I, P, P, I, P, S, I, P], I),
             "hsq_w4a4_group_partials": ([P, I, I, I, P, P, I, I, I, I, P, P, S, I, P], I),
             "hsq_w4a4_quantize_stage": ([P, I, I, I, I, P, P, I, P, S, P], I),
@@ -251,6 +253,37 @@ def w4a4_lowrank_linear(X, lam, packed_w, sw, L1=None, L2=None, bias=None, *, N:
     else:
         _check(lib.hsq_w4a4_lowrank_linear_g(_ptr(X), M, K, N, batch, group, *args),
                "hsq_w4a4_lowrank_linear_g")
+    return out
+
+
+def w4a4_lowrank_linear_noalloc(X, lam, packed_w, sw, L1=None, L2=None, bias=None, *, N: int,
+                                batch: int = 1, y_dtype: str = "bf16", out=None):
+    """The fused layer (group 64, symmetric activations) with its workspace
+    in the library's static per-device scratch (hsq_w4a4_lowrank_linear_noalloc):
+    no workspace argument and no allocation inside the call.  ``out`` must
+    be given by callers that cannot allocate (this wrapper allocates it
+    otherwise).  Calls that overlap in time on one GPU race on the scratch."""
+    torch = _torch()
+    lib = _load()
+    _dev_tensor(X, "X", _half_types())
+    M, K = X.shape
+    _dev_tensor(lam, "lambda", _half_types(), (K,))
+    _dev_tensor(packed_w, "packed_w", (torch.uint8,), (batch * lib.hsq_packed_weight_bytes(K, N),))
+    _dev_tensor(sw, "sw", _half_types(), (batch, K // 64, N))
+    r = 0 if L1 is None else int(L1.shape[-1])
+    if r:
+        _dev_tensor(L1, "L1", _half_types(), (batch, K, r))
+        _dev_tensor(L2, "L2", _half_types(), (batch, r, N))
+    if bias is not None:
+        _dev_tensor(bias, "bias", _half_types(), (batch, N))
+    ydt = {"bf16": (BF16, torch.bfloat16), "f32": (F32, torch.float32)}[y_dtype]
+    if out is None:
+        out = torch.empty((batch, M, N), dtype=ydt[1], device=X.device)
+    _dev_tensor(out, "out", (ydt[1],), (batch, M, N))
+    _check(lib.hsq_w4a4_lowrank_linear_noalloc(_ptr(X), M, K, N, batch, _ptr(lam), _ptr(packed_w), _ptr(sw),
+                                               _ptr(L1) if r else None, _ptr(L2) if r else None, r, _ptr(bias),
+                                               _ptr(out), ydt[0], _stream()),
+           "hsq_w4a4_lowrank_linear_noalloc")
     return out
 
 

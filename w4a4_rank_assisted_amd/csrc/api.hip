@@ -4,8 +4,10 @@
 #include "hsq.h"
 #include "hsq_internal.h"
 
+#include <atomic>
 #include <climits>
 #include <cstdint>
+#include <mutex>
 
 namespace hsq {
 
@@ -305,6 +307,45 @@ bool aq_ok(int aq) { return aq == HSQ_AQ_SYMMETRIC || aq == HSQ_AQ_ASYMMETRIC; }
 
 }  // namespace
 
+// ---------------------------------------------------------------------------
+// Static scratch of hsq_w4a4_lowrank_linear_noalloc: the layer's workspace in
+// a device array of fixed size, for callers that cannot allocate.  Every GPU
+// the library runs on holds its own copy of it until the process ends.  In
+// host code `scratch` only names the symbol: its device address on the
+// current GPU comes from hipGetSymbolAddress (once per device, on the first
+// no-alloc call with that device current) and only that address is passed
+// to the kernels.
+static __device__ __align__(256) unsigned char scratch[HSQ_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::atomic<void *> g_scratch_ptr[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// Device address of the current device's scratch array.
+int scratch_of_current_device(void **out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e);
+  if (dev < 0 || dev >= kMaxDevices) return HSQ_E_INVAL;
+  void *p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (!p) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+    if (!p) {
+      e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+      if (e != hipSuccess) return hip_status(e);
+      if (!p) return HSQ_E_HIP;
+      g_scratch_ptr[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return HSQ_OK;
+}
+
+}  // namespace
+
 extern "C" {
 
 int hsq_layout_version(void) { return 1; }
@@ -317,6 +358,7 @@ const char *hsq_status_string(int status) {
     case HSQ_E_ALIGN: return "pointer not 16-byte aligned";
     case HSQ_E_WORKSPACE: return "workspace missing or too small";
     case HSQ_E_HIP: return "HIP launch failed";
+    case HSQ_E_SCRATCH: return "the sizes need more workspace than the no-alloc entry point's static scratch holds";
     default: return "unknown status";
   }
 }
@@ -384,6 +426,30 @@ int hsq_w4a4_lowrank_linear(const uint16_t *X, int M, int K, int N, int batch,
                             size_t ws_bytes, void *stream) {
   return run_linear(X, M, K, N, batch, kGroup, lambda, packed_w, sw, L1, L2, r, bias, Y, y_dtype,
                     workspace, ws_bytes, HSQ_KERNEL_AUTO, stream, nullptr, 0, 0, 0, 0);
+}
+
+int hsq_w4a4_lowrank_linear_noalloc(const uint16_t *X, int M, int K, int N, int batch,
+                                    const uint16_t *lambda, const uint8_t *packed_w,
+                                    const uint16_t *sw, const uint16_t *L1, const uint16_t *L2,
+                                    int r, const uint16_t *bias, void *Y, int y_dtype,
+                                    void *stream) {
+  // every argument is checked before any device call: sizes, the bound of
+  // the static scratch, then the pointers (with an aligned placeholder in
+  // the workspace's place); only then is the scratch's address looked up
+  int st = check_sizes(M, K, N, r, batch);
+  if (st != HSQ_OK) return st;
+  if (plan_workspace(M, K, N, r, batch, kGroup).total > (size_t)HSQ_NOALLOC_SCRATCH_BYTES)
+    return HSQ_E_SCRATCH;
+  int kernel = HSQ_KERNEL_AUTO;
+  void *const placeholder = reinterpret_cast<void *>((uintptr_t)256);
+  st = validate(X, M, K, N, batch, kGroup, lambda, packed_w, sw, L1, L2, r, bias, Y, y_dtype, placeholder,
+                (size_t)HSQ_NOALLOC_SCRATCH_BYTES, &kernel, true, true, nullptr, 0, 0, 0, 0);
+  if (st != HSQ_OK) return st;
+  void *ws = nullptr;
+  st = scratch_of_current_device(&ws);
+  if (st != HSQ_OK) return st;
+  return run_linear(X, M, K, N, batch, kGroup, lambda, packed_w, sw, L1, L2, r, bias, Y, y_dtype, ws,
+                    (size_t)HSQ_NOALLOC_SCRATCH_BYTES, HSQ_KERNEL_AUTO, stream, nullptr, 0, 0, 0, 0);
 }
 
 int hsq_w4a4_lowrank_linear_ex(const uint16_t *X, int M, int K, int N, int batch,
