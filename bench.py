@@ -293,6 +293,134 @@ def summarize_profiles(args):
     return 0
 
 
+PROBE_LIB = os.path.join(ROOT, "w4a4_rank_assisted_amd", "_lib", "libhsq_probe.so")
+PROBE_MODES = {0: "mfma_only", 1: "mfma_plus_1_fma_per_element", 2: "mfma_plus_2_fma_per_element",
+               3: "mfma_plus_2_fma_plus_lds_reads"}
+
+
+def _probe_lib():
+    """libhsq_probe (measurement kernels), loaded after torch so that it binds
+    to torch's HIP runtime."""
+    import ctypes
+
+    import torch  # noqa: F401
+
+    if not os.path.exists(PROBE_LIB):
+        raise OSError(f"{PROBE_LIB} is missing; build it with w4a4_rank_assisted_amd.build.build()")
+    lib = ctypes.CDLL(PROBE_LIB)
+    P, I, S = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+    lib.hsq_probe_mfma.argtypes = [I, I, I, I, P, P]
+    lib.hsq_probe_read.argtypes = [P, S, I, P, P]
+    lib.hsq_probe_copy.argtypes = [P, S, I, P, P]
+    for f in (lib.hsq_probe_mfma, lib.hsq_probe_read, lib.hsq_probe_copy):
+        f.restype = I
+    return lib
+
+
+def _time_graph(torch, launch, reps: int):
+    """Milliseconds per launch: `reps` launches captured in one HIP graph,
+    replayed between events on the capture stream (after one untimed
+    replay); the median of three timed replays."""
+    cap = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(cap):
+        launch(cap)                          # eager warm-up
+        with torch.cuda.graph(g, stream=cap):
+            for i in range(reps):
+                launch(cap, i)
+    torch.cuda.synchronize()
+    g.replay()
+    torch.cuda.synchronize()
+    ts = []
+    for _ in range(3):
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        with torch.cuda.stream(cap):
+            t0.record(cap)
+            g.replay()
+            t1.record(cap)
+        torch.cuda.synchronize()
+        ts.append(t0.elapsed_time(t1) / reps)
+    return sorted(ts)[1]
+
+
+def measure_peaks(torch, full: bool = False):
+    """Measured ceilings of this GPU (libhsq_probe): the int8 MFMA rate with
+    the tiled contraction's wave tile and occupancy (512 workgroups of 8
+    waves, 4 waves per SIMD), alone and with the contraction's per-element
+    rescale work (and, with `full`, its LDS reads, and more occupancies);
+    HBM read and copy rates of 16-byte loads over 1 GiB and over 27 MB
+    buffers rotated through 540 MB (the size of a 16-token layer's weight
+    stream, past the 256 MB MALL)."""
+    import ctypes
+
+    lib = _probe_lib()
+    dev = torch.device("cuda:0")
+    blocks, waves, iters = 512, 8, 2000
+    sink = torch.empty(1024 * 64 * 16, dtype=torch.int32, device=dev)
+    res = {"int8_mfma_tops": {}, "hbm_gbs": {}}
+    configs = [(0, blocks, waves), (2, blocks, waves)]
+    if full:
+        configs = [(m, blocks, waves) for m in (0, 1, 2, 3)] + [(0, 256, 4), (0, 256, 8), (0, 512, 16)]
+    for mode, nb, nw in configs:
+        def launch(stream, i=0, mode=mode, nb=nb, nw=nw):
+            assert lib.hsq_probe_mfma(mode, iters, nb, nw, ctypes.c_void_p(sink.data_ptr()),
+                                      ctypes.c_void_p(stream.cuda_stream)) == 0
+        ms = _time_graph(torch, launch, 5)
+        ops = nb * nw * iters * 8 * 2 * 16 * 16 * 64
+        key = PROBE_MODES[mode] + ("" if (nb, nw) == (blocks, waves) else f"_{nb}x{nw}waves")
+        res["int8_mfma_tops"][key] = round(ops / (ms * 1e-3) / 1e12, 1)
+    sblocks = 256 * 8
+    big = 1 << 30
+    src = torch.empty(big, dtype=torch.uint8, device=dev).fill_(3)
+    dst = torch.empty(big, dtype=torch.uint8, device=dev)
+    for kind, fn in (("read", lib.hsq_probe_read), ("copy", lib.hsq_probe_copy)):
+        out = sink if kind == "read" else dst
+
+        def launch_big(stream, i=0, fn=fn, out=out):
+            assert fn(ctypes.c_void_p(src.data_ptr()), big, sblocks, ctypes.c_void_p(out.data_ptr()),
+                      ctypes.c_void_p(stream.cuda_stream)) == 0
+        ms = _time_graph(torch, launch_big, 3)
+        res["hbm_gbs"][f"{kind}_1GiB"] = round(big * (1 if kind == "read" else 2) / (ms * 1e-3) / 1e9, 1)
+        small, nbuf = 27 * 1000 * 1000 // 16 * 16, 20
+
+        def launch_small(stream, i=0, fn=fn, out=out):
+            off = (i % nbuf) * small
+            o = out.data_ptr() + (0 if kind == "read" else off)
+            assert fn(ctypes.c_void_p(src.data_ptr() + off), small, sblocks, ctypes.c_void_p(o),
+                      ctypes.c_void_p(stream.cuda_stream)) == 0
+        ms = _time_graph(torch, launch_small, nbuf)
+        res["hbm_gbs"][f"{kind}_27MB_rotated"] = round(small * (1 if kind == "read" else 2) / (ms * 1e-3) / 1e9, 1)
+    del src, dst
+    return res
+
+
+def probe_main(args):
+    """The measured ceilings of this GPU as one JSON line (bench.py --probe)."""
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU; use --gpus 1", file=sys.stderr)
+        return 2
+    import torch
+
+    res = measure_peaks(torch, full=True)
+    mf = res["int8_mfma_tops"]
+    out = {
+        "metric": "measured ceilings of the MI355X for the W4A4 contraction",
+        "int8_mfma_tops": mf,
+        "int8_mfma_frac_of_spec": {k: round(v / PEAK_INT8_TOPS, 4) for k, v in mf.items()},
+        "hbm_gbs": res["hbm_gbs"],
+        "hbm_frac_of_spec": {k: round(v / PEAK_HBM_GBS, 4) for k, v in res["hbm_gbs"].items()},
+        "notes": ("MFMA probe: 512 workgroups x 8 waves (4 waves per SIMD) unless named, each wave the "
+                  "tiled contraction's 4 x 2 tiles of v_mfma_i32_16x16x64_i8 per step with register "
+                  "operands; the rescale modes add 1 or 2 fp32 FMAs per MFMA result element on the previous "
+                  "step's results, the lds mode also the step's LDS operand reads. HBM: 16-byte "
+                  "non-temporal loads (and stores), 2048 workgroups of 256 threads."),
+        "device": device_info(torch),
+    }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
 def calib_cpu_baseline(lay, W, seconds: float):
     """The calibration oracle (NumPy fp64) on the same projection: H, the
     deflation and the closed-form L2, repeated until `seconds` have passed."""
@@ -680,12 +808,19 @@ def main(argv=None):
     ap.add_argument("--chain", action="store_true",
                     help="time the fused two-layer chain (FLUX.1 MLP: flux_up, GELU, flux_down) against "
                          "the two layers run one after the other")
+    ap.add_argument("--probe", action="store_true",
+                    help="measure this GPU's ceilings (int8 MFMA alone and with the rescale work, HBM "
+                         "read and copy) with the kernels of libhsq_probe")
+    ap.add_argument("--no-peaks", action="store_true",
+                    help="skip the measured-peak probes of the default run")
     ap.add_argument("--calib", action="store_true",
                     help="time the calibration kernels (Hessian, deflation, closed-form L2) on the "
                          "layer instead of the inference path")
     args = ap.parse_args(argv)
     if args.summarize:
         return summarize_profiles(args)
+    if args.probe:
+        return probe_main(args)
     if args.calib:
         return calib_main(args)
     if args.chain:
@@ -880,6 +1015,21 @@ def linear_main(args):
         roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": traffic,
                 "kernel": kname, "bytes_per_launch": cbytes // nl}
+
+    # the same launch against this GPU's measured ceilings (libhsq_probe):
+    # the int8 MFMA probe's rate (MFMAs only, and with the exact two-FMA
+    # rescale per element), or the HBM read rate of a 27 MB / 1 GiB stream
+    if not args.no_peaks:
+        peaks = measure_peaks(torch)
+        roof["measured_peaks"] = peaks
+        if roof["bound"] == "mfma":
+            mp = peaks["int8_mfma_tops"]
+            roof["frac_measured"] = round(roof["achieved"] / mp["mfma_only"], 4)
+            roof["frac_of_rescale_ceiling"] = round(roof["achieved"] / mp["mfma_plus_2_fma_per_element"], 4)
+        else:
+            hb = peaks["hbm_gbs"]
+            ref = hb["read_27MB_rotated"] if cbytes / nl < 64e6 else hb["read_1GiB"]
+            roof["frac_measured"] = round(roof["achieved"] / ref, 4)
 
     sp0 = specs[0]
     cfg = {"workload": f"{wl_name}: {wl_desc or sp0.description}"}

@@ -292,3 +292,39 @@ def test_noalloc_entry_validates_before_any_device_call():
     assert "#define HSQ_NOALLOC_SCRATCH_BYTES (64u << 20)" in text
     assert "#define HSQ_E_SCRATCH    -6" in text
     assert b"static scratch" in lib.hsq_status_string(hsq.E_SCRATCH)
+
+
+def test_every_header_is_exported_by_its_library():
+    # include/hsq.h -> libhsq.so, include/hsq_probe.h -> libhsq_probe.so
+    import glob
+    import os
+
+    libs = {"hsq.h": hsq.LIB_PATH,
+            "hsq_probe.h": os.path.join(os.path.dirname(hsq.LIB_PATH), "libhsq_probe.so")}
+    headers = sorted(os.path.basename(h) for h in glob.glob(os.path.join(os.path.dirname(hsq.HEADER), "*.h")))
+    assert headers == sorted(libs)
+    for h, so in libs.items():
+        text = open(os.path.join(os.path.dirname(hsq.HEADER), h)).read()
+        names = set(re.findall(r"\b(hsq_[a-z0-9_]+)\s*\(", text))
+        assert names, h
+        out = subprocess.run(["nm", "-D", "--defined-only", so], capture_output=True, text=True,
+                             check=True).stdout
+        assert names <= set(re.findall(r"\bT (hsq_\w+)", out)), h
+
+
+def test_probe_entry_points_validate_without_launching():
+    import os
+
+    plib = ctypes.CDLL(os.path.join(os.path.dirname(hsq.LIB_PATH), "libhsq_probe.so"))
+    I, S = ctypes.c_int, ctypes.c_size_t
+    plib.hsq_probe_mfma.argtypes = [I, I, I, I, P, P]
+    plib.hsq_probe_read.argtypes = [P, S, I, P, P]
+    plib.hsq_probe_copy.argtypes = [P, S, I, P, P]
+    assert plib.hsq_probe_mfma(4, 10, 1, 8, A, None) == -1      # no such mode
+    assert plib.hsq_probe_mfma(0, 10, 1, 17, A, None) == -1     # more than 16 waves
+    assert plib.hsq_probe_mfma(0, 0, 1, 8, A, None) == -1
+    assert plib.hsq_probe_mfma(0, 10, 1, 8, None, None) == -1
+    assert plib.hsq_probe_mfma(0, 10, 1, 8, A + 4, None) == -3
+    assert plib.hsq_probe_read(A, 100, 8, A, None) == -1        # not a multiple of 16
+    assert plib.hsq_probe_read(None, 1024, 8, A, None) == -1
+    assert plib.hsq_probe_copy(A, 1024, 8, A + 8, None) == -3

@@ -1,4 +1,5 @@
-"""Build libhsq.so in-tree with hipcc for gfx950.
+"""Build libhsq.so (the layer) and libhsq_probe.so (measurement kernels)
+in-tree with hipcc for gfx950.
 
 Every HIP source is compiled with
   * --offload-arch=gfx950, -O3, C++17;
@@ -44,20 +45,31 @@ def _compile(src: str, extra) -> str:
     return obj
 
 
-def build(extra_flags=(), verbose: bool = False) -> str:
-    """Compile every source and link libhsq.so; returns its path."""
-    os.makedirs(BUILD_DIR, exist_ok=True)
-    os.makedirs(LIB_DIR, exist_ok=True)
-    with concurrent.futures.ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
-        objs = list(ex.map(lambda s: _compile(s, list(extra_flags)), SOURCES))
-    tmp = LIB + ".tmp"
+PROBE_SOURCES = ["probe.hip"]
+PROBE_LIB = os.path.join(LIB_DIR, "libhsq_probe.so")
+
+
+def _link(objs, out):
+    tmp = out + ".tmp"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, out)
+
+
+def build(extra_flags=(), verbose: bool = False) -> str:
+    """Compile every source and link libhsq.so; returns its path."""
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    os.makedirs(LIB_DIR, exist_ok=True)
+    srcs = SOURCES + PROBE_SOURCES
+    with concurrent.futures.ThreadPoolExecutor(max_workers=len(srcs)) as ex:
+        objs = list(ex.map(lambda s: _compile(s, list(extra_flags)), srcs))
+    _link(objs[: len(SOURCES)], LIB)
+    # the measurement kernels: a library of their own, never loaded by the layer
+    _link(objs[len(SOURCES):], PROBE_LIB)
     if verbose:
-        print(f"built {LIB}")
+        print(f"built {LIB} and {PROBE_LIB}")
     return LIB
 
 
