@@ -41,9 +41,10 @@
  *     C++ exception crosses this interface.
  *   - Limits: K % 64 == 0 and K >= 64; M, N >= 1; 0 <= r <= 32;
  *     1 <= batch <= 16; M * K, M * N, K * N < 2^31; and, for the linear,
- *     16*ceil(M/16) * Kp < 2^32 and 16*ceil(N/16) * Kp / 2 < 2^32 with
+ *     16*ceil(M/16) * Kp < 2^32 and 16*ceil(N/16) * Kp < 2^32 with
  *     Kp = K rounded up to 128 (the padded int8 activation codes and the
- *     packed residual are addressed through 32-bit buffer resources).
+ *     int8 part of the packed residual are addressed through 32-bit buffer
+ *     resources).
  */
 #ifndef HSQ_H
 #define HSQ_H
@@ -78,7 +79,8 @@ extern "C" {
 #define HSQ_KERNEL_SKINNY  2  /* weight-streaming kernel for M <= 64: the waves of a
                                  workgroup split K and reduce in a fixed order */
 
-/* Version of the packed-weight layout written by hsq_pack_weights. */
+/* Version of the packed-weight layout written by hsq_pack_weights (2:
+ * nibbles, then int8 operands; see hsq_packed_weight_bytes). */
 int hsq_layout_version(void);
 
 /* Static text for a status code (never NULL). */
@@ -90,8 +92,13 @@ const char *hsq_status_string(int status);
 const char *hsq_last_hip_error(void);
 
 /* Bytes of one packed residual (K x N int4 codes) as hsq_pack_weights
- * writes it: N rounded up to 16 times K rounded up to 128, over 2.
- * Returns 0 if K or N is invalid. */
+ * writes it (layout version 2): Np * Kp / 2 bytes of nibbles followed by
+ * Np * Kp bytes of the same codes as int8 operands, Np = N rounded up to
+ * 16, Kp = K rounded up to 128; 3/2 * Np * Kp in all.  The weight-streaming
+ * contraction for few tokens reads the nibbles (half a byte per weight);
+ * the tiled contraction for many tokens moves the int8 operands into LDS
+ * unchanged, which saves its vector ALU -- the unit that bounds it -- the
+ * nibble unpacking.  Returns 0 if K or N is invalid. */
 size_t hsq_packed_weight_bytes(int K, int N);
 
 /* Pack residual codes into the layout the contraction kernels read.

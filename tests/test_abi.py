@@ -40,15 +40,17 @@ def test_constants_match_header():
 def test_status_strings():
     for s in (0, -1, -2, -3, -4, -5, 7):
         assert isinstance(lib.hsq_status_string(s), bytes)
-    assert lib.hsq_layout_version() == 1
+    assert lib.hsq_layout_version() == 2
 
 
+# layout version 2: nibbles (column tiles x group pairs x 1 KiB), then the
+# int8 operands (column tiles x padded groups x 1 KiB)
 @pytest.mark.parametrize("K,N,expect", [
-    (64, 16, 1024),            # one 16-column tile, one (padded) group pair
-    (128, 16, 1024),
-    (192, 17, 2 * 2 * 1024),   # 2 column tiles x 2 group pairs
-    (1152, 4608, 288 * 9 * 1024),
-    (2240, 2240, 140 * 18 * 1024),  # 35 groups pad to 36
+    (64, 16, 1024 + 2 * 1024),            # one 16-column tile, one (padded) group pair
+    (128, 16, 1024 + 2 * 1024),
+    (192, 17, 2 * 2 * 1024 + 2 * 4 * 1024),   # 2 column tiles x 2 group pairs
+    (1152, 4608, 288 * 9 * 1024 + 288 * 18 * 1024),
+    (2240, 2240, 140 * 18 * 1024 + 140 * 36 * 1024),  # 35 groups pad to 36
     (63, 16, 0), (0, 16, 0), (64, 0, 0),
 ])
 def test_packed_weight_bytes(K, N, expect):

@@ -120,6 +120,27 @@ def test_pack_unpack_roundtrip(K, N):
     assert np.array_equal(back, codes)
 
 
+@pytest.mark.parametrize("K,N", [(64, 16), (192, 37), (1152, 300)])
+def test_pack_operand_part_layout(K, N):
+    # layout version 2: after the nibbles, the codes as int8 16*code in MFMA
+    # operand order: NT x Gp blocks of 1 KiB, column-tile-major; block
+    # (nt, g), lane slot l = column 16 nt + l % 16, channels 64 g + 16 (l // 16)
+    # + p at byte p; pad columns and the pad group are zero
+    rng = np.random.default_rng(K + 3 * N)
+    codes = rng.integers(-8, 8, (K, N), dtype=np.int8)
+    packed, st = hsq.pack_weights(dev8(codes))
+    raw = packed.cpu().numpy()
+    NT, Gp = -(-N // 16), -(-K // 64 // 2) * 2
+    nib = NT * (Gp // 2) * 1024
+    assert raw.size == nib + NT * Gp * 1024
+    ops = raw[nib:].view(np.int8).reshape(NT, Gp, 4, 16, 16)        # nt, g, kq, col, p
+    dense = ops.transpose(1, 2, 4, 0, 3).reshape(Gp * 64, NT * 16)  # (g, kq, p) x (nt, col)
+    want = np.zeros((Gp * 64, NT * 16), np.int32)
+    want[:K, :N] = 16 * codes.astype(np.int32)
+    assert np.array_equal(dense.astype(np.int32), ((want + 128) % 256) - 128)
+    assert int(st[0].item()) == 0
+
+
 def test_pack_flags_out_of_range_codes():
     codes = np.zeros((128, 16), np.int8)
     codes[5, 3] = 9

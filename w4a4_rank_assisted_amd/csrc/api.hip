@@ -31,7 +31,7 @@ WsLayout plan_workspace(int M, int K, int N, int r, int batch, int group) {
   L.uw_off = off;
   off = align_up(off + (size_t)L.u_slices * batch * r * L.Mpad * sizeof(float), 256);
   L.part_off = off;
-  off = align_up(off + tiled_partial_bytes(M, N, K, batch, group), 256);
+  off = align_up(off + tiled_partial_bytes(M, N, K, r, batch, group), 256);
   L.total = off;
   return L;
 }
@@ -52,11 +52,12 @@ int check_sizes(int M, int K, int N, int r, int batch) {
     return HSQ_E_INVAL;
   // The contraction kernels address the padded operand blobs through 32-bit
   // buffer resources: the int8 activation codes (rows padded to 16, K to
-  // 128) and the packed residual (columns padded to 16) must each stay
-  // below 2^32 bytes, or the resource size would wrap and every load read 0.
+  // 128) and the int8 operand part of the packed residual (columns padded
+  // to 16) must each stay below 2^32 bytes, or the resource size would wrap
+  // and every load read 0.
   const long long kpad = (long long)padded_groups(K) * kGroup;
   if ((long long)ceil_div(M, kTile) * kTile * kpad >= (1LL << 32) ||
-      (long long)ceil_div(N, kTile) * kTile * kpad / 2 >= (1LL << 32))
+      (long long)ceil_div(N, kTile) * kTile * kpad >= (1LL << 32))
     return HSQ_E_INVAL;
   return HSQ_OK;
 }
@@ -150,6 +151,7 @@ int contract_stage(int M, int K, int N, int batch, int group, const uint8_t *pac
   g.sxs = (const uint16_t *)(ws + L.sxs_off);
   g.w = packed_w;
   g.w_stride = packed_bytes(K, N);
+  g.w_ops = nibble_bytes(K, N);
   g.sw = sw;
   g.uw = (const float *)(ws + L.uw_off);
   g.u_slices = u_slices >= 0 ? u_slices : L.u_slices;
@@ -264,6 +266,7 @@ int run_chain(const uint16_t *X, int M, int K, int H, int N, const uint16_t *lam
   g.sxs = (const uint16_t *)(wup + c.up.sxs_off);
   g.w = packed_up;
   g.w_stride = packed_bytes(K, H);
+  g.w_ops = nibble_bytes(K, H);
   g.sw = sw_up;
   g.uw = (const float *)(wup + c.up.uw_off);
   g.u_slices = c.up.u_slices;
@@ -348,7 +351,7 @@ int scratch_of_current_device(void **out) {
 
 extern "C" {
 
-int hsq_layout_version(void) { return 1; }
+int hsq_layout_version(void) { return 2; }
 
 const char *hsq_status_string(int status) {
   switch (status) {

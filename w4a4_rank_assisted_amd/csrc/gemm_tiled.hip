@@ -7,32 +7,34 @@
 //
 // One 16x16x64 int8 MFMA covers exactly one group of one 16x16 output tile.
 // Operands: A = activation codes (int8, written by K1 in MFMA lane order),
-// B = residual codes unpacked from nibbles to 16*code on the way into LDS,
-// so the MFMA yields 16*P.  The MFMA accumulator input is the bit pattern of
-// 1.5*2^23; the result bits then read as the float 1.5*2^23 + 16P exactly,
-// and two FMAs per element finish the group:
+// B = residual codes as int8 bytes 16*code (the packed blob's operand part,
+// in MFMA lane order), so the MFMA yields 16*P.  The MFMA accumulator input
+// is the bit pattern of 1.5*2^23; the result bits then read as the float
+// 1.5*2^23 + 16P exactly, and two FMAs per element finish the group:
 //   u   = fma(D, sw/16, -1.5*2^23*sw/16)   (= P*sw rounded once; the
 //                                            constant product is exact)
 //   acc = fma(u, sx, acc)                   (sx read as fp16: v_fma_mix_f32)
-// Those two VALU FMAs per element and group, not the MFMA, bound the kernel:
-// the 8 FMAs that follow each MFMA (4 elements per lane) cap the matrix core
-// at roughly 37 % busy on gfx950 even with all operands in registers
-// (measured; about 60 % with one FMA, 96 % with none).  The loop keeps the
-// VALU fed: within a stage the row tiles run as a software pipeline (LDS
-// read one step ahead, MFMAs of step s, rescale of step s-1).
+// Those two VALU FMAs per element and group bound the kernel: measured on
+// gfx950 with all operands in registers, the 8 FMAs that follow each MFMA
+// (4 elements per lane) hold the matrix core near 42 % busy (85-96 % with
+// none).  So the loop spends no other VALU work per group: both operands
+// move global -> LDS with direct-to-LDS buffer loads (no register staging,
+// no unpacking), and within a stage the row tiles run as a software
+// pipeline (LDS read one step ahead, MFMAs of step k, rescale of step k-1).
 //
 // Workgroup: 512 threads = 8 waves in 2 (M) x 4 (N), tile BM x BN =
-// 128 x 128; each wave owns 64 x 32 outputs = 4 x 2 MFMA tiles.  K advances
-// one group per stage.  Global loads run two stages ahead into two register
-// sets (slot = stage parity, fixed at compile time by unrolling the stage
-// loop by two); a set is written to one of two LDS buffers one stage before
-// it is consumed, so each load has two stages of compute to arrive in.  One
-// barrier per stage.  Workgroups are mapped so that each XCD (own L2) walks
-// a compact block of output tiles.
+// 128 x 128; each wave owns 64 x 32 outputs = 4 x 2 MFMA tiles.  A stage is
+// one pair of 64-channel blocks (two groups, or one group of 128): 16 KB of
+// A and 16 KB of B, four 1 KB direct-to-LDS loads per wave, in one of two
+// LDS buffers.  The loads of stage s+1 are issued as stage s starts, so they
+// have the whole stage to arrive; one barrier per stage (an explicit wait on
+// this wave's loads and LDS writes, then s_barrier: no fence, which would
+// also drain the loads in flight).  Workgroups are mapped so that each XCD
+// (own L2) walks a compact block of output tiles.
 //
 // Split K: when the output has too few tiles to fill the chip (a few hundred
 // tokens against a long K), S workgroups share a tile, each over a range of
-// group pairs, and store their fp32 accumulators as partial tiles in the
+// stages, and store their fp32 accumulators as partial tiles in the
 // workspace; a second launch of the same kernel sums the S partials of a
 // tile in split order (deterministic) and runs the epilogue.
 //
@@ -44,39 +46,42 @@
 // from a cost model fitted to measured times.
 #include "hsq_internal.h"
 
+#include <cstddef>
 #include <type_traits>
 
 namespace hsq {
 
 namespace {
 
-constexpr uint32_t kNibMask = 0xF0F0F0F0u;
 constexpr int BM = 128, BN = 128;
 constexpr int TMB = BM / 16, TNB = BN / 16;   // MFMA tiles per block
 constexpr int WM = 2, WN = 4;                 // waves along M and N
 constexpr int NTH = 64 * WM * WN;             // threads per workgroup
 constexpr int TM = TMB / WM, TN = TNB / WN;   // MFMA tiles per wave (64 x 32 outputs)
 constexpr int kGroupM = 8;                    // m-blocks per tile-order group
-constexpr int kSlots = 2;                     // register slots: loads run kSlots stages ahead
 // kernel modes: the whole K range with the epilogue, one split's partial
 // tile, or the sum of the partial tiles with the epilogue
 constexpr int kFull = 0, kSplit = 1, kReduce = 2;
 constexpr int kCUs = 256;                     // compute units of the MI355X
 constexpr int kMaxSplits = 16;
-constexpr int kMinSplitPairs = 4;             // group pairs per split, at least
+constexpr int kMinSplitStages = 4;            // stages (block pairs) per split, at least
 constexpr int kAccPerThread = TM * TN * 4;
-static_assert(TMB * 64 == NTH && TNB * 64 == NTH, "one A chunk and one B slot per thread");
-static_assert(TMB * 16 <= NTH / 2 && BN <= NTH / 2, "scale loads: sx in the first half, sw in the second");
+static_assert(TMB == WM * WN && TNB == WM * WN, "one A and one B tile per wave and block");
+static_assert(TMB * 16 == 128 && BN == 128, "scale staging: 128 values per scale group and two waves");
 
-// One stage is one scale group: one 64-channel block (BPG = 1) or a block
-// pair (BPG = 2, group 128).
+// One stage is one pair of 64-channel blocks: two scale groups (BPG = 1,
+// group 64) or one (BPG = 2, group 128).
 template <int BPG>
 struct alignas(16) Stages {
-  int8_t a[2][BPG][TMB][64][16];      // [buf][block][m-tile][lane][bytes]   16 KB per block
-  int8_t b[2][BPG][TNB][64][16];      // [buf][block][n-tile][lane][bytes]   16 KB per block
-  float2 sw[2][BN];                   // [buf][col] = (sw, -magic*sw)/16      2 KB
-  uint16_t sx[2][TMB][16];            // [buf][m-tile][row] fp16             512 B
+  static constexpr int SPS = 2 / BPG;  // scale groups per stage
+  int8_t a[2][2][TMB][64][16];         // [buf][block][m-tile][lane][bytes]   16 KB per buffer
+  int8_t b[2][2][TNB][64][16];         // [buf][block][n-tile][lane][bytes]   16 KB per buffer
+  float2 sw[2][SPS][BN];               // [buf][group][col] = (sw, -magic*sw)/16
+  uint16_t sx[2][SPS][TMB][16];        // [buf][group][m-tile][row] fp16
 };
+static_assert(offsetof(Stages<1>, a) == 0 && offsetof(Stages<1>, b) == sizeof(Stages<1>::a) &&
+              offsetof(Stages<2>, a) == 0 && offsetof(Stages<2>, b) == sizeof(Stages<2>::a),
+              "the direct-to-LDS addresses assume A then B at the start of a stage set");
 
 // Epilogue operands of the block: U (rank columns padded to RPT) for its
 // BM rows, L2 for its BN columns, bias.  Filled at kernel start.
@@ -118,12 +123,55 @@ struct int_c {
 __device__ __forceinline__ void pin(v4i &x) { asm volatile("" : "+v"(x)); }
 __device__ __forceinline__ void pin(float &x) { asm volatile("" : "+v"(x)); }
 
+// End of a stage: this wave's loads (the next stage's direct-to-LDS blocks
+// and its scale loads, all issued this stage) and its LDS reads and writes
+// are complete, then the workgroup barrier.  After it every wave sees the
+// next stage's operands in LDS, and no wave still reads the buffer the
+// following stage's loads will overwrite.  (__syncthreads would add a
+// release fence, which waits the same way but also stops the compiler from
+// keeping loads in flight across it; here nothing is in flight.)
+__device__ __forceinline__ void stage_barrier() {
+  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// Direct-to-LDS load of one 1 KB operand block (buffer_load_dwordx4 ...
+// lds): lane l's 16 bytes, at voffset + soffset of the buffer resource rs
+// (four dwords: base, stride, size, flags), land at LDS byte address
+// lds + 16 l.  Written as an instruction of its own so that the compiler
+// neither waits for it (the loads of stage s+1 stay in flight while stage s
+// reads the other buffer) nor moves LDS accesses across it; stage_barrier
+// is the wait.  It has no register results.
+__device__ __forceinline__ void block_to_lds(v4u rs, uint32_t lds, uint32_t voffset, uint32_t soffset) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+               :
+               : "s"(lds), "v"(voffset), "s"(rs), "s"(soffset)
+               : "memory", "m0");
+}
+
+// A raw buffer resource as four scalar dwords (the layout the buffer
+// instructions read): 48-bit base, stride 0, size in bytes (reads past it
+// return zero), the same flags as buffer_rsrc.
+__device__ __forceinline__ v4u raw_rsrc(const void *p, uint32_t bytes) {
+  const uint64_t a = (uint64_t)(uintptr_t)p;
+  return (v4u){(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)a),
+               (uint32_t)__builtin_amdgcn_readfirstlane((int)((uint32_t)(a >> 32) & 0xFFFFu)),
+               (uint32_t)__builtin_amdgcn_readfirstlane((int)bytes), 0x00020000u};
+}
+
+// LDS byte address of a __shared__ object (for m0).
+__device__ __forceinline__ uint32_t lds_addr(const void *p) {
+  return (uint32_t)__builtin_amdgcn_readfirstlane(
+      (int)(uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char *)p);
+}
+
 template <bool DUMP, int RPT, int MODE, int BPG, int KH, bool CHAIN = false>
-__global__ __launch_bounds__(NTH * KH, 2) void k_gemm_tiled(GemmArgs a, int nblk, int mblk) {
+__global__ __launch_bounds__(NTH * KH, 4) void k_gemm_tiled(GemmArgs a, int nblk, int mblk) {
   static_assert(MODE != kSplit || RPT == 0, "a split pass has no epilogue");
   static_assert(KH == 1 || (!DUMP && MODE != kReduce), "the K halves serve the stage loop");
   static_assert(!CHAIN || (MODE == kFull && KH == 1 && BPG == 1 && !DUMP), "the chain epilogue: one unsplit pass");
   constexpr bool EPI = !DUMP && MODE != kSplit;   // this pass writes Y
+  constexpr int SPS = Stages<BPG>::SPS;           // scale groups per stage
+  constexpr int NSTEP = SPS * TM;                 // pipeline steps per stage (one row tile and scale group each)
   __shared__ Smem<RPT, BPG, KH> smem;
 
   const int lane = threadIdx.x & 63;
@@ -138,94 +186,86 @@ __global__ __launch_bounds__(NTH * KH, 2) void k_gemm_tiled(GemmArgs a, int nblk
   xcd_tile_of(blockIdx.x, nblk, mblk, kGroupM, mb, nb);
   const int mt0 = mb * TMB, nt0 = nb * TNB;
   const int MT = a.Mpad / 16, NT = (a.N + 15) / 16;
-  const int GP = a.Gp / 2;            // group pairs in the packed residual
-  const uint8_t *w = a.w + (size_t)proj * a.w_stride;
+  const uint8_t *w = a.w + (size_t)proj * a.w_stride + a.w_ops;   // int8 operand part
   const uint16_t *sw = DUMP ? nullptr : a.sw + (size_t)proj * a.G * a.N;
   if (DUMP && ((mt0 + TMB) * 16 <= a.m0 || mt0 * 16 >= a.m0 + a.mc ||
                (nt0 + TNB) * 16 <= a.n0 || nt0 * 16 >= a.n0 + a.nc))
     return;  // whole block outside the window (uniform: before any barrier)
-  // stages: one per scale group, padded to even (a pad stage has weight
-  // scale 0: it adds exactly 0); [g0, g1): all of them, or one split's
-  // stage pairs
-  const int nstg = BPG == 1 ? a.Gp : (a.G + 1) / 2 * 2;
-  const int last = (BPG == 1 ? a.Gp : a.G) - 1;  // last stage with data (loads clamp to it)
-  int g0 = 0, g1 = nstg;
+  // stages: block pairs, [s0, s1): all of them, or one split's range
+  const int nst = a.Gp / 2;
+  int s0 = 0, s1 = nst;
   if (MODE == kSplit) {
-    const int S = (int)gridDim.z, z = (int)blockIdx.z, pairs = nstg / 2;
-    g0 = 2 * (z * pairs / S);
-    g1 = 2 * ((z + 1) * pairs / S);
+    const int S = (int)gridDim.z, z = (int)blockIdx.z;
+    s0 = z * nst / S;
+    s1 = (z + 1) * nst / S;
   }
-  // stages with data for this workgroup: [g0, gend); with two K halves,
-  // half h runs [g0 + h*L, g0 + (h+1)*L), L even, so both make the same
-  // number of steps (barriers); stages of half 1 past gend get weight
-  // scale 0 and add exactly 0
-  const int gend = min(g1, a.G);
+  // stages with data for this workgroup end at send; with two K halves,
+  // half h runs [s0 + h*L, s0 + (h+1)*L), so both make the same number of
+  // steps (barriers); stages of half 1 past send get weight scale 0 and
+  // add exactly 0
+  const int send = s1;
   if constexpr (KH == 2) {
-    const int L = ((g1 - g0) / 2 + 1) & ~1;
-    g0 += half * L;
-    g1 = g0 + L;
+    const int L = (s1 - s0 + 1) / 2;
+    s0 += half * L;
+    s1 = s0 + L;
   }
   // this tile's partial tiles: [proj][tile][split][chunk][thread] float4
   float *part_tile = a.part + (((size_t)proj * nblk * mblk + (size_t)mb * nblk + nb) * a.splits) *
                                   (NTH * kAccPerThread);
 
-  // ---- global -> registers (two slots) -> LDS (two buffers) ----
-  // Loads past the matrix edges read the last valid block (clamped
-  // addresses, straight-line code); the edge masks are applied on the way
-  // into LDS, where only masked rows / columns see those values.
+  // ---- global -> LDS ----
+  // Operand blocks: wave w moves A block (row tile mt0 + w) and B block
+  // (column tile nt0 + w) for both blocks of the stage's pair.  Tiles past
+  // the matrix edges load the last real tile (clamped: straight-line code);
+  // their rows and columns are masked by zero scales and at the store.
   const int G = a.G;                  // scale groups
-  using RB = std::conditional_t<BPG == 1, v2u, v4u>;
-  v4u ra[kSlots][BPG];
-  RB rb[kSlots];
-  uint32_t rsx[kSlots];
-  uint32_t rsw[kSlots];
-  // Addresses: buffer resources over the operands, a fixed 32-bit byte
-  // offset per lane (computed once) and a per-stage scalar offset, so a
-  // stage costs no vector address math.
-  const __amdgpu_buffer_rsrc_t rs_a = buffer_rsrc(a.qa, (uint32_t)MT * a.Gp * 1024);
-  const __amdgpu_buffer_rsrc_t rs_w = buffer_rsrc(w, (uint32_t)NT * GP * 1024);
+  const v4u rs_a = raw_rsrc(a.qa, (uint32_t)MT * a.Gp * 1024);
+  const v4u rs_w = raw_rsrc(w, (uint32_t)NT * a.Gp * 1024);
   const __amdgpu_buffer_rsrc_t rs_x = buffer_rsrc(a.sxs, (uint32_t)MT * a.SG * 32);
   const __amdgpu_buffer_rsrc_t rs_s = buffer_rsrc(sw, DUMP ? 0u : (uint32_t)G * a.N * 2);
-  // thread t: 16-byte chunk t of the A tile, lane slot t of the B tile;
-  // the first half also one activation scale, the second one weight scale
-  const uint32_t offa = ((uint32_t)min(mt0 + (tid >> 6), MT - 1) * a.Gp * 64 + (tid & 63)) * 16;
-  const uint32_t offb = ((uint32_t)min(nt0 + (tid >> 6), NT - 1) * GP * 64 + (tid & 63)) * 16;
-  const uint32_t offsx = ((uint32_t)min(mt0 + ((tid >> 4) & (TMB - 1)), MT - 1) * a.SG * 16 + (tid & 15)) * 2;
-  const uint32_t offsw = (uint32_t)min(nt0 * 16 + (tid & (BN - 1)), a.N - 1) * 2;
-  // Straight-line code with a fixed number of loads per stage (the stage
-  // index is clamped near the end instead of skipping the loads), so the
-  // compiler's wait counting stays exact and waits only for the older slot.
-  auto load_stage = [&](int g, auto slotc) __attribute__((always_inline)) {
-    constexpr int SL = decltype(slotc)::value;
-    const int gl = min(g, last);
+  const uint32_t offa = ((uint32_t)min(mt0 + wave, MT - 1) * a.Gp * 64 + lane) * 16;
+  const uint32_t offb = ((uint32_t)min(nt0 + wave, NT - 1) * a.Gp * 64 + lane) * 16;
+  // scales, one per thread and stage: waves 0-3 stage activation scales
+  // (scale group (wave & 3) / 2 of the stage, row tile, row), waves 4-7
+  // weight scales (scale group, column); every condition below is uniform
+  // over a wave
+  const bool sx_wave = wave < 4;
+  const int sgs = (wave & 3) >> 1;                       // scale group within the stage
+  const bool stages_sx = sx_wave && sgs < SPS;
+  const bool stages_sw = !DUMP && !sx_wave && sgs < SPS;
+  const int sq = tid & 127;
+  const int smi = sq >> 4, srow = sq & 15, scol = sq;
+  const uint32_t offsx = ((uint32_t)min(mt0 + smi, MT - 1) * a.SG * 16 + srow) * 2;
+  const uint32_t offsw = (uint32_t)min(nt0 * 16 + scol, a.N - 1) * 2;
+  const int last = nst - 1;
+  // LDS byte addresses of this wave's A and B blocks in buffer 0, block 0
+  // (the stage buffers open the shared object; a buffer is 2 x 8 KB per
+  // operand)
+  const uint32_t lds_st = lds_addr(&smem) + (uint32_t)half * (uint32_t)sizeof(Stages<BPG>);
+  const uint32_t lds_a = lds_st + (uint32_t)wave * 1024;
+  const uint32_t lds_b = lds_st + (uint32_t)sizeof(sm.a) + (uint32_t)wave * 1024;
+  uint32_t rscale = 0;
+  auto load_stage = [&](int st, int buf) __attribute__((always_inline)) {
+    const int sl = min(st, last);     // past the end: a clamped reload (its scales are 0)
 #pragma unroll
-    for (int b = 0; b < BPG; ++b)
-      ra[SL][b] = __builtin_amdgcn_raw_buffer_load_b128(rs_a, offa, (gl * BPG + b) * 1024, 0);
-    if constexpr (BPG == 1)           // half a block pair: this group's 16 columns x 64 channels
-      rb[SL] = __builtin_amdgcn_raw_buffer_load_b64(rs_w, offb, (gl >> 1) * 1024 + 8 * (gl & 1), 0);
-    else                              // the whole pair: one 128-channel group
-      rb[SL] = __builtin_amdgcn_raw_buffer_load_b128(rs_w, offb, gl * 1024, 0);
-    rsx[SL] = __builtin_amdgcn_raw_buffer_load_b16(rs_x, offsx, gl * 32, 0);
-    if (!DUMP) rsw[SL] = __builtin_amdgcn_raw_buffer_load_b16(rs_s, offsw, min(g, G - 1) * a.N * 2, 0);
-  };
-  auto store_stage = [&](int g, auto slotc, int buf) __attribute__((always_inline)) {
-    constexpr int SL = decltype(slotc)::value;
-#pragma unroll
-    for (int b = 0; b < BPG; ++b)
-      *reinterpret_cast<v4u *>(&sm.a[buf][b][tid >> 6][tid & 63][0]) = ra[SL][b];
-#pragma unroll
-    for (int b = 0; b < BPG; ++b) {
-      const uint32_t w0 = rb[SL][2 * b], w1 = rb[SL][2 * b + 1];
-      *reinterpret_cast<v4u *>(&sm.b[buf][b][tid >> 6][tid & 63][0]) =
-          (v4u){w0 & kNibMask, (w0 << 4) & kNibMask, w1 & kNibMask, (w1 << 4) & kNibMask};
+    for (int b = 0; b < 2; ++b) {
+      const uint32_t blk = (uint32_t)(buf * 2 + b) * TMB * 1024;
+      block_to_lds(rs_a, lds_a + blk, offa, (uint32_t)(2 * sl + b) * 1024);
+      block_to_lds(rs_w, lds_b + blk, offb, (uint32_t)(2 * sl + b) * 1024);
     }
-    if (tid < TMB * 16) {
-      const int mi = tid >> 4, row = tid & 15;
-      sm.sx[buf][mi][row] = (mt0 + mi < MT) ? (uint16_t)rsx[SL] : (uint16_t)0;
-    } else if (!DUMP && tid >= NTH / 2 && tid < NTH / 2 + BN) {
-      const int col = tid - NTH / 2, n = nt0 * 16 + col;
-      const float sv = (g < gend && n < a.N) ? f16_to_f32((uint16_t)rsw[SL]) : 0.0f;
-      sm.sw[buf][col] = make_float2(sv * 0.0625f, -kMagic * 0.0625f * sv);
+    const int sg = min(sl * SPS + sgs, (BPG == 1 ? a.Gp : G) - 1);
+    if (stages_sx)
+      rscale = __builtin_amdgcn_raw_buffer_load_b16(rs_x, offsx, sg * 32, 0);
+    else if (stages_sw)
+      rscale = __builtin_amdgcn_raw_buffer_load_b16(rs_s, offsw, min(sg, G - 1) * a.N * 2, 0);
+  };
+  auto store_scales = [&](int st, int buf) __attribute__((always_inline)) {
+    if (stages_sx) {
+      sm.sx[buf][sgs][smi][srow] = (mt0 + smi < MT) ? (uint16_t)rscale : (uint16_t)0;
+    } else if (stages_sw) {
+      const int g = st * SPS + sgs, n = nt0 * 16 + scol;
+      const float sv = (g < G && st < send && n < a.N) ? f16_to_f32((uint16_t)rscale) : 0.0f;
+      sm.sw[buf][sgs][scol] = make_float2(sv * 0.0625f, -kMagic * 0.0625f * sv);
     }
   };
 
@@ -242,7 +282,7 @@ __global__ __launch_bounds__(NTH * KH, 2) void k_gemm_tiled(GemmArgs a, int nblk
   const int colq = lane & 15;
 
   // ---- epilogue operands: loads issued first, so that their latency
-  // overlaps the first stages' loads; parked in LDS below ----
+  // overlaps the first stage's loads; parked in LDS below ----
   constexpr int EU = RPT * BM / NTH;  // (rank column, row) pairs per thread
   constexpr int US = RPT <= 8 ? kMaxUSlices : kMaxUSlices / 2;  // U slices prefetched
   float eu[EU > 0 ? EU : 1][US], el2[EU > 0 ? EU : 1], ebias = 0.0f;
@@ -261,14 +301,7 @@ __global__ __launch_bounds__(NTH * KH, 2) void k_gemm_tiled(GemmArgs a, int nblk
     if (a.bias) ebias = bf16_to_f32(a.bias[(size_t)proj * a.N + min(nt0 * 16 + (tid & (BN - 1)), a.N - 1)]);
   }
 
-  if constexpr (MODE != kReduce) {
-    load_stage(g0, int_c<0>{});
-    load_stage(g0 + 1, int_c<1>{});   // g1 - g0 >= 2; stages past the end are clamped reloads
-    if constexpr (kSlots > 2) {
-      load_stage(g0 + 2, int_c<2 % kSlots>{});
-      load_stage(g0 + 3, int_c<3 % kSlots>{});
-    }
-  }
+  if constexpr (MODE != kReduce) load_stage(s0, 0);
   if (EPI && half == 0) {
 #pragma unroll
     for (int e = 0; e < EU; ++e) {
@@ -289,26 +322,27 @@ __global__ __launch_bounds__(NTH * KH, 2) void k_gemm_tiled(GemmArgs a, int nblk
     }
     if (tid < BN) smem.ep.bias[tid] = (nt0 * 16 + tid < a.N) ? ebias : 0.0f;
   }
-  if constexpr (MODE != kReduce) store_stage(g0, int_c<0>{}, 0);
-  __syncthreads();
+  if constexpr (MODE != kReduce) store_scales(s0, 0);
+  stage_barrier();
 
   if constexpr (MODE != kReduce) {
 
-  // ---- the stage loop: TM row tiles per stage, software-pipelined across
-  // stages.  Step s of stage g issues the MFMAs of row s and rescales the
-  // row before it: row s-1 of stage g, or, at s = 0, the last row of stage
-  // g-1 (its MFMA results, weight scales and activation scales are carried
-  // over; its FMAs go first, while the stage's first LDS reads are in
-  // flight), so the pipeline never drains at a stage boundary.
+  // ---- the stage loop, software-pipelined across steps and stages.  Step
+  // k of a stage (row tile k % TM of scale group k / TM) issues its MFMAs
+  // and rescales step k-1: a step of this stage, or, at k = 0, the last
+  // step of the previous stage (its MFMA results, weight scales and
+  // activation scales are carried over; its FMAs go first, while the
+  // stage's first LDS reads are in flight), so the pipeline never drains
+  // at a stage boundary.
   v4i d[TM][TN];                      // MFMA results (row TM-1 carried)
-  float2 swv[2][TN];                  // weight scales per LDS buffer
-  v4h sxv[TM], sx_carry;              // activation scales (fp16); last row of the previous stage
+  float2 swc[TN];                     // weight scales of the carried step
+  v4h sxc;                            // activation scales of the carried step
 #pragma unroll
   for (int j = 0; j < TN; ++j) {
     d[TM - 1][j] = magic;             // a first carry that adds exactly 0
-    swv[1][j] = make_float2(0.0f, 0.0f);
+    swc[j] = make_float2(0.0f, 0.0f);
   }
-  sx_carry = (v4h){0, 0, 0, 0};
+  sxc = (v4h){0, 0, 0, 0};
 
   // rescale one row tile: acc += (D - magic) * sw * sx, or, for the test
   // export, the group partials of the window
@@ -344,57 +378,67 @@ __global__ __launch_bounds__(NTH * KH, 2) void k_gemm_tiled(GemmArgs a, int nblk
     }
   };
 
-  auto stage = [&](int g, auto slotc) __attribute__((always_inline)) {
-    constexpr int SL = decltype(slotc)::value;  // register slot == g % kSlots
-    constexpr int BUF = SL & 1;                   // LDS buffer == g & 1
-    load_stage(g + kSlots, slotc);    // past the end: a clamped, unused reload
+  auto stage = [&](int st, auto bufc) __attribute__((always_inline)) {
+    constexpr int BUF = decltype(bufc)::value;    // LDS buffer == (st - s0) & 1
+    // the next stage's operands and scales: in flight during this stage
+    // (past the end: a clamped, unused reload)
+    load_stage(st + 1, BUF ^ 1);
 
-    v4i bv[TN][BPG];
-    v4i av[TM][BPG];
+    v4i bv[2][TN];                    // B operands of the pair's blocks
+    float2 swv[SPS][TN];              // weight scales of the stage's scale groups
+    v4i av[NSTEP][BPG];
+    v4h sxv[NSTEP];
+    auto read_b = [&](int b) __attribute__((always_inline)) {
 #pragma unroll
-    for (int j = 0; j < TN; ++j) {
-#pragma unroll
-      for (int b = 0; b < BPG; ++b)
-        bv[j][b] = *reinterpret_cast<const v4i *>(&sm.b[BUF][b][wn * TN + j][lane][0]);
-      swv[BUF][j] = sm.sw[BUF][(wn * TN + j) * 16 + colq];
-    }
-    auto read_a = [&](int i) __attribute__((always_inline)) {
-#pragma unroll
-      for (int b = 0; b < BPG; ++b)
-        av[i][b] = *reinterpret_cast<const v4i *>(&sm.a[BUF][b][wm * TM + i][lane][0]);
-      sxv[i] = *reinterpret_cast<const v4h *>(&sm.sx[BUF][wm * TM + i][rowq]);
+      for (int j = 0; j < TN; ++j)
+        bv[b][j] = *reinterpret_cast<const v4i *>(&sm.b[BUF][b][wn * TN + j][lane][0]);
     };
-    // one row tile's MFMAs: a group's blocks accumulate in int32 (the
-    // second block's MFMA takes the first one's result as its input)
-    auto mfma_row = [&](int s) __attribute__((always_inline)) {
+    auto read_step = [&](int k) __attribute__((always_inline)) {
+      const int sg = k / TM, s = k % TM;
+#pragma unroll
+      for (int bb = 0; bb < BPG; ++bb)
+        av[k][bb] = *reinterpret_cast<const v4i *>(&sm.a[BUF][sg * BPG + bb][wm * TM + s][lane][0]);
+      sxv[k] = *reinterpret_cast<const v4h *>(&sm.sx[BUF][sg][wm * TM + s][rowq]);
+    };
+    // one step's MFMAs: a group-128 scale group's two blocks accumulate in
+    // int32 (the second MFMA takes the first one's result as its input)
+    auto mfma_step = [&](int k) __attribute__((always_inline)) {
+      const int sg = k / TM, s = k % TM;
 #pragma unroll
       for (int j = 0; j < TN; ++j) {
-        d[s][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(av[s][0], bv[j][0], magic, 0, 0, 0);
+        d[s][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(av[k][0], bv[sg * BPG][j], magic, 0, 0, 0);
         if constexpr (BPG == 2)
-          d[s][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(av[s][1], bv[j][1], d[s][j], 0, 0, 0);
+          d[s][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(av[k][1], bv[1][j], d[s][j], 0, 0, 0);
       }
     };
-    read_a(0);
+    read_b(0);
 #pragma unroll
-    for (int s = 0; s < TM; ++s) {
+    for (int sg = 0; sg < SPS; ++sg)
+#pragma unroll
+      for (int j = 0; j < TN; ++j) swv[sg][j] = sm.sw[BUF][sg][(wn * TN + j) * 16 + colq];
+    read_step(0);
+    if constexpr (BPG == 2) read_b(1);
+#pragma unroll
+    for (int k = 0; k < NSTEP; ++k) {
       // step boundary: nothing moves across it
       __builtin_amdgcn_sched_barrier(0);
-      if (s == 0) {
-        // the carried row first: its FMAs need no LDS data, so they cover
+      if (k == 0) {
+        // the carried step first: its FMAs need no LDS data, so they cover
         // the latency of this stage's first reads (issued just above)
-        if (TM > 1) read_a(1);
-        rescale(TM - 1, swv[BUF ^ 1], sx_carry, g - 1);
+        if (NSTEP > 1) read_step(1);
+        rescale(TM - 1, swc, sxc, st * SPS - 1);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int b = 0; b < BPG; ++b) pin(av[0][b]);
-        mfma_row(0);
+        for (int bb = 0; bb < BPG; ++bb) pin(av[0][bb]);
+        mfma_step(0);
         continue;
       }
 #pragma unroll
-      for (int b = 0; b < BPG; ++b) pin(av[s][b]);
-      if (s + 1 < TM) read_a(s + 1);
-      mfma_row(s);
-      rescale(s - 1, swv[BUF], sxv[s - 1], g);
+      for (int bb = 0; bb < BPG; ++bb) pin(av[k][bb]);
+      if (k + 1 < NSTEP) read_step(k + 1);
+      if (BPG == 1 && k == TM - 1) read_b(1);     // the second block's B, one step ahead
+      mfma_step(k);
+      rescale((k - 1) % TM, swv[(k - 1) / TM], sxv[k - 1], st * SPS + (k - 1) / TM);
       // issue order within the step: one tile's MFMAs, then the eight
       // rescale FMAs of one tile, and so on, so the matrix core works while
       // the VALU rescales
@@ -407,29 +451,23 @@ __global__ __launch_bounds__(NTH * KH, 2) void k_gemm_tiled(GemmArgs a, int nblk
       }
     }
     __builtin_amdgcn_sched_barrier(0);
-    sx_carry = sxv[TM - 1];
+#pragma unroll
+    for (int j = 0; j < TN; ++j) swc[j] = swv[SPS - 1][j];
+    sxc = sxv[NSTEP - 1];
 
-    // stage g+1 (loaded kSlots-1 stages ago) into the other LDS buffer
-    if (g + 1 < g1) store_stage(g + 1, int_c<(SL + 1) % kSlots>{}, BUF ^ 1);
-    __syncthreads();
+    // the next stage's scales into the other buffer, then the barrier
+    store_scales(st + 1, BUF ^ 1);
+    stage_barrier();
   };
-  // stages in groups of kSlots (compile-time register slots), then the
-  // remaining two (g0 and g1 are even)
-  int g = g0;
-  for (; g + kSlots <= g1; g += kSlots) {
-    stage(g, int_c<0>{});
-    stage(g + 1, int_c<1>{});
-    if constexpr (kSlots > 2) {
-      stage(g + 2, int_c<2 % kSlots>{});
-      stage(g + 3, int_c<3 % kSlots>{});
-    }
+  // stages in pairs (compile-time LDS buffers), then an odd last one
+  int st = s0;
+  for (; st + 2 <= s1; st += 2) {
+    stage(st, int_c<0>{});
+    stage(st + 1, int_c<1>{});
   }
-  if (g < g1) {
-    stage(g, int_c<0>{});
-    stage(g + 1, int_c<1>{});
-  }
-  // drain: the last row of the last stage (g1 - 1 is odd: LDS buffer 1)
-  rescale(TM - 1, swv[1], sx_carry, g1 - 1);
+  if (st < s1) stage(st, int_c<0>{});
+  // drain: the last step of the last stage
+  rescale(TM - 1, swc, sxc, s1 * SPS - 1);
   }  // MODE != kReduce
 
   if (DUMP) return;
@@ -673,7 +711,9 @@ hipError_t launch_epi(const GemmArgs &a, int batch, int nblk, int mblk, hipStrea
   if (a.r <= 4) return launch_rpt<4, MODE, BPG, KH>(a, batch, nblk, mblk, s);
   if (a.r <= 8) return launch_rpt<8, MODE, BPG, KH>(a, batch, nblk, mblk, s);
   if (a.r <= 16) return launch_rpt<16, MODE, BPG, KH>(a, batch, nblk, mblk, s);
-  return launch_rpt<32, MODE, BPG, KH>(a, batch, nblk, mblk, s);
+  // two K halves with a rank above 16 exceed the LDS (tiled_plan never asks)
+  if constexpr (KH == 2) return hipErrorInvalidValue;
+  else return launch_rpt<32, MODE, BPG, KH>(a, batch, nblk, mblk, s);
 }
 
 struct TiledPlan {
@@ -683,27 +723,29 @@ struct TiledPlan {
 
 // Plan of the tiled contraction: the (K halves, splits) pair with the
 // least modelled time.  Units: the time a CU running two eight-wave
-// workgroups takes for one tile and one stage pair (about 1 us on the
-// MI355X); each of the two then advances at half that rate.  The other
-// constants are fitted to measured contraction times: one eight-wave
-// workgroup alone on a CU needs 1.4 units per stage pair plus 1.2 for its
-// prologue and epilogue (nothing else hides them); a sixteen-wave
-// workgroup (two K halves, one per CU) needs 1.2 per stage pair, its
-// pairs rounded up to even so the halves match, plus 2.3 (its halves
-// share every barrier, and half 0 alone runs the epilogue).  It therefore
-// pays only where the alternative is a split: each split tile beyond the
-// first writes and reads a 64 KB fp32 partial tile, about 0.03 units at
-// the HBM rate such traffic reaches.  Group 128 keeps eight waves: its
-// block-pair stage needs more registers than sixteen waves per CU leave.
-TiledPlan tiled_plan(int M, int N, int K, int batch, int group) {
+// workgroups takes for one tile and one stage (a 128-channel block pair);
+// each of the two then advances at half that rate.  The other constants
+// are fitted to measured contraction times: one eight-wave workgroup alone
+// on a CU needs 1.4 units per stage plus 1.2 for its prologue and epilogue
+// (nothing else hides them); a sixteen-wave workgroup (two K halves, one
+// per CU) needs 1.2 per stage, its stages rounded up to even so the halves
+// match, plus 2.3 (its halves share every barrier, and half 0 alone runs
+// the epilogue).  It therefore pays only where the alternative is a split:
+// each split tile beyond the first writes and reads a 64 KB fp32 partial
+// tile, about 0.03 units at the HBM rate such traffic reaches.  Sixteen
+// waves need two sets of stage buffers (2 x 69 KB of LDS): with the
+// epilogue operands of a rank above 16 they do not fit the CU's 160 KB, and
+// group 128 keeps eight waves.
+TiledPlan tiled_plan(int M, int N, int K, int r, int batch, int group) {
   const long long tiles = (long long)ceil_div(N, BN) * ceil_div(M, BM) * batch;
-  const int pairs = group == kGroup ? padded_groups(K) / 2 : (K / group + 1) / 2;
+  const int stages = padded_groups(K) / 2;
+  const int max_kh = (group == kGroup && r <= 16) ? 2 : 1;
   TiledPlan best{1, 1};
   double best_t = -1.0;
-  for (int kh = 1; kh <= (group == kGroup ? 2 : 1); ++kh)
-    for (int S = 1; S <= kMaxSplits && (S == 1 || S * kMinSplitPairs <= pairs); ++S) {
+  for (int kh = 1; kh <= max_kh; ++kh)
+    for (int S = 1; S <= kMaxSplits && (S == 1 || S * kMinSplitStages <= stages); ++S) {
       const long long wgs = tiles * S;
-      const double per = (double)ceil_div(pairs, S);
+      const double per = (double)ceil_div(stages, S);
       double t;
       if (kh == 1)
         t = wgs <= kCUs ? 1.4 * per + 1.2 : 2.0 * (double)((wgs + 2 * kCUs - 1) / (2 * kCUs)) * per;
@@ -720,10 +762,12 @@ TiledPlan tiled_plan(int M, int N, int K, int batch, int group) {
 
 }  // namespace
 
-int tiled_splits(int M, int N, int K, int batch, int group) { return tiled_plan(M, N, K, batch, group).splits; }
+int tiled_splits(int M, int N, int K, int r, int batch, int group) {
+  return tiled_plan(M, N, K, r, batch, group).splits;
+}
 
-size_t tiled_partial_bytes(int M, int N, int K, int batch, int group) {
-  const int S = tiled_splits(M, N, K, batch, group);
+size_t tiled_partial_bytes(int M, int N, int K, int r, int batch, int group) {
+  const int S = tiled_splits(M, N, K, r, batch, group);
   if (S <= 1) return 0;
   return (size_t)S * ceil_div(N, BN) * ceil_div(M, BM) * batch * NTH * kAccPerThread * sizeof(float);
 }
@@ -750,7 +794,7 @@ hipError_t launch_tiled_bpg(const GemmArgs &a, int batch, bool dump, hipStream_t
                        0, s, a, nblk, mblk);
     return hipGetLastError();
   }
-  const TiledPlan p = tiled_plan(a.M, a.N, a.G * kGroup * BPG, batch, kGroup * BPG);
+  const TiledPlan p = tiled_plan(a.M, a.N, a.G * kGroup * BPG, a.r, batch, kGroup * BPG);
   if constexpr (BPG == 1)
     if (p.kh == 2) return launch_tiled_kh<BPG, 2>(a, batch, p.splits, nblk, mblk, s);
   return launch_tiled_kh<BPG, 1>(a, batch, p.splits, nblk, mblk, s);

@@ -40,6 +40,13 @@ inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 //   byte b in 4..7 : high nibble p = b + 4,  low nibble p = b + 8
 // so that (w & 0xF0F0F0F0) and ((w << 4) & 0xF0F0F0F0) of the two little-
 // endian dwords give the 16 int8 MFMA operand bytes 16*code in order p.
+// The skinny contraction streams this part (half a byte per code).
+//
+// Layout version 2 appends the same codes as int8 operand bytes 16*code
+// (the tiled contraction's B operand, moved global -> LDS unchanged): NT x
+// Gp blocks of 1024 bytes, column-tile-major; block (nt, g) holds 64 lane
+// slots of 16 bytes, slot l = output column 16*nt + l%16, channels
+// 64g + 16*(l/16) + p at byte p.  Pad columns and the pad group hold 0.
 // ---------------------------------------------------------------------------
 inline int padded_groups(int K) { return ceil_div(K / kGroup, 2) * 2; }
 // Scale groups of `group` channels (64 or 128): one scale per (row or
@@ -47,9 +54,12 @@ inline int padded_groups(int K) { return ceil_div(K / kGroup, 2) * 2; }
 // one block pair of the packed residual.  The activation scales are stored
 // per row tile for every padded 64-block (group 64) or every group (128).
 inline int scale_groups_stored(int K, int group) { return group == kGroup ? padded_groups(K) : K / group; }
-inline size_t packed_bytes(int K, int N) {
+// nibble part (offset 0), int8 operand part (offset nibble_bytes), whole blob
+inline size_t nibble_bytes(int K, int N) {
   return (size_t)ceil_div(N, kTile) * (size_t)(padded_groups(K) / 2) * 1024u;
 }
+inline size_t operand_bytes(int K, int N) { return (size_t)ceil_div(N, kTile) * (size_t)padded_groups(K) * 1024u; }
+inline size_t packed_bytes(int K, int N) { return nibble_bytes(K, N) + operand_bytes(K, N); }
 
 // ---------------------------------------------------------------------------
 // Workspace of the fused linear.  MT = ceil(M/16) row tiles.
@@ -105,8 +115,9 @@ struct QuantArgs {
 struct GemmArgs {
   const int8_t *qa;
   const uint16_t *sxs;
-  const uint8_t *w;        // packed residual of projection 0
-  size_t w_stride;         // bytes between projections
+  const uint8_t *w;        // packed residual blob of projection 0 (nibble part first)
+  size_t w_stride;         // bytes between projections' blobs
+  size_t w_ops;            // offset of the int8 operand part within a blob
   const uint16_t *sw;      // batch x G x N fp16
   const float *uw;         // U slices (see WsLayout)
   int u_slices;
@@ -154,8 +165,8 @@ int quant_slices(int M, int K, int r, int batch, int group);
 hipError_t launch_gemm_tiled(const GemmArgs &a, int batch, bool dump, hipStream_t s);
 // Split-K factor of the tiled contraction for this shape (1: no split) and
 // the workspace bytes of its partial tiles.
-int tiled_splits(int M, int N, int K, int batch, int group);
-size_t tiled_partial_bytes(int M, int N, int K, int batch, int group);
+int tiled_splits(int M, int N, int K, int r, int batch, int group);
+size_t tiled_partial_bytes(int M, int N, int K, int r, int batch, int group);
 hipError_t launch_gemm_skinny(const GemmArgs &a, int batch, bool dump, hipStream_t s);
 // The tiled contraction with the CHAIN epilogue (one projection, unsplit,
 // 8-wave workgroups), and the sum of its U partials into the next layer's

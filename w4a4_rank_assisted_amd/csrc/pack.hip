@@ -1,5 +1,6 @@
-// pack.hip -- K0: residual codes (K x N int8) <-> the tiled nibble blob the
-// contraction kernels stream (layout described in hsq_internal.h).
+// pack.hip -- K0: residual codes (K x N int8) <-> the packed blob the
+// contraction kernels stream (layout version 2, described in
+// hsq_internal.h): tiled nibbles, then the same codes as int8 operand bytes.
 // Offline, once per weight; one thread per 16-byte lane slot.
 #include "hsq_internal.h"
 
@@ -12,8 +13,11 @@ __device__ __forceinline__ int code_at(const int8_t *codes, int K, int N, int k,
   return (k < K && n < N) ? (int)codes[(size_t)k * N + n] : 0;
 }
 
+// One thread per 16-byte slot of the nibble part (a group pair of one lane
+// slot); it also writes the slot's two 16-byte int8 operand slots (one per
+// group of the pair) of the second part.
 __global__ void k_pack(const int8_t *__restrict__ codes, int K, int N, int NT, int GP,
-                       uint8_t *__restrict__ packed, int *__restrict__ status) {
+                       uint8_t *__restrict__ packed, uint8_t *__restrict__ ops, int *__restrict__ status) {
   size_t slot = (size_t)blockIdx.x * blockDim.x + threadIdx.x;  // one 16-byte slot
   size_t nslots = (size_t)NT * GP * 64;
   if (slot >= nslots) return;
@@ -26,6 +30,15 @@ __global__ void k_pack(const int8_t *__restrict__ codes, int K, int N, int NT, i
   uint32_t out[4];
   for (int h = 0; h < 2; ++h) {
     int kb = (2 * gp + h) * kGroup + 16 * (lane / 16);
+    uint32_t o[4];
+    for (int d = 0; d < 4; ++d) {          // operand bytes p = 4d .. 4d+3: 16 * code
+      uint32_t w = 0;
+      for (int b = 0; b < 4; ++b)
+        w |= (uint32_t)(uint8_t)(16 * code_at(codes, K, N, kb + 4 * d + b, n)) << (8 * b);
+      o[d] = w;
+    }
+    *reinterpret_cast<uint4 *>(ops + (((size_t)nt * 2 * GP + 2 * gp + h) * 64 + lane) * 16) =
+        make_uint4(o[0], o[1], o[2], o[3]);
     for (int d = 0; d < 2; ++d) {          // dword d covers bytes 4d .. 4d+3
       uint32_t w = 0;
       for (int b = 0; b < 4; ++b) {
@@ -74,7 +87,8 @@ hipError_t launch_pack(const int8_t *codes, int K, int N, uint8_t *packed, int *
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   unsigned blocks = (unsigned)((nslots + 255) / 256);
-  hipLaunchKernelGGL(k_pack, dim3(blocks), dim3(256), 0, s, codes, K, N, NT, GP, packed, status);
+  hipLaunchKernelGGL(k_pack, dim3(blocks), dim3(256), 0, s, codes, K, N, NT, GP, packed,
+                     packed + nibble_bytes(K, N), status);
   return hipGetLastError();
 }
 
