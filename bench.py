@@ -295,7 +295,8 @@ def summarize_profiles(args):
 
 PROBE_LIB = os.path.join(ROOT, "w4a4_rank_assisted_amd", "_lib", "libhsq_probe.so")
 PROBE_MODES = {0: "mfma_only", 1: "mfma_plus_1_fma_per_element", 2: "mfma_plus_2_fma_per_element",
-               3: "mfma_plus_2_fma_plus_lds_reads"}
+               3: "mfma_plus_2_fma_plus_lds_reads", 4: "wide_tile_mfma_plus_2_fma",
+               5: "wide_tile_mfma_plus_2_fma_plus_lds_reads"}
 
 
 def _probe_lib():
@@ -360,14 +361,15 @@ def measure_peaks(torch, full: bool = False):
     res = {"int8_mfma_tops": {}, "hbm_gbs": {}}
     configs = [(0, blocks, waves), (2, blocks, waves)]
     if full:
-        configs = [(m, blocks, waves) for m in (0, 1, 2, 3)] + [(0, 256, 4), (0, 256, 8), (0, 512, 16)]
+        configs = ([(m, blocks, waves) for m in (0, 1, 2, 3)] + [(0, 256, 4), (0, 256, 8), (0, 512, 16)] +
+                   [(4, 256, 8), (5, 256, 8), (4, 512, 8), (5, 512, 8)])
     for mode, nb, nw in configs:
         def launch(stream, i=0, mode=mode, nb=nb, nw=nw):
             assert lib.hsq_probe_mfma(mode, iters, nb, nw, ctypes.c_void_p(sink.data_ptr()),
                                       ctypes.c_void_p(stream.cuda_stream)) == 0
         ms = _time_graph(torch, launch, 5)
-        ops = nb * nw * iters * 8 * 2 * 16 * 16 * 64
-        key = PROBE_MODES[mode] + ("" if (nb, nw) == (blocks, waves) else f"_{nb}x{nw}waves")
+        ops = nb * nw * iters * (16 if mode >= 4 else 8) * 2 * 16 * 16 * 64
+        key = PROBE_MODES[mode] + ("" if (nb, nw) == (blocks, waves) and mode < 4 else f"_{nb}x{nw}waves")
         res["int8_mfma_tops"][key] = round(ops / (ms * 1e-3) / 1e12, 1)
     sblocks = 256 * 8
     big = 1 << 30

@@ -189,7 +189,7 @@ int hsq_w4a4_lowrank_linear_ex(const uint16_t *X, int M, int K, int N, int batch
  * Sizes whose workspace (hsq_workspace_bytes(M, K, N, r, batch)) exceeds
  * the array return HSQ_E_SCRATCH before anything is enqueued; every
  * configuration of the diffusion and LLM layers here fits (the largest,
- * 4608 tokens x 12288 channels, needs about 59 MB).
+ * 4608 tokens x 12288 channels, needs about 64 MB).
  * Other arguments and errors as for hsq_w4a4_lowrank_linear. */
 #define HSQ_NOALLOC_SCRATCH_BYTES (64u << 20)
 int hsq_w4a4_lowrank_linear_noalloc(const uint16_t *X, int M, int K, int N, int batch,

@@ -30,16 +30,21 @@ extern "C" {
  *                         u = fma(D, sw, c), acc = fma(u, sx, acc))
  *   HSQ_PROBE_MFMA_FMA2_LDS  + the per-step LDS operand reads of the tiled
  *                         contraction (4 A and 2 B 16-byte reads per lane,
- *                         weight and activation scales) */
+ *                         weight and activation scales)
+ *   HSQ_PROBE_WIDE_FMA2, HSQ_PROBE_WIDE_FMA2_LDS  the FMA2 and FMA2_LDS
+ *                         bodies with a wave tile of 4 x 4 MFMA tiles
+ *                         (64 x 64 outputs: 16 MFMAs per step, 4 B reads) */
 #define HSQ_PROBE_MFMA          0
 #define HSQ_PROBE_MFMA_FMA1     1
 #define HSQ_PROBE_MFMA_FMA2     2
 #define HSQ_PROBE_MFMA_FMA2_LDS 3
+#define HSQ_PROBE_WIDE_FMA2     4
+#define HSQ_PROBE_WIDE_FMA2_LDS 5
 
-/* Enqueue the MFMA probe: `blocks` workgroups of `waves` waves (1..16)
- * each; every wave runs `iters` steps (8 MFMAs of 16*16*64 multiply-adds
- * each).  out: blocks * waves * 64 int32, written so the work is not
- * optimised away. */
+/* Enqueue the MFMA probe: `blocks` workgroups of `waves` waves (1..16; at
+ * most 8 for the wide modes) each; every wave runs `iters` steps (8 MFMAs
+ * of 16*16*64 multiply-adds each, 16 for the wide modes).  out: blocks *
+ * waves * 64 int32, written so the work is not optimised away. */
 int hsq_probe_mfma(int mode, int iters, int blocks, int waves, int32_t *out, void *stream);
 
 /* Stream probes over `bytes` bytes (a multiple of 16):

@@ -77,9 +77,10 @@ def test_workspace_holds_split_k_partials():
     # keeps fp32 partial tiles (128 x 128 per split) in the workspace
     M, K, N = 256, 12288, 4096                # 2 x 32 tiles, 4 splits (of two K halves each)
     codes = (M // 16) * 192 * 1024
+    pairs = (192 + 2) * N * 8                 # weight-scale pairs of the tiled contraction
     ws = lib.hsq_workspace_bytes(M, K, N, 4, 1)
-    assert ws >= codes + 4 * 2 * 32 * 128 * 128 * 4
-    assert ws < codes + 5 * 2 * 32 * 128 * 128 * 4
+    assert ws >= codes + 4 * 2 * 32 * 128 * 128 * 4 + pairs
+    assert ws < codes + 5 * 2 * 32 * 128 * 128 * 4 + pairs
     # enough tiles: no partials
     assert lib.hsq_workspace_bytes(4096, 1152, 4608, 4, 1) < 32 << 20
 
@@ -322,7 +323,8 @@ def test_probe_entry_points_validate_without_launching():
     plib.hsq_probe_mfma.argtypes = [I, I, I, I, P, P]
     plib.hsq_probe_read.argtypes = [P, S, I, P, P]
     plib.hsq_probe_copy.argtypes = [P, S, I, P, P]
-    assert plib.hsq_probe_mfma(4, 10, 1, 8, A, None) == -1      # no such mode
+    assert plib.hsq_probe_mfma(6, 10, 1, 8, A, None) == -1      # no such mode
+    assert plib.hsq_probe_mfma(4, 10, 1, 16, A, None) == -1     # the wide tile takes 8 waves at most
     assert plib.hsq_probe_mfma(0, 10, 1, 17, A, None) == -1     # more than 16 waves
     assert plib.hsq_probe_mfma(0, 0, 1, 8, A, None) == -1
     assert plib.hsq_probe_mfma(0, 10, 1, 8, None, None) == -1

@@ -32,6 +32,10 @@ WsLayout plan_workspace(int M, int K, int N, int r, int batch, int group) {
   off = align_up(off + (size_t)L.u_slices * batch * r * L.Mpad * sizeof(float), 256);
   L.part_off = off;
   off = align_up(off + tiled_partial_bytes(M, N, K, r, batch, group), 256);
+  L.swr = sw_pair_rows(K, group);
+  L.npad = ceil_div(N, kTile) * kTile;
+  L.swp_off = off;
+  off = align_up(off + (size_t)batch * L.swr * L.npad * 8, 256);
   L.total = off;
   return L;
 }
@@ -163,9 +167,16 @@ int contract_stage(int M, int K, int N, int batch, int group, const uint8_t *pac
   g.bpg = L.bpg; g.SG = L.SG;
   g.P = P; g.m0 = m0; g.mc = mc; g.n0 = n0; g.nc = nc;
   g.part = (float *)(ws + L.part_off);
+  g.swp = (const float2 *)(ws + L.swp_off);
+  g.swr = L.swr;
+  g.npad = L.npad;
   const bool dump = P != nullptr;
-  return hip_status(kernel == HSQ_KERNEL_SKINNY ? launch_gemm_skinny(g, batch, dump, s)
-                                                : launch_gemm_tiled(g, batch, dump, s));
+  if (kernel == HSQ_KERNEL_SKINNY) return hip_status(launch_gemm_skinny(g, batch, dump, s));
+  if (!dump) {
+    const hipError_t e = launch_sw_pairs(g, batch, s);
+    if (e != hipSuccess) return hip_status(e);
+  }
+  return hip_status(launch_gemm_tiled(g, batch, dump, s));
 }
 
 int run_linear(const uint16_t *X, int M, int K, int N, int batch, int group,
@@ -284,6 +295,11 @@ int run_chain(const uint16_t *X, int M, int K, int H, int N, const uint16_t *lam
   g.sxs2 = (uint16_t *)(wdn + c.dn.sxs_off);
   g.upart2 = (float *)(ws + c.upart_off);
   g.yhid = yhid;
+  g.swp = (const float2 *)(wup + c.up.swp_off);
+  g.swr = c.up.swr;
+  g.npad = c.up.npad;
+  st = hip_status(launch_sw_pairs(g, 1, s));
+  if (st != HSQ_OK) return st;
   st = hip_status(launch_gemm_tiled_chain(g, s));
   if (st != HSQ_OK) return st;
   // 3. the down layer's U: the column-block shares summed in order

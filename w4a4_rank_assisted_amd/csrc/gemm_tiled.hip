@@ -76,12 +76,14 @@ struct alignas(16) Stages {
   static constexpr int SPS = 2 / BPG;  // scale groups per stage
   int8_t a[2][2][TMB][64][16];         // [buf][block][m-tile][lane][bytes]   16 KB per buffer
   int8_t b[2][2][TNB][64][16];         // [buf][block][n-tile][lane][bytes]   16 KB per buffer
-  float2 sw[2][SPS][BN];               // [buf][group][col] = (sw, -magic*sw)/16
-  uint16_t sx[2][SPS][TMB][16];        // [buf][group][m-tile][row] fp16
+  float2 sw[2][2][BN];                 // [buf][group][col] = (sw, -magic*sw)/16          2 KB per buffer
+  uint16_t sx[2][TMB][2][16];          // [buf][m-tile][group][row] fp16                 512 B per buffer
 };
 static_assert(offsetof(Stages<1>, a) == 0 && offsetof(Stages<1>, b) == sizeof(Stages<1>::a) &&
               offsetof(Stages<2>, a) == 0 && offsetof(Stages<2>, b) == sizeof(Stages<2>::a),
               "the direct-to-LDS addresses assume A then B at the start of a stage set");
+static_assert(sizeof(Stages<1>::sw[0][0]) == 1024 && sizeof(Stages<1>::sx[0]) == 512,
+              "one direct-to-LDS load per scale group of weight scales, half of one for the activation scales");
 
 // Epilogue operands of the block: U (rank columns padded to RPT) for its
 // BM rows, L2 for its BN columns, bias.  Filled at kernel start.
@@ -221,51 +223,42 @@ __global__ __launch_bounds__(NTH * KH, 4) void k_gemm_tiled(GemmArgs a, int nblk
   const int G = a.G;                  // scale groups
   const v4u rs_a = raw_rsrc(a.qa, (uint32_t)MT * a.Gp * 1024);
   const v4u rs_w = raw_rsrc(w, (uint32_t)NT * a.Gp * 1024);
-  const __amdgpu_buffer_rsrc_t rs_x = buffer_rsrc(a.sxs, (uint32_t)MT * a.SG * 32);
-  const __amdgpu_buffer_rsrc_t rs_s = buffer_rsrc(sw, DUMP ? 0u : (uint32_t)G * a.N * 2);
+  const v4u rs_x = raw_rsrc(a.sxs, (uint32_t)MT * a.SG * 32);
+  const uint32_t swp_bytes = (uint32_t)a.swr * (uint32_t)a.npad * 8u;
+  const v4u rs_p = raw_rsrc(DUMP ? nullptr : (const char *)a.swp + (size_t)proj * swp_bytes, DUMP ? 0u : swp_bytes);
   const uint32_t offa = ((uint32_t)min(mt0 + wave, MT - 1) * a.Gp * 64 + lane) * 16;
   const uint32_t offb = ((uint32_t)min(nt0 + wave, NT - 1) * a.Gp * 64 + lane) * 16;
-  // scales, one per thread and stage: waves 0-3 stage activation scales
-  // (scale group (wave & 3) / 2 of the stage, row tile, row), waves 4-7
-  // weight scales (scale group, column); every condition below is uniform
-  // over a wave
-  const bool sx_wave = wave < 4;
-  const int sgs = (wave & 3) >> 1;                       // scale group within the stage
-  const bool stages_sx = sx_wave && sgs < SPS;
-  const bool stages_sw = !DUMP && !sx_wave && sgs < SPS;
-  const int sq = tid & 127;
-  const int smi = sq >> 4, srow = sq & 15, scol = sq;
-  const uint32_t offsx = ((uint32_t)min(mt0 + smi, MT - 1) * a.SG * 16 + srow) * 2;
-  const uint32_t offsw = (uint32_t)min(nt0 * 16 + scol, a.N - 1) * 2;
+  // scales: wave 0's first 32 lanes move the activation scales of the
+  // stage's two 64-channel groups for the 8 row tiles (64 bytes per tile,
+  // 16 per lane), waves 1 .. SPS the weight-scale pairs of one scale group
+  // for the 128 columns (1 KB); stages past the workgroup's range read the
+  // zero rows of the pair array, so they add exactly 0
+  const uint32_t offsx = (uint32_t)min(mt0 + (lane >> 2), MT - 1) * a.SG * 32 + (uint32_t)(lane & 3) * 16;
+  const uint32_t offsw = (uint32_t)nt0 * 16 * 8 + (uint32_t)lane * 16;
+  const int swg = BPG == 1 ? a.Gp : G;     // scale groups of the pair array before its zero rows
   const int last = nst - 1;
   // LDS byte addresses of this wave's A and B blocks in buffer 0, block 0
   // (the stage buffers open the shared object; a buffer is 2 x 8 KB per
-  // operand)
+  // operand), and of the scales
   const uint32_t lds_st = lds_addr(&smem) + (uint32_t)half * (uint32_t)sizeof(Stages<BPG>);
   const uint32_t lds_a = lds_st + (uint32_t)wave * 1024;
-  const uint32_t lds_b = lds_st + (uint32_t)sizeof(sm.a) + (uint32_t)wave * 1024;
-  uint32_t rscale = 0;
+  const uint32_t lds_b = lds_st + (uint32_t)offsetof(Stages<BPG>, b) + (uint32_t)wave * 1024;
+  const uint32_t lds_sw = lds_st + (uint32_t)offsetof(Stages<BPG>, sw);
+  const uint32_t lds_sx = lds_st + (uint32_t)offsetof(Stages<BPG>, sx);
   auto load_stage = [&](int st, int buf) __attribute__((always_inline)) {
-    const int sl = min(st, last);     // past the end: a clamped reload (its scales are 0)
+    const int sl = min(st, last);     // past the end: a clamped reload (its weight scales are 0)
 #pragma unroll
     for (int b = 0; b < 2; ++b) {
       const uint32_t blk = (uint32_t)(buf * 2 + b) * TMB * 1024;
       block_to_lds(rs_a, lds_a + blk, offa, (uint32_t)(2 * sl + b) * 1024);
       block_to_lds(rs_w, lds_b + blk, offb, (uint32_t)(2 * sl + b) * 1024);
     }
-    const int sg = min(sl * SPS + sgs, (BPG == 1 ? a.Gp : G) - 1);
-    if (stages_sx)
-      rscale = __builtin_amdgcn_raw_buffer_load_b16(rs_x, offsx, sg * 32, 0);
-    else if (stages_sw)
-      rscale = __builtin_amdgcn_raw_buffer_load_b16(rs_s, offsw, min(sg, G - 1) * a.N * 2, 0);
-  };
-  auto store_scales = [&](int st, int buf) __attribute__((always_inline)) {
-    if (stages_sx) {
-      sm.sx[buf][sgs][smi][srow] = (mt0 + smi < MT) ? (uint16_t)rscale : (uint16_t)0;
-    } else if (stages_sw) {
-      const int g = st * SPS + sgs, n = nt0 * 16 + scol;
-      const float sv = (g < G && st < send && n < a.N) ? f16_to_f32((uint16_t)rscale) : 0.0f;
-      sm.sw[buf][sgs][scol] = make_float2(sv * 0.0625f, -kMagic * 0.0625f * sv);
+    if (wave == 0) {
+      if (lane < 32) block_to_lds(rs_x, lds_sx + (uint32_t)buf * 512, offsx, (uint32_t)(SPS * sl) * 32);
+    } else if (!DUMP && wave <= SPS) {
+      const int sg = wave - 1;
+      const int row = st < send ? SPS * st + sg : swg + sg;
+      block_to_lds(rs_p, lds_sw + (uint32_t)(buf * 2 + sg) * 1024, offsw, (uint32_t)row * (uint32_t)a.npad * 8u);
     }
   };
 
@@ -322,7 +315,6 @@ __global__ __launch_bounds__(NTH * KH, 4) void k_gemm_tiled(GemmArgs a, int nblk
     }
     if (tid < BN) smem.ep.bias[tid] = (nt0 * 16 + tid < a.N) ? ebias : 0.0f;
   }
-  if constexpr (MODE != kReduce) store_scales(s0, 0);
   stage_barrier();
 
   if constexpr (MODE != kReduce) {
@@ -398,7 +390,7 @@ __global__ __launch_bounds__(NTH * KH, 4) void k_gemm_tiled(GemmArgs a, int nblk
 #pragma unroll
       for (int bb = 0; bb < BPG; ++bb)
         av[k][bb] = *reinterpret_cast<const v4i *>(&sm.a[BUF][sg * BPG + bb][wm * TM + s][lane][0]);
-      sxv[k] = *reinterpret_cast<const v4h *>(&sm.sx[BUF][sg][wm * TM + s][rowq]);
+      sxv[k] = *reinterpret_cast<const v4h *>(&sm.sx[BUF][wm * TM + s][sg][rowq]);
     };
     // one step's MFMAs: a group-128 scale group's two blocks accumulate in
     // int32 (the second MFMA takes the first one's result as its input)
@@ -455,8 +447,6 @@ __global__ __launch_bounds__(NTH * KH, 4) void k_gemm_tiled(GemmArgs a, int nblk
     for (int j = 0; j < TN; ++j) swc[j] = swv[SPS - 1][j];
     sxc = sxv[NSTEP - 1];
 
-    // the next stage's scales into the other buffer, then the barrier
-    store_scales(st + 1, BUF ^ 1);
     stage_barrier();
   };
   // stages in pairs (compile-time LDS buffers), then an odd last one
@@ -800,6 +790,20 @@ hipError_t launch_tiled_bpg(const GemmArgs &a, int batch, bool dump, hipStream_t
   return launch_tiled_kh<BPG, 1>(a, batch, p.splits, nblk, mblk, s);
 }
 
+// The pre-pass: sw (batch x G x N fp16) -> (sw/16, -1.5*2^23*sw/16) pairs,
+// batch x swr x npad, zero past column N and past group G (the pad group and
+// the zero stage).  One thread per pair.
+__global__ __launch_bounds__(256) void k_sw_pairs(const uint16_t *__restrict__ sw, int G, int N, int swr, int npad,
+                                                  size_t total, float2 *__restrict__ out) {
+  const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= total) return;
+  const int n = (int)(i % npad);
+  const size_t bg = i / npad;
+  const int g = (int)(bg % swr), b = (int)(bg / swr);
+  const float sv = (g < G && n < N) ? f16_to_f32(sw[((size_t)b * G + g) * N + n]) : 0.0f;
+  out[i] = make_float2(sv * 0.0625f, -kMagic * 0.0625f * sv);
+}
+
 template <int RPT>
 hipError_t launch_chain_rpt(const GemmArgs &a, int nblk, int mblk, hipStream_t s) {
   hipLaunchKernelGGL((k_gemm_tiled<false, RPT, kFull, 1, 1, true>), dim3((unsigned)(nblk * mblk), 1u), dim3(NTH),
@@ -829,6 +833,13 @@ hipError_t launch_gemm_tiled_chain(const GemmArgs &a, hipStream_t s) {
 hipError_t launch_chain_ureduce(const float *upart, int nblk, int r2, int Mpad, float *uw, hipStream_t s) {
   hipLaunchKernelGGL(k_chain_ureduce, dim3((unsigned)ceil_div(r2 * Mpad, 256)), dim3(256), 0, s, upart, nblk, r2,
                      Mpad, uw);
+  return hipGetLastError();
+}
+
+hipError_t launch_sw_pairs(const GemmArgs &a, int batch, hipStream_t s) {
+  const size_t total = (size_t)batch * a.swr * a.npad;
+  hipLaunchKernelGGL(k_sw_pairs, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, a.sw, a.G, a.N, a.swr,
+                     a.npad, total, const_cast<float2 *>(a.swp));
   return hipGetLastError();
 }
 

@@ -73,13 +73,27 @@ inline size_t packed_bytes(int K, int N) { return nibble_bytes(K, N) + operand_b
 //         quantization pass, summed in slice order by the consumer
 //   part: split-K partial tiles of the tiled contraction when its grid is
 //         too small for the chip (tiled_partial_bytes; empty otherwise)
+//   swp : batch x SWR x Npad float2, the weight scales as the tiled
+//         contraction applies them, (sw/16, -1.5*2^23*sw/16) per (scale
+//         group, column), written by its pre-pass; rows SG_w .. SWR-1, pad
+//         columns and pad groups are zero (SWR = sw_pair_rows, Npad = N
+//         rounded up to 16)
 // ---------------------------------------------------------------------------
 struct WsLayout {
   int MT = 0, G = 0, Gp = 0, Mpad = 0;
   int group = kGroup, bpg = 1, SG = 0;  // G = K/group scale groups; bpg = group/64 blocks each
   int u_slices = 0;      // S_u: K-slices of the quantization pass
-  size_t qa_off = 0, sxs_off = 0, uw_off = 0, part_off = 0, total = 0;
+  int swr = 0, npad = 0; // weight-scale pair rows and columns
+  size_t qa_off = 0, sxs_off = 0, uw_off = 0, part_off = 0, swp_off = 0, total = 0;
 };
+
+// Rows of the weight-scale pair array: the scale groups of the stages (a
+// stage is a 128-channel block pair: two groups of 64 or one of 128, the
+// 64-channel groups padded to even), then one stage of zero rows that the
+// stages past a workgroup's range read.
+inline int sw_pair_rows(int K, int group) {
+  return group == kGroup ? padded_groups(K) + 2 : K / group + 1;
+}
 
 // Plans the workspace for (M, K, N, r, batch, group).  Pure host arithmetic.
 WsLayout plan_workspace(int M, int K, int N, int r, int batch, int group);
@@ -134,6 +148,9 @@ struct GemmArgs {
   // number per output tile
   float *part;
   int splits;
+  // weight-scale pairs of the tiled contraction (see WsLayout)
+  const float2 *swp;
+  int swr, npad;
   // fused chain (tiled contraction, CHAIN mode): instead of Y, the epilogue
   // writes the next layer's input: act(Y) smoothed by lam2 and quantized
   // into that layer's workspace (codes qa2, scales sxs2), and the partial
@@ -163,6 +180,9 @@ hipError_t launch_quant_act(const QuantArgs &a, hipStream_t s);
 hipError_t launch_quant_tiles(const QuantArgs &a, hipStream_t s);
 int quant_slices(int M, int K, int r, int batch, int group);
 hipError_t launch_gemm_tiled(const GemmArgs &a, int batch, bool dump, hipStream_t s);
+// The tiled contraction's pre-pass: sw (batch x G x N fp16) -> the pair
+// array a.swp (batch x a.swr x a.npad float2, layout in WsLayout).
+hipError_t launch_sw_pairs(const GemmArgs &a, int batch, hipStream_t s);
 // Split-K factor of the tiled contraction for this shape (1: no split) and
 // the workspace bytes of its partial tiles.
 int tiled_splits(int M, int N, int K, int r, int batch, int group);

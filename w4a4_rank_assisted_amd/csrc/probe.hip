@@ -20,7 +20,7 @@ typedef unsigned v4u __attribute__((ext_vector_type(4)));
 typedef _Float16 v4h __attribute__((ext_vector_type(4)));
 
 constexpr int kMagicBits = 0x4B400000;   // bits of 1.5 * 2^23
-constexpr int TM = 4, TN = 2;            // MFMA tiles per wave (64 x 32 outputs)
+constexpr int TM = 4;                    // MFMA row tiles per wave (64 rows)
 
 __device__ __forceinline__ void pin(v4i &x) { asm volatile("" : "+v"(x)); }
 __device__ __forceinline__ void pin(float &x) { asm volatile("" : "+v"(x)); }
@@ -38,8 +38,9 @@ struct alignas(16) StageLds {
 };
 constexpr int kMaxWaves = 16;
 
-template <int MODE>
-__global__ __launch_bounds__(64 * kMaxWaves) void k_probe_mfma(int iters, float s0, int32_t *out) {
+// the wide tile needs about 150 registers: at most 8 waves per workgroup
+template <int MODE, int TN>
+__global__ __launch_bounds__(TN == 4 ? 512 : 64 * kMaxWaves) void k_probe_mfma(int iters, float s0, int32_t *out) {
   __shared__ StageLds lds;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
@@ -113,8 +114,8 @@ __global__ __launch_bounds__(64 * kMaxWaves) void k_probe_mfma(int iters, float 
       const int bf = it & 1;
 #pragma unroll
       for (int j = 0; j < TN; ++j) {
-        b[j] = *reinterpret_cast<const v4i *>(&lds.b[bf][wn * TN + j][lane][0]);
-        sw[j] = lds.sw[bf][(wn * TN + j) * 16 + colq];
+        b[j] = *reinterpret_cast<const v4i *>(&lds.b[bf][(wn * TN + j) & 7][lane][0]);
+        sw[j] = lds.sw[bf][((wn * TN + j) & 7) * 16 + colq];
       }
 #pragma unroll
       for (int i = 0; i < TM; ++i) {
@@ -201,15 +202,18 @@ int status(hipError_t e) { return e == hipSuccess ? 0 : -5; }
 extern "C" {
 
 int hsq_probe_mfma(int mode, int iters, int blocks, int waves, int32_t *out, void *stream) {
-  if (mode < 0 || mode > 3 || iters < 1 || blocks < 1 || waves < 1 || waves > kMaxWaves || !out) return -1;
+  if (mode < 0 || mode > 5 || iters < 1 || blocks < 1 || waves < 1 || waves > (mode >= 4 ? 8 : kMaxWaves) || !out)
+    return -1;
   if (!aligned16(out)) return -3;
   const dim3 grid((unsigned)blocks), block((unsigned)(64 * waves));
   hipStream_t s = (hipStream_t)stream;
   switch (mode) {
-    case 0: hipLaunchKernelGGL(k_probe_mfma<0>, grid, block, 0, s, iters, 1.0f, out); break;
-    case 1: hipLaunchKernelGGL(k_probe_mfma<1>, grid, block, 0, s, iters, 1.0f, out); break;
-    case 2: hipLaunchKernelGGL(k_probe_mfma<2>, grid, block, 0, s, iters, 1.0f, out); break;
-    default: hipLaunchKernelGGL(k_probe_mfma<3>, grid, block, 0, s, iters, 1.0f, out); break;
+    case 0: hipLaunchKernelGGL((k_probe_mfma<0, 2>), grid, block, 0, s, iters, 1.0f, out); break;
+    case 1: hipLaunchKernelGGL((k_probe_mfma<1, 2>), grid, block, 0, s, iters, 1.0f, out); break;
+    case 2: hipLaunchKernelGGL((k_probe_mfma<2, 2>), grid, block, 0, s, iters, 1.0f, out); break;
+    case 3: hipLaunchKernelGGL((k_probe_mfma<3, 2>), grid, block, 0, s, iters, 1.0f, out); break;
+    case 4: hipLaunchKernelGGL((k_probe_mfma<2, 4>), grid, block, 0, s, iters, 1.0f, out); break;
+    default: hipLaunchKernelGGL((k_probe_mfma<3, 4>), grid, block, 0, s, iters, 1.0f, out); break;
   }
   return status(hipGetLastError());
 }
