@@ -792,16 +792,26 @@ hipError_t launch_tiled_bpg(const GemmArgs &a, int batch, bool dump, hipStream_t
 
 // The pre-pass: sw (batch x G x N fp16) -> (sw/16, -1.5*2^23*sw/16) pairs,
 // batch x swr x npad, zero past column N and past group G (the pad group and
-// the zero stage).  One thread per pair.
+// the zero stage).  One thread per 8 pairs (npad is a multiple of 16): 8
+// coalesced fp16 reads, four 16-byte stores.
 __global__ __launch_bounds__(256) void k_sw_pairs(const uint16_t *__restrict__ sw, int G, int N, int swr, int npad,
-                                                  size_t total, float2 *__restrict__ out) {
+                                                  size_t total8, float4 *__restrict__ out) {
   const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
-  if (i >= total) return;
-  const int n = (int)(i % npad);
-  const size_t bg = i / npad;
+  if (i >= total8) return;
+  const int n0 = (int)(i % (npad / 8)) * 8;
+  const size_t bg = i / (npad / 8);
   const int g = (int)(bg % swr), b = (int)(bg / swr);
-  const float sv = (g < G && n < N) ? f16_to_f32(sw[((size_t)b * G + g) * N + n]) : 0.0f;
-  out[i] = make_float2(sv * 0.0625f, -kMagic * 0.0625f * sv);
+  const uint16_t *row = sw + ((size_t)b * G + g) * N;
+  float v[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const int n = n0 + e;
+    v[e] = (g < G && n < N) ? f16_to_f32(row[n]) : 0.0f;
+  }
+#pragma unroll
+  for (int e = 0; e < 8; e += 2)
+    out[i * 4 + e / 2] = make_float4(v[e] * 0.0625f, -kMagic * 0.0625f * v[e], v[e + 1] * 0.0625f,
+                                     -kMagic * 0.0625f * v[e + 1]);
 }
 
 template <int RPT>
@@ -837,9 +847,9 @@ hipError_t launch_chain_ureduce(const float *upart, int nblk, int r2, int Mpad, 
 }
 
 hipError_t launch_sw_pairs(const GemmArgs &a, int batch, hipStream_t s) {
-  const size_t total = (size_t)batch * a.swr * a.npad;
-  hipLaunchKernelGGL(k_sw_pairs, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, a.sw, a.G, a.N, a.swr,
-                     a.npad, total, const_cast<float2 *>(a.swp));
+  const size_t total8 = (size_t)batch * a.swr * (a.npad / 8);
+  hipLaunchKernelGGL(k_sw_pairs, dim3((unsigned)((total8 + 255) / 256)), dim3(256), 0, s, a.sw, a.G, a.N, a.swr,
+                     a.npad, total8, reinterpret_cast<float4 *>(const_cast<float2 *>(a.swp)));
   return hipGetLastError();
 }
 
