@@ -909,13 +909,13 @@ def linear_main(args):
                                group=args.group)
 
     def step(i):
+        # one call of the layer's entry point per layer (its quantization
+        # pass and contraction on one stream)
         for L in layers:
             sp, st = L["spec"], L["sets"][i % L["nsets"]]
-            hsq.quantize_stage(st["X"], L["lam"], L["L1"], N=sp.N, batch=sp.batch, workspace=L["ws"],
-                               group=args.group, act_quant=args.act_quant)
-            hsq.contract_stage(sp.M, sp.K, st["packed"], st["sw"], L["L2"], L["bias"], st["Y"], N=sp.N,
-                               batch=sp.batch, r=sp.r, workspace=L["ws"], kernel=L["kernel"],
-                               group=args.group)
+            hsq.w4a4_lowrank_linear(st["X"], L["lam"], st["packed"], st["sw"], L["L1"], L["L2"], L["bias"],
+                                    N=sp.N, batch=sp.batch, y_dtype=args.y_dtype, out=st["Y"], workspace=L["ws"],
+                                    kernel=L["kernel"], group=args.group, act_quant=args.act_quant)
 
     for i in range(args.warmup):
         step(i)

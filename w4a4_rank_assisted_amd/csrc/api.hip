@@ -125,7 +125,7 @@ int validate(const uint16_t *X, int M, int K, int N, int batch, int group,
 
 int quant_stage(const uint16_t *X, int M, int K, int N, int batch, int group,
                 const uint16_t *lambda, const uint16_t *L1, int r, void *workspace, hipStream_t s,
-                int aq = HSQ_AQ_SYMMETRIC) {
+                int aq = HSQ_AQ_SYMMETRIC, const uint16_t *pair_sw = nullptr) {
   const WsLayout L = plan_workspace(M, K, N, r, batch, group);
   char *ws = (char *)workspace;
   QuantArgs q{};
@@ -141,13 +141,18 @@ int quant_stage(const uint16_t *X, int M, int K, int N, int batch, int group,
   q.uw = (float *)(ws + L.uw_off);
   q.Gp = L.Gp; q.Mpad = L.Mpad; q.ucols = batch * r;
   q.asym = aq == HSQ_AQ_ASYMMETRIC;
+  if (pair_sw != nullptr) {   // the tiled contraction's weight-scale pairs ride along
+    q.sw = pair_sw;
+    q.swp = (float4 *)(ws + L.swp_off);
+    q.swG = L.G; q.swN = N; q.swr = L.swr; q.swnpad = L.npad;
+  }
   return hip_status(launch_quant_tiles(q, s));
 }
 
 int contract_stage(int M, int K, int N, int batch, int group, const uint8_t *packed_w,
                    const uint16_t *sw, const uint16_t *L2, int r, const uint16_t *bias, void *Y,
                    int y_dtype, void *workspace, int kernel, hipStream_t s, int32_t *P, int m0,
-                   int mc, int n0, int nc, int u_slices = -1) {
+                   int mc, int n0, int nc, int u_slices = -1, bool pairs_written = false) {
   const WsLayout L = plan_workspace(M, K, N, r, batch, group);
   char *ws = (char *)workspace;
   GemmArgs g{};
@@ -172,7 +177,7 @@ int contract_stage(int M, int K, int N, int batch, int group, const uint8_t *pac
   g.npad = L.npad;
   const bool dump = P != nullptr;
   if (kernel == HSQ_KERNEL_SKINNY) return hip_status(launch_gemm_skinny(g, batch, dump, s));
-  if (!dump) {
+  if (!dump && !pairs_written) {
     const hipError_t e = launch_sw_pairs(g, batch, s);
     if (e != hipSuccess) return hip_status(e);
   }
@@ -189,10 +194,13 @@ int run_linear(const uint16_t *X, int M, int K, int N, int batch, int group,
                     workspace, ws_bytes, &kernel, true, true, P, m0, mc, n0, nc);
   if (st != HSQ_OK) return st;
   hipStream_t s = (hipStream_t)stream;
-  st = quant_stage(X, M, K, N, batch, group, lambda, L1, r, workspace, s, aq);
+  // the tiled contraction's weight-scale pairs are written by the
+  // quantization pass's launch (no launch of their own)
+  const bool pairs = kernel == HSQ_KERNEL_TILED && P == nullptr;
+  st = quant_stage(X, M, K, N, batch, group, lambda, L1, r, workspace, s, aq, pairs ? sw : nullptr);
   if (st != HSQ_OK) return st;
   return contract_stage(M, K, N, batch, group, packed_w, sw, L2, r, bias, Y, y_dtype, workspace,
-                        kernel, s, P, m0, mc, n0, nc);
+                        kernel, s, P, m0, mc, n0, nc, -1, pairs);
 }
 
 int quantize_stage_g(const uint16_t *X, int M, int K, int N, int batch, int group,
@@ -267,8 +275,9 @@ int run_chain(const uint16_t *X, int M, int K, int H, int N, const uint16_t *lam
   hipStream_t s = (hipStream_t)stream;
   char *ws = (char *)workspace;
   char *wup = ws + c.up_off, *wdn = ws + c.dn_off;
-  // 1. the up layer's quantization pass
-  st = quant_stage(X, M, K, H, 1, kGroup, lam_up, L1_up, r1, wup, s);
+  // 1. the up layer's quantization pass (with its contraction's weight-scale
+  //    pairs)
+  st = quant_stage(X, M, K, H, 1, kGroup, lam_up, L1_up, r1, wup, s, HSQ_AQ_SYMMETRIC, sw_up);
   if (st != HSQ_OK) return st;
   // 2. its contraction, whose epilogue quantizes act(Y) into the down
   //    layer's workspace
@@ -298,8 +307,6 @@ int run_chain(const uint16_t *X, int M, int K, int H, int N, const uint16_t *lam
   g.swp = (const float2 *)(wup + c.up.swp_off);
   g.swr = c.up.swr;
   g.npad = c.up.npad;
-  st = hip_status(launch_sw_pairs(g, 1, s));
-  if (st != HSQ_OK) return st;
   st = hip_status(launch_gemm_tiled_chain(g, s));
   if (st != HSQ_OK) return st;
   // 3. the down layer's U: the column-block shares summed in order

@@ -790,28 +790,12 @@ hipError_t launch_tiled_bpg(const GemmArgs &a, int batch, bool dump, hipStream_t
   return launch_tiled_kh<BPG, 1>(a, batch, p.splits, nblk, mblk, s);
 }
 
-// The pre-pass: sw (batch x G x N fp16) -> (sw/16, -1.5*2^23*sw/16) pairs,
-// batch x swr x npad, zero past column N and past group G (the pad group and
-// the zero stage).  One thread per 8 pairs (npad is a multiple of 16): 8
-// coalesced fp16 reads, four 16-byte stores.
+// The weight-scale pairs of the stage loop (sw_pair_item), one thread per 8
+// pairs; the linear writes them from its quantization pass instead.
 __global__ __launch_bounds__(256) void k_sw_pairs(const uint16_t *__restrict__ sw, int G, int N, int swr, int npad,
                                                   size_t total8, float4 *__restrict__ out) {
   const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
-  if (i >= total8) return;
-  const int n0 = (int)(i % (npad / 8)) * 8;
-  const size_t bg = i / (npad / 8);
-  const int g = (int)(bg % swr), b = (int)(bg / swr);
-  const uint16_t *row = sw + ((size_t)b * G + g) * N;
-  float v[8];
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const int n = n0 + e;
-    v[e] = (g < G && n < N) ? f16_to_f32(row[n]) : 0.0f;
-  }
-#pragma unroll
-  for (int e = 0; e < 8; e += 2)
-    out[i * 4 + e / 2] = make_float4(v[e] * 0.0625f, -kMagic * 0.0625f * v[e], v[e + 1] * 0.0625f,
-                                     -kMagic * 0.0625f * v[e + 1]);
+  if (i < total8) sw_pair_item(sw, G, N, swr, npad, i, out);
 }
 
 template <int RPT>

@@ -124,6 +124,12 @@ struct QuantArgs {
   uint16_t *sxs;
   float *uw;
   int Gp, Mpad, ucols;
+  // optional: the tiled contraction's weight-scale pairs, written by extra
+  // workgroups of the first pass (swp == nullptr: none); sw is batch x swG x
+  // swN fp16, the table batch x swr x swnpad pairs (sw_pair_item)
+  const uint16_t *sw;
+  float4 *swp;
+  int swG, swN, swr, swnpad;
 };
 
 struct GemmArgs {
@@ -316,6 +322,36 @@ __device__ __forceinline__ float f16_to_f32(uint16_t h) {
 // Round to nearest even (v_cvt_f16_f32 in the default rounding mode).
 __device__ __forceinline__ uint16_t f32_to_f16(float f) {
   return __builtin_bit_cast(uint16_t, (_Float16)f);
+}
+
+// Weight-scale pairs of the tiled contraction: item i covers 8 adjacent
+// columns of one (projection, pair row) of the batch x swr x npad table and
+// writes (sw/16, -1.5*2^23*sw/16) for each, zero past column N and past scale
+// group G (the pad group and the zero stage); four 16-byte stores.
+__device__ __forceinline__ void sw_pair_item(const uint16_t *__restrict__ sw, int G, int N, int swr, int npad,
+                                             size_t i, float4 *__restrict__ out) {
+  const int n0 = (int)(i % (npad / 8)) * 8;
+  const size_t bg = i / (npad / 8);
+  const int g = (int)(bg % swr), b = (int)(bg / swr);
+  const uint16_t *row = sw + ((size_t)b * G + g) * N;
+  float v[8];
+  if ((N & 7) == 0 && g < G && n0 < N) {
+    // whole 16-byte run (rows start 16-byte aligned when N % 8 == 0)
+    const uint4 w = *reinterpret_cast<const uint4 *>(row + n0);
+    const uint32_t h[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = f16_to_f32((uint16_t)(h[e / 2] >> (16 * (e & 1))));
+  } else {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int n = n0 + e;
+      v[e] = (g < G && n < N) ? f16_to_f32(row[n]) : 0.0f;
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < 8; e += 2)
+    out[i * 4 + e / 2] = make_float4(v[e] * 0.0625f, -kMagic * 0.0625f * v[e], v[e + 1] * 0.0625f,
+                                     -kMagic * 0.0625f * v[e + 1]);
 }
 
 // fp32 -> bf16, round to nearest even (inputs are finite).

@@ -93,6 +93,16 @@ __global__ __launch_bounds__(1024) void k_quant_tiles(QuantArgs a, int gpb) {
   // (per 64-block and channel block: 16 channels x NR columns); after the
   // loop, U shares [waves][NR][64]
   extern __shared__ float lds[];
+  const int MT = a.Mpad / kTile;
+  if ((int)blockIdx.x >= MT) {
+    // workgroups past the row tiles write the contraction's weight-scale
+    // pairs (first pass only), grid-strided over the table
+    const size_t total8 = (size_t)a.batch * a.swr * (a.swnpad / 8);
+    const size_t px = gridDim.x - (unsigned)MT, step = px * gridDim.y * blockDim.x;
+    for (size_t i = ((size_t)(blockIdx.x - MT) + px * blockIdx.y) * blockDim.x + threadIdx.x; i < total8; i += step)
+      sw_pair_item(a.sw, a.swG, a.swN, a.swr, a.swnpad, i, a.swp);
+    return;
+  }
   float *ilam = lds;
   float *l1s = ilam + gpb * BPG * 4 * kLamKq;
   float *upart = lds;
@@ -317,7 +327,16 @@ __global__ __launch_bounds__(1024) void k_quant_tiles(QuantArgs a, int gpb) {
 
 template <int NR, int BPG>
 hipError_t launch_pass(const QuantArgs &a, const TilePlan &p, int cm, hipStream_t s) {
-  const dim3 grid((unsigned)(a.Mpad / kTile), (unsigned)p.slices);
+  // extra columns of workgroups for the weight-scale pairs: one item of 8
+  // pairs per thread (a loop of several per thread outlasts the pass at
+  // small M)
+  int px = 0;
+  if (a.swp != nullptr) {
+    const size_t total8 = (size_t)a.batch * a.swr * (a.swnpad / 8);
+    const size_t per = (size_t)64 * p.waves * p.slices;
+    px = (int)((total8 + per - 1) / per);
+  }
+  const dim3 grid((unsigned)(a.Mpad / kTile + px), (unsigned)p.slices);
   const dim3 block((unsigned)(64 * p.waves));
   const size_t lds = plan_lds(p.gpb, BPG, NR, p.waves);
   if (cm == kSymCodes)
@@ -360,6 +379,7 @@ hipError_t launch_quant_tiles(const QuantArgs &a0, hipStream_t s) {
     a.c0 = c0;
     a.cb = total - c0 < kRankPass ? total - c0 : kRankPass;
     const int cm = c0 != 0 ? kNoCodes : a.asym ? kAsymCodes : kSymCodes;
+    if (c0 != 0) a.swp = nullptr;
     const hipError_t e = a.bpg == 2 ? launch_width<2>(a, p, cm, s) : launch_width<1>(a, p, cm, s);
     if (e != hipSuccess) return e;
     c0 += kRankPass;
