@@ -347,8 +347,8 @@ int hsq_mx_lowrank_linear(const uint16_t *X, int M, int K, int N, const uint16_t
  * All other arguments as for hsq_w4a4_lowrank_linear, per layer.
  * Performance: on an MI355X this call is SLOWER than the two layers run
  * as separate hsq_w4a4_lowrank_linear calls (FLUX.1 MLP, 4608 tokens:
- * 0.786 ms fused vs 0.701 ms separate, the separate path without any
- * activation pass).  The up contraction is bound by its per-group VALU
+ * 0.70-0.71 ms fused vs 0.60-0.61 ms separate, the separate path without
+ * any activation pass).  The up contraction is bound by its per-group VALU
  * rescale, and the fused epilogue adds about 50 VALU instructions per
  * output element (GELU, smoothing, absmax, codes, rank-r dot product) to
  * it, more than the bf16 round trip and quantization pass it removes.  Use

@@ -471,3 +471,34 @@ def test_group_entry_at_64_equals_plain_entry():
         torch.cuda.synchronize()
         outs.append(out.view(torch.int32).cpu().numpy())
     assert np.array_equal(outs[0], outs[1])
+
+
+@pytest.mark.parametrize("M,K,N,r,batch,group", [
+    (200, 1024, 300, 4, 2, 64),      # N % 8 != 0 (pair table's scalar loads), two projections
+    (300, 2048, 512, 4, 1, 64),      # N % 8 == 0 (16-byte loads)
+    (256, 4096, 1200, 7, 1, 128),    # group 128, odd rank
+    (130, 1152, 4608, 4, 3, 64),     # SANA-like: three projections sharing X
+])
+def test_layer_call_equals_stage_calls(M, K, N, r, batch, group):
+    # the layer call writes the tiled contraction's weight-scale pairs from
+    # extra workgroups of its quantization pass; the contraction stage called
+    # on its own writes them with a pre-pass kernel; the outputs must agree
+    # bit for bit (the workspace starts with stale bytes each time)
+    lay = make_random_layer(500 + M + N, M, K, N, r=r, batch=batch, outlier_channels=2, group=group)
+    up = Uploaded(lay)
+    say(f"[layer vs stages] M={M} K={K} N={N} r={r} batch={batch} group={group}")
+    outs = []
+    for how in ("layer", "stages"):
+        ws = torch.empty(hsq.workspace_bytes(M, K, N, r, batch, group), dtype=torch.uint8, device=DEV)
+        ws.fill_(0x5A if how == "layer" else 0xA5)
+        out = torch.empty((batch, M, N), dtype=torch.float32, device=DEV)
+        if how == "layer":
+            hsq.w4a4_lowrank_linear(up.X, up.lam, up.packed, up.sw, up.L1, up.L2, up.bias, N=N, batch=batch,
+                                    y_dtype="f32", out=out, workspace=ws, kernel="tiled", group=group)
+        else:
+            hsq.quantize_stage(up.X, up.lam, up.L1, N=N, batch=batch, workspace=ws, group=group)
+            hsq.contract_stage(M, K, up.packed, up.sw, up.L2, up.bias, out, N=N, batch=batch, r=r,
+                               workspace=ws, kernel="tiled", group=group)
+        torch.cuda.synchronize()
+        outs.append(out.view(torch.int32).cpu().numpy())
+    assert np.array_equal(outs[0], outs[1])
