@@ -36,6 +36,11 @@
  *   - Arguments are validated before anything is enqueued; on an error the
  *     call returns a negative HSQ_E_* code and enqueues nothing.  Faults that
  *     happen while kernels run surface at the caller's next synchronisation.
+ *   - Debugging: with HSQ_DEBUG set in the environment (any value but "0"),
+ *     every call that enqueues work waits for its stream before returning
+ *     and reports a failure of its own kernels as HSQ_E_HIP, with
+ *     hsq_last_hip_error() naming it.  While the stream is being captured
+ *     into a graph the call does not wait (waiting is not allowed there).
  *   - The library keeps no state between calls (except the per-device
  *     scratch of hsq_w4a4_lowrank_linear_noalloc) and is thread-safe; no
  *     C++ exception crosses this interface.

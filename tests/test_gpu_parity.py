@@ -502,3 +502,27 @@ def test_layer_call_equals_stage_calls(M, K, N, r, batch, group):
         torch.cuda.synchronize()
         outs.append(out.view(torch.int32).cpu().numpy())
     assert np.array_equal(outs[0], outs[1])
+
+
+def test_debug_env_waits_and_keeps_results(monkeypatch):
+    # HSQ_DEBUG: each call waits for its stream and checks its kernels; the
+    # results are those of the asynchronous calls, and a call being captured
+    # into a graph does not wait (capture and replay still work)
+    up = uploaded("tiny")
+    ref = up.linear("f32").view(torch.int32).cpu().numpy()
+    monkeypatch.setenv("HSQ_DEBUG", "1")
+    got = up.linear("f32").view(torch.int32).cpu().numpy()
+    assert np.array_equal(got, ref)
+    out = torch.empty((up.B, up.M, up.N), dtype=torch.float32, device=DEV)
+    ws = torch.empty(hsq.workspace_bytes(up.M, up.K, up.N, up.r, up.B), dtype=torch.uint8, device=DEV)
+    cap = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(cap):
+        with torch.cuda.graph(g, stream=cap):
+            hsq.w4a4_lowrank_linear(up.X, up.lam, up.packed, up.sw, up.L1, up.L2, up.bias, N=up.N,
+                                    batch=up.B, y_dtype="f32", out=out, workspace=ws)
+    for _ in range(2):
+        out.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(out.view(torch.int32).cpu().numpy(), ref)

@@ -6,6 +6,7 @@
 
 #include <atomic>
 #include <climits>
+#include <cstdlib>
 #include <cstdint>
 #include <mutex>
 
@@ -73,6 +74,27 @@ int hip_status(hipError_t e) {
   if (e == hipSuccess) return HSQ_OK;
   g_last_hip_error = e;
   return HSQ_E_HIP;
+}
+
+// HSQ_DEBUG set (and not "0") in the environment: a call that enqueued work
+// waits for its stream and reports an asynchronous failure of its kernels
+// as HSQ_E_HIP (hsq_last_hip_error names it) -- except while the stream is
+// being captured into a graph, where waiting is not allowed.
+bool debug_enabled() {
+  const char *v = getenv("HSQ_DEBUG");
+  return v != nullptr && v[0] != '\0' && !(v[0] == '0' && v[1] == '\0');
+}
+
+int debug_check(int st, void *stream) {
+  if (st != HSQ_OK || !debug_enabled()) return st;
+  hipStream_t s = (hipStream_t)stream;
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  const hipError_t ce = hipStreamIsCapturing(s, &cs);
+  if (ce != hipSuccess) return hip_status(ce);
+  if (cs != hipStreamCaptureStatusNone) return st;
+  hipError_t e = hipStreamSynchronize(s);
+  if (e == hipSuccess) e = hipGetLastError();
+  return hip_status(e);
 }
 
 bool group_ok(int group) { return group == 64 || group == 128; }
@@ -404,7 +426,7 @@ int hsq_pack_weights(const int8_t *codes, int K, int N, uint8_t *packed, int *d_
   if (K % kGroup != 0) return HSQ_E_SHAPE;
   if ((long long)K * N >= INT_MAX) return HSQ_E_INVAL;
   if (!aligned16(codes) || !aligned16(packed) || !aligned16(d_status)) return HSQ_E_ALIGN;
-  return hip_status(launch_pack(codes, K, N, packed, d_status, (hipStream_t)stream));
+  return debug_check(hip_status(launch_pack(codes, K, N, packed, d_status, (hipStream_t)stream)), stream);
 }
 
 int hsq_unpack_weights(const uint8_t *packed, int K, int N, int8_t *codes, void *stream) {
@@ -412,7 +434,7 @@ int hsq_unpack_weights(const uint8_t *packed, int K, int N, int8_t *codes, void 
   if (K % kGroup != 0) return HSQ_E_SHAPE;
   if ((long long)K * N >= INT_MAX) return HSQ_E_INVAL;
   if (!aligned16(codes) || !aligned16(packed)) return HSQ_E_ALIGN;
-  return hip_status(launch_unpack(packed, K, N, codes, (hipStream_t)stream));
+  return debug_check(hip_status(launch_unpack(packed, K, N, codes, (hipStream_t)stream)), stream);
 }
 
 int hsq_quantize_act(const uint16_t *X, int M, int K, const uint16_t *lambda,
@@ -434,7 +456,7 @@ int hsq_quantize_act(const uint16_t *X, int M, int K, const uint16_t *lambda,
   q.kend = K;
   q.qx = qx; q.sx = sx; q.u_pub = r > 0 ? U : nullptr;
   q.ucols = r;
-  return hip_status(launch_quant_act(q, (hipStream_t)stream));
+  return debug_check(hip_status(launch_quant_act(q, (hipStream_t)stream)), stream);
 }
 
 size_t hsq_workspace_bytes(int M, int K, int N, int r, int batch) {
@@ -450,8 +472,8 @@ int hsq_w4a4_lowrank_linear(const uint16_t *X, int M, int K, int N, int batch,
                             const uint16_t *sw, const uint16_t *L1, const uint16_t *L2, int r,
                             const uint16_t *bias, void *Y, int y_dtype, void *workspace,
                             size_t ws_bytes, void *stream) {
-  return run_linear(X, M, K, N, batch, kGroup, lambda, packed_w, sw, L1, L2, r, bias, Y, y_dtype,
-                    workspace, ws_bytes, HSQ_KERNEL_AUTO, stream, nullptr, 0, 0, 0, 0);
+  return debug_check(run_linear(X, M, K, N, batch, kGroup, lambda, packed_w, sw, L1, L2, r, bias, Y, y_dtype,
+                    workspace, ws_bytes, HSQ_KERNEL_AUTO, stream, nullptr, 0, 0, 0, 0), stream);
 }
 
 int hsq_w4a4_lowrank_linear_noalloc(const uint16_t *X, int M, int K, int N, int batch,
@@ -474,8 +496,8 @@ int hsq_w4a4_lowrank_linear_noalloc(const uint16_t *X, int M, int K, int N, int 
   void *ws = nullptr;
   st = scratch_of_current_device(&ws);
   if (st != HSQ_OK) return st;
-  return run_linear(X, M, K, N, batch, kGroup, lambda, packed_w, sw, L1, L2, r, bias, Y, y_dtype, ws,
-                    (size_t)HSQ_NOALLOC_SCRATCH_BYTES, HSQ_KERNEL_AUTO, stream, nullptr, 0, 0, 0, 0);
+  return debug_check(run_linear(X, M, K, N, batch, kGroup, lambda, packed_w, sw, L1, L2, r, bias, Y, y_dtype, ws,
+                    (size_t)HSQ_NOALLOC_SCRATCH_BYTES, HSQ_KERNEL_AUTO, stream, nullptr, 0, 0, 0, 0), stream);
 }
 
 int hsq_w4a4_lowrank_linear_ex(const uint16_t *X, int M, int K, int N, int batch,
@@ -483,8 +505,8 @@ int hsq_w4a4_lowrank_linear_ex(const uint16_t *X, int M, int K, int N, int batch
                                const uint16_t *sw, const uint16_t *L1, const uint16_t *L2,
                                int r, const uint16_t *bias, void *Y, int y_dtype,
                                void *workspace, size_t ws_bytes, int kernel, void *stream) {
-  return run_linear(X, M, K, N, batch, kGroup, lambda, packed_w, sw, L1, L2, r, bias, Y, y_dtype,
-                    workspace, ws_bytes, kernel, stream, nullptr, 0, 0, 0, 0);
+  return debug_check(run_linear(X, M, K, N, batch, kGroup, lambda, packed_w, sw, L1, L2, r, bias, Y, y_dtype,
+                    workspace, ws_bytes, kernel, stream, nullptr, 0, 0, 0, 0), stream);
 }
 
 int hsq_w4a4_lowrank_linear_g(const uint16_t *X, int M, int K, int N, int batch, int group,
@@ -492,52 +514,52 @@ int hsq_w4a4_lowrank_linear_g(const uint16_t *X, int M, int K, int N, int batch,
                               const uint16_t *sw, const uint16_t *L1, const uint16_t *L2,
                               int r, const uint16_t *bias, void *Y, int y_dtype,
                               void *workspace, size_t ws_bytes, int kernel, void *stream) {
-  return run_linear(X, M, K, N, batch, group, lambda, packed_w, sw, L1, L2, r, bias, Y, y_dtype,
-                    workspace, ws_bytes, kernel, stream, nullptr, 0, 0, 0, 0);
+  return debug_check(run_linear(X, M, K, N, batch, group, lambda, packed_w, sw, L1, L2, r, bias, Y, y_dtype,
+                    workspace, ws_bytes, kernel, stream, nullptr, 0, 0, 0, 0), stream);
 }
 
 int hsq_w4a4_quantize_stage(const uint16_t *X, int M, int K, int N, int batch,
                             const uint16_t *lambda, const uint16_t *L1, int r, void *workspace,
                             size_t ws_bytes, void *stream) {
-  return quantize_stage_g(X, M, K, N, batch, kGroup, lambda, L1, r, workspace, ws_bytes, stream);
+  return debug_check(quantize_stage_g(X, M, K, N, batch, kGroup, lambda, L1, r, workspace, ws_bytes, stream), stream);
 }
 
 int hsq_w4a4_quantize_stage_g(const uint16_t *X, int M, int K, int N, int batch, int group,
                               const uint16_t *lambda, const uint16_t *L1, int r, void *workspace,
                               size_t ws_bytes, void *stream) {
-  return quantize_stage_g(X, M, K, N, batch, group, lambda, L1, r, workspace, ws_bytes, stream);
+  return debug_check(quantize_stage_g(X, M, K, N, batch, group, lambda, L1, r, workspace, ws_bytes, stream), stream);
 }
 
 int hsq_w4a4_contract_stage(int M, int K, int N, int batch, const uint8_t *packed_w,
                             const uint16_t *sw, const uint16_t *L2, int r, const uint16_t *bias,
                             void *Y, int y_dtype, void *workspace, size_t ws_bytes, int kernel,
                             void *stream) {
-  return contract_stage_g(M, K, N, batch, kGroup, packed_w, sw, L2, r, bias, Y, y_dtype, workspace,
-                          ws_bytes, kernel, stream);
+  return debug_check(contract_stage_g(M, K, N, batch, kGroup, packed_w, sw, L2, r, bias, Y, y_dtype, workspace,
+                          ws_bytes, kernel, stream), stream);
 }
 
 int hsq_w4a4_contract_stage_g(int M, int K, int N, int batch, int group, const uint8_t *packed_w,
                               const uint16_t *sw, const uint16_t *L2, int r, const uint16_t *bias,
                               void *Y, int y_dtype, void *workspace, size_t ws_bytes, int kernel,
                               void *stream) {
-  return contract_stage_g(M, K, N, batch, group, packed_w, sw, L2, r, bias, Y, y_dtype, workspace,
-                          ws_bytes, kernel, stream);
+  return debug_check(contract_stage_g(M, K, N, batch, group, packed_w, sw, L2, r, bias, Y, y_dtype, workspace,
+                          ws_bytes, kernel, stream), stream);
 }
 
 int hsq_w4a4_group_partials(const uint16_t *X, int M, int K, int N, const uint16_t *lambda,
                             const uint8_t *packed_w, int m0, int mc, int n0, int nc,
                             int32_t *P, void *workspace, size_t ws_bytes, int kernel,
                             void *stream) {
-  return group_partials_g(X, M, K, N, kGroup, lambda, packed_w, m0, mc, n0, nc, P, workspace,
-                          ws_bytes, kernel, stream);
+  return debug_check(group_partials_g(X, M, K, N, kGroup, lambda, packed_w, m0, mc, n0, nc, P, workspace,
+                          ws_bytes, kernel, stream), stream);
 }
 
 int hsq_w4a4_group_partials_g(const uint16_t *X, int M, int K, int N, int group,
                               const uint16_t *lambda, const uint8_t *packed_w, int m0, int mc,
                               int n0, int nc, int32_t *P, void *workspace, size_t ws_bytes,
                               int kernel, void *stream) {
-  return group_partials_g(X, M, K, N, group, lambda, packed_w, m0, mc, n0, nc, P, workspace,
-                          ws_bytes, kernel, stream);
+  return debug_check(group_partials_g(X, M, K, N, group, lambda, packed_w, m0, mc, n0, nc, P, workspace,
+                          ws_bytes, kernel, stream), stream);
 }
 
 int hsq_w4a4_lowrank_linear_aq(const uint16_t *X, int M, int K, int N, int batch, int group,
@@ -546,16 +568,16 @@ int hsq_w4a4_lowrank_linear_aq(const uint16_t *X, int M, int K, int N, int batch
                                const uint16_t *bias, void *Y, int y_dtype, void *workspace,
                                size_t ws_bytes, int kernel, void *stream) {
   if (!aq_ok(act_quant)) return HSQ_E_INVAL;
-  return run_linear(X, M, K, N, batch, group, lambda, packed_w, sw, L1, L2, r, bias, Y, y_dtype,
-                    workspace, ws_bytes, kernel, stream, nullptr, 0, 0, 0, 0, act_quant);
+  return debug_check(run_linear(X, M, K, N, batch, group, lambda, packed_w, sw, L1, L2, r, bias, Y, y_dtype,
+                    workspace, ws_bytes, kernel, stream, nullptr, 0, 0, 0, 0, act_quant), stream);
 }
 
 int hsq_w4a4_quantize_stage_aq(const uint16_t *X, int M, int K, int N, int batch, int group,
                                int act_quant, const uint16_t *lambda, const uint16_t *L1, int r,
                                void *workspace, size_t ws_bytes, void *stream) {
   if (!aq_ok(act_quant)) return HSQ_E_INVAL;
-  return quantize_stage_g(X, M, K, N, batch, group, lambda, L1, r, workspace, ws_bytes, stream,
-                          act_quant);
+  return debug_check(quantize_stage_g(X, M, K, N, batch, group, lambda, L1, r, workspace, ws_bytes, stream,
+                          act_quant), stream);
 }
 
 int hsq_w4a4_group_partials_aq(const uint16_t *X, int M, int K, int N, int group, int act_quant,
@@ -563,8 +585,8 @@ int hsq_w4a4_group_partials_aq(const uint16_t *X, int M, int K, int N, int group
                                int n0, int nc, int32_t *P, void *workspace, size_t ws_bytes,
                                int kernel, void *stream) {
   if (!aq_ok(act_quant)) return HSQ_E_INVAL;
-  return group_partials_g(X, M, K, N, group, lambda, packed_w, m0, mc, n0, nc, P, workspace,
-                          ws_bytes, kernel, stream, act_quant);
+  return debug_check(group_partials_g(X, M, K, N, group, lambda, packed_w, m0, mc, n0, nc, P, workspace,
+                          ws_bytes, kernel, stream, act_quant), stream);
 }
 
 // ---------------------------------------------------------------- MX-fp4 variant
@@ -579,7 +601,7 @@ int hsq_mx_pack_weights(const float *R, int K, int N, uint8_t *packed, void *str
   if (K % kGroup != 0) return HSQ_E_SHAPE;
   if ((long long)K * N >= INT_MAX) return HSQ_E_INVAL;
   if (!aligned16(R) || !aligned16(packed)) return HSQ_E_ALIGN;
-  return hip_status(launch_mx_pack(R, K, N, packed, (hipStream_t)stream));
+  return debug_check(hip_status(launch_mx_pack(R, K, N, packed, (hipStream_t)stream)), stream);
 }
 
 size_t hsq_mx_workspace_bytes(int M, int K, int r) {
@@ -611,7 +633,7 @@ int hsq_mx_lowrank_linear(const uint16_t *X, int M, int K, int N, const uint16_t
   a.Y = Y; a.y_bf16 = y_dtype == HSQ_BF16;
   a.M = M; a.K = K; a.N = N; a.r = r; a.KS = L.KS; a.KS4 = L.KS4; a.Mpad = L.Mpad;
   a.u_slices = L.KS4;
-  return hip_status(launch_mx_linear(a, (hipStream_t)stream));
+  return debug_check(hip_status(launch_mx_linear(a, (hipStream_t)stream)), stream);
 }
 
 // ---------------------------------------------------------------- fused chain
@@ -628,9 +650,9 @@ int hsq_w4a4_lowrank_mlp(const uint16_t *X, int M, int K, int H, int N, const ui
                          const uint16_t *sw_down, const uint16_t *L1_down, const uint16_t *L2_down,
                          int r_down, const uint16_t *bias_down, void *Y, int y_dtype, float *Y_hidden,
                          void *workspace, size_t ws_bytes, void *stream) {
-  return run_chain(X, M, K, H, N, lambda_up, packed_up, sw_up, L1_up, L2_up, r_up, bias_up, act,
+  return debug_check(run_chain(X, M, K, H, N, lambda_up, packed_up, sw_up, L1_up, L2_up, r_up, bias_up, act,
                    lambda_down, packed_down, sw_down, L1_down, L2_down, r_down, bias_down, Y, y_dtype,
-                   Y_hidden, workspace, ws_bytes, stream);
+                   Y_hidden, workspace, ws_bytes, stream), stream);
 }
 
 // ---------------------------------------------------------------- calibration
@@ -654,7 +676,7 @@ int hsq_hessian_accumulate(const uint16_t *X, int M, int K, const uint16_t *lamb
   HessArgs a{};
   a.X = X; a.lam = lambda; a.H = H; a.M = M; a.K = K; a.accumulate = accumulate;
   a.part = (float *)workspace;
-  return hip_status(launch_hessian(a, (hipStream_t)stream));
+  return debug_check(hip_status(launch_hessian(a, (hipStream_t)stream)), stream);
 }
 
 size_t hsq_deflate_workspace_bytes(int K, int r) {
@@ -675,7 +697,7 @@ int hsq_deflate_hessian(const float *H, int K, const uint16_t *L1, int r, float 
   a.H = H; a.Hperp = Hperp; a.L1 = L1; a.HL1 = HL1; a.Cinv = Cinv; a.K = K; a.r = r;
   a.L1f = (float *)workspace;
   a.Cpart = (double *)((char *)workspace + align_up((size_t)K * rank_pad(r) * sizeof(float), 256));
-  return hip_status(launch_deflate(a, (hipStream_t)stream));
+  return debug_check(hip_status(launch_deflate(a, (hipStream_t)stream)), stream);
 }
 
 size_t hsq_closed_form_l2_workspace_bytes(int K, int N, int r) {
@@ -700,7 +722,7 @@ int hsq_closed_form_l2(const float *HL1, const double *Cinv, int K, int N, int r
   a.HL1 = HL1; a.Cinv = Cinv; a.W = W; a.packed = packed_w; a.sw = sw; a.L2 = L2;
   a.Tpart = (float *)workspace;
   a.K = K; a.N = N; a.r = r; a.group = group;
-  return hip_status(launch_l2(a, (hipStream_t)stream));
+  return debug_check(hip_status(launch_l2(a, (hipStream_t)stream)), stream);
 }
 
 }  // extern "C"
