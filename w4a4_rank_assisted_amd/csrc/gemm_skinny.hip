@@ -186,14 +186,14 @@ __global__ __launch_bounds__(64 * max_waves(MT)) void k_gemm_skinny(GemmArgs a, 
     const int c = p / (MT * 16), row = p % (MT * 16);
     const float *up = a.uw + ((size_t)proj * a.r + c) * a.Mpad + row;
     const size_t sstride = (size_t)a.ucols * a.Mpad;
-    float us[kMaxUSlices];                              // the first slices loaded together
+    float us[kMaxUSlicesSkinny];                        // the first slices loaded together
 #pragma unroll
-    for (int sl = 0; sl < kMaxUSlices; ++sl) us[sl] = up[(size_t)min(sl, a.u_slices - 1) * sstride];
+    for (int sl = 0; sl < kMaxUSlicesSkinny; ++sl) us[sl] = up[(size_t)min(sl, a.u_slices - 1) * sstride];
     float u = 0.0f;
 #pragma unroll
-    for (int sl = 0; sl < kMaxUSlices; ++sl)
+    for (int sl = 0; sl < kMaxUSlicesSkinny; ++sl)
       if (sl < a.u_slices) u += us[sl];
-    for (int sl = kMaxUSlices; sl < a.u_slices; ++sl) u += up[(size_t)sl * sstride];
+    for (int sl = kMaxUSlicesSkinny; sl < a.u_slices; ++sl) u += up[(size_t)sl * sstride];
     eu[p] = u;
   }
   for (int p = tid; p < ELN; p += nthr)

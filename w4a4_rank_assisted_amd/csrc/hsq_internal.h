@@ -16,6 +16,7 @@ constexpr int kMaxRank = 32;     // largest rank r of the high-precision branch
 constexpr int kMaxBatch = 16;    // projections sharing one input
 constexpr int kRankBlock = 32;   // rank columns one quantization pass accumulates
 constexpr int kMaxUSlices = 8;   // U slices the contraction kernels prefetch (more: summed in a loop)
+constexpr int kMaxUSlicesSkinny = 16;  // U slices the skinny contraction prefetches
 constexpr int kMaxSliceGroups = 192;  // groups per workgroup of the quantization pass (LDS)
 constexpr int kQuantActMaxK = kMaxSliceGroups * kGroup;  // hsq_quantize_act: one slice
 

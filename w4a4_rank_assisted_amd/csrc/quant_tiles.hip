@@ -70,6 +70,11 @@ TilePlan tile_plan(int M, int K, int r, int batch, int group) {
   const int want = ceil_div(kTargetWaves, MT * 4);
   const int more = want < kMaxUSlices ? want : kMaxUSlices;
   if (more > S) S = more;
+  // few tokens: the pass is a chain of latencies, so no wave takes a second
+  // unit -- at most 16 units per slice, one per wave of a 16-wave workgroup
+  // (Qwen3 down at 16 tokens: 8 slices of 24 units, 17.0 us per layer, ->
+  // 12 slices of 16; the skinny contraction prefetches up to 16 U slices)
+  if (M <= kSkinnyMaxM && S < ceil_div(Gp, 16)) S = ceil_div(Gp, 16);
   if (S > Gp) S = Gp;
   p.gpb = ceil_div(Gp, S);
   p.slices = ceil_div(Gp, p.gpb);
