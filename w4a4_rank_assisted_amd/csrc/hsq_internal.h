@@ -425,5 +425,57 @@ __device__ __forceinline__ float gelu_tanh_f32(float y) {
   return y / (1.0f + exp_f32_basic(-2.0f * z));
 }
 
+// Direct-to-LDS staging, shared by the tiled int4 and the MX contraction.
+//
+// End of a stage: this wave's loads (the next stage's direct-to-LDS blocks
+// and its scale loads, all issued this stage) and its LDS reads and writes
+// are complete, then the workgroup barrier.  After it every wave sees the
+// next stage's operands in LDS, and no wave still reads the buffer the
+// following stage's loads will overwrite.  (__syncthreads would add a
+// release fence, which waits the same way but also stops the compiler from
+// keeping loads in flight across it; here nothing is in flight.)
+__device__ __forceinline__ void stage_barrier() {
+  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// Direct-to-LDS load of one 1 KB operand block (buffer_load_dwordx4 ...
+// lds): lane l's 16 bytes, at voffset + soffset of the buffer resource rs
+// (four dwords: base, stride, size, flags), land at LDS byte address
+// lds + 16 l.  Written as an instruction of its own so that the compiler
+// neither waits for it (the loads of stage s+1 stay in flight while stage s
+// reads the other buffer) nor moves LDS accesses across it; stage_barrier
+// is the wait.  It has no register results.
+__device__ __forceinline__ void block_to_lds(v4u rs, uint32_t lds, uint32_t voffset, uint32_t soffset) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+               :
+               : "s"(lds), "v"(voffset), "s"(rs), "s"(soffset)
+               : "memory", "m0");
+}
+
+// The same for one dword per lane (256 bytes per wave): lane l's 4 bytes
+// land at lds + 4 l.
+__device__ __forceinline__ void dword_to_lds(v4u rs, uint32_t lds, uint32_t voffset, uint32_t soffset) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, %3 offen lds"
+               :
+               : "s"(lds), "v"(voffset), "s"(rs), "s"(soffset)
+               : "memory", "m0");
+}
+
+// A raw buffer resource as four scalar dwords (the layout the buffer
+// instructions read): 48-bit base, stride 0, size in bytes (reads past it
+// return zero), the same flags as buffer_rsrc.
+__device__ __forceinline__ v4u raw_rsrc(const void *p, uint32_t bytes) {
+  const uint64_t a = (uint64_t)(uintptr_t)p;
+  return (v4u){(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)a),
+               (uint32_t)__builtin_amdgcn_readfirstlane((int)((uint32_t)(a >> 32) & 0xFFFFu)),
+               (uint32_t)__builtin_amdgcn_readfirstlane((int)bytes), 0x00020000u};
+}
+
+// LDS byte address of a __shared__ object (for m0).
+__device__ __forceinline__ uint32_t lds_addr(const void *p) {
+  return (uint32_t)__builtin_amdgcn_readfirstlane(
+      (int)(uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char *)p);
+}
+
 }  // namespace hsq
 #endif

@@ -185,40 +185,43 @@ __global__ __launch_bounds__(256) void k_mx_quant(MxArgs a) {
   }
 }
 
-template <int V>
-struct int_c {
-  static constexpr int value = V;
-};
+// The residual contraction with the epilogue.  Workgroup 128 x 128 outputs:
+// 2 x 4 waves, each 64 x 32 = 4 x 2 MFMA tiles.  A stage is two k-steps
+// (256 channels): wave w moves A tile w and B tile w of both k-steps global
+// -> LDS with direct-to-LDS loads (four 1 KB blocks, no register staging),
+// into one of two stage buffers; the loads of stage t + 1 are issued as
+// stage t starts, and one barrier ends each stage (the wait of
+// stage_barrier covers the loads).  The e8m0 scales (one dword per tile and
+// lane for a group of four k-steps, byte j = k-step 4g + j) move the same
+// way, one group ahead, into one of two scale buffers; a wave reads its
+// tiles' dwords at the first stage of each group.  An odd last k-step
+// skips the second half of its stage.  Workgroups walk the tiles in the
+// XCD-grouped order of xcd_tile_of.  The epilogue operands (U summed over
+// its K-slices in order, L2, bias) are loaded with the first stage for rank
+// up to 4, after the last one into the then free stage buffers otherwise
+// (their arrays would not leave room for two workgroups per CU).
+template <int RPT, int GROUPM = 8>
+__global__ __launch_bounds__(512, 2) void k_mx_gemm(MxArgs a) {
+  constexpr int TMW = 4, TNW = 2, WGM = 2, WGN = 4, NTHR = 64 * WGM * WGN;
+  constexpr int AT = TMW * WGM, BT = TNW * WGN;           // tiles of the workgroup (one per wave)
+  static_assert(AT == NTHR / 64 && BT == NTHR / 64, "wave w moves A tile w and B tile w");
+  constexpr int BMR = AT * 16, BNC = BT * 16;             // rows, columns of the workgroup
+  constexpr int KSS = 2;                                  // k-steps per stage
+  struct Ops {
+    uint8_t a[KSS][AT][64][16];
+    uint8_t b[KSS][BT][64][16];
+  };
+  __shared__ alignas(16) Ops ops[2];
+  __shared__ uint32_t ssc[2][(AT + BT) * 64];             // [group parity][A tiles, then B tiles][lane]
+  constexpr bool EARLY = RPT <= 4;                        // epilogue operands with the first stage
+  constexpr int RE = RPT > 0 ? RPT : 1;
+  __shared__ float epi_early[EARLY ? 2 * RE * 128 + 128 : 1];
+  static_assert(RE * BMR * 4 <= (int)sizeof(ops[1].a) && RE * BNC * 4 <= (int)sizeof(ops[1].b) &&
+                BNC * 4 <= (int)sizeof(ops[0].b), "late epilogue operands fit the stage buffers");
+  float *eu = EARLY ? epi_early : reinterpret_cast<float *>(&ops[1].a[0][0][0][0]);          // [RPT][BMR]
+  float *el2 = EARLY ? epi_early + RE * BMR : reinterpret_cast<float *>(&ops[1].b[0][0][0][0]);  // [RPT][BNC]
+  float *eb = EARLY ? epi_early + 2 * RE * 128 : reinterpret_cast<float *>(&ops[0].b[0][0][0][0]);  // [BNC]
 
-// The residual contraction with the epilogue.  A workgroup of WGM x WGN
-// waves owns (TMW * WGM) x (TNW * WGN) MFMA tiles; each wave TMW x TNW of
-// them.  One k-step (128 channels) per stage; the operand blocks go
-// global -> registers -> LDS with the loads of stage s + 2 issued at the
-// start of stage s into one of two register slots (slot = stage parity,
-// fixed at compile time by unrolling), two LDS buffers, one barrier per
-// stage.  The e8m0 scales (one dword per tile and lane for four k-steps,
-// byte j picked by a shift) ride the same pipeline: a group of four
-// k-steps needs (AT + BT) x 64 dwords, loaded a quarter per stage with the
-// operands of the group before and written into one of two LDS scale
-// buffers, so that the first stage of a group reads its scales from LDS
-// instead of waiting on memory.  Workgroups walk the tiles in the
-// XCD-grouped order of xcd_tile_of.
-template <int TMW, int TNW, int WGM, int WGN, int RPT, int GROUPM = 8>
-__global__ __launch_bounds__(64 * WGM * WGN, 2) void k_mx_gemm(MxArgs a) {
-  constexpr int NTHR = 64 * WGM * WGN;
-  constexpr int AT = TMW * WGM, BT = TNW * WGN;          // tiles of the workgroup
-  constexpr int LA = AT * 64 / NTHR, LB = BT * 64 / NTHR; // 16-byte slots per thread and stage
-  static_assert(AT * 64 % NTHR == 0 && BT * 64 % NTHR == 0, "whole slots per thread");
-  constexpr int BMR = AT * 16, BNC = BT * 16;            // rows, columns of the workgroup
-  __shared__ alignas(16) uint8_t opa[2][AT][64][16];
-  __shared__ alignas(16) uint8_t opb[2][BT][64][16];
-  constexpr int SCW = (AT + BT) * 64;                     // scale dwords of a group of four k-steps
-  constexpr int SQ = SCW / 4;                             // scale dwords per stage: a quarter of a group's
-  static_assert(AT == BT && SQ % 64 == 0 && SQ <= NTHR, "quarters 0, 1: A tiles; 2, 3: B tiles; one dword per thread");
-  __shared__ uint32_t ssc[2][SCW];                        // [group parity][A tiles, then B tiles][lane]
-  __shared__ float eu[RPT > 0 ? RPT : 1][BMR];
-  __shared__ float el2[RPT > 0 ? RPT : 1][BNC];
-  __shared__ float ebias[BNC];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / WGN, wn = wave % WGN;
@@ -227,14 +230,50 @@ __global__ __launch_bounds__(64 * WGM * WGN, 2) void k_mx_gemm(MxArgs a) {
   xcd_tile_of(blockIdx.x, nblk, mblk, GROUPM, mb, nb);
   const int mt0 = mb * AT, nt0 = nb * BT;
   const int MT = a.Mpad / 16, NT = (a.N + 15) / 16;
-  const int KS = a.KS, KS4 = a.KS4;
-  // buffer loads: one per-lane offset, the tile and k-step in a scalar
-  // offset (the tile a thread loads depends on its wave only)
-  const __amdgpu_buffer_rsrc_t rs_qa = buffer_rsrc(a.qa, (uint32_t)MT * KS * 1024);
-  const __amdgpu_buffer_rsrc_t rs_wq = buffer_rsrc(a.wq, (uint32_t)NT * KS * 1024);
-  const __amdgpu_buffer_rsrc_t rs_sa = buffer_rsrc(a.sa, (uint32_t)MT * KS4 * 256);
-  const __amdgpu_buffer_rsrc_t rs_sb = buffer_rsrc(a.ws, (uint32_t)NT * KS4 * 256);
+  const int KS = a.KS, KS4 = a.KS4, nst = (KS + 1) / 2;
+  // tiles past the matrix reload the last one (their outputs are not stored)
+  const int ta = min(mt0 + wave, MT - 1), tb = min(nt0 + wave, NT - 1);
+  const v4u rq = raw_rsrc(a.qa, (uint32_t)MT * KS * 1024), rw = raw_rsrc(a.wq, (uint32_t)NT * KS * 1024);
+  const v4u rsa = raw_rsrc(a.sa, (uint32_t)MT * KS4 * 256), rsb = raw_rsrc(a.ws, (uint32_t)NT * KS4 * 256);
   const uint32_t vo16 = (uint32_t)lane * 16, vo4 = (uint32_t)lane * 4;
+
+  auto issue_stage = [&](int t, int buf) __attribute__((always_inline)) {
+#pragma unroll
+    for (int kk = 0; kk < KSS; ++kk) {
+      const int k = min(KSS * t + kk, KS - 1);
+      block_to_lds(rq, lds_addr(&ops[buf].a[kk][wave][0][0]), vo16, (uint32_t)(ta * KS + k) * 1024u);
+      block_to_lds(rw, lds_addr(&ops[buf].b[kk][wave][0][0]), vo16, (uint32_t)(tb * KS + k) * 1024u);
+    }
+  };
+  auto issue_scales = [&](int g) __attribute__((always_inline)) {
+    uint32_t *dst = ssc[g & 1];
+    dword_to_lds(rsa, lds_addr(dst + wave * 64), vo4, (uint32_t)(ta * KS4 + g) * 256u);
+    dword_to_lds(rsb, lds_addr(dst + (AT + wave) * 64), vo4, (uint32_t)(tb * KS4 + g) * 256u);
+  };
+  auto load_epilogue = [&]() __attribute__((always_inline)) {
+    for (int p = tid; p < RPT * BMR; p += NTHR) {
+      const int c = p / BMR, rr = p % BMR, m = mt0 * 16 + rr;
+      const int cc = min(c, a.r - 1), mm = min(m, a.Mpad - 1);
+      float us[kMaxUSlices];
+#pragma unroll
+      for (int sl = 0; sl < kMaxUSlices; ++sl)
+        us[sl] = a.U[((size_t)min(sl, a.u_slices - 1) * a.r + cc) * a.Mpad + mm];
+      float u = 0.0f;
+#pragma unroll
+      for (int sl = 0; sl < kMaxUSlices; ++sl)
+        if (sl < a.u_slices) u += us[sl];
+      for (int sl = kMaxUSlices; sl < a.u_slices; ++sl) u += a.U[((size_t)sl * a.r + cc) * a.Mpad + mm];
+      eu[c * BMR + rr] = (c < a.r && m < a.M) ? u : 0.0f;
+    }
+    for (int p = tid; p < RPT * BNC; p += NTHR) {
+      const int c = p / BNC, cc = p % BNC, n = nt0 * 16 + cc;
+      el2[c * BNC + cc] = (c < a.r && n < a.N) ? bf16_to_f32(a.L2[(size_t)c * a.N + n]) : 0.0f;
+    }
+    for (int p = tid; p < BNC; p += NTHR) {
+      const int n = nt0 * 16 + p;
+      eb[p] = (a.bias && n < a.N) ? bf16_to_f32(a.bias[n]) : 0.0f;
+    }
+  };
 
   v4f acc[TMW][TNW];
 #pragma unroll
@@ -242,136 +281,61 @@ __global__ __launch_bounds__(64 * WGM * WGN, 2) void k_mx_gemm(MxArgs a) {
 #pragma unroll
     for (int j = 0; j < TNW; ++j) acc[i][j] = (v4f){0.f, 0.f, 0.f, 0.f};
 
-  // the scale dword of quarter P of a group: A tiles (P = 0, 1: tiles 4P ..
-  // 4P + 3) or B tiles (P = 2, 3), one lane slot per thread
-  auto scale_word = [&](int g, auto pc) __attribute__((always_inline)) -> uint32_t {
-    constexpr int P = decltype(pc)::value;
-    const int tile = (P & 1) * (SQ / 64) + wave;      // (threads tid < SQ, waves wave < SQ / 64)
-    if constexpr (P < 2)
-      return __builtin_amdgcn_raw_buffer_load_b32(rs_sa, vo4, (min(mt0 + tile, MT - 1) * KS4 + g) * 256, 0);
-    else
-      return __builtin_amdgcn_raw_buffer_load_b32(rs_sb, vo4, (min(nt0 + tile, NT - 1) * KS4 + g) * 256, 0);
-  };
-  v4u ra[2][LA], rb[2][LB];
-  uint32_t rs[2];
-  // operands of k-step ks and quarter P = ks % 4 of the next group's scales
-  auto load = [&](int ks, auto sc, auto pc) __attribute__((always_inline)) {
-    constexpr int SL = decltype(sc)::value;
-    const int k = min(ks, KS - 1);                   // past the end: a clamped, unused reload
-#pragma unroll
-    for (int u = 0; u < LA; ++u)
-      ra[SL][u] = __builtin_amdgcn_raw_buffer_load_b128(rs_qa, vo16, (min(mt0 + wave + u * (NTHR / 64), MT - 1) * KS + k) * 1024, 0);
-#pragma unroll
-    for (int u = 0; u < LB; ++u)
-      rb[SL][u] = __builtin_amdgcn_raw_buffer_load_b128(rs_wq, vo16, (min(nt0 + wave + u * (NTHR / 64), NT - 1) * KS + k) * 1024, 0);
-    if (SQ == NTHR || tid < SQ) rs[SL] = scale_word(min(ks / 4 + 1, KS4 - 1), pc);
-  };
-  auto store = [&](int buf, int ks, auto sc, auto pc) __attribute__((always_inline)) {
-    constexpr int SL = decltype(sc)::value;
-    constexpr int P = decltype(pc)::value;
-#pragma unroll
-    for (int u = 0; u < LA; ++u)
-      *reinterpret_cast<v4u *>(&opa[buf][(tid >> 6) + u * (NTHR / 64)][lane][0]) = ra[SL][u];
-#pragma unroll
-    for (int u = 0; u < LB; ++u)
-      *reinterpret_cast<v4u *>(&opb[buf][(tid >> 6) + u * (NTHR / 64)][lane][0]) = rb[SL][u];
-    if (SQ == NTHR || tid < SQ) ssc[(ks / 4 + 1) & 1][P * SQ + tid] = rs[SL];
-  };
-
-  // prologue: group 0's scales, the first two k-steps' operands and the
-  // epilogue operands all in flight together, so the first stores wait on
-  // one memory round trip
-  uint32_t s0[4] = {0u, 0u, 0u, 0u};
-  if (SQ == NTHR || tid < SQ) {
-    s0[0] = scale_word(0, int_c<0>{});
-    s0[1] = scale_word(0, int_c<1>{});
-    s0[2] = scale_word(0, int_c<2>{});
-    s0[3] = scale_word(0, int_c<3>{});
-  }
-  load(0, int_c<0>{}, int_c<0>{});
-  load(1, int_c<1>{}, int_c<1>{});
-  // epilogue operands: U (its K-slices summed in order; the first
-  // kMaxUSlices loaded together, clamped addresses), L2, bias
-  for (int p = tid; p < RPT * BMR; p += NTHR) {
-    const int c = p / BMR, rr = p % BMR, m = mt0 * 16 + rr;
-    const int cc = min(c, a.r - 1), mm = min(m, a.Mpad - 1);
-    float us[kMaxUSlices];
-#pragma unroll
-    for (int sl = 0; sl < kMaxUSlices; ++sl)
-      us[sl] = a.U[((size_t)min(sl, a.u_slices - 1) * a.r + cc) * a.Mpad + mm];
-    float u = 0.0f;
-#pragma unroll
-    for (int sl = 0; sl < kMaxUSlices; ++sl)
-      if (sl < a.u_slices) u += us[sl];
-    for (int sl = kMaxUSlices; sl < a.u_slices; ++sl) u += a.U[((size_t)sl * a.r + cc) * a.Mpad + mm];
-    eu[c][rr] = (c < a.r && m < a.M) ? u : 0.0f;
-  }
-  for (int p = tid; p < RPT * BNC; p += NTHR) {
-    const int c = p / BNC, cc = p % BNC, n = nt0 * 16 + cc;
-    el2[c][cc] = (c < a.r && n < a.N) ? bf16_to_f32(a.L2[(size_t)c * a.N + n]) : 0.0f;
-  }
-  for (int p = tid; p < BNC; p += NTHR) {
-    const int n = nt0 * 16 + p;
-    ebias[p] = (a.bias && n < a.N) ? bf16_to_f32(a.bias[n]) : 0.0f;
-  }
-  if (SQ == NTHR || tid < SQ) {
-    ssc[0][tid] = s0[0];
-    ssc[0][SQ + tid] = s0[1];
-    ssc[0][2 * SQ + tid] = s0[2];
-    ssc[0][3 * SQ + tid] = s0[3];
-  }
-  store(0, 0, int_c<0>{}, int_c<0>{});
-  __syncthreads();
+  issue_scales(0);
+  issue_stage(0, 0);
+  if constexpr (EARLY) load_epilogue();
+  stage_barrier();
 
   uint32_t scA[TMW], scB[TNW];
-  // stage ks: J = ks % 4 (scale byte), slot and buffer = ks % 2
-  auto stage = [&](int ks, auto jc) __attribute__((always_inline)) {
-    constexpr int J = decltype(jc)::value;
-    constexpr int SL = J & 1;
-    if (J == 0) {
-      const uint32_t *sc = ssc[(ks >> 2) & 1];
+  for (int t = 0; t < nst; ++t) {
+    const int buf = t & 1;
+    if (t + 1 < nst) issue_stage(t + 1, buf ^ 1);
+    if ((t & 1) == 0) {
+      // first stage of group g: its scales arrived a stage ago (or in the
+      // prologue); the next group's go to the other scale buffer, whose
+      // last readers finished before the previous barrier
+      const int g = t >> 1;
+      const uint32_t *sc = ssc[g & 1];
 #pragma unroll
       for (int i = 0; i < TMW; ++i) scA[i] = sc[(wm * TMW + i) * 64 + lane];
 #pragma unroll
-      for (int j = 0; j < TNW; ++j) scB[j] = sc[AT * 64 + (wn * TNW + j) * 64 + lane];
-    }
-    load(ks + 2, int_c<SL>{}, int_c<(J + 2) & 3>{});  // this slot's data went to LDS a stage ago
-    v8i bv[TNW];
-#pragma unroll
-    for (int j = 0; j < TNW; ++j) {
-      const v4u v = *reinterpret_cast<const v4u *>(&opb[SL][wn * TNW + j][lane][0]);
-      bv[j] = (v8i){(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
+      for (int j = 0; j < TNW; ++j) scB[j] = sc[(AT + wn * TNW + j) * 64 + lane];
+      if (g + 1 < KS4) issue_scales(g + 1);
     }
 #pragma unroll
-    for (int i = 0; i < TMW; ++i) {
-      const v4u v = *reinterpret_cast<const v4u *>(&opa[SL][wm * TMW + i][lane][0]);
-      const v8i av = (v8i){(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
-      const int sa_b = (int)((scA[i] >> (8 * J)) & 0xFFu);
+    for (int kk = 0; kk < KSS; ++kk) {
+      if (kk > 0 && KSS * t + kk >= KS) break;          // odd last k-step (uniform)
+      const int J = 2 * (t & 1) + kk;                    // scale byte of this k-step
+      v8i bv[TNW];
 #pragma unroll
-      for (int j = 0; j < TNW; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv[j], acc[i][j], 4, 4, 0, sa_b, 0,
-                                                                     (int)((scB[j] >> (8 * J)) & 0xFFu));
+      for (int j = 0; j < TNW; ++j) {
+        const v4u v = *reinterpret_cast<const v4u *>(&ops[buf].b[kk][wn * TNW + j][lane][0]);
+        bv[j] = (v8i){(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
+      }
+#pragma unroll
+      for (int i = 0; i < TMW; ++i) {
+        const v4u v = *reinterpret_cast<const v4u *>(&ops[buf].a[kk][wm * TMW + i][lane][0]);
+        const v8i av = (v8i){(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
+        const int sa_b = (int)((scA[i] >> (8 * J)) & 0xFFu);
+#pragma unroll
+        for (int j = 0; j < TNW; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv[j], acc[i][j], 4, 4, 0, sa_b, 0,
+                                                                       (int)((scB[j] >> (8 * J)) & 0xFFu));
+      }
     }
-    if (ks + 1 < KS) store(SL ^ 1, ks + 1, int_c<SL ^ 1>{}, int_c<(J + 1) & 3>{});
-    __syncthreads();
-  };
-  int ks = 0;
-  for (; ks + 4 <= KS; ks += 4) {
-    stage(ks, int_c<0>{});
-    stage(ks + 1, int_c<1>{});
-    stage(ks + 2, int_c<2>{});
-    stage(ks + 3, int_c<3>{});
+    stage_barrier();
   }
-  if (ks < KS) stage(ks, int_c<0>{});
-  if (ks + 1 < KS) stage(ks + 1, int_c<1>{});
-  if (ks + 2 < KS) stage(ks + 2, int_c<2>{});
+  if constexpr (!EARLY) {
+    load_epilogue();
+    __syncthreads();
+  }
 
   // epilogue: Y = acc + U L2 + bias; per row tile the wave's 16 x WCOL
-  // values go through a wave-private LDS region (the operand buffers are
-  // free after the last barrier) and leave as 16-byte row-contiguous stores
+  // values go through a wave-private LDS region of stage buffer 0's A part
+  // and leave as 16-byte row-contiguous stores
   constexpr int WCOL = TNW * 16;
-  static_assert(WGM * WGN * 16 * WCOL * 4 <= (int)sizeof(opa), "transpose region");
-  char *tb = reinterpret_cast<char *>(&opa[0][0][0][0]) + wave * (16 * WCOL * 4);
+  static_assert(WGM * WGN * 16 * WCOL * 4 <= (int)sizeof(ops[0].a), "transpose region");
+  char *tbuf = reinterpret_cast<char *>(&ops[0].a[0][0][0][0]) + wave * (16 * WCOL * 4);
   const int rowq = 4 * (lane >> 4), colq = lane & 15;
   const int yb = a.y_bf16 ? 2 : 4, per16 = 16 / yb, cpr = WCOL / per16;
   const bool vec_ok = (a.N % per16) == 0;
@@ -386,13 +350,13 @@ __global__ __launch_bounds__(64 * WGM * WGN, 2) void k_mx_gemm(MxArgs a) {
         const int rr = (wm * TMW + i) * 16 + rowq + qq;
         float y = acc[i][j][qq];
 #pragma unroll
-        for (int c = 0; c < RPT; ++c) y = __builtin_fmaf(eu[c][rr], el2[c][cc], y);
-        y += ebias[cc];
+        for (int c = 0; c < RPT; ++c) y = __builtin_fmaf(eu[c * BMR + rr], el2[c * BNC + cc], y);
+        y += eb[cc];
         const int off = (rowq + qq) * WCOL + j * 16 + colq;
         if (a.y_bf16)
-          reinterpret_cast<uint16_t *>(tb)[off] = f32_to_bf16(y);
+          reinterpret_cast<uint16_t *>(tbuf)[off] = f32_to_bf16(y);
         else
-          reinterpret_cast<float *>(tb)[off] = y;
+          reinterpret_cast<float *>(tbuf)[off] = y;
       }
     }
     const int mrow0 = (mt0 + wm * TMW + i) * 16;
@@ -400,7 +364,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, 2) void k_mx_gemm(MxArgs a) {
       const int row = k / cpr, ch = k % cpr;
       const int m = mrow0 + row, n = ncol0 + ch * per16;
       if (m >= a.M || n >= a.N) continue;
-      const v4u v = *reinterpret_cast<const v4u *>(tb + (row * WCOL + ch * per16) * yb);
+      const v4u v = *reinterpret_cast<const v4u *>(tbuf + (row * WCOL + ch * per16) * yb);
       char *dst = reinterpret_cast<char *>(a.Y) + ((size_t)m * a.N + n) * yb;
       if (vec_ok && n + per16 <= a.N) {
         *reinterpret_cast<v4u *>(dst) = v;
@@ -417,15 +381,15 @@ __global__ __launch_bounds__(64 * WGM * WGN, 2) void k_mx_gemm(MxArgs a) {
   }
 }
 
-// workgroup 128 x 128: 2 x 4 waves of 64 x 32 (104 VGPRs, four waves per
-// SIMD).  Measured against 2 x 2 waves of 64 x 64 (248 VGPRs, two waves
-// per SIMD): 13 % faster at pixart size, 8 % on the FLUX and Qwen3 up
-// layers; a 256 x 128 workgroup ran at one wave per SIMD and was slower.
-template <int RP, int TMW>
+// workgroup 128 x 128: 2 x 4 waves of 64 x 32, two workgroups per CU.
+// Measured with the register-staged loads of an earlier version against
+// 2 x 2 waves of 64 x 64 (248 VGPRs, two waves per SIMD): 13 % faster at
+// pixart size, 8 % on the FLUX and Qwen3 up layers; a 256 x 128 workgroup
+// ran at one wave per SIMD and was slower.
+template <int RP>
 hipError_t launch_mx_gemm(const MxArgs &a, hipStream_t s) {
-  constexpr int TNW = 2, WGM = 2, WGN = 4;
-  const int tiles = ceil_div(a.N, 16 * TNW * WGN) * ceil_div(a.M, 16 * TMW * WGM);
-  hipLaunchKernelGGL((k_mx_gemm<TMW, TNW, WGM, WGN, RP>), dim3((unsigned)tiles), dim3(64 * WGM * WGN), 0, s, a);
+  const int tiles = ceil_div(a.N, 128) * ceil_div(a.M, 128);
+  hipLaunchKernelGGL((k_mx_gemm<RP>), dim3((unsigned)tiles), dim3(512), 0, s, a);
   return hipGetLastError();
 }
 
@@ -434,7 +398,7 @@ hipError_t launch_mx_rp(const MxArgs &a, hipStream_t s) {
   hipLaunchKernelGGL(k_mx_quant<RP>, dim3((unsigned)(a.Mpad / 16), (unsigned)a.u_slices), dim3(256), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  return launch_mx_gemm<RP, 4>(a, s);
+  return launch_mx_gemm<RP>(a, s);
 }
 
 }  // namespace
