@@ -213,6 +213,7 @@ def _sample_rows(M, n=48, seed=0):
 
 @pytest.mark.parametrize("name,M", [("pixart_up", None), ("sana_qkv", None), ("flux_up", None),
                                     ("flux_down", None), ("qwen3_up", 16), ("qwen3_down", 16),
+                                    ("qwen3_up", 64), ("qwen3_down", 64),    # four row tiles; 12 U slices
                                     ("qwen3_up", 256), ("qwen3_down", 256),
                                     ("qwen3_up", 2048), ("qwen3_down", 2048)])
 def test_full_size_outputs_sampled_rows(oracle, name, M):
