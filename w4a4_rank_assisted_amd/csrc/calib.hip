@@ -39,24 +39,27 @@ namespace hsq {
 namespace {
 
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef short v4s __attribute__((ext_vector_type(4)));
+typedef short v8s __attribute__((ext_vector_type(8)));
 
 // ---------------------------------------------------------------- Hessian
 constexpr int HB = 128;            // block of H (rows = columns)
 constexpr int HKC = 64;            // tokens per stage
 constexpr int HNT = 512;           // threads: 8 waves, 2 x 4, 64 x 32 each
-constexpr int HLD = HKC + 8;       // LDS pitch in bf16 (144 bytes: conflict-free 16-byte reads)
 constexpr int kHessFull = 0, kHessSplit = 1, kHessReduce = 2;
 constexpr int HTM = 4, HTN = 2;    // 16 x 16 tiles per wave
 constexpr int kHessAcc = HTM * HTN * 4;  // accumulators per thread
 
 struct alignas(16) HessSmem {
-  uint16_t t[2][2][HB][HLD];       // [buffer][A, B][channel in block][token in stage]
+  uint16_t t[2][2][HKC][HB];       // [buffer][row, column strip][token in stage][channel, swizzled]
 };
 
-template <int V>
-struct int_c {
-  static constexpr int value = V;
-};
+// Swizzle of a token row's sixteen 16-byte chunks (eight channels each):
+// logical chunk c sits at c ^ hess_swz(t).  The transposing reads of a k-step
+// touch four consecutive token rows and two adjacent chunks per 16-lane
+// group; with this even XOR the 32 lanes of two groups (tokens t .. t + 3 and
+// t + 8 .. t + 11) reach 16 distinct chunk positions.
+__device__ __forceinline__ int hess_swz(int t) { return 2 * ((t & 3) | (((t >> 3) & 1) << 2)); }
 
 constexpr int kSuper = 8;          // blocks per side of a super-block
 
@@ -126,52 +129,68 @@ __global__ __launch_bounds__(HNT, 2) void k_hessian(HessArgs a) {
     const int nst = (a.M + HKC - 1) / HKC, S = (int)gridDim.y, z = (int)blockIdx.y;
     const int s0 = z * nst / S, s1 = (z + 1) * nst / S;
     const int m_end = min(a.M, s1 * HKC);
-    // the first half of the threads loads the row strip (channels I0 ..),
-    // the second the column strip (J0 ..): thread t of a half loads tokens
-    // 4*(t%16) .. +3 of channels 8*(t/16) .. +7 (four 16-byte loads) and
-    // writes them transposed
-    const int strip = tid >> 8, t8 = tid & 255, c8 = t8 >> 4, r4 = t8 & 15;
-    const __amdgpu_buffer_rsrc_t rx = buffer_rsrc(a.X, (uint32_t)((size_t)a.M * a.K * 2));
-    const uint32_t kBad = 0x80000000u;                // past the buffer: the load returns 0
-    const int cs = (strip ? J0 : I0) + 8 * c8;
-    // two register slots: a stage's loads are issued two stages before its
-    // tiles are consumed (slot = stage parity, fixed by unrolling by two);
-    // tokens past the split's end load as zeros
-    v4u ra[2][4];
-    auto load = [&](int s, auto slotc) __attribute__((always_inline)) {
-      constexpr int SL = decltype(slotc)::value;
+    // Stage loads: waves 0-3 move the row strip (channels I0 ..), waves 4-7
+    // the column strip (J0 ..); wave w's four direct-to-LDS loads cover
+    // token rows 16 (w % 4) .. + 15 of the stage, four rows (1 KB) each.
+    // Lane l of a load fills token row 4d + l / 16 at physical chunk l % 16,
+    // i.e. logical chunk (l % 16) ^ hess_swz(row): the channels 8c .. 8c + 7
+    // of that token.  Tokens past the split's end and channels past K read
+    // zero (an offset past the buffer).
+    const v4u rx = raw_rsrc(a.X, (uint32_t)((size_t)a.M * a.K * 2));
+    const uint32_t kBad = 0x80000000u;
+    const int strip = wave >> 2, d0 = 4 * (wave & 3);
+    const int trow = lane >> 4;                             // token row within a load
+    const int cbase = strip ? J0 : I0;
+    auto issue = [&](int s, int buf) __attribute__((always_inline)) {
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        const int m = s * HKC + 4 * r4 + u;
-        const bool mok = m < m_end;
-        const uint32_t rowoff = (uint32_t)m * (uint32_t)a.K * 2u;
-        ra[SL][u] = __builtin_amdgcn_raw_buffer_load_b128(rx, (mok && cs < a.K) ? rowoff + cs * 2 : kBad, 0, 0);
+        const int t = 4 * (d0 + u) + trow, m = s * HKC + t;
+        const int ch = cbase + 8 * ((lane & 15) ^ hess_swz(t));
+        const uint32_t off = (m < m_end && ch < a.K) ? ((uint32_t)m * (uint32_t)a.K + (uint32_t)ch) * 2u : kBad;
+        block_to_lds(rx, lds_addr(&sm.t[buf][strip][4 * (d0 + u)][0]), off, 0u);
       }
     };
-    auto store = [&](auto slotc, int buf) __attribute__((always_inline)) {
-      constexpr int SL = decltype(slotc)::value;
+    // Operand reads: the MFMA's lane l takes channel (tile base) + l % 16 and
+    // tokens 8 (l / 16) .. + 7 of the k-step.  ds_read_b64_tr_b16 gives lane
+    // i of each 16-lane group element j = the 16-bit value at element i % 4
+    // of the 8 bytes that lane 4 j + i / 4 of the group addressed; so lane
+    // L = 4 jt + q addresses token jt (of four) and channels 4 q .. 4 q + 3,
+    // and two reads (tokens 0-3, then 4-7) give the eight values.  The
+    // swizzle of a token row depends only on jt and bit 3 of the token, both
+    // fixed per lane, so each tile's byte offset is fixed per lane.
+    const int g = lane >> 4, L = lane & 15, jt = L >> 2, q = L & 3;
+    const int sw = hess_swz(8 * g + jt);                    // = the swizzle of every token this lane reads
+    uint32_t offa[HTM], offb[HTN];
 #pragma unroll
-      for (int c = 0; c < 8; ++c) {
-        const int k = c >> 1;
-        const uint32_t sel = (c & 1) ? 0x07060302u : 0x05040100u;
-        const uint32_t lo = __builtin_amdgcn_perm(ra[SL][1][k], ra[SL][0][k], sel);
-        const uint32_t hi = __builtin_amdgcn_perm(ra[SL][3][k], ra[SL][2][k], sel);
-        *reinterpret_cast<v2u *>(&sm.t[buf][strip][8 * c8 + c][4 * r4]) = (v2u){lo, hi};
-      }
+    for (int i = 0; i < HTM; ++i) {
+      const int c = (64 * wr + 16 * i) / 8 + (q >> 1);
+      offa[i] = (uint32_t)((8 * g + jt) * HB * 2 + ((c ^ sw) * 16) + (q & 1) * 8);
+    }
+#pragma unroll
+    for (int j = 0; j < HTN; ++j) {
+      const int c = (32 * wc + 16 * j) / 8 + (q >> 1);
+      offb[j] = (uint32_t)((8 * g + jt) * HB * 2 + ((c ^ sw) * 16) + (q & 1) * 8);
+    }
+    auto rd = [&](int buf, int st, uint32_t off) __attribute__((always_inline)) -> v4s {
+      const char *p = reinterpret_cast<const char *>(&sm.t[buf][st][0][0]) + off;
+      return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s *)p);
     };
-    // (a diagonal block loads its one strip twice: branch-free loads keep
-    // the compiler's wait counting exact, so every load stays in flight)
     auto compute = [&](int buf) __attribute__((always_inline)) {
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
+        constexpr uint32_t kRow4 = 4 * HB * 2;               // four token rows
+        const uint32_t kofs = (uint32_t)kk * 32 * HB * 2;   // the k-step's 32 token rows
         v8bf av[HTM], bv[HTN];
-        const int tk = 32 * kk + 8 * (lane >> 4);
 #pragma unroll
-        for (int i = 0; i < HTM; ++i)
-          av[i] = *reinterpret_cast<const v8bf *>(&sm.t[buf][0][64 * wr + 16 * i + (lane & 15)][tk]);
+        for (int i = 0; i < HTM; ++i) {
+          const v4s lo = rd(buf, 0, offa[i] + kofs), hi = rd(buf, 0, offa[i] + kofs + kRow4);
+          av[i] = __builtin_bit_cast(v8bf, (v8s){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
+        }
 #pragma unroll
-        for (int j = 0; j < HTN; ++j)
-          bv[j] = *reinterpret_cast<const v8bf *>(&sm.t[buf][1][32 * wc + 16 * j + (lane & 15)][tk]);
+        for (int j = 0; j < HTN; ++j) {
+          const v4s lo = rd(buf, 1, offb[j] + kofs), hi = rd(buf, 1, offb[j] + kofs + kRow4);
+          bv[j] = __builtin_bit_cast(v8bf, (v8s){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
+        }
 #pragma unroll
         for (int i = 0; i < HTM; ++i)
 #pragma unroll
@@ -182,23 +201,15 @@ __global__ __launch_bounds__(HNT, 2) void k_hessian(HessArgs a) {
           }
       }
     };
-    if (s0 < s1) {
-      load(s0, int_c<0>{});
-      load(s0 + 1, int_c<1>{});
-      store(int_c<0>{}, 0);
-    }
-    __syncthreads();
-    for (int s = s0; s < s1; s += 2) {
-      load(s + 2, int_c<0>{});
-      compute(0);
-      if (s + 1 < s1) store(int_c<1>{}, 1);
-      __syncthreads();
-      if (s + 1 < s1) {
-        load(s + 3, int_c<1>{});
-        compute(1);
-        if (s + 2 < s1) store(int_c<0>{}, 0);
-        __syncthreads();
-      }
+    // one stage ahead in the other buffer; stage_barrier waits for this
+    // wave's loads and LDS reads, then the workgroup
+    if (s0 < s1) issue(s0, 0);
+    stage_barrier();
+    for (int s = s0; s < s1; ++s) {
+      const int buf = (s - s0) & 1;
+      if (s + 1 < s1) issue(s + 1, buf ^ 1);
+      compute(buf);
+      stage_barrier();
     }
   }
 
