@@ -247,23 +247,28 @@ def test_ragged_shapes_match_oracle(oracle, M, K, N, r, batch):
         assert np.array_equal(got, oracle.group_partials(q, lay["qw"][0]))
 
 
-@pytest.mark.parametrize("M,K,N,r", [
+@pytest.mark.parametrize("M,K,N,r,group", [
     # more than a round of workgroups (two per CU): 17 x 33 = 561 tiles,
     # the last column tile 4 columns wide; ragged rows
-    (2100, 256, 4100, 4),
-    (2100, 192, 4100, 0),     # rank 0, a pad group
-    (2100, 256, 4600, 8),     # 612 tiles, the last one 120 columns wide; rank 8
-    (2100, 128, 3000, 4),     # 408 tiles: one round
+    (2100, 256, 4100, 4, 64),
+    (2100, 192, 4100, 0, 64),     # rank 0, a pad group
+    (2100, 256, 4600, 8, 64),     # 612 tiles, the last one 120 columns wide; rank 8
+    (2100, 128, 3000, 4, 64),     # 408 tiles: one round
+    (4100, 768, 8200, 4, 64),     # 2145 tiles: about four rounds, 6 stages
+    (1100, 1024, 8200, 16, 64),   # rank 16 (one workgroup per CU): 585 tiles, 8 stages
+    (1000, 512, 8300, 32, 64),    # rank 32: 520 tiles over 256 workgroups
+    (2100, 512, 4100, 4, 128),    # group 128: 561 tiles, 4 stages
+    (2100, 640, 4100, 4, 64),     # an odd stage count (5)
 ])
-def test_many_tiles_ragged_full_output(oracle, M, K, N, r):
-    lay = make_random_layer(M + N + r, M, K, N, r=r, outlier_channels=2)
+def test_many_tiles_ragged_full_output(oracle, M, K, N, r, group):
+    lay = make_random_layer(M + N + r, M, K, N, r=r, outlier_channels=2, group=group)
     up = Uploaded(lay)
-    say(f"[many tiles] M={M} K={K} N={N} r={r}")
+    say(f"[many tiles] M={M} K={K} N={N} r={r} group={group}")
     check_linear_rows(oracle, up, np.arange(M), "tiled")
-    q, _ = oracle.quantize(lay["X"], lay["lam"])
+    q, _ = oracle.quantize(lay["X"], lay["lam"], group=group)
     m0, n0 = M - 150, N - 200
     got = up.partials(m0, 150, n0, 200, "tiled")
-    assert np.array_equal(got, oracle.group_partials(q, lay["qw"][0], m0, 150, n0, 200))
+    assert np.array_equal(got, oracle.group_partials(q, lay["qw"][0], m0, 150, n0, 200, group=group))
 
 
 def test_zero_groups_subnormal_and_saturated_scales(oracle):
