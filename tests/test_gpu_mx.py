@@ -120,6 +120,22 @@ def test_mx_matches_oracle(M, K, N, r):
     run_case(make_random_layer(700 + M, M, K, N, r=r, outlier_channels=3))
 
 
+@pytest.mark.parametrize("K,r", [
+    (1536, 4),    # 12 k-steps: three whole groups of four
+    (1152, 4),    # 9: one k-step past the last group
+    (1280, 0),    # 10: two past it, rank 0
+    (1408, 2),    # 11: three past it, rank 2
+])
+def test_mx_wide_tiles_sampled_rows(K, r):
+    # 2100 x 4100 at rank <= 4 runs the 128 x 256 workgroups (17 x 17 of
+    # them, the last row and column tiles ragged); sampled rows cover every
+    # column
+    M, N = 2100, 4100
+    rows = np.array(sorted(set([0, 127, 128, M - 1]) |
+                           set(np.random.default_rng(K).choice(M, 40, replace=False).tolist())))
+    run_case(make_random_layer(900 + K + r, M, K, N, r=r, outlier_channels=3), rows)
+
+
 def test_mx_pixart_full_size_sampled_rows():
     lay = make_layer("pixart_up")
     rows = np.array(sorted(set([0, 4095]) | set(np.random.default_rng(5).choice(4096, 30, replace=False).tolist())))

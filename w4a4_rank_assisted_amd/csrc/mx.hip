@@ -22,12 +22,16 @@
 // holds 1/lambda, the activation blob, its scales and U.
 #include "hsq_internal.h"
 
+#include <type_traits>
+
 namespace hsq {
 
 namespace {
 
 
 typedef int v8i __attribute__((ext_vector_type(8)));
+
+constexpr int kMxCUs = 256;   // compute units of the MI355X
 
 // e8m0 byte of a block's absmax: floor(log2 amax) is the fp32 exponent
 // field minus 127 for a normal amax; a subnormal amax gives byte 0 (clamp)
@@ -381,13 +385,246 @@ __global__ __launch_bounds__(512, 2) void k_mx_gemm(MxArgs a) {
   }
 }
 
-// workgroup 128 x 128: 2 x 4 waves of 64 x 32, two workgroups per CU.
-// Measured with the register-staged loads of an earlier version against
-// 2 x 2 waves of 64 x 64 (248 VGPRs, two waves per SIMD): 13 % faster at
-// pixart size, 8 % on the FLUX and Qwen3 up layers; a 256 x 128 workgroup
-// ran at one wave per SIMD and was slower.
+// Wide wave tiles: workgroup 128 x 256 outputs, 2 x 4 waves of 64 x 64
+// (4 x 4 MFMA tiles).  Per k-step a wave reads 4 A and 4 B operand blocks
+// for 16 MFMAs: half an LDS read per MFMA, where 64 x 32 needs three
+// quarters.  A stage is one k-step: wave w moves A tile w and B tiles w and
+// w + 8 (three 1 KB direct-to-LDS loads) into one of two stage buffers; the
+// e8m0 scales of a group of four k-steps (the same tiles) move one group
+// ahead.  The four k-steps of a group are unrolled, so the MFMA takes its
+// scale byte from the group's dword by its byte select (op_sel), with no
+// extraction.  Epilogue operands load with the first stage.
+template <int RPT, int GROUPM = 8>
+__global__ __launch_bounds__(512, 4) void k_mx_gemm_w(MxArgs a) {
+  constexpr int TMW = 4, TNW = 4, WGM = 2, WGN = 4, NTHR = 64 * WGM * WGN;
+  constexpr int AT = TMW * WGM, BT = TNW * WGN;           // 8 A tiles, 16 B tiles
+  static_assert(AT == NTHR / 64 && BT == 2 * AT, "wave w moves A tile w and B tiles w, w + AT");
+  constexpr int BMR = AT * 16, BNC = BT * 16;             // 128 rows, 256 columns
+  struct Ops {
+    uint8_t a[AT][64][16];
+    uint8_t b[BT][64][16];
+  };
+  __shared__ alignas(16) Ops ops[2];
+  __shared__ uint32_t ssc[2][(AT + BT) * 64];             // [group parity][A tiles, then B tiles][lane]
+  constexpr int RE = RPT > 0 ? RPT : 1;
+  __shared__ float eu[RE * BMR], el2[RE * BNC], eb[BNC];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / WGN, wn = wave % WGN;
+  const int nblk = (a.N + BNC - 1) / BNC, mblk = (a.Mpad / 16 + AT - 1) / AT;
+  int mb, nb;
+  xcd_tile_of(blockIdx.x, nblk, mblk, GROUPM, mb, nb);
+  const int mt0 = mb * AT, nt0 = nb * BT;
+  const int MT = a.Mpad / 16, NT = (a.N + 15) / 16;
+  const int KS = a.KS, KS4 = a.KS4;
+  // tiles past the matrix reload the last one (their outputs are not stored)
+  const int ta = min(mt0 + wave, MT - 1);
+  const int tb0 = min(nt0 + wave, NT - 1), tb1 = min(nt0 + AT + wave, NT - 1);
+  const v4u rq = raw_rsrc(a.qa, (uint32_t)MT * KS * 1024), rw = raw_rsrc(a.wq, (uint32_t)NT * KS * 1024);
+  const v4u rsa = raw_rsrc(a.sa, (uint32_t)MT * KS4 * 256), rsb = raw_rsrc(a.ws, (uint32_t)NT * KS4 * 256);
+  const uint32_t vo16 = (uint32_t)lane * 16, vo4 = (uint32_t)lane * 4;
+
+  auto issue_stage = [&](int k, int buf) __attribute__((always_inline)) {
+    block_to_lds(rq, lds_addr(&ops[buf].a[wave][0][0]), vo16, (uint32_t)(ta * KS + k) * 1024u);
+    block_to_lds(rw, lds_addr(&ops[buf].b[wave][0][0]), vo16, (uint32_t)(tb0 * KS + k) * 1024u);
+    block_to_lds(rw, lds_addr(&ops[buf].b[AT + wave][0][0]), vo16, (uint32_t)(tb1 * KS + k) * 1024u);
+  };
+  auto issue_scales = [&](int g) __attribute__((always_inline)) {
+    uint32_t *dst = ssc[g & 1];
+    dword_to_lds(rsa, lds_addr(dst + wave * 64), vo4, (uint32_t)(ta * KS4 + g) * 256u);
+    dword_to_lds(rsb, lds_addr(dst + (AT + wave) * 64), vo4, (uint32_t)(tb0 * KS4 + g) * 256u);
+    dword_to_lds(rsb, lds_addr(dst + (2 * AT + wave) * 64), vo4, (uint32_t)(tb1 * KS4 + g) * 256u);
+  };
+  auto load_epilogue = [&]() __attribute__((always_inline)) {
+    for (int p = tid; p < RPT * BMR; p += NTHR) {
+      const int c = p / BMR, rr = p % BMR, m = mt0 * 16 + rr;
+      const int cc = min(c, a.r - 1), mm = min(m, a.Mpad - 1);
+      float us[kMaxUSlices];
+#pragma unroll
+      for (int sl = 0; sl < kMaxUSlices; ++sl)
+        us[sl] = a.U[((size_t)min(sl, a.u_slices - 1) * a.r + cc) * a.Mpad + mm];
+      float u = 0.0f;
+#pragma unroll
+      for (int sl = 0; sl < kMaxUSlices; ++sl)
+        if (sl < a.u_slices) u += us[sl];
+      for (int sl = kMaxUSlices; sl < a.u_slices; ++sl) u += a.U[((size_t)sl * a.r + cc) * a.Mpad + mm];
+      eu[c * BMR + rr] = (c < a.r && m < a.M) ? u : 0.0f;
+    }
+    for (int p = tid; p < RPT * BNC; p += NTHR) {
+      const int c = p / BNC, cc = p % BNC, n = nt0 * 16 + cc;
+      el2[c * BNC + cc] = (c < a.r && n < a.N) ? bf16_to_f32(a.L2[(size_t)c * a.N + n]) : 0.0f;
+    }
+    for (int p = tid; p < BNC; p += NTHR) {
+      const int n = nt0 * 16 + p;
+      eb[p] = (a.bias && n < a.N) ? bf16_to_f32(a.bias[n]) : 0.0f;
+    }
+  };
+
+  v4f acc[TMW][TNW];
+#pragma unroll
+  for (int i = 0; i < TMW; ++i)
+#pragma unroll
+    for (int j = 0; j < TNW; ++j) acc[i][j] = (v4f){0.f, 0.f, 0.f, 0.f};
+
+  issue_scales(0);
+  issue_stage(0, 0);
+  load_epilogue();
+  stage_barrier();
+
+  // one k-step: its operands are in stage buffer J & 1 (the group's first
+  // k-step is even), its scales in byte J of the group's dwords
+  auto kstep = [&](auto jc, const uint32_t (&scA)[TMW], const uint32_t (&scB)[TNW]) __attribute__((always_inline)) {
+    constexpr int J = decltype(jc)::value, BUF = J & 1;
+    v8i bv[TNW];
+#pragma unroll
+    for (int j = 0; j < TNW; ++j) {
+      const v4u v = *reinterpret_cast<const v4u *>(&ops[BUF].b[wn * TNW + j][lane][0]);
+      bv[j] = (v8i){(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int i = 0; i < TMW; ++i) {
+      const v4u v = *reinterpret_cast<const v4u *>(&ops[BUF].a[wm * TMW + i][lane][0]);
+      const v8i av = (v8i){(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
+#pragma unroll
+      for (int j = 0; j < TNW; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv[j], acc[i][j], 4, 4, J, (int)scA[i], J,
+                                                                     (int)scB[j]);
+    }
+    // the k-step's results pinned here: the next k-step's MFMAs cannot
+    // move above its barrier (interleaved k-steps keep twice the
+    // accumulators alive)
+#pragma unroll
+    for (int i = 0; i < TMW; ++i)
+#pragma unroll
+      for (int j = 0; j < TNW; ++j) asm volatile("" : "+v"(acc[i][j]));
+  };
+  // k-step t = 4 g + J: the next k-step's operands are issued first (into
+  // the other buffer); one barrier ends the k-step
+  auto step = [&](auto jc, int t, const uint32_t (&scA)[TMW], const uint32_t (&scB)[TNW])
+      __attribute__((always_inline)) {
+    constexpr int J = decltype(jc)::value;
+    if (t + 1 < KS) issue_stage(t + 1, (J & 1) ^ 1);
+    kstep(jc, scA, scB);
+    stage_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  // the group's scales arrived before the last barrier; the next group's go
+  // to the other scale buffer, whose last readers finished before the
+  // barrier of the previous group's first k-step
+  auto group_scales = [&](int g, uint32_t (&scA)[TMW], uint32_t (&scB)[TNW]) __attribute__((always_inline)) {
+    const uint32_t *sc = ssc[g & 1];
+#pragma unroll
+    for (int i = 0; i < TMW; ++i) scA[i] = sc[(wm * TMW + i) * 64 + lane];
+#pragma unroll
+    for (int j = 0; j < TNW; ++j) scB[j] = sc[(AT + wn * TNW + j) * 64 + lane];
+    if (g + 1 < KS4) issue_scales(g + 1);
+  };
+  const int G = KS / 4;                                  // whole groups of four k-steps
+  for (int g = 0; g < G; ++g) {
+    uint32_t scA[TMW], scB[TNW];
+    group_scales(g, scA, scB);
+    step(std::integral_constant<int, 0>{}, 4 * g, scA, scB);
+    step(std::integral_constant<int, 1>{}, 4 * g + 1, scA, scB);
+    step(std::integral_constant<int, 2>{}, 4 * g + 2, scA, scB);
+    step(std::integral_constant<int, 3>{}, 4 * g + 3, scA, scB);
+  }
+  if (const int rem = KS - 4 * G; rem > 0) {             // the last group's 1 .. 3 k-steps
+    uint32_t scA[TMW], scB[TNW];
+    group_scales(G, scA, scB);
+    step(std::integral_constant<int, 0>{}, 4 * G, scA, scB);
+    if (rem > 1) step(std::integral_constant<int, 1>{}, 4 * G + 1, scA, scB);
+    if (rem > 2) step(std::integral_constant<int, 2>{}, 4 * G + 2, scA, scB);
+  }
+
+  // epilogue: Y = acc + U L2 + bias; per row tile the wave's 16 x WCOL
+  // values go through a wave-private LDS region of the stage buffers and
+  // leave as 16-byte row-contiguous stores
+  constexpr int WCOL = TNW * 16;
+  static_assert(WGM * WGN * 16 * WCOL * 4 <= (int)sizeof(ops), "transpose region");
+  char *tbuf = reinterpret_cast<char *>(&ops[0]) + wave * (16 * WCOL * 4);
+  const int rowq = 4 * (lane >> 4), colq = lane & 15;
+  const int yb = a.y_bf16 ? 2 : 4, per16 = 16 / yb, cpr = WCOL / per16;
+  const bool vec_ok = (a.N % per16) == 0;
+  const int ncol0 = (nt0 + wn * TNW) * 16;
+#pragma unroll
+  for (int i = 0; i < TMW; ++i) {
+#pragma unroll
+    for (int j = 0; j < TNW; ++j) {
+      const int cc = (wn * TNW + j) * 16 + colq;
+#pragma unroll
+      for (int qq = 0; qq < 4; ++qq) {
+        const int rr = (wm * TMW + i) * 16 + rowq + qq;
+        float y = acc[i][j][qq];
+#pragma unroll
+        for (int c = 0; c < RPT; ++c) y = __builtin_fmaf(eu[c * BMR + rr], el2[c * BNC + cc], y);
+        y += eb[cc];
+        const int off = (rowq + qq) * WCOL + j * 16 + colq;
+        if (a.y_bf16)
+          reinterpret_cast<uint16_t *>(tbuf)[off] = f32_to_bf16(y);
+        else
+          reinterpret_cast<float *>(tbuf)[off] = y;
+      }
+    }
+    const int mrow0 = (mt0 + wm * TMW + i) * 16;
+    for (int k = lane; k < 16 * cpr; k += 64) {
+      const int row = k / cpr, ch = k % cpr;
+      const int m = mrow0 + row, n = ncol0 + ch * per16;
+      if (m >= a.M || n >= a.N) continue;
+      const v4u v = *reinterpret_cast<const v4u *>(tbuf + (row * WCOL + ch * per16) * yb);
+      char *dst = reinterpret_cast<char *>(a.Y) + ((size_t)m * a.N + n) * yb;
+      if (vec_ok && n + per16 <= a.N) {
+        *reinterpret_cast<v4u *>(dst) = v;
+      } else if (a.y_bf16) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          if (n + e < a.N) reinterpret_cast<uint16_t *>(dst)[e] = (uint16_t)(v[e >> 1] >> (16 * (e & 1)));
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (n + e < a.N) reinterpret_cast<uint32_t *>(dst)[e] = v[e];
+      }
+    }
+  }
+}
+
+// Workgroup shape.  128 x 128 (2 x 4 waves of 64 x 32) and, for rank up
+// to 4, 128 x 256 (2 x 4 waves of 64 x 64); two workgroups per CU either
+// way.  Measured with the register-staged loads of an earlier version
+// against 2 x 2 waves of 64 x 64 (248 VGPRs, two waves per SIMD): 13 %
+// faster at pixart size, 8 % on the FLUX and Qwen3 up layers; a 256 x 128
+// workgroup ran at one wave per SIMD and was slower.  The wide tile does a
+// k-step's MFMAs with a third fewer LDS operand reads, but has half as many
+// workgroups to spread over the CUs.  Model, in the time a CU running two
+// 128 x 128 workgroups takes per k-step: 2.0 per 128 x 128 tile pair-wise,
+// 1.4 for one alone on its CU, and 1.25 times faster per output for the wide
+// tile (3.2 and 2.24 per wide tile); workgroups fill the CUs in rounds of
+// two per CU, a last round of at most one per CU runs at the lone rate.
+// Fitted to FLUX.1 up and down, Qwen3 up and down at 256 and 2048 tokens,
+// SANA QKV and pixart, where it picks the faster shape on each; the wide
+// shape must win by 2 %.
+double mx_rounds_time(long long tiles, double pair, double alone) {
+  const long long slots = 2LL * kMxCUs, full = tiles / slots, rest = tiles % slots;
+  return (double)full * pair + (rest == 0 ? 0.0 : rest <= kMxCUs ? alone : pair);
+}
+
+bool mx_wide(int M, int N, int r) {
+  if (r > 4) return false;    // the wide kernel keeps its epilogue operands for rank <= 4 only
+  const long long mblk = ceil_div(M, 128);
+  const double narrow = mx_rounds_time(ceil_div(N, 128) * mblk, 2.0, 1.4);
+  const double wide = mx_rounds_time(ceil_div(N, 256) * mblk, 3.2, 2.24);
+  return wide < 0.98 * narrow;
+}
+
 template <int RP>
 hipError_t launch_mx_gemm(const MxArgs &a, hipStream_t s) {
+  if constexpr (RP <= 4) {
+    if (mx_wide(a.M, a.N, a.r)) {
+      const int tiles = ceil_div(a.N, 256) * ceil_div(a.M, 128);
+      hipLaunchKernelGGL((k_mx_gemm_w<RP>), dim3((unsigned)tiles), dim3(512), 0, s, a);
+      return hipGetLastError();
+    }
+  }
   const int tiles = ceil_div(a.N, 128) * ceil_div(a.M, 128);
   hipLaunchKernelGGL((k_mx_gemm<RP>), dim3((unsigned)tiles), dim3(512), 0, s, a);
   return hipGetLastError();
