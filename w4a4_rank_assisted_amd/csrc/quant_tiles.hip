@@ -28,6 +28,8 @@
 // so both produce zero codes, scales and U without a branch.
 #include "hsq_internal.h"
 
+#include <type_traits>
+
 namespace hsq {
 
 namespace {
@@ -92,7 +94,7 @@ TilePlan tile_plan(int M, int K, int r, int batch, int group) {
 // code modes: rank pass only, symmetric codes, asymmetric codes
 constexpr int kNoCodes = 0, kSymCodes = 1, kAsymCodes = 2;
 
-template <int NR, int CM, int BPG>
+template <int NR, int CM, int BPG, bool ONE>
 __global__ __launch_bounds__(1024) void k_quant_tiles(QuantArgs a, int gpb) {
   // dynamic LDS: 1/lambda [gpb*BPG][4][kLamKq], L1 [gpb*BPG][4][kqs(NR)]
   // (per 64-block and channel block: 16 channels x NR columns); after the
@@ -139,9 +141,24 @@ __global__ __launch_bounds__(1024) void k_quant_tiles(QuantArgs a, int gpb) {
       x[2 * b + 1] = __builtin_amdgcn_raw_buffer_load_b128(rs_x, offx, bc * 128 + 16, 0);
     }
   };
-  int g = gs + wave;
+  // the wave's units are g0, g0 + W, ...; the first loads during the table
+  // staging.  ONE (at most one unit per wave): a wave past the slice loads
+  // with the out-of-range lane offset (zero, no memory traffic), and no
+  // further load follows.  Otherwise the next unit is in flight while one
+  // is processed.
+  const int g0 = gs + wave;
   v4u x[2 * BPG];
-  load_x(min(g, ge - 1), x);                  // in flight during the staging (unused past the slice)
+  if constexpr (ONE) {
+    const uint32_t off = g0 < ge ? offx : xbytes;
+#pragma unroll
+    for (int b = 0; b < BPG; ++b) {
+      const int bc = min(g0 * BPG + b, a.G - 1);
+      x[2 * b] = __builtin_amdgcn_raw_buffer_load_b128(rs_x, off, bc * 128, 0);
+      x[2 * b + 1] = __builtin_amdgcn_raw_buffer_load_b128(rs_x, off, bc * 128 + 16, 0);
+    }
+  } else {
+    load_x(min(g0, ge - 1), x);               // in flight during the staging (unused past the slice)
+  }
 
   // ---- slice tables: 1/lambda, 8 channels per item ----
   const int bs = gs * BPG;                    // first 64-block of the slice
@@ -195,11 +212,7 @@ __global__ __launch_bounds__(1024) void k_quant_tiles(QuantArgs a, int gpb) {
 #pragma unroll
   for (int j = 0; j < (NR > 0 ? NR : 1); ++j) u[j] = 0.0f;
 
-  for (; g < ge; g += W) {
-    // next unit of this wave in flight (past the slice: a clamped, unused
-    // load, so that the code stays straight-line and the waits exact)
-    v4u nx[2 * BPG];
-    load_x(min(g + W, ge - 1), nx);
+  auto unit = [&](int g, const v4u (&x)[2 * BPG]) __attribute__((always_inline)) {
     const int gl = g - gs;
     float xh[16 * BPG];
 #pragma unroll
@@ -308,8 +321,19 @@ __global__ __launch_bounds__(1024) void k_quant_tiles(QuantArgs a, int gpb) {
           }
       }
     }
+  };
+  if constexpr (ONE) {
+    if (g0 < ge) unit(g0, x);
+  } else {
+    for (int g = g0; g < ge; g += W) {
+      // next unit of this wave in flight (past the slice: a clamped, unused
+      // load, so that the code stays straight-line and the waits exact)
+      v4u nx[2 * BPG];
+      load_x(min(g + W, ge - 1), nx);
+      unit(g, x);
 #pragma unroll
-    for (int t = 0; t < 2 * BPG; ++t) x[t] = nx[t];
+      for (int t = 0; t < 2 * BPG; ++t) x[t] = nx[t];
+    }
   }
 
   // ---- U of the slice: shares of (wave, channel block) summed in that
@@ -344,12 +368,22 @@ hipError_t launch_pass(const QuantArgs &a, const TilePlan &p, int cm, hipStream_
   const dim3 grid((unsigned)(a.Mpad / kTile + px), (unsigned)p.slices);
   const dim3 block((unsigned)(64 * p.waves));
   const size_t lds = plan_lds(p.gpb, BPG, NR, p.waves);
-  if (cm == kSymCodes)
-    hipLaunchKernelGGL((k_quant_tiles<NR, kSymCodes, BPG>), grid, block, lds, s, a, p.gpb);
-  else if (cm == kAsymCodes)
-    hipLaunchKernelGGL((k_quant_tiles<NR, kAsymCodes, BPG>), grid, block, lds, s, a, p.gpb);
-  else
-    hipLaunchKernelGGL((k_quant_tiles<NR, kNoCodes, BPG>), grid, block, lds, s, a, p.gpb);
+  // at most one unit per wave (the plan's one-unit-per-wave widths): no
+  // look-ahead load.  Measured: Qwen3 down at 16 tokens 5.8 -> 5.5 us, pixart
+  // 8.9 -> 8.5 us per pass.  Loading every unit of a wave before the staging
+  // instead of one ahead was slower on the large layers (FLUX.1 MLP 27.1 ->
+  // 30.3 us per pass, SANA QKV 17.2 -> 18.6 us) and is not used.
+  auto go = [&](auto onec) {
+    constexpr bool O = decltype(onec)::value;
+    if (cm == kSymCodes)
+      hipLaunchKernelGGL((k_quant_tiles<NR, kSymCodes, BPG, O>), grid, block, lds, s, a, p.gpb);
+    else if (cm == kAsymCodes)
+      hipLaunchKernelGGL((k_quant_tiles<NR, kAsymCodes, BPG, O>), grid, block, lds, s, a, p.gpb);
+    else
+      hipLaunchKernelGGL((k_quant_tiles<NR, kNoCodes, BPG, O>), grid, block, lds, s, a, p.gpb);
+  };
+  if (p.gpb <= p.waves) go(std::true_type{});
+  else go(std::false_type{});
   return hipGetLastError();
 }
 
