@@ -125,6 +125,7 @@ def test_mx_matches_oracle(M, K, N, r):
     (1152, 4),    # 9: one k-step past the last group
     (1280, 0),    # 10: two past it, rank 0
     (1408, 2),    # 11: three past it, rank 2
+    (256, 4),     # 2: no whole group at all
 ])
 def test_mx_wide_tiles_sampled_rows(K, r):
     # 2100 x 4100 at rank <= 4 runs the 128 x 256 workgroups (17 x 17 of
