@@ -225,6 +225,8 @@ def test_full_size_outputs_sampled_rows(oracle, name, M):
 # ------------------------------------------------------------- edge cases
 @pytest.mark.parametrize("M,K,N,r,batch", [
     (1, 64, 16, 4, 1),        # one token, one group, one tile
+    (3, 128, 1, 4, 1),        # one output column
+    (65, 192, 2, 4, 2),       # two output columns, one row past the skinny limit, two projections
     (5, 192, 33, 0, 1),       # rank 0, odd group count, ragged N
     (70, 640, 300, 4, 1),     # ragged M and N over several tiles
     (200, 384, 129, 32, 2),   # largest rank, two projections
