@@ -886,11 +886,13 @@ def linear_main(args):
         sets = [dict(X=X0.clone(), packed=packed0.clone(), sw=sw0.clone(),
                      Y=torch.empty((B, M, N), dtype=ydt, device=dev)) for _ in range(nsets)]
         del X0, sw0, packed0
+        # the stage calls name their contraction kernel; the layer call takes
+        # the library's own choice unless one is forced
         kernel = args.kernel
         if kernel == "auto":
             kernel = "skinny" if M <= 64 else "tiled"
         layers.append(dict(
-            spec=spec, lay=lay, sets=sets, nsets=nsets, kernel=kernel,
+            spec=spec, lay=lay, sets=sets, nsets=nsets, kernel=kernel, call_kernel=args.kernel,
             lam=d16(lay["lam"]), L1=d16(lay["L1"]) if r else None, L2=d16(lay["L2"]) if r else None,
             bias=d16(lay["bias"]),
             ws=torch.empty(hsq.workspace_bytes(M, K, N, r, B, args.group), dtype=torch.uint8, device=dev)))
@@ -915,7 +917,7 @@ def linear_main(args):
             sp, st = L["spec"], L["sets"][i % L["nsets"]]
             hsq.w4a4_lowrank_linear(st["X"], L["lam"], st["packed"], st["sw"], L["L1"], L["L2"], L["bias"],
                                     N=sp.N, batch=sp.batch, y_dtype=args.y_dtype, out=st["Y"], workspace=L["ws"],
-                                    kernel=L["kernel"], group=args.group, act_quant=args.act_quant)
+                                    kernel=L["call_kernel"], group=args.group, act_quant=args.act_quant)
 
     for i in range(args.warmup):
         step(i)

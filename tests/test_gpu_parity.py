@@ -249,6 +249,38 @@ def test_ragged_shapes_match_oracle(oracle, M, K, N, r, batch):
         assert np.array_equal(got, oracle.group_partials(q, lay["qw"][0]))
 
 
+@pytest.mark.parametrize("M,K,N,r,batch", [
+    (1, 64, 16, 4, 1),        # one token, one block (a pad block in the pair)
+    (5, 192, 33, 0, 1),       # rank 0, odd block count, ragged N
+    (16, 4096, 300, 4, 1),    # five K-slices, ragged N
+    (11, 1152, 1, 4, 1),      # one output column
+    (16, 2240, 200, 4, 3),    # three projections, a pad block
+    (9, 20480, 45, 4, 1),     # long K: many slices
+    (16, 512, 256, 8, 1),     # rank 8
+])
+def test_few_token_layer_default_path(oracle, M, K, N, r, batch):
+    # the layer call with the library's own kernel choice at 16 tokens or
+    # fewer: every row against the oracle, the workspace's codes and scales
+    # bit for bit, and two calls bit for bit
+    lay = make_random_layer(M * 17 + N + r, M, K, N, r=r, batch=batch, outlier_channels=2)
+    up = Uploaded(lay)
+    say(f"[few tokens] M={M} K={K} N={N} r={r} batch={batch}")
+    check_linear_rows(oracle, up, np.arange(M), "auto")
+    ws = torch.empty(hsq.workspace_bytes(M, K, N, r, batch), dtype=torch.uint8, device=DEV).fill_(0x5A)
+    outs = []
+    for _ in range(2):
+        out = torch.empty((batch, M, N), dtype=torch.float32, device=DEV)
+        hsq.w4a4_lowrank_linear(up.X, up.lam, up.packed, up.sw, up.L1, up.L2, up.bias, N=N, batch=batch,
+                                y_dtype="f32", out=out, workspace=ws)
+        torch.cuda.synchronize()
+        outs.append(out.view(torch.int32).cpu().numpy())
+    assert np.array_equal(outs[0], outs[1])
+    codes, scales = _workspace_codes_scales(up, ws)
+    q_ref, s_ref = oracle.quantize(lay["X"], lay["lam"])
+    assert np.array_equal(scales, s_ref)
+    assert np.array_equal(codes, q_ref)
+
+
 @pytest.mark.parametrize("M,K,N,r,group", [
     # more than a round of workgroups (two per CU): 17 x 33 = 561 tiles,
     # the last column tile 4 columns wide; ragged rows
