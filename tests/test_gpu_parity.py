@@ -437,6 +437,43 @@ def test_linear_workspace_codes_scales_bit_exact(oracle, name, M):
     assert np.array_equal(codes2, q_ref)
 
 
+@pytest.mark.parametrize("name,M", [("tiny", None), ("pixart_up", None), ("sana_qkv", None),
+                                    ("flux_up", None), ("flux_down", None),
+                                    ("qwen3_up", 16), ("qwen3_down", 16), ("qwen3_up", 256),
+                                    ("qwen3_down", 256), ("qwen3_up", 2048), ("qwen3_down", 2048)])
+def test_linear_lowrank_down_through_identity_l2(oracle, name, M):
+    # U = xh * L1 as the fused layer's own quantization pass forms it (its
+    # K-slice partials, summed by the contraction in slice order), on every
+    # row: the layer's X, lambda and L1 with a zero residual, zero bias and
+    # L2 = [I_r | 0] over 128 output columns, so the fp32 output's first r
+    # columns are U exactly (P = 0 adds exactly 0; the epilogue multiplies by
+    # 1 and adds 0).  The pass's plan does not depend on N, so this is the
+    # launch the full layer runs.  Bar: relative Frobenius <= 1e-5 against
+    # the oracle's fp64 U.
+    up = uploaded(name, M)
+    say(f"[U via identity L2] {name} M={up.M} K={up.K} batch={up.B}")
+    B, K, r, N = up.B, up.K, up.r, 128
+    G = K // up.group
+    blobs = [hsq.pack_weights(torch.zeros((K, N), dtype=torch.int8, device=DEV))[0] for _ in range(B)]
+    packed = torch.cat(blobs)
+    sw = torch.full((B, G, N), 0x3C00, dtype=torch.int16, device=DEV)            # fp16 1.0
+    l2 = np.zeros((B, r, N), np.uint16)
+    for j in range(r):
+        l2[:, j, j] = 0x3F80                                                         # bf16 1.0
+    L2 = dev16(l2)
+    bias = torch.zeros((B, N), dtype=torch.int16, device=DEV)
+    Y = hsq.w4a4_lowrank_linear(up.X, up.lam, packed, sw, up.L1, L2, bias, N=N, batch=B, y_dtype="f32")
+    torch.cuda.synchronize()
+    Y = Y.cpu().numpy()
+    _, _, xh = oracle.quantize(up.lay["X"], up.lay["lam"], want_xh=True)
+    for b in range(B):
+        U_ref = oracle.lowrank_down(xh, up.lay["L1"][b])
+        e = rel(Y[b][:, :r].astype(np.float64), U_ref)
+        say(f"    proj {b}: U rel {e:.3e}")
+        assert e <= 1e-5
+        assert not Y[b][:, r:].any()
+
+
 @pytest.mark.parametrize("name,M", [("qwen3_up", 16), ("qwen3_down", 256), ("qwen3_up", 2048)])
 def test_group128_codes_scales_bit_exact(oracle, name, M):
     up = uploaded(name, M, 128)
