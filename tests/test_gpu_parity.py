@@ -437,11 +437,13 @@ def test_linear_workspace_codes_scales_bit_exact(oracle, name, M):
     assert np.array_equal(codes2, q_ref)
 
 
-@pytest.mark.parametrize("name,M", [("tiny", None), ("pixart_up", None), ("sana_qkv", None),
-                                    ("flux_up", None), ("flux_down", None),
-                                    ("qwen3_up", 16), ("qwen3_down", 16), ("qwen3_up", 256),
-                                    ("qwen3_down", 256), ("qwen3_up", 2048), ("qwen3_down", 2048)])
-def test_linear_lowrank_down_through_identity_l2(oracle, name, M):
+@pytest.mark.parametrize("name,M,group", [("tiny", None, 64), ("pixart_up", None, 64), ("sana_qkv", None, 64),
+                                          ("flux_up", None, 64), ("flux_down", None, 64),
+                                          ("qwen3_up", 16, 64), ("qwen3_down", 16, 64), ("qwen3_up", 256, 64),
+                                          ("qwen3_down", 256, 64), ("qwen3_up", 2048, 64),
+                                          ("qwen3_down", 2048, 64), ("qwen3_up", 16, 128),
+                                          ("qwen3_down", 256, 128), ("qwen3_up", 2048, 128)])
+def test_linear_lowrank_down_through_identity_l2(oracle, name, M, group):
     # U = xh * L1 as the fused layer's own quantization pass forms it (its
     # K-slice partials, summed by the contraction in slice order), on every
     # row: the layer's X, lambda and L1 with a zero residual, zero bias and
@@ -450,8 +452,8 @@ def test_linear_lowrank_down_through_identity_l2(oracle, name, M):
     # 1 and adds 0).  The pass's plan does not depend on N, so this is the
     # launch the full layer runs.  Bar: relative Frobenius <= 1e-5 against
     # the oracle's fp64 U.
-    up = uploaded(name, M)
-    say(f"[U via identity L2] {name} M={up.M} K={up.K} batch={up.B}")
+    up = uploaded(name, M, group if group != 64 else None)
+    say(f"[U via identity L2] {name} M={up.M} K={up.K} batch={up.B} group={up.group}")
     B, K, r, N = up.B, up.K, up.r, 128
     G = K // up.group
     blobs = [hsq.pack_weights(torch.zeros((K, N), dtype=torch.int8, device=DEV))[0] for _ in range(B)]
@@ -462,7 +464,8 @@ def test_linear_lowrank_down_through_identity_l2(oracle, name, M):
         l2[:, j, j] = 0x3F80                                                         # bf16 1.0
     L2 = dev16(l2)
     bias = torch.zeros((B, N), dtype=torch.int16, device=DEV)
-    Y = hsq.w4a4_lowrank_linear(up.X, up.lam, packed, sw, up.L1, L2, bias, N=N, batch=B, y_dtype="f32")
+    Y = hsq.w4a4_lowrank_linear(up.X, up.lam, packed, sw, up.L1, L2, bias, N=N, batch=B, y_dtype="f32",
+                                group=up.group)
     torch.cuda.synchronize()
     Y = Y.cpu().numpy()
     _, _, xh = oracle.quantize(up.lay["X"], up.lay["lam"], want_xh=True)
