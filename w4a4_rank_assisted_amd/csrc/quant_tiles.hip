@@ -133,10 +133,12 @@ __global__ __launch_bounds__(1024) void k_quant_tiles(QuantArgs a, int gpb) {
   const __amdgpu_buffer_rsrc_t rs_x = buffer_rsrc(a.X, xbytes);
   const uint32_t offx = m < a.M ? ((uint32_t)m * (uint32_t)a.K + 16u * kq) * 2u : xbytes;
   // the unit's BPG blocks, two 16-byte loads each
+  // (the block index is uniform; readfirstlane lets the compiler see it, or
+  // it wraps each load in a loop over the lanes' values)
   auto load_x = [&](int g, v4u (&x)[2 * BPG]) __attribute__((always_inline)) {
 #pragma unroll
     for (int b = 0; b < BPG; ++b) {
-      const int bc = min(g * BPG + b, a.G - 1);
+      const int bc = __builtin_amdgcn_readfirstlane(min(g * BPG + b, a.G - 1));
       x[2 * b] = __builtin_amdgcn_raw_buffer_load_b128(rs_x, offx, bc * 128, 0);
       x[2 * b + 1] = __builtin_amdgcn_raw_buffer_load_b128(rs_x, offx, bc * 128 + 16, 0);
     }
